@@ -1,0 +1,295 @@
+"""Checks that pin the fp64 oracle to facts other than itself.
+
+Each check raises AssertionError on failure.  They are collected as tests in
+test_oracle_pins.py, and test_oracle_mutations.py plants plausible mistakes in
+the oracle (on the CPU) to show that at least one check catches each.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from oracle import moe_zc as om
+from oracle import bruteforce as bf
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def random_layer(T, d, I, N, Z, seed=0, bias_scale=0.05, residual=True):
+    """Small random fp64 layer (test-local; not a product workload)."""
+    r = _rng(seed)
+    E = N + Z
+    x = r.standard_normal((T, d))
+    wr = r.standard_normal((E, d)) / math.sqrt(d)
+    b = r.uniform(-bias_scale, bias_scale, E).astype(np.float32)
+    wg = r.standard_normal((N, I, d)) / math.sqrt(d)
+    wu = r.standard_normal((N, I, d)) / math.sqrt(d)
+    wd = r.standard_normal((N, d, I)) / math.sqrt(I)
+    res = r.standard_normal((T, d)) if residual else None
+    return dict(x=x, w_router=wr, bias=b, w_gate=wg, w_up=wu, w_down=wd,
+                residual=res)
+
+
+# ---------------------------------------------------------------- golden --
+def check_hand_example():
+    with open(os.path.join(GOLDEN, "hand_example.json")) as f:
+        G = json.load(f)
+    N, Z = G["shapes"]["N"], G["shapes"]["Z"]
+    x = np.array(G["x"])
+    wg, wu, wd = (np.array(G[k]) for k in ("w_gate", "w_up", "w_down"))
+    for case in G["cases"]:
+        # the router weights reproduce the case's logits for x = [1, 2]
+        wr = np.zeros((N + Z, 2))
+        wr[:, 0] = case["logits"]
+        l64 = om.router_logits(x, wr)
+        assert np.allclose(l64[0], case["logits"], rtol=0, atol=1e-15), case["name"]
+        out = om.forward(x, wr, np.array(case["bias"], np.float32), wg, wu, wd,
+                         N, Z, case["K"])
+        assert out["idx"][0].tolist() == case["idx"], (case["name"], out["idx"])
+        assert np.allclose(out["gate"][0], case["gate"], rtol=0, atol=1e-7), case["name"]
+        assert np.allclose(out["y"][0], case["y"], rtol=0, atol=case["tol"]), \
+            (case["name"], out["y"][0], case["y"])
+
+
+def check_pid_golden():
+    with open(os.path.join(GOLDEN, "pid_example.json")) as f:
+        G = json.load(f)
+    g = G["gains"]
+    tgt = np.array(G["target"])
+    b = np.array(G["bias0"])
+    e1 = np.zeros_like(b)
+    e2 = np.zeros_like(b)
+    for st in G["steps"]:
+        b, e1, e2 = om.pid_step(st["loads"], tgt, b, e1, e2, g["kp"], g["ki"], g["kd"])
+        assert np.array_equal(e1, np.array(st["e"])), (e1, st["e"])
+        assert np.array_equal(b, np.array(st["bias"])), (b, st["bias"])
+
+
+# ------------------------------------------------------------ brute force --
+def check_bruteforce_tiny(T=16, d=24, I=20, N=5, Z=3, K=3, seed=1):
+    L = random_layer(T, d, I, N, Z, seed=seed, bias_scale=0.1)
+    ref = bf.forward(L["x"], L["w_router"], L["bias"], L["w_gate"], L["w_up"],
+                     L["w_down"], N, Z, K, L["residual"])
+    out = om.forward(L["x"], L["w_router"], L["bias"], L["w_gate"], L["w_up"],
+                     L["w_down"], N, Z, K, L["residual"], logits32=ref["logits32"])
+    l_bf = np.array(bf.logits(L["x"], L["w_router"]))
+    assert np.allclose(out["logits64"], l_bf, rtol=0, atol=1e-13)
+    assert np.array_equal(out["idx"], ref["idx"]), "top-K differs from subset enumeration"
+    assert np.array_equal(out["gate"], ref["gate"])
+    assert np.array_equal(out["loads"], ref["loads"])
+    assert np.array_equal(out["perm"], ref["perm"])
+    assert np.array_equal(out["pos"], ref["pos"])
+    err = np.abs(out["y"] - ref["y"]).max()
+    assert err <= 1e-12 * max(1.0, np.abs(ref["y"]).max()), err
+
+
+def check_topk_ties_enumeration(seed=3, T=200, E=8, K=3):
+    r = _rng(seed)
+    keys = r.choice(np.array([0.1, 0.2, 0.3, 0.2], np.float32), size=(T, E))
+    idx = om.select_topk(keys, K)
+    for t in range(T):
+        assert idx[t].tolist() == bf.topk_by_enumeration(keys[t].tolist(), K), t
+
+
+def check_softmax_bruteforce(seed=4, T=20, E=12):
+    l32 = (_rng(seed).standard_normal((T, E)) * 3).astype(np.float32)
+    p = om.softmax_fp64(l32)
+    for t in range(T):
+        ref = bf.softmax_row(l32[t])
+        assert np.allclose(p[t], ref, rtol=1e-14, atol=0)
+    assert np.allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------- special cases -------
+def _dense_swiglu_torch(x, wg, wu, wd):
+    x, wg, wu, wd = (torch.as_tensor(np.asarray(a), dtype=torch.float64)
+                     for a in (x, wg, wu, wd))
+    return ((F.silu(x @ wg.T) * (x @ wu.T)) @ wd.T).numpy()
+
+
+def check_single_forced_ffn(T=12, d=16, seed=5):
+    # N=1, Z=0, K=1: the only expert has p = 1, so the layer is a dense SwiGLU
+    # FFN plus the residual.  d == I so that a transposed operand cannot hide.
+    L = random_layer(T, d, d, 1, 0, seed=seed)
+    out = om.forward(L["x"], L["w_router"], L["bias"], L["w_gate"], L["w_up"],
+                     L["w_down"], 1, 0, 1, L["residual"])
+    ref = _dense_swiglu_torch(L["x"], L["w_gate"][0], L["w_up"][0], L["w_down"][0]) + L["residual"]
+    assert np.allclose(out["gate"], 1.0, rtol=0, atol=0)
+    assert np.allclose(out["y"], ref, rtol=1e-12, atol=1e-12)
+    # A +10 bias forces expert e into slot 0 with gate p_e (bias is not a gate).
+    N, Z = 4, 2
+    L = random_layer(T, d, d, N, Z, seed=seed + 1, residual=False)
+    e = 2
+    b = np.zeros(N + Z, np.float32)
+    b[e] = 10.0
+    out = om.forward(L["x"], L["w_router"], b, L["w_gate"], L["w_up"], L["w_down"], N, Z, 1)
+    p = torch.softmax(torch.as_tensor(out["logits64"]).float().double(), dim=1).numpy()
+    assert (out["idx"][:, 0] == e).all()
+    assert np.allclose(out["gate"][:, 0], p[:, e], rtol=1e-6, atol=0)
+    ref = p[:, e:e + 1] * _dense_swiglu_torch(L["x"], L["w_gate"][e], L["w_up"][e], L["w_down"][e])
+    assert np.allclose(out["y"], ref, rtol=1e-6, atol=1e-9)
+
+
+def check_all_identity(T=32, d=16, I=8, N=6, Z=5, K=3, seed=6):
+    # every FFN expert biased by -10: all K slots go to identity experts and
+    # y = (sum of their gates) x + r, gates = the K largest identity-expert
+    # probabilities of a library softmax.
+    L = random_layer(T, d, I, N, Z, seed=seed)
+    b = np.zeros(N + Z, np.float32)
+    b[:N] = -10.0
+    out = om.forward(L["x"], L["w_router"], b, L["w_gate"], L["w_up"], L["w_down"],
+                     N, Z, K, L["residual"])
+    p = torch.softmax(torch.as_tensor(out["logits64"].astype(np.float32)).double(), dim=1)
+    top = torch.topk(p[:, N:], K, dim=1).values.sum(dim=1).numpy()
+    assert (out["idx"] >= N).all()
+    ref = top[:, None] * L["x"] + L["residual"]
+    assert np.allclose(out["y"], ref, rtol=1e-6, atol=1e-7)
+    assert out["n_rows"] == 0
+    # N = 0 (identity experts only) gives the same closed form
+    out0 = om.forward(L["x"], L["w_router"][N:], np.zeros(Z, np.float32),
+                      L["w_gate"][:0], L["w_up"][:0], L["w_down"][:0], 0, Z, K, None)
+    p0 = torch.softmax(torch.as_tensor(out0["logits64"].astype(np.float32)).double(), dim=1)
+    ref0 = torch.topk(p0, K, dim=1).values.sum(dim=1).numpy()[:, None] * L["x"]
+    assert np.allclose(out0["y"], ref0, rtol=1e-6, atol=1e-7)
+
+
+def check_k_equals_e(T=24, d=16, I=8, N=5, Z=3, seed=7):
+    # K = E: every expert is chosen, so the output no longer depends on b:
+    # y = sum_{i<N} p_i FFN_i(x) + (sum_{i>=N} p_i) x + r
+    L = random_layer(T, d, I, N, Z, seed=seed)
+    E = N + Z
+    outs = []
+    for bseed in (0, 1):
+        b = _rng(100 + bseed).uniform(-0.3, 0.3, E).astype(np.float32)
+        outs.append(om.forward(L["x"], L["w_router"], b, L["w_gate"], L["w_up"],
+                               L["w_down"], N, Z, E, L["residual"]))
+    p = torch.softmax(torch.as_tensor(outs[0]["logits64"].astype(np.float32)).double(), dim=1).numpy()
+    ref = L["residual"] + p[:, N:].sum(axis=1, keepdims=True) * L["x"]
+    for i in range(N):
+        ref = ref + p[:, i:i + 1] * _dense_swiglu_torch(L["x"], L["w_gate"][i], L["w_up"][i], L["w_down"][i])
+    for o in outs:
+        assert np.allclose(o["y"], ref, rtol=1e-6, atol=1e-6)
+    assert np.allclose(outs[0]["y"], outs[1]["y"], rtol=0, atol=1e-12)
+
+
+def check_z_zero_textbook_moe(T=40, d=16, I=12, N=7, K=2, seed=8):
+    # Z = 0: a plain softmax top-K MoE whose gates are not renormalised,
+    # written with library routines (torch.softmax, torch.topk, F.silu).
+    L = random_layer(T, d, I, N, 0, seed=seed, bias_scale=0.0)
+    out = om.forward(L["x"], L["w_router"], np.zeros(N, np.float32), L["w_gate"],
+                     L["w_up"], L["w_down"], N, 0, K, None)
+    p = torch.softmax(torch.as_tensor(out["logits64"].astype(np.float32)).double(), dim=1)
+    val, ind = torch.topk(p, K, dim=1)
+    ref = np.zeros_like(L["x"])
+    for t in range(T):
+        for k in range(K):
+            e = int(ind[t, k])
+            ref[t] += float(val[t, k]) * _dense_swiglu_torch(
+                L["x"][t:t + 1], L["w_gate"][e], L["w_up"][e], L["w_down"][e])[0]
+    assert np.array_equal(np.sort(out["idx"], axis=1), np.sort(ind.numpy(), axis=1))
+    assert np.allclose(out["y"], ref, rtol=1e-6, atol=1e-7)
+
+
+# -------------------------------------------------------------- invariants --
+def check_permutation_invariants(T=300, E=20, N=13, K=4, seed=9):
+    l32 = _rng(seed).standard_normal((T, E)).astype(np.float32)
+    b = _rng(seed + 1).uniform(-0.05, 0.05, E).astype(np.float32)
+    rt = om.route(l32, b, K, N)
+    idx, perm, pos, loads, off = rt["idx"], rt["perm"], rt["pos"], rt["loads"], rt["offsets"]
+    assert loads.sum() == T * K
+    assert (np.diff(off) >= 0).all() and off[0] == 0 and off[N] == rt["n_rows"]
+    assert np.array_equal(np.diff(off), loads[:N])
+    # grouped order = stable sort of the FFN slots by expert (library sort)
+    tt, kk = np.nonzero(idx < N)                  # slots in token-major order
+    order = np.argsort(idx[tt, kk], kind="stable")
+    assert np.array_equal(perm, tt[order])
+    assert np.array_equal(pos[tt[order], kk[order]], np.arange(len(order)))
+    assert (pos[idx >= N] == -1).all()
+    # perm is a bijection onto the FFN slots; round trip is the identity
+    assert len(perm) == int((idx < N).sum())
+    rows = np.arange(T, dtype=np.float64)[perm][:, None] * np.ones((1, 3))
+    back = om.unpermute(rows, pos, idx, N)
+    ffn = idx < N
+    assert np.array_equal(back[ffn][:, 0], np.nonzero(ffn)[0].astype(np.float64))
+    # each expert appears at most once per token
+    for t in range(T):
+        assert len(set(idx[t].tolist())) == K
+
+
+def check_token_independence(T=48, d=16, I=8, N=6, Z=3, K=3, seed=10):
+    L = random_layer(T, d, I, N, Z, seed=seed)
+    full = om.forward(L["x"], L["w_router"], L["bias"], L["w_gate"], L["w_up"],
+                      L["w_down"], N, Z, K, L["residual"])
+    sub = np.array([3, 17, 5, 40])
+    part = om.forward(L["x"][sub], L["w_router"], L["bias"], L["w_gate"], L["w_up"],
+                      L["w_down"], N, Z, K, L["residual"][sub])
+    assert np.array_equal(part["idx"], full["idx"][sub])
+    assert np.allclose(part["y"], full["y"][sub], rtol=0, atol=1e-12)
+    assert np.allclose(full["p64"].sum(axis=1), 1.0, atol=1e-14)
+    assert (full["gate"].astype(np.float64).sum(axis=1) <= 1.0 + 1e-6).all()
+
+
+def check_ffn_count_hypergeometric(T=20000, N=512, Z=256, K=12, seed=11):
+    """With zero bias and iid logits the chosen set is a uniform K-subset, so
+    the FFN count per token is Hypergeometric(E, N, K)."""
+    from scipy.stats import hypergeom
+    E = N + Z
+    l32 = _rng(seed).standard_normal((T, E)).astype(np.float32)
+    rt = om.route(l32, np.zeros(E, np.float32), K, N)
+    c = om.ffn_count_per_token(rt["idx"], N)
+    mean = K * N / E
+    var = K * (N / E) * (Z / E) * (E - K) / (E - 1)
+    assert abs(c.mean() - mean) < 4 * math.sqrt(var / T), (c.mean(), mean)
+    assert abs(c.var() - var) < 0.05 * var, (c.var(), var)
+    pmf = hypergeom(E, N, K).pmf(np.arange(K + 1))
+    hist = np.bincount(c, minlength=K + 1) / T
+    assert np.abs(hist - pmf).max() < 0.01, (hist, pmf)
+
+
+# ----------------------------------------------------------------- PID -----
+def check_pid_properties(E=64, seed=12):
+    r = _rng(seed)
+    tgt = np.full(E, 12.0)
+    b0 = r.uniform(-0.01, 0.01, E)
+    # zero error: no change
+    b, e1, e2 = om.pid_step(tgt.copy(), tgt, b0, np.zeros(E), np.zeros(E), 0.7, 0.3, 0.2)
+    assert np.array_equal(b, b0) and not e1.any()
+    # equal totals: the updates sum to zero; the overloaded expert falls
+    loads = tgt.copy()
+    loads[0] += 5
+    loads[1] -= 3
+    loads[2] -= 2
+    assert loads.sum() == tgt.sum()
+    b, e1, _ = om.pid_step(loads, tgt, b0, np.zeros(E), np.zeros(E), 0.7, 0.3, 0.2)
+    db = b - b0
+    assert abs(db.sum()) < 1e-12
+    assert np.array_equal(np.sign(db), np.sign(tgt - loads))
+    # velocity form accumulates to the positional form
+    kp, ki, kd = 0.4, 0.3, 0.2
+    b, e1, e2 = b0.copy(), np.zeros(E), np.zeros(E)
+    es = []
+    for s in range(5):
+        ld = r.integers(0, 25, E).astype(np.float64)
+        b, e1, e2 = om.pid_step(ld, tgt, b, e1, e2, kp, ki, kd)
+        es.append(e1)
+    pos_form = b0 + kp * es[-1] + ki * np.sum(es, axis=0) + kd * (es[-1] - es[-2])
+    assert np.allclose(b, pos_form, rtol=0, atol=1e-14)
+
+
+ALL_CHECKS = [
+    check_hand_example, check_pid_golden, check_bruteforce_tiny,
+    check_topk_ties_enumeration, check_softmax_bruteforce,
+    check_single_forced_ffn, check_all_identity, check_k_equals_e,
+    check_z_zero_textbook_moe, check_permutation_invariants,
+    check_token_independence, check_ffn_count_hypergeometric,
+    check_pid_properties,
+]
