@@ -1,0 +1,227 @@
+"""Benchmark of the MoE layer with zero-computation experts on one MI355X.
+
+One step = one moe_zc_forward (router GEMM, softmax + bias top-K, histogram,
+scan, permute, grouped GEMM gate/up + SwiGLU, grouped GEMM down, combine with
+the identity experts and the residual) followed by one moe_zc_bias_update
+(PID step toward uniform load) on the same stream.  Inputs are seeded and
+synthetic, resident in HBM before the timed region.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload prefill]
+
+Prints one JSON line.  Per-stage times come from HIP events that the library
+records on the launch stream at its stage boundaries.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + activated TFLOP/s (% of bf16 MFMA peak) on 1 MI355X"
+PEAK_BF16 = 2.5e15      # dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12       # HBM3E, B/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill",
+                    choices=["tiny", "mid", "decode", "prefill", "skew"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-experts", type=int, default=24,
+                    help="experts the CPU-baseline sample evaluates")
+    return ap.parse_args()
+
+
+def algorithmic(w, S, touched, es):
+    """Algorithmic bytes / FLOPs per launch of each stage (inputs read once,
+    outputs written once)."""
+    T, d, I, N, E, K = w.T, w.d, w.I, w.N, w.E, w.K
+    return {
+        "router_gemm": {"flop": 2.0 * T * d * E,
+                        "bytes": T * d * es + E * d * 4 + T * E * 4},
+        "softmax_topk": {"bytes": T * E * 4 + E * 4 + T * K * 8},
+        "permute": {"bytes": T * d * es + S * d * es + T * K * 4 * 3},
+        "gemm_gate_up_swiglu": {"flop": 4.0 * d * I * S,
+                                "bytes": touched * 2 * I * d * es + S * d * es + S * I * es},
+        "gemm_down": {"flop": 2.0 * d * I * S,
+                      "bytes": touched * d * I * es + S * I * es + S * d * es},
+        "combine": {"bytes": S * d * es + 3 * T * d * es + T * K * 12},
+    }
+
+
+def cpu_baseline(w, inp, n_experts):
+    """The fp64 oracle on the host cores: routing of every token, the SwiGLU
+    experts 0..n_experts-1 with all their rows (scaled to all touched
+    experts), and the combine of every token."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    cores = min(threads, len(os.sched_getaffinity(0)))
+    x = inp["x"].cpu()
+    wr = inp["w_router"].cpu()
+    b = inp["bias"].cpu().numpy()
+    res = inp["residual"].cpu() if inp["residual"] is not None else None
+    n_exp = min(n_experts, w.N)
+    weights = [(inp["w_gate"][e].cpu(), inp["w_up"][e].cpu(), inp["w_down"][e].cpu())
+               for e in range(n_exp)]
+    t0 = time.perf_counter()
+    l64 = oracle.router_logits(x, wr)
+    rt = oracle.route(l64.astype(np.float32), b, w.K, w.N)
+    t1 = time.perf_counter()
+    idx = rt["idx"]
+    x64 = oracle.moe_zc._f64(x)
+    rows = np.zeros((w.T, w.K, w.d))
+    for e in range(n_exp):
+        tt, kk = np.nonzero(idx == e)
+        rows[tt, kk] = oracle.swiglu_ffn(x64[tt], *weights[e])
+    t2 = time.perf_counter()
+    oracle.combine(x64, idx, rt["gate"], rows, w.N, res)
+    t3 = time.perf_counter()
+    touched = int((rt["loads"][: w.N] > 0).sum())
+    sampled_rows = int(rt["loads"][:n_exp].sum())
+    t_ffn = (t2 - t1) * touched / max(1, n_exp)
+    total = (t1 - t0) + t_ffn + (t3 - t2)
+    return {"value": w.T / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"fp64 oracle: routing of all {w.T} tokens ({t1 - t0:.2f} s); SwiGLU "
+                       f"experts 0..{n_exp - 1} with all their {sampled_rows} rows "
+                       f"({t2 - t1:.2f} s), scaled by {touched}/{n_exp} touched experts; "
+                       f"combine of all tokens ({t3 - t2:.2f} s); estimated layer time "
+                       f"{total:.1f} s"),
+            "seconds_measured": round(t3 - t0, 2)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; the multi-GPU path (expert "
+              "sharding with all-to-all) is not built. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_bias_amd as m
+    from workloads import get_workload, make_inputs
+
+    w = get_workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(w, device=dev)
+    dt = inp["x"].dtype
+    es = inp["x"].element_size()
+    need = m.moe_zc_workspace_size(w.T, w.d, w.I, w.N, w.Z, w.K, dt)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    aux = m.alloc_aux(w.T, w.N, w.Z, w.K, dev, keys=("loads", "offsets"))
+    y = torch.empty(w.T, w.d, dtype=dt, device=dev)
+    bias = inp["bias"].clone()
+    pid = m.PidState(w.E, dev, kp=0.5, ki=0.5, kd=0.0)
+    target = torch.full((w.E,), w.T * w.K / w.E, dtype=torch.float32, device=dev)
+
+    def step(events=None):
+        m.moe_zc_forward(inp["x"], inp["w_router"], bias, inp["w_gate"], inp["w_up"],
+                         inp["w_down"], w.N, w.Z, w.K, residual=inp["residual"], out=y,
+                         aux=aux, workspace=ws, events=events)
+        m.moe_zc_bias_update(aux["loads"], target, bias, pid)
+
+    for _ in range(args.warmup):
+        step()
+    events = [m.StageEvents() for _ in range(args.steps)]
+    S_list, touched_list = [], []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # per-stage averages over the timed steps (events were recorded inside them)
+    stage = {k: 0.0 for k in m.STAGE_NAMES}
+    for ev in events:
+        for k, v in ev.stage_ms().items():
+            stage[k] += v / args.steps
+    # routing statistics of the last step (the PID moves them only slightly)
+    loads = aux["loads"].cpu().numpy()
+    S = int(aux["offsets"][w.N].item())
+    touched = int((loads[: w.N] > 0).sum())
+    alg = algorithmic(w, S, touched, es)
+    flop_act = 2.0 * w.T * w.d * w.E + 6.0 * w.d * w.I * S
+    t_step = ms_per_step / 1e3
+    gemm_s = (stage["gemm_gate_up_swiglu"] + stage["gemm_down"]) / 1e3
+    mfma_frac = 6.0 * w.d * w.I * S / gemm_s / PEAK_BF16 if gemm_s > 0 else None
+
+    dom = "gemm_gate_up_swiglu"
+    a = alg[dom]
+    t_dom = stage[dom] / 1e3
+    t_b, t_f = a["bytes"] / PEAK_HBM, a["flop"] / PEAK_BF16
+    if t_b >= t_f:
+        roof = {"bound": "hbm", "achieved": a["bytes"] / t_dom / 1e9, "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": a["flop"] / t_dom / 1e12, "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["avg_launch_ms"] = stage[dom]
+
+    stage_roof = {}
+    for k, v in alg.items():
+        ts = stage[k] / 1e3
+        if ts <= 0:
+            continue
+        entry = {"ms": round(stage[k], 4), "GB/s": round(v["bytes"] / ts / 1e9, 1),
+                 "hbm_frac": round(v["bytes"] / ts / PEAK_HBM, 4)}
+        if "flop" in v:
+            entry["TFLOP/s"] = round(v["flop"] / ts / 1e12, 1)
+            entry["mfma_frac"] = round(v["flop"] / ts / PEAK_BF16, 4)
+        stage_roof[k] = entry
+    for k in ("chunk_hist", "scan"):
+        stage_roof[k] = {"ms": round(stage[k], 4)}
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_experts)
+    ffn_per_token = S / w.T
+    out = {
+        "metric": METRIC,
+        "value": w.T / t_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Gaussian inputs, random-init expert weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "I": w.I, "N": w.N, "Z": w.Z,
+                   "K": w.K, "expert_ffn": "SwiGLU", "residual": True,
+                   "step": "moe_zc_forward + moe_zc_bias_update", "parallelism": "none (1 GPU)"},
+        "activated_tflops": flop_act / t_step / 1e12,
+        "activated_mfma_frac": flop_act / t_step / PEAK_BF16,
+        "grouped_gemm_mfma_frac": mfma_frac,
+        "ffn_rows": S,
+        "ffn_experts_per_token": ffn_per_token,
+        "touched_experts": touched,
+        "stages": stage_roof,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * moe_zc.h -- C ABI of the MI355X (gfx950) MoE layer with zero-computation
+ * experts.
+ *
+ * The layer (LongCat-Flash; page 『衝上熱搜！美團大模型，靠「快」火了』,
+ * section 零計算專家 -- its defining equation was an image that did not survive,
+ * so the formula below is rebuilt from that section's symbol legend):
+ *   a pool of E = N + Z experts: N SwiGLU FFN experts (indices 0..N-1) and Z
+ *   zero-computation experts (indices N..E-1) that return their input as is;
+ *   a softmax router R; a per-expert bias b_i that only steers which K experts
+ *   a token goes to.  For each token t:
+ *     l[t,i] = x_t . W_router[i]                     (fp32)
+ *     p[t,i] = softmax over all E experts of l[t,:]   (evaluated in fp64)
+ *     key    = fl32(fl32(p) + b_i); top-K by key descending, ties to the lower
+ *              expert index
+ *     g      = fl32(p) of each chosen expert (unbiased, not renormalised)
+ *     y_t    = r_t + sum over chosen slots, in key order, of
+ *              g * (W_down_i (silu(W_gate_i x_t) * (W_up_i x_t)))  for i < N
+ *              g * x_t                                             for i >= N
+ *   The bias is adjusted between forwards by a PID controller on the expert
+ *   loads (same section; page 『美团的 LongCat-Flash：用 27B 激活算力跑起一个
+ *   560B 模型』, section 关键要点).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous,
+ *     owned by the caller.  The library keeps no pointer after a call returns
+ *     and allocates no device memory: scratch comes from the caller's
+ *     workspace.
+ *   - Work is enqueued on `stream` (0 = the null stream) and runs
+ *     asynchronously; no call synchronises the device.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     validation error nothing is enqueued and outputs are untouched.
+ *   - A launch failure returns MOE_ZC_ERR_HIP.  Faults inside kernels surface
+ *     at the caller's next synchronisation.
+ *   - Non-finite inputs are outside the contract (results are undefined).
+ *   - Results are bitwise reproducible run to run: no floating-point atomics,
+ *     fixed reduction orders.
+ *   - Calls on different streams with disjoint outputs and workspaces may run
+ *     concurrently; the library has no mutable global state.
+ */
+#ifndef MOE_ZC_H
+#define MOE_ZC_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ZC_ABI_VERSION 1
+
+typedef enum {
+  MOE_ZC_OK = 0,
+  MOE_ZC_ERR_INVALID = 1,      /* bad argument: NULL, negative size, K > E ... */
+  MOE_ZC_ERR_WORKSPACE = 2,    /* workspace NULL or smaller than required     */
+  MOE_ZC_ERR_UNSUPPORTED = 3,  /* valid but outside what the kernels handle   */
+  MOE_ZC_ERR_HIP = 4           /* a HIP launch or runtime call failed         */
+} moe_zc_status;
+
+typedef enum {
+  MOE_ZC_F32 = 0,   /* x, FFN weights, residual, y in fp32 (fp32 FMA path)     */
+  MOE_ZC_BF16 = 1   /* x, FFN weights, residual, y in bf16 (bf16 MFMA path)    */
+} moe_zc_dtype;
+
+/* Limits of this implementation (else MOE_ZC_ERR_UNSUPPORTED):
+ *   E = N + Z in [1, 2048]; K in [1, min(E, 32)];
+ *   bf16: d and I multiples of 64;  f32: d and I multiples of 4;
+ *   T * min(K, N) < 2^31 and T * max(d, I, E) < 2^40. */
+#define MOE_ZC_MAX_EXPERTS 2048
+#define MOE_ZC_MAX_TOPK 32
+
+/* Timed stages of moe_zc_forward (see moe_zc_aux.stage_events), in order:
+ * 0 router GEMM, 1 softmax + bias + top-K, 2 per-chunk expert histogram,
+ * 3 scan (loads, offsets, tile schedule), 4 permute (grouping and row
+ * gather), 5 grouped GEMM gate/up + SwiGLU, 6 grouped GEMM down, 7 combine.
+ * Event i is recorded just before stage i, event 8 after the combine. */
+#define MOE_ZC_NUM_STAGES 8
+#define MOE_ZC_NUM_EVENTS (MOE_ZC_NUM_STAGES + 1)
+
+/* Optional extra outputs of moe_zc_forward.  Every field may be NULL (not
+ * produced).  All arrays are device memory owned by the caller.
+ *   logits      [T, E]  fp32 router logits l
+ *   topk_idx    [T, K]  chosen experts, key descending, ties to lower index
+ *   topk_gate   [T, K]  fl32(p) of the chosen experts
+ *   loads       [E]     slots routed to each expert (FFN and zero alike);
+ *                       this is what moe_zc_bias_update consumes
+ *   offsets     [N + 1] exclusive prefix sum of loads[0..N-1]; offsets[N] = S,
+ *                       the number of (token, FFN expert) rows
+ *   perm        [T * min(K, N)]  token held by grouped row s (first S valid);
+ *                       rows are grouped by expert, tokens ascending
+ *   pos         [T, K]  grouped row of slot (t,k), -1 for a zero expert
+ *   stage_events [MOE_ZC_NUM_EVENTS] created HIP events, recorded on
+ *                       `stream` at stage boundaries (for timing), or NULL */
+typedef struct moe_zc_aux {
+  float* logits;
+  int32_t* topk_idx;
+  float* topk_gate;
+  int32_t* loads;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* pos;
+  hipEvent_t* stage_events;
+} moe_zc_aux;
+
+/* Bytes of device workspace moe_zc_forward needs for these sizes (0 if the
+ * sizes are invalid).  Host only; enqueues nothing. */
+size_t moe_zc_workspace_size(int64_t T, int64_t d, int64_t I, int32_t N,
+                             int32_t Z, int32_t K, moe_zc_dtype dt);
+
+/* Forward of the layer for T tokens (definition at the top of this file).
+ *   x         [T, d]      dt
+ *   w_router  [E, d]      fp32   (E = N + Z; row i scores expert i)
+ *   bias      [E]         fp32   selection bias b
+ *   w_gate    [N, I, d]   dt     (nn.Linear layout [out, in])
+ *   w_up      [N, I, d]   dt
+ *   w_down    [N, d, I]   dt
+ *   residual  [T, d]      dt or NULL (then y = MoE(x))
+ *   y         [T, d]      dt     output; may not alias any input
+ *   aux       NULL or extra outputs (see moe_zc_aux)
+ *   workspace device buffer of at least moe_zc_workspace_size(...) bytes,
+ *             256-byte aligned; contents on entry are ignored.
+ * N may be 0 (every expert is a zero expert; the FFN weights may be NULL).
+ * T = 0 returns MOE_ZC_OK and enqueues nothing.
+ * Precision: router logits fp32 (bf16 path: x times a two-term bf16 split of
+ * W_router on MFMA, fp32 accumulation); softmax in fp64; FFN on bf16 MFMA
+ * with fp32 accumulation, SiLU in fp32, the hidden activation and expert
+ * outputs stored in dt; combine accumulated in fp32 and rounded once. */
+moe_zc_status moe_zc_forward(const void* x, const float* w_router,
+                             const float* bias, const void* w_gate,
+                             const void* w_up, const void* w_down,
+                             const void* residual, void* y, int64_t T,
+                             int64_t d, int64_t I, int32_t N, int32_t Z,
+                             int32_t K, moe_zc_dtype dt, moe_zc_aux* aux,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Routing alone, from given fp32 logits [T, E] and bias [E]: the softmax,
+ * bias key and top-K step of the forward, bit for bit.
+ *   topk_idx [T, K] int32 and topk_gate [T, K] fp32 outputs (device).
+ * Same validation rules and limits as moe_zc_forward. */
+moe_zc_status moe_zc_route(const float* logits, const float* bias, int64_t T,
+                           int32_t E, int32_t K, int32_t* topk_idx,
+                           float* topk_gate, hipStream_t stream);
+
+/* PID controller state for moe_zc_bias_update.  Gains live on the host; the
+ * error histories are device arrays of E floats, owned by the caller, zeroed
+ * before the first step and carried between steps (save and restore them with
+ * the bias to resume). */
+typedef struct moe_zc_pid {
+  float kp, ki, kd;
+  float* e_prev;    /* [E] error of the previous step        */
+  float* e_prev2;   /* [E] error of the step before that     */
+} moe_zc_pid;
+
+/* One PID step on the expert bias from measured loads (pages: a PID
+ * controller tunes the expert bias in real time from recent usage --
+ * 『衝上熱搜！美團大模型，靠「快」火了』, section 零計算專家; busy experts get
+ * less work, idle ones more -- 『美团 LongCat-Flash 这个5600亿参数的懒AI，
+ * 竟然比勤奋的模型跑得更快？』).  With e_i = (target_i - loads_i) / sum(target):
+ *   bias_i += kp (e_i - e1_i) + ki e_i + kd (e_i - 2 e1_i + e2_i)
+ *   e2 <- e1, e1 <- e        (computed in fp64, stored in fp32)
+ *   loads [E] int32 (e.g. moe_zc_aux.loads), target [E] fp32 with a positive
+ *   sum, bias [E] fp32 updated in place.  E in [1, MOE_ZC_MAX_EXPERTS]. */
+moe_zc_status moe_zc_bias_update(const int32_t* loads, const float* target,
+                                 float* bias, const moe_zc_pid* pid, int32_t E,
+                                 hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* moe_zc_status_string(moe_zc_status s);
+
+/* MOE_ZC_ABI_VERSION of the built library. */
+int32_t moe_zc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ZC_H */

@@ -1,0 +1,12 @@
+"""MI355X (gfx950) MoE layer with zero-computation experts.
+
+The layer runs in hand-written HIP kernels behind the C ABI of
+include/moe_zc.h (libmoe_zc.so, built in-tree by ``_build.build()``); this
+package is its thin Python binding.
+"""
+from .api import (  # noqa: F401
+    AUX_KEYS, MoeZcError, PidState, StageEvents, alloc_aux, moe_zc_abi_version,
+    moe_zc_bias_update, moe_zc_forward, moe_zc_route, moe_zc_status_string,
+    moe_zc_workspace_size,
+)
+from ._lib import LIB_PATH, STAGE_NAMES  # noqa: F401

@@ -1,0 +1,237 @@
+"""Python binding of the C ABI in include/moe_zc.h.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, then their device pointers and the current HIP stream are handed
+to libmoe_zc.so.  Every step of the layer runs in the library's kernels; if
+the library is missing this module raises (there is no fallback path).
+PyTorch only provides device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.MOE_ZC_F32, torch.bfloat16: _lib.MOE_ZC_BF16}
+AUX_KEYS = ("logits", "topk_idx", "topk_gate", "loads", "offsets", "perm", "pos")
+
+
+class MoeZcError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {moe_zc_status_string(code)} (status {code})")
+
+
+def moe_zc_status_string(code: int) -> str:
+    return _lib.load().moe_zc_status_string(int(code)).decode()
+
+
+def moe_zc_abi_version() -> int:
+    return int(_lib.load().moe_zc_abi_version())
+
+
+def _dtype_code(dt) -> int:
+    if isinstance(dt, int):
+        return dt
+    if isinstance(dt, str):
+        return {"f32": _lib.MOE_ZC_F32, "bf16": _lib.MOE_ZC_BF16}[dt]
+    return _DT[dt]
+
+
+def moe_zc_workspace_size(T: int, d: int, I: int, N: int, Z: int, K: int, dtype) -> int:
+    return int(_lib.load().moe_zc_workspace_size(T, d, I, N, Z, K, _dtype_code(dtype)))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _aux_spec(T: int, N: int, Z: int, K: int):
+    E = N + Z
+    return {"logits": ((T, E), torch.float32), "topk_idx": ((T, K), torch.int32),
+            "topk_gate": ((T, K), torch.float32), "loads": ((E,), torch.int32),
+            "offsets": ((N + 1,), torch.int32),
+            "perm": ((max(1, T * min(K, N)),), torch.int32), "pos": ((T, K), torch.int32)}
+
+
+def alloc_aux(T: int, N: int, Z: int, K: int, device, keys=AUX_KEYS) -> Dict[str, torch.Tensor]:
+    """Caller-owned tensors for the optional outputs of moe_zc_forward."""
+    spec = _aux_spec(T, N, Z, K)
+    return {k: torch.empty(*spec[k][0], dtype=spec[k][1], device=device) for k in keys}
+
+
+class StageEvents:
+    """HIP events recorded by moe_zc_forward at its stage boundaries."""
+
+    def __init__(self):
+        h = _lib.hip()
+        self._ev = (ctypes.c_void_p * _lib.MOE_ZC_NUM_EVENTS)()
+        for i in range(_lib.MOE_ZC_NUM_EVENTS):
+            ev = ctypes.c_void_p()
+            if h.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self._ev[i] = ev.value
+
+    @property
+    def array(self):
+        return self._ev
+
+    def stage_ms(self) -> Dict[str, float]:
+        """Per-stage milliseconds of the last recorded forward (synchronises)."""
+        h = _lib.hip()
+        if h.hipEventSynchronize(self._ev[_lib.MOE_ZC_NUM_EVENTS - 1]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        out = {}
+        for i, name in enumerate(_lib.STAGE_NAMES):
+            ms = ctypes.c_float()
+            if h.hipEventElapsedTime(ctypes.byref(ms), self._ev[i], self._ev[i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out[name] = float(ms.value)
+        return out
+
+    def __del__(self):
+        try:
+            h = _lib.hip()
+            for i in range(_lib.MOE_ZC_NUM_EVENTS):
+                if self._ev[i]:
+                    h.hipEventDestroy(self._ev[i])
+        except Exception:
+            pass
+
+
+def moe_zc_forward(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
+                   w_gate: Optional[torch.Tensor], w_up: Optional[torch.Tensor],
+                   w_down: Optional[torch.Tensor], N: int, Z: int, K: int,
+                   residual: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None,
+                   aux: Optional[Dict[str, torch.Tensor]] = None,
+                   workspace: Optional[torch.Tensor] = None,
+                   events: Optional[StageEvents] = None) -> torch.Tensor:
+    """y = MoE-ZC(x) (+ residual); see include/moe_zc.h for the definition."""
+    lib = _lib.load()
+    if x.dim() != 2:
+        raise ValueError("x must be [T, d]")
+    T, d = x.shape
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    dt = x.dtype
+    if dt not in _DT:
+        raise ValueError(f"unsupported dtype {dt}")
+    E = N + Z
+    _need(x, "x", dt, (T, d), dev)
+    _need(w_router, "w_router", torch.float32, (E, d), dev)
+    _need(bias, "bias", torch.float32, (E,), dev)
+    if N > 0:
+        I = w_gate.shape[1]
+        _need(w_gate, "w_gate", dt, (N, I, d), dev)
+        _need(w_up, "w_up", dt, (N, I, d), dev)
+        _need(w_down, "w_down", dt, (N, d, I), dev)
+    else:
+        I = w_gate.shape[1] if w_gate is not None else 64
+    if residual is not None:
+        _need(residual, "residual", dt, (T, d), dev)
+    if out is None:
+        out = torch.empty(T, d, dtype=dt, device=dev)
+    _need(out, "out", dt, (T, d), dev)
+    need = moe_zc_workspace_size(T, d, I, N, Z, K, dt)
+    if need == 0:
+        code = lib.moe_zc_forward(None, None, None, None, None, None, None, None, T, d, I, N, Z,
+                                  K, _DT[dt], None, None, 0, None)
+        raise MoeZcError(code, "moe_zc_forward")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on x's device")
+    a = _lib.MoeZcAux()
+    if aux:
+        spec = _aux_spec(T, N, Z, K)
+        for k, t in aux.items():
+            if k not in AUX_KEYS:
+                raise ValueError(f"unknown aux key {k!r}")
+            _need(t, f"aux[{k!r}]", spec[k][1], spec[k][0], dev)
+            setattr(a, k, t.data_ptr())
+    if events is not None:
+        a.stage_events = ctypes.cast(events.array, ctypes.c_void_p).value
+    code = lib.moe_zc_forward(
+        _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate) if N > 0 else None,
+        _ptr(w_up) if N > 0 else None, _ptr(w_down) if N > 0 else None, _ptr(residual),
+        _ptr(out), T, d, I, N, Z, K, _DT[dt], ctypes.byref(a), _ptr(workspace),
+        workspace.numel(), _stream(dev))
+    if code != _lib.MOE_ZC_OK:
+        raise MoeZcError(code, "moe_zc_forward")
+    return out
+
+
+def moe_zc_route(logits: torch.Tensor, bias: torch.Tensor, K: int,
+                 topk_idx: Optional[torch.Tensor] = None,
+                 topk_gate: Optional[torch.Tensor] = None):
+    """(topk_idx, topk_gate) from fp32 logits [T, E] and bias [E]."""
+    lib = _lib.load()
+    T, E = logits.shape
+    dev = logits.device
+    _need(logits, "logits", torch.float32, (T, E), dev)
+    _need(bias, "bias", torch.float32, (E,), dev)
+    if topk_idx is None:
+        topk_idx = torch.empty(T, K, dtype=torch.int32, device=dev)
+    if topk_gate is None:
+        topk_gate = torch.empty(T, K, dtype=torch.float32, device=dev)
+    _need(topk_idx, "topk_idx", torch.int32, (T, K), dev)
+    _need(topk_gate, "topk_gate", torch.float32, (T, K), dev)
+    code = lib.moe_zc_route(_ptr(logits), _ptr(bias), T, E, K, _ptr(topk_idx), _ptr(topk_gate),
+                            _stream(dev))
+    if code != _lib.MOE_ZC_OK:
+        raise MoeZcError(code, "moe_zc_route")
+    return topk_idx, topk_gate
+
+
+class PidState:
+    """Gains (host) and error histories (device) of the bias controller."""
+
+    def __init__(self, E: int, device, kp: float = 0.5, ki: float = 0.5, kd: float = 0.0):
+        self.kp, self.ki, self.kd = float(kp), float(ki), float(kd)
+        self.e_prev = torch.zeros(E, dtype=torch.float32, device=device)
+        self.e_prev2 = torch.zeros(E, dtype=torch.float32, device=device)
+
+    def as_struct(self) -> _lib.MoeZcPid:
+        return _lib.MoeZcPid(self.kp, self.ki, self.kd, self.e_prev.data_ptr(),
+                             self.e_prev2.data_ptr())
+
+
+def moe_zc_bias_update(loads: torch.Tensor, target: torch.Tensor, bias: torch.Tensor,
+                       pid: PidState) -> torch.Tensor:
+    """One PID step on ``bias`` (in place) from ``loads``; returns ``bias``."""
+    lib = _lib.load()
+    E = bias.shape[0]
+    dev = bias.device
+    _need(loads, "loads", torch.int32, (E,), dev)
+    _need(target, "target", torch.float32, (E,), dev)
+    _need(bias, "bias", torch.float32, (E,), dev)
+    _need(pid.e_prev, "pid.e_prev", torch.float32, (E,), dev)
+    _need(pid.e_prev2, "pid.e_prev2", torch.float32, (E,), dev)
+    st = pid.as_struct()
+    code = lib.moe_zc_bias_update(_ptr(loads), _ptr(target), _ptr(bias), ctypes.byref(st), E,
+                                  _stream(dev))
+    if code != _lib.MOE_ZC_OK:
+        raise MoeZcError(code, "moe_zc_bias_update")
+    return bias

@@ -1,0 +1,257 @@
+// C ABI of the MoE layer with zero-computation experts: argument checks,
+// workspace plan and the stream-ordered launch sequence.  See
+// include/moe_zc.h for the contract of each entry point.
+#include "../../include/moe_zc.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "kernels.hpp"
+
+using namespace moezc;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Shape {
+  int64_t T, d, I;
+  int32_t N, Z, K, E;
+  moe_zc_dtype dt;
+  int64_t smax;  // T * min(K, N): most (token, FFN expert) rows possible
+  int64_t chunks;
+  size_t es;     // element size of dt
+  int ffn_tile_rows;
+};
+
+// Host-side shape validation shared by every entry point that takes sizes.
+moe_zc_status check_shape(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z, int32_t K,
+                          moe_zc_dtype dt, Shape* s) {
+  if (dt != MOE_ZC_F32 && dt != MOE_ZC_BF16) return MOE_ZC_ERR_INVALID;
+  if (T < 0 || d <= 0 || I <= 0 || N < 0 || Z < 0 || K < 1) return MOE_ZC_ERR_INVALID;
+  const int64_t E = (int64_t)N + Z;
+  if (E < 1 || K > E) return MOE_ZC_ERR_INVALID;
+  if (E > MOE_ZC_MAX_EXPERTS || K > MOE_ZC_MAX_TOPK) return MOE_ZC_ERR_UNSUPPORTED;
+  const int64_t mult = (dt == MOE_ZC_BF16) ? 64 : 32;
+  if (d % mult != 0 || I % mult != 0) return MOE_ZC_ERR_UNSUPPORTED;
+  const int64_t smax = T * std::min<int64_t>(K, N);
+  if (smax >= (int64_t(1) << 31) || T * K >= (int64_t(1) << 31) || T >= (int64_t(1) << 31))
+    return MOE_ZC_ERR_UNSUPPORTED;
+  const int64_t widest = std::max<int64_t>(std::max<int64_t>(d, I), E);
+  if (T > 0 && widest > (int64_t(1) << 40) / T) return MOE_ZC_ERR_UNSUPPORTED;
+  if (d >= (int64_t(1) << 24) || I >= (int64_t(1) << 24)) return MOE_ZC_ERR_UNSUPPORTED;
+  s->T = T; s->d = d; s->I = I; s->N = N; s->Z = Z; s->K = K; s->E = (int32_t)E; s->dt = dt;
+  s->smax = smax;
+  s->chunks = (T + kChunk - 1) / kChunk;
+  s->es = (dt == MOE_ZC_BF16) ? 2 : 4;
+  if (dt == MOE_ZC_BF16) {
+    const int64_t expected = (N > 0) ? (T * K) / E : 0;  // rows per expert, symmetric routing
+    int tr = mfma_tile_rows(expected);
+    if (tr == 32 && I % 128 != 0) tr = 128;
+    s->ffn_tile_rows = tr;
+  } else {
+    s->ffn_tile_rows = kSimtTileRows;
+  }
+  return MOE_ZC_OK;
+}
+
+struct Plan {
+  size_t logits, idx, gate, pos, loads, offsets, perm, counts, tiles, wr2, xp, h, o, total;
+};
+
+Plan make_plan(const Shape& s) {
+  Plan p{};
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t here = at;
+    at += align_up(bytes);
+    return here;
+  };
+  p.logits = take((size_t)s.T * s.E * 4);
+  p.idx = take((size_t)s.T * s.K * 4);
+  p.gate = take((size_t)s.T * s.K * 4);
+  p.pos = take((size_t)s.T * s.K * 4);
+  p.loads = take((size_t)s.E * 4);
+  p.offsets = take((size_t)(s.N + 1) * 4);
+  p.perm = take((size_t)std::max<int64_t>(s.smax, 1) * 4);
+  p.counts = take((size_t)s.chunks * s.E * 4);
+  p.tiles = take((size_t)(s.N + 1) * 4);
+  p.wr2 = take(s.dt == MOE_ZC_BF16 ? (size_t)s.E * 2 * s.d * 2 : 0);
+  p.xp = take((size_t)s.smax * s.d * s.es);
+  p.h = take((size_t)s.smax * s.I * s.es);
+  p.o = take((size_t)s.smax * s.d * s.es);
+  p.total = at;
+  return p;
+}
+
+#define MOE_ZC_TRY(expr)                          \
+  do {                                            \
+    if ((expr) != hipSuccess) return MOE_ZC_ERR_HIP; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_zc_abi_version(void) { return MOE_ZC_ABI_VERSION; }
+
+const char* moe_zc_status_string(moe_zc_status s) {
+  switch (s) {
+    case MOE_ZC_OK: return "ok";
+    case MOE_ZC_ERR_INVALID: return "invalid argument";
+    case MOE_ZC_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ZC_ERR_UNSUPPORTED: return "sizes outside what the kernels support";
+    case MOE_ZC_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+size_t moe_zc_workspace_size(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z, int32_t K,
+                             moe_zc_dtype dt) {
+  Shape s;
+  if (check_shape(T, d, I, N, Z, K, dt, &s) != MOE_ZC_OK) return 0;
+  return make_plan(s).total;
+}
+
+moe_zc_status moe_zc_forward(const void* x, const float* w_router, const float* bias,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const void* residual, void* y, int64_t T, int64_t d, int64_t I,
+                             int32_t N, int32_t Z, int32_t K, moe_zc_dtype dt, moe_zc_aux* aux,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  const moe_zc_status st = check_shape(T, d, I, N, Z, K, dt, &s);
+  if (st != MOE_ZC_OK) return st;
+  if (T == 0) return MOE_ZC_OK;
+  if (!x || !w_router || !bias || !y) return MOE_ZC_ERR_INVALID;
+  if (N > 0 && (!w_gate || !w_up || !w_down)) return MOE_ZC_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(w_router) || (residual && !aligned16(residual)))
+    return MOE_ZC_ERR_INVALID;
+  if (N > 0 && (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down)))
+    return MOE_ZC_ERR_INVALID;
+  const Plan pl = make_plan(s);
+  if (!workspace || workspace_bytes < pl.total) return MOE_ZC_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ZC_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  float* logits = (aux && aux->logits) ? aux->logits : reinterpret_cast<float*>(ws + pl.logits);
+  int32_t* idx = (aux && aux->topk_idx) ? aux->topk_idx : reinterpret_cast<int32_t*>(ws + pl.idx);
+  float* gate = (aux && aux->topk_gate) ? aux->topk_gate : reinterpret_cast<float*>(ws + pl.gate);
+  int32_t* pos = (aux && aux->pos) ? aux->pos : reinterpret_cast<int32_t*>(ws + pl.pos);
+  int32_t* loads = (aux && aux->loads) ? aux->loads : reinterpret_cast<int32_t*>(ws + pl.loads);
+  int32_t* offsets =
+      (aux && aux->offsets) ? aux->offsets : reinterpret_cast<int32_t*>(ws + pl.offsets);
+  int32_t* perm = (aux && aux->perm) ? aux->perm : reinterpret_cast<int32_t*>(ws + pl.perm);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + pl.counts);
+  int32_t* tiles = reinterpret_cast<int32_t*>(ws + pl.tiles);
+  hipEvent_t* ev = (aux && aux->stage_events) ? aux->stage_events : nullptr;
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+
+  const bool bf = (dt == MOE_ZC_BF16);
+  void* xp = ws + pl.xp;
+  void* h = ws + pl.h;
+  void* o = ws + pl.o;
+  const int E = s.E;
+
+  // stage 0: router logits
+  MOE_ZC_TRY(mark(0));
+  {
+    GemmProblem p{};
+    p.A = x; p.lda = d; p.a_kwrap = (int)d;
+    p.C = logits; p.ldc = E; p.Nout = E;
+    p.G = 1; p.M = (int)T;
+    if (bf) {
+      bf16_t* wr2 = reinterpret_cast<bf16_t*>(ws + pl.wr2);
+      MOE_ZC_TRY(launch_split_router(w_router, wr2, E, (int)d, stream));
+      p.B0 = wr2; p.ldb = 2 * d; p.K = (int)(2 * d);
+      MOE_ZC_TRY(launch_mfma_gemm(p, kStoreF32, 128, T, stream));
+    } else {
+      p.B0 = w_router; p.ldb = d; p.K = (int)d;
+      MOE_ZC_TRY(launch_simt_gemm(p, kStoreF32, T, stream));
+    }
+  }
+  // stage 1: softmax, bias key, top-K
+  MOE_ZC_TRY(mark(1));
+  MOE_ZC_TRY(launch_topk(logits, bias, T, E, K, idx, gate, stream));
+  // stage 2: per-chunk histogram and in-chunk ranks (into pos)
+  MOE_ZC_TRY(mark(2));
+  MOE_ZC_TRY(launch_chunk_hist(idx, T, K, E, N, counts, pos, stream));
+  // stage 3: loads, offsets, tile schedule
+  MOE_ZC_TRY(mark(3));
+  MOE_ZC_TRY(launch_scan(counts, (int)s.chunks, E, N, loads, offsets, s.ffn_tile_rows, tiles,
+                         stream));
+  // stage 4: grouping permutation and row gather
+  MOE_ZC_TRY(mark(4));
+  if (bf)
+    MOE_ZC_TRY(launch_permute<bf16_t>(static_cast<const bf16_t*>(x), idx, counts, offsets, pos,
+                                      perm, static_cast<bf16_t*>(xp), T, (int)d, K, E, N, stream));
+  else
+    MOE_ZC_TRY(launch_permute<float>(static_cast<const float*>(x), idx, counts, offsets, pos,
+                                     perm, static_cast<float*>(xp), T, (int)d, K, E, N, stream));
+  // stages 5, 6: expert FFNs as grouped GEMMs
+  MOE_ZC_TRY(mark(5));
+  if (N > 0) {
+    GemmProblem p{};
+    p.A = xp; p.lda = d; p.a_kwrap = (int)d; p.K = (int)d;
+    p.B0 = w_gate; p.B1 = w_up; p.ldb = d; p.b_group_stride = I * d;
+    p.C = h; p.ldc = I; p.Nout = (int)I;
+    p.row_offsets = offsets; p.tile_prefix = tiles; p.G = N; p.M = 0;
+    if (bf)
+      MOE_ZC_TRY(launch_mfma_gemm(p, kSwiGLU_BF16, s.ffn_tile_rows, s.smax, stream));
+    else
+      MOE_ZC_TRY(launch_simt_gemm(p, kSwiGLU_F32, s.smax, stream));
+  }
+  MOE_ZC_TRY(mark(6));
+  if (N > 0) {
+    GemmProblem p{};
+    p.A = h; p.lda = I; p.a_kwrap = (int)I; p.K = (int)I;
+    p.B0 = w_down; p.ldb = I; p.b_group_stride = d * I;
+    p.C = o; p.ldc = d; p.Nout = (int)d;
+    p.row_offsets = offsets; p.tile_prefix = tiles; p.G = N; p.M = 0;
+    if (bf)
+      MOE_ZC_TRY(launch_mfma_gemm(p, kStoreBF16, s.ffn_tile_rows, s.smax, stream));
+    else
+      MOE_ZC_TRY(launch_simt_gemm(p, kStoreF32, s.smax, stream));
+  }
+  // stage 7: combine with the identity experts and the residual
+  MOE_ZC_TRY(mark(7));
+  if (bf)
+    MOE_ZC_TRY(launch_combine<bf16_t>(static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(o),
+                                      static_cast<const bf16_t*>(residual), idx, gate, pos,
+                                      static_cast<bf16_t*>(y), T, (int)d, K, N, stream));
+  else
+    MOE_ZC_TRY(launch_combine<float>(static_cast<const float*>(x), static_cast<const float*>(o),
+                                     static_cast<const float*>(residual), idx, gate, pos,
+                                     static_cast<float*>(y), T, (int)d, K, N, stream));
+  MOE_ZC_TRY(mark(8));
+  return MOE_ZC_OK;
+}
+
+moe_zc_status moe_zc_route(const float* logits, const float* bias, int64_t T, int32_t E,
+                           int32_t K, int32_t* topk_idx, float* topk_gate, hipStream_t stream) {
+  if (T < 0 || E < 1 || K < 1 || K > E) return MOE_ZC_ERR_INVALID;
+  if (E > MOE_ZC_MAX_EXPERTS || K > MOE_ZC_MAX_TOPK) return MOE_ZC_ERR_UNSUPPORTED;
+  if (T * K >= (int64_t(1) << 31) || T >= (int64_t(1) << 33)) return MOE_ZC_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_ZC_OK;
+  if (!logits || !bias || !topk_idx || !topk_gate) return MOE_ZC_ERR_INVALID;
+  MOE_ZC_TRY(launch_topk(logits, bias, T, E, K, topk_idx, topk_gate, stream));
+  return MOE_ZC_OK;
+}
+
+moe_zc_status moe_zc_bias_update(const int32_t* loads, const float* target, float* bias,
+                                 const moe_zc_pid* pid, int32_t E, hipStream_t stream) {
+  if (!loads || !target || !bias || !pid || !pid->e_prev || !pid->e_prev2)
+    return MOE_ZC_ERR_INVALID;
+  if (E < 1) return MOE_ZC_ERR_INVALID;
+  if (E > MOE_ZC_MAX_EXPERTS) return MOE_ZC_ERR_UNSUPPORTED;
+  MOE_ZC_TRY(launch_pid(loads, target, bias, pid->e_prev, pid->e_prev2, E, pid->kp, pid->ki,
+                        pid->kd, stream));
+  return MOE_ZC_OK;
+}
+
+}  // extern "C"

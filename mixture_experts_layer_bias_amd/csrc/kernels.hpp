@@ -1,0 +1,78 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace moezc {
+
+// Rows of tokens handled by one histogram chunk (one wavefront: one bit each).
+constexpr int kChunk = 64;
+constexpr int kMaxExperts = 2048;
+constexpr int kMaxTopK = 32;
+
+// ---- routing (route.hip) ----------------------------------------------------
+// W_router fp32 [E, d] -> [E, 2d] bf16: columns [0, d) = bf16(w),
+// columns [d, 2d) = bf16(w - bf16(w)).
+hipError_t launch_split_router(const float* w, bf16_t* w2, int E, int d, hipStream_t s);
+// fp64 softmax, fp32 bias key, top-K with lowest-index tie-break.
+hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int K,
+                       int32_t* idx, float* gate, hipStream_t s);
+// Per 64-token chunk: expert counts [C, E] and each FFN slot's rank among the
+// chunk's earlier tokens (written to rank[T, K], -1 for zero experts).
+hipError_t launch_chunk_hist(const int32_t* idx, int64_t T, int K, int E, int N,
+                             int32_t* counts, int32_t* rank, hipStream_t s);
+// counts [C, E] -> exclusive per-expert chunk bases (in place); loads [E];
+// offsets [N+1]; m-tile prefix [N+1] for tiles of `bm` rows.
+hipError_t launch_scan(int32_t* counts, int C, int E, int N, int32_t* loads,
+                       int32_t* offsets, int bm, int32_t* tile_prefix, hipStream_t s);
+// Grouped rows: pos (rank -> row), perm, and xp[row] = x[token].
+template <typename T>
+hipError_t launch_permute(const T* x, const int32_t* idx, const int32_t* chunk_base,
+                          const int32_t* offsets, int32_t* pos, int32_t* perm, T* xp,
+                          int64_t Tn, int d, int K, int E, int N, hipStream_t s);
+// y = r + sum_k g * (FFN row or x).
+template <typename T>
+hipError_t launch_combine(const T* x, const T* o, const T* res, const int32_t* idx,
+                          const float* gate, const int32_t* pos, T* y, int64_t Tn,
+                          int d, int K, int N, hipStream_t s);
+hipError_t launch_pid(const int32_t* loads, const float* target, float* bias, float* e1,
+                      float* e2, int E, float kp, float ki, float kd, hipStream_t s);
+
+// ---- grouped GEMMs ------------------------------------------------------------
+// C[rows of group g, :] = A[rows, :K] * B_g[:, :K]^T.  Groups are the FFN
+// experts (rows = their grouped slots) or one group of M rows (router).
+struct GemmProblem {
+  const void* A;           // [rows, K] (row stride lda)
+  int64_t lda;
+  int a_kwrap;             // A column = k % a_kwrap (router: d; else K)
+  const void* B0;          // [G][Nout or I][K] weights (gate or plain)
+  const void* B1;          // up weights for SwiGLU, else null
+  int64_t ldb;             // row stride of B
+  int64_t b_group_stride;  // elements between groups of B
+  void* C;                 // output
+  int64_t ldc;
+  int K;                   // reduction length
+  int Nout;                // output columns (SwiGLU: I)
+  const int32_t* row_offsets;  // [G+1] device, or null: one group of M rows
+  const int32_t* tile_prefix;  // [G+1] device m-tile prefix, or null
+  int G;
+  int M;
+};
+
+enum Epilogue { kStoreF32 = 0, kStoreBF16 = 1, kSwiGLU_BF16 = 2, kSwiGLU_F32 = 3 };
+
+// bf16 MFMA path (gemm_mfma.hip).  `tile_rows` selects the row-tile variant
+// (128 for many rows per expert, 32 for a few); the scan must have used it.
+hipError_t launch_mfma_gemm(const GemmProblem& p, int epilogue, int tile_rows,
+                            int64_t max_rows, hipStream_t s);
+int mfma_tile_rows(int64_t expected_rows_per_group);
+
+// fp32 FMA path (gemm_simt.hip).
+hipError_t launch_simt_gemm(const GemmProblem& p, int epilogue, int64_t max_rows,
+                            hipStream_t s);
+constexpr int kSimtTileRows = 64;
+
+}  // namespace moezc

@@ -1,0 +1,425 @@
+// Routing-side kernels of the MoE layer with zero-computation experts (gfx950):
+// router-weight split, softmax + bias key + top-K, expert histogram, scan,
+// grouping permutation, combine and the PID bias update.
+//
+// Layer definition: LongCat-Flash pages, 『衝上熱搜！美團大模型，靠「快」火了』,
+// section 零計算專家 (softmax router over N FFN + Z identity experts, bias b_i
+// used for selection, K experts per token; PID tuning of the bias).
+#include <math.h>
+
+#include "kernels.hpp"
+
+namespace moezc {
+
+// ---------------------------------------------------------------------------
+// Router weight split: w = hi + lo + r with |r| <= 2^-17 |w|, hi, lo in bf16.
+// x (bf16) times [hi | lo] on MFMA with fp32 accumulation then gives the fp32
+// logits to about 1e-5 absolute at d = 6144 (one bf16 term alone: ~1e-3).
+__global__ __launch_bounds__(256) void split_router_kernel(const float* __restrict__ w,
+                                                           bf16_t* __restrict__ w2,
+                                                           int E, int d) {
+  const int64_t n = (int64_t)E * d;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = i / d, k = i - e * d;
+    const float v = w[i];
+    const bf16_t hi = f32_to_bf16(v);
+    const bf16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+    w2[e * 2 * d + k] = hi;
+    w2[e * 2 * d + d + k] = lo;
+  }
+}
+
+hipError_t launch_split_router(const float* w, bf16_t* w2, int E, int d, hipStream_t s) {
+  const int64_t n = (int64_t)E * d;
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(split_router_kernel, dim3(blocks), dim3(256), 0, s, w, w2, E, d);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Softmax + bias key + top-K.  One wavefront per token; lane l holds experts
+// l, l+64, ...  The softmax runs in fp64 from the fp32 logits (max, exp,
+// sum, divide), its result is rounded once to fp32 (the gate), and the
+// selection key is the fp32 sum fl32(p32 + b).  The K winners are taken one at
+// a time by a wavefront arg-max on (key descending, index ascending), so an
+// exact tie goes to the lower expert index and the output order is the key
+// order.  Reductions are xor butterflies: every lane ends with the same,
+// run-to-run reproducible value.
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+                                                   const float* __restrict__ bias,
+                                                   int64_t T, int E, int K,
+                                                   int32_t* __restrict__ idx_out,
+                                                   float* __restrict__ gate_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + t * E;
+
+  float l[EPL];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int j = lane + 64 * i;
+    l[i] = (j < E) ? row[j] : -INFINITY;
+    m = fmaxf(m, l[i]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+
+  double ex[EPL];
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int j = lane + 64 * i;
+    ex[i] = (j < E) ? exp((double)l[i] - (double)m) : 0.0;
+    s += ex[i];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+
+  float p32[EPL], key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int j = lane + 64 * i;
+    p32[i] = (float)(ex[i] / s);
+    key[i] = (j < E) ? __fadd_rn(p32[i], bias[j]) : -INFINITY;
+  }
+
+  uint32_t taken = 0u;
+  for (int r = 0; r < K; ++r) {
+    float bk = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int j = lane + 64 * i;
+      // j grows with i, so a strict '>' keeps the lower index on a tie
+      if (j < E && !((taken >> i) & 1u) && (key[i] > bk || bi == 0x7fffffff)) {
+        bk = key[i];
+        bi = j;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ok = __shfl_xor(bk, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ok > bk || (ok == bk && oi < bi)) {
+        bk = ok;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) {
+      const int sel = bi >> 6;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        if (i == sel) {
+          taken |= 1u << i;
+          idx_out[t * K + r] = bi;
+          gate_out[t * K + r] = p32[i];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int K,
+                       int32_t* idx, float* gate, hipStream_t s) {
+  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  const int epl = (E + 63) / 64;
+  if (epl <= 1)
+    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+  else if (epl <= 2)
+    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+  else if (epl <= 4)
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+  else if (epl <= 8)
+    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+  else if (epl <= 12)
+    hipLaunchKernelGGL(topk_kernel<12>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+  else if (epl <= 16)
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+  else if (epl <= 32)
+    hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk expert histogram and stable in-chunk ranks.  One wavefront per
+// chunk of 64 tokens: lane l (token c*64+l) sets bit l of the 64-bit mask of
+// each expert it chose (an LDS OR, order independent).  A token's rank among
+// the chunk's tokens routed to expert e is the popcount of the mask bits
+// below its own; a token picks an expert at most once, so this orders the
+// expert's rows by token.  counts[c][e] = popcount(mask[e]).
+__global__ __launch_bounds__(64) void chunk_hist_kernel(const int32_t* __restrict__ idx,
+                                                        int64_t T, int K, int E, int N,
+                                                        int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ rank) {
+  __shared__ unsigned long long mask[kMaxExperts];
+  const int lane = threadIdx.x;
+  const int64_t c = blockIdx.x;
+  for (int e = lane; e < E; e += 64) mask[e] = 0ull;
+  __syncthreads();
+  const int64_t t = c * kChunk + lane;
+  if (t < T) {
+    for (int k = 0; k < K; ++k) atomicOr(&mask[idx[t * K + k]], 1ull << lane);
+  }
+  __syncthreads();
+  if (t < T) {
+    const unsigned long long below = (1ull << lane) - 1ull;
+    for (int k = 0; k < K; ++k) {
+      const int e = idx[t * K + k];
+      rank[t * K + k] = (e < N) ? __popcll(mask[e] & below) : -1;
+    }
+  }
+  for (int e = lane; e < E; e += 64) counts[c * E + e] = __popcll(mask[e]);
+}
+
+hipError_t launch_chunk_hist(const int32_t* idx, int64_t T, int K, int E, int N,
+                             int32_t* counts, int32_t* rank, hipStream_t s) {
+  const int64_t C = (T + kChunk - 1) / kChunk;
+  hipLaunchKernelGGL(chunk_hist_kernel, dim3((unsigned)C), dim3(64), 0, s, idx, T, K, E, N,
+                     counts, rank);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup of 16 wavefronts turns the chunk counts into:
+//   counts[c][e] <- sum_{c' < c} counts[c'][e]   (exclusive, in place)
+//   loads[e]      = sum_c counts[c][e]
+//   offsets[e]    = sum_{e' < e, e' < N} loads[e']            (offsets[N] = S)
+//   tile_prefix[e] = sum_{e' < e} ceil(loads[e'] / bm)        (FFN experts)
+// Wave w owns the chunk range [C*w/16, C*(w+1)/16); all sums are integer.
+constexpr int kScanWaves = 16;
+__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts, int C, int E,
+                                                    int N, int32_t* __restrict__ loads,
+                                                    int32_t* __restrict__ offsets, int bm,
+                                                    int32_t* __restrict__ tile_prefix) {
+  __shared__ int32_t part[kScanWaves][kMaxExperts];
+  __shared__ int32_t tot[kMaxExperts];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int c0 = (int)(((int64_t)C * w) / kScanWaves);
+  const int c1 = (int)(((int64_t)C * (w + 1)) / kScanWaves);
+  for (int e = lane; e < E; e += 64) {
+    int s = 0;
+    for (int c = c0; c < c1; ++c) s += counts[(int64_t)c * E + e];
+    part[w][e] = s;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) {
+    int run = 0;
+    for (int v = 0; v < kScanWaves; ++v) {
+      const int x = part[v][e];
+      part[v][e] = run;
+      run += x;
+    }
+    tot[e] = run;
+    loads[e] = run;
+  }
+  __syncthreads();
+  for (int e = lane; e < E; e += 64) {
+    int run = part[w][e];
+    for (int c = c0; c < c1; ++c) {
+      const int64_t q = (int64_t)c * E + e;
+      const int x = counts[q];
+      counts[q] = run;
+      run += x;
+    }
+  }
+  if (w == 0) {
+    // lane owns the contiguous expert segment [lane*seg, lane*seg + seg)
+    const int seg = (N + 63) / 64;
+    const int e0 = lane * seg;
+    const int e1 = min(N, e0 + seg);
+    int sr = 0, st = 0;
+    for (int e = e0; e < e1; ++e) {
+      sr += tot[e];
+      st += (tot[e] + bm - 1) / bm;
+    }
+    int ir = sr, it = st;  // inclusive scan over lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int a = __shfl_up(ir, off), b = __shfl_up(it, off);
+      if (lane >= off) {
+        ir += a;
+        it += b;
+      }
+    }
+    int rr = ir - sr, rt = it - st;
+    for (int e = e0; e < e1; ++e) {
+      offsets[e] = rr;
+      tile_prefix[e] = rt;
+      rr += tot[e];
+      rt += (tot[e] + bm - 1) / bm;
+    }
+    if (lane == 63) {
+      offsets[N] = ir;
+      tile_prefix[N] = it;
+    }
+  }
+}
+
+hipError_t launch_scan(int32_t* counts, int C, int E, int N, int32_t* loads, int32_t* offsets,
+                       int bm, int32_t* tile_prefix, hipStream_t s) {
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, counts, C, E, N, loads, offsets, bm,
+                     tile_prefix);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Grouping.  One workgroup per token: the first K threads turn each FFN slot's
+// in-chunk rank into its grouped row offsets[e] + base[c][e] + rank, write
+// pos and perm; then the whole workgroup copies the token's row of x into
+// each of its FFN rows (x read once, 16-byte vector accesses).
+template <typename T>
+__global__ __launch_bounds__(256) void permute_kernel(const T* __restrict__ x,
+                                                      const int32_t* __restrict__ idx,
+                                                      const int32_t* __restrict__ base,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ pos,
+                                                      int32_t* __restrict__ perm,
+                                                      T* __restrict__ xp, int d, int K,
+                                                      int E, int N) {
+  __shared__ int32_t rows[kMaxTopK];
+  const int64_t t = blockIdx.x;
+  const int64_t c = t / kChunk;
+  if ((int)threadIdx.x < K) {
+    const int k = threadIdx.x;
+    const int e = idx[t * K + k];
+    int row = -1;
+    if (e < N) {
+      row = offsets[e] + base[c * E + e] + pos[t * K + k];
+      perm[row] = (int32_t)t;
+    }
+    pos[t * K + k] = row;
+    rows[k] = row;
+  }
+  __syncthreads();
+  constexpr int kVec = 16 / sizeof(T);  // elements per 16-byte access
+  const uint4* src = reinterpret_cast<const uint4*>(x + t * d);
+  for (int v = threadIdx.x; v < d / kVec; v += blockDim.x) {
+    const uint4 val = src[v];
+    for (int k = 0; k < K; ++k) {
+      const int row = rows[k];
+      if (row >= 0) reinterpret_cast<uint4*>(xp + (int64_t)row * d)[v] = val;
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_permute(const T* x, const int32_t* idx, const int32_t* chunk_base,
+                          const int32_t* offsets, int32_t* pos, int32_t* perm, T* xp,
+                          int64_t Tn, int d, int K, int E, int N, hipStream_t s) {
+  hipLaunchKernelGGL(permute_kernel<T>, dim3((unsigned)Tn), dim3(256), 0, s, x, idx, chunk_base,
+                     offsets, pos, perm, xp, d, K, E, N);
+  return hipGetLastError();
+}
+template hipError_t launch_permute<float>(const float*, const int32_t*, const int32_t*,
+                                          const int32_t*, int32_t*, int32_t*, float*, int64_t,
+                                          int, int, int, int, hipStream_t);
+template hipError_t launch_permute<bf16_t>(const bf16_t*, const int32_t*, const int32_t*,
+                                           const int32_t*, int32_t*, int32_t*, bf16_t*, int64_t,
+                                           int, int, int, int, hipStream_t);
+
+// ---------------------------------------------------------------------------
+// Combine.  One workgroup per token; y_t = r_t + sum_k g[t,k] * src_k with
+// src_k the grouped FFN output row pos[t,k] or, for a zero-computation
+// expert, x_t itself (the identity expert is never materialised).  fp32
+// accumulation in slot order, one rounding to the output type.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ x,
+                                                      const T* __restrict__ o,
+                                                      const T* __restrict__ res,
+                                                      const int32_t* __restrict__ idx,
+                                                      const float* __restrict__ gate,
+                                                      const int32_t* __restrict__ pos,
+                                                      T* __restrict__ y, int d, int K, int N) {
+  __shared__ float g_s[kMaxTopK];
+  __shared__ int32_t row_s[kMaxTopK];
+  const int64_t t = blockIdx.x;
+  if ((int)threadIdx.x < K) {
+    const int k = threadIdx.x;
+    g_s[k] = gate[t * K + k];
+    row_s[k] = (idx[t * K + k] < N) ? pos[t * K + k] : -1;
+  }
+  __syncthreads();
+  const T* xt = x + t * d;
+  for (int v = threadIdx.x; v < d / 8; v += blockDim.x) {
+    float acc[8];
+    if (res) {
+      load8(res + t * d + v * 8, acc);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    }
+    for (int k = 0; k < K; ++k) {
+      const int row = row_s[k];
+      const T* src = (row >= 0) ? o + (int64_t)row * d : xt;
+      float vals[8];
+      load8(src + v * 8, vals);
+      const float g = g_s[k];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, vals[i], acc[i]);
+    }
+    store8(y + t * d + v * 8, acc);
+  }
+}
+
+template <typename T>
+hipError_t launch_combine(const T* x, const T* o, const T* res, const int32_t* idx,
+                          const float* gate, const int32_t* pos, T* y, int64_t Tn, int d, int K,
+                          int N, hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel<T>, dim3((unsigned)Tn), dim3(256), 0, s, x, o, res, idx,
+                     gate, pos, y, d, K, N);
+  return hipGetLastError();
+}
+template hipError_t launch_combine<float>(const float*, const float*, const float*,
+                                          const int32_t*, const float*, const int32_t*, float*,
+                                          int64_t, int, int, int, hipStream_t);
+template hipError_t launch_combine<bf16_t>(const bf16_t*, const bf16_t*, const bf16_t*,
+                                           const int32_t*, const float*, const int32_t*, bf16_t*,
+                                           int64_t, int, int, int, hipStream_t);
+
+// ---------------------------------------------------------------------------
+// PID step on the expert bias (velocity form; one workgroup).
+//   e_i = (target_i - loads_i) / sum(target)
+//   bias_i += kp (e_i - e1_i) + ki e_i + kd (e_i - 2 e1_i + e2_i)
+// Sums and updates in fp64 with a fixed reduction tree; state stored in fp32.
+__global__ __launch_bounds__(1024) void pid_kernel(const int32_t* __restrict__ loads,
+                                                   const float* __restrict__ target,
+                                                   float* __restrict__ bias,
+                                                   float* __restrict__ e1,
+                                                   float* __restrict__ e2, int E, double kp,
+                                                   double ki, double kd) {
+  __shared__ double red[1024];
+  const int tid = threadIdx.x;
+  double s = 0.0;
+  for (int e = tid; e < E; e += 1024) s += (double)target[e];
+  red[tid] = s;
+  __syncthreads();
+  for (int w = 512; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  const double total = red[0];
+  for (int e = tid; e < E; e += 1024) {
+    const double err = ((double)target[e] - (double)loads[e]) / total;
+    const double p1 = (double)e1[e], p2 = (double)e2[e];
+    const double db = kp * (err - p1) + ki * err + kd * (err - 2.0 * p1 + p2);
+    bias[e] = (float)((double)bias[e] + db);
+    e2[e] = (float)p1;
+    e1[e] = (float)err;
+  }
+}
+
+hipError_t launch_pid(const int32_t* loads, const float* target, float* bias, float* e1,
+                      float* e2, int E, float kp, float ki, float kd, hipStream_t s) {
+  hipLaunchKernelGGL(pid_kernel, dim3(1), dim3(1024), 0, s, loads, target, bias, e1, e2, E,
+                     (double)kp, (double)ki, (double)kd);
+  return hipGetLastError();
+}
+
+}  // namespace moezc

@@ -1,0 +1,121 @@
+"""The C ABI library loads, exports what include/moe_zc.h declares, and its
+host-side validation paths answer without a GPU (nothing is enqueued on any
+of these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_bias_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_zc.h")
+
+F32, BF16 = _lib.MOE_ZC_F32, _lib.MOE_ZC_BF16
+OK, INVALID, WORKSPACE, UNSUPPORTED = (_lib.MOE_ZC_OK, _lib.MOE_ZC_ERR_INVALID,
+                                       _lib.MOE_ZC_ERR_WORKSPACE, _lib.MOE_ZC_ERR_UNSUPPORTED)
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_zc_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.moe_zc_abi_version() == 1
+    for code in range(5):
+        assert lib.moe_zc_status_string(code)
+    assert lib.moe_zc_status_string(99) == b"unknown status"
+
+
+def test_workspace_size_rules(lib):
+    ws = lib.moe_zc_workspace_size
+    assert ws(64, 128, 256, 8, 4, 3, F32) > 0
+    assert ws(16384, 6144, 2048, 512, 256, 12, BF16) > 5 * 10**9
+    assert ws(0, 128, 256, 8, 4, 3, F32) > 0          # T = 0 is valid
+    assert ws(64, 100, 256, 8, 4, 3, BF16) == 0        # d not a multiple of 64
+    assert ws(64, 128, 256, 8, 4, 13, BF16) == 0       # K > E
+    assert ws(64, 128, 256, 2000, 100, 3, BF16) == 0   # E > 2048
+    assert ws(64, 128, 256, 8, 4, 0, BF16) == 0        # K < 1
+    assert ws(64, 128, 256, 0, 4, 3, BF16) > 0         # N = 0 allowed
+    assert ws(-1, 128, 256, 8, 4, 3, BF16) == 0
+    a = ws(1000, 128, 256, 8, 4, 3, BF16)
+    b = ws(2000, 128, 256, 8, 4, 3, BF16)
+    assert b > a
+
+
+def _fwd(lib, T=64, d=128, I=128, N=8, Z=4, K=3, dt=BF16, x=FAKE, wr=FAKE, b=FAKE,
+         wg=FAKE, wu=FAKE, wd=FAKE, y=FAKE, ws=FAKE, nbytes=None):
+    if nbytes is None:
+        nbytes = lib.moe_zc_workspace_size(T, d, I, N, Z, K, dt)
+    return lib.moe_zc_forward(x, wr, b, wg, wu, wd, None, y, T, d, I, N, Z, K, dt, None, ws,
+                              nbytes, None)
+
+
+def test_forward_validation(lib):
+    assert _fwd(lib, T=0) == OK                               # no work, no launch
+    assert _fwd(lib, K=13) == INVALID
+    assert _fwd(lib, K=0) == INVALID
+    assert _fwd(lib, dt=7) == INVALID
+    assert _fwd(lib, N=-1) == INVALID
+    assert _fwd(lib, d=100) == UNSUPPORTED
+    assert _fwd(lib, d=100, dt=F32) == UNSUPPORTED             # f32 needs multiples of 32
+    assert _fwd(lib, N=3000, Z=4) == UNSUPPORTED
+    assert _fwd(lib, K=33, N=40) == UNSUPPORTED
+    assert _fwd(lib, x=None) == INVALID
+    assert _fwd(lib, y=None) == INVALID
+    assert _fwd(lib, wg=None) == INVALID
+    assert _fwd(lib, ws=None) == WORKSPACE
+    assert _fwd(lib, nbytes=100) == WORKSPACE
+    assert _fwd(lib, ws=ctypes.c_void_p((1 << 20) + 16)) == WORKSPACE   # not 256-aligned
+    assert _fwd(lib, x=ctypes.c_void_p((1 << 20) + 2)) == INVALID       # not 16-aligned
+
+
+def test_route_and_bias_update_validation(lib):
+    r = lib.moe_zc_route
+    assert r(FAKE, FAKE, 0, 12, 3, FAKE, FAKE, None) == OK
+    assert r(FAKE, FAKE, 10, 12, 13, FAKE, FAKE, None) == INVALID
+    assert r(FAKE, FAKE, 10, 0, 1, FAKE, FAKE, None) == INVALID
+    assert r(None, FAKE, 10, 12, 3, FAKE, FAKE, None) == INVALID
+    assert r(FAKE, FAKE, 10, 4096, 3, FAKE, FAKE, None) == UNSUPPORTED
+    u = lib.moe_zc_bias_update
+    pid = _lib.MoeZcPid(0.5, 0.5, 0.0, 1 << 20, 1 << 21)
+    assert u(FAKE, FAKE, FAKE, None, 12, None) == INVALID
+    assert u(FAKE, FAKE, FAKE, ctypes.byref(pid), 0, None) == INVALID
+    assert u(None, FAKE, FAKE, ctypes.byref(pid), 12, None) == INVALID
+    assert u(FAKE, FAKE, FAKE, ctypes.byref(pid), 5000, None) == UNSUPPORTED
+    bad = _lib.MoeZcPid(0.5, 0.5, 0.0, None, 1 << 21)
+    assert u(FAKE, FAKE, FAKE, ctypes.byref(bad), 12, None) == INVALID
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    import mixture_experts_layer_bias_amd as m
+    x = torch.zeros(4, 64)
+    with pytest.raises(ValueError):
+        m.moe_zc_forward(x, torch.zeros(3, 64), torch.zeros(3), None, None, None, 0, 3, 1)
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "mixture_experts_layer_bias_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in txt and "from oracle" not in txt, f
+                assert "oracle/" not in txt, f
