@@ -66,8 +66,9 @@ typedef enum {
 
 /* Limits of this implementation (else MOE_ZC_ERR_UNSUPPORTED):
  *   E = N + Z in [1, 2048]; K in [1, min(E, 32)];
- *   bf16: d and I multiples of 64;  f32: d and I multiples of 4;
- *   T * min(K, N) < 2^31 and T * max(d, I, E) < 2^40. */
+ *   bf16: d a multiple of 64 and I of 128;  f32: d and I multiples of 32;
+ *   d * I < 2^31, 2 * d * E < 2^31, T * min(K, N) < 2^31 and
+ *   T * max(d, I, E) < 2^40. */
 #define MOE_ZC_MAX_EXPERTS 2048
 #define MOE_ZC_MAX_TOPK 32
 

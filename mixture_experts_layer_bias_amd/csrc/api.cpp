@@ -38,8 +38,9 @@ moe_zc_status check_shape(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z,
   const int64_t E = (int64_t)N + Z;
   if (E < 1 || K > E) return MOE_ZC_ERR_INVALID;
   if (E > MOE_ZC_MAX_EXPERTS || K > MOE_ZC_MAX_TOPK) return MOE_ZC_ERR_UNSUPPORTED;
-  const int64_t mult = (dt == MOE_ZC_BF16) ? 64 : 32;
-  if (d % mult != 0 || I % mult != 0) return MOE_ZC_ERR_UNSUPPORTED;
+  if (dt == MOE_ZC_BF16 ? (d % 64 != 0 || I % 128 != 0) : (d % 32 != 0 || I % 32 != 0))
+    return MOE_ZC_ERR_UNSUPPORTED;
+  if (d * I >= (int64_t(1) << 31) || 2 * d * E >= (int64_t(1) << 31)) return MOE_ZC_ERR_UNSUPPORTED;
   const int64_t smax = T * std::min<int64_t>(K, N);
   if (smax >= (int64_t(1) << 31) || T * K >= (int64_t(1) << 31) || T >= (int64_t(1) << 31))
     return MOE_ZC_ERR_UNSUPPORTED;
@@ -52,9 +53,7 @@ moe_zc_status check_shape(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z,
   s->es = (dt == MOE_ZC_BF16) ? 2 : 4;
   if (dt == MOE_ZC_BF16) {
     const int64_t expected = (N > 0) ? (T * K) / E : 0;  // rows per expert, symmetric routing
-    int tr = mfma_tile_rows(expected);
-    if (tr == 32 && I % 128 != 0) tr = 128;
-    s->ffn_tile_rows = tr;
+    s->ffn_tile_rows = mfma_tile_rows(expected);
   } else {
     s->ffn_tile_rows = kSimtTileRows;
   }

@@ -12,6 +12,9 @@ typedef uint16_t bf16_t;  // raw bf16 storage (upper half of an fp32)
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+// 16 bytes as a native vector (HIP's uint4 is a struct whose copies become
+// memcpy through private memory, which keeps staging arrays out of registers)
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 // fp32 -> bf16, IEEE round to nearest, ties to even (NaN stays a quiet NaN).
 __device__ __host__ inline bf16_t f32_to_bf16(float f) {
