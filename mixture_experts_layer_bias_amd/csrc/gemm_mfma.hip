@@ -34,8 +34,6 @@ namespace moezc {
 
 namespace {
 
-constexpr int BK = 64;
-constexpr int LDS_STRIDE = BK + 8;  // bf16 elements per LDS row
 
 struct TileCoord {
   int g, m0, m_end, n0;
@@ -78,71 +76,130 @@ __device__ __forceinline__ bool map_tile(const GemmProblem& p, int n_tiles, int 
   return true;
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wavefront are outstanding (gfx9 encoding; other counters unchanged).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | 0x0F70 | (n & 15));
+}
+
+// Workgroup barrier for the LDS ring: this wavefront's direct loads older
+// than the newest n have landed in LDS and all its LDS reads are complete
+// (s_waitcnt vmcnt(n) lgkmcnt(0)), then s_barrier.  No memory fence: a fence
+// would wait for every load in flight and empty the ring.
+template <int n>
+__device__ __forceinline__ void ring_barrier() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | 0x0070 | (n & 15));
+  __builtin_amdgcn_s_barrier();
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// Stage geometry of the LDS ring: BKS = 64 k per stage, rows of 128 bytes
+// (eight 16-byte chunks, one full cache line per row) with no padding; chunk c
+// of row r is stored at position c ^ ((r >> 1) & 7), which makes the 16-byte
+// fragment reads of 16 consecutive rows hit distinct banks.  Global data
+// reaches LDS by direct loads (global_load_lds_dwordx4: lane l's 16 bytes
+// land at base + 16 l), so no registers stage it.  Whole-line row pieces
+// matter: half-line (64-byte) pieces stream several times slower from L2.
+constexpr int BKS = 64;
+constexpr int NSLOT = 2;       // ring slots: one stage in flight ahead of use
+constexpr int ROWB = BKS * 2;  // bytes per LDS row
+constexpr int CPR = ROWB / 16; // 16-byte chunks per row
+constexpr int RPI = 64 / CPR;  // rows filled by one direct load instruction
+
+// LDS bytes of one workgroup: the ring, or the bf16 output staging of the
+// epilogue (one padded tile per wavefront), whichever is larger.
+template <int BM, int BN, int WAVES_M, int WAVES_N>
+constexpr int smem_bytes() {
+  constexpr int ring = NSLOT * (BM + BN) * ROWB;
+  constexpr int epi = WAVES_M * WAVES_N * 32 * (BN / WAVES_N + 8) * 2;
+  return ring > epi ? ring : epi;
+}
+
 template <int EPI, int BM, int BN, int WAVES_M, int WAVES_N, int NA>
 __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& c,
-                                         bf16_t* __restrict__ As, bf16_t* __restrict__ Bs) {
-  constexpr int NT = 64 * WAVES_M * WAVES_N;
-  constexpr int WTM = BM / WAVES_M;
+                                         char* __restrict__ smem) {
+  constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WTN = BN / WAVES_N;
   constexpr int CB = WTN / 32;
   constexpr bool SWIGLU = (EPI == kSwiGLU_BF16);
   constexpr int HB = CB / 2;
-  constexpr int ROWS_PER_LD = NT / 8;           // tile rows covered by one load round
-  constexpr int A_LD = BM / ROWS_PER_LD;        // 16-byte loads per thread per stage
-  constexpr int B_LD = BN / ROWS_PER_LD;
-  constexpr int B_GATE_LD = (BN / 2) / ROWS_PER_LD;
-  constexpr int STAGE_A = BM * LDS_STRIDE, STAGE_B = BN * LDS_STRIDE;
   constexpr int NAc = NA > 0 ? NA : 1;
+  constexpr int SLOT_A = BM * ROWB, SLOT_B = BN * ROWB;  // bytes per stage
+  constexpr int SLOT = SLOT_A + SLOT_B;
+  constexpr int IA = BM / RPI, IB = BN / RPI;  // direct loads per stage
+  constexpr int DA = (IA + NW - 1) / NW;      // per wavefront (a few may repeat: same bytes)
+  constexpr int DB = (IB + NW - 1) / NW;
+  constexpr int DPS = DA + DB;                // direct loads per wavefront per stage
+  constexpr int KS = BKS / 16;                // MFMA substeps per stage
 
   const bf16_t* __restrict__ A = static_cast<const bf16_t*>(p.A);
   const bf16_t* __restrict__ B0 =
       static_cast<const bf16_t*>(p.B0) + (int64_t)c.g * p.b_group_stride;
   const bf16_t* __restrict__ B1 =
       SWIGLU ? static_cast<const bf16_t*>(p.B1) + (int64_t)c.g * p.b_group_stride : nullptr;
-
-  const int tid = threadIdx.x;
-  const int lrow = tid >> 3, lc = (tid & 7) * 8;
-  // Uniform per-tile bases (scalar registers) plus constant 32-bit byte
-  // offsets per thread, so each load is "scalar base + vector offset" and
-  // needs one vector register.  Rows past the end are clamped to a valid row;
-  // their products only reach accumulator rows that are never stored.
   const char* A_tile = reinterpret_cast<const char*>(A + (int64_t)c.m0 * p.lda);
   const char* B_gate = reinterpret_cast<const char*>(B0 + (int64_t)c.n0 * p.ldb);
   const char* B_up = SWIGLU ? reinterpret_cast<const char*>(B1 + (int64_t)c.n0 * p.ldb) : nullptr;
-  uint32_t a_off[A_LD], b_off[B_LD];
-#pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int r = min(lrow + ROWS_PER_LD * i, c.m_end - 1 - c.m0);
-    a_off[i] = (uint32_t)((r * (int)p.lda + lc) * 2);
-  }
-#pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int r = lrow + ROWS_PER_LD * i;
-    int n;
-    if (SWIGLU) n = (i < B_GATE_LD) ? r : r - BN / 2;
-    else n = min(c.n0 + r, p.Nout - 1) - c.n0;
-    b_off[i] = (uint32_t)((n * (int)p.ldb + lc) * 2);
-  }
 
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  // row block i of this wavefront starts at tile row (i * WAVES_M + wm) * 32:
-  // interleaved so a partly filled tile keeps both wavefront rows busy
-  int brow[CB];
+
+  // ---- direct-load sources: instruction t of this wavefront covers tile rows
+  // [RPI j, RPI j + RPI) with j = (wave + NW t) mod IA; lane l fills chunk
+  // position l % CPR of row RPI j + l / CPR, i.e. logical chunk
+  // (l % CPR) ^ swizzle(row).  Rows past the end are clamped to a valid row
+  // (their products only reach accumulator rows that are never stored).
+  uint32_t a_src[DA], b_src[DB];
+  int a_dst[DA], b_dst[DB];
+  bool b_up[DB];
+#pragma unroll
+  for (int t = 0; t < DA; ++t) {
+    const int j = (wave + NW * t) % IA;
+    const int r = RPI * j + lane / CPR;
+    const int lc = (lane % CPR) ^ ((r >> 1) & 7);
+    const int rr = min(r, c.m_end - 1 - c.m0);
+    a_src[t] = (uint32_t)(rr * (int)p.lda * 2 + lc * 16);
+    a_dst[t] = RPI * j * ROWB;
+  }
+#pragma unroll
+  for (int t = 0; t < DB; ++t) {
+    const int j = (wave + NW * t) % IB;
+    const int r = RPI * j + lane / CPR;
+    const int lc = (lane % CPR) ^ ((r >> 1) & 7);
+    int n;
+    if (SWIGLU) {
+      b_up[t] = r >= BN / 2;
+      n = b_up[t] ? r - BN / 2 : r;
+    } else {
+      b_up[t] = false;
+      n = min(c.n0 + r, p.Nout - 1) - c.n0;
+    }
+    b_src[t] = (uint32_t)(n * (int)p.ldb * 2 + lc * 16);
+    b_dst[t] = SLOT_A + RPI * j * ROWB;
+  }
+
+  // ---- fragment addresses (bytes within a slot) -------------------------
+  // lane l reads row (base + l % 32), logical chunk 2 ks + l / 32; bases are
+  // multiples of 32 rows, so the swizzle depends on the lane only
+  const int swz = ((lane & 31) >> 1) & 7;
+  int fr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) fr[ks] = (lane & 31) * ROWB + ((2 * ks + (lane >> 5)) ^ swz) * 16;
+  int a_row[NAc], b_row[CB];
+#pragma unroll
+  for (int i = 0; i < NAc; ++i) a_row[i] = (i * WAVES_M + wm) * 32 * ROWB;
 #pragma unroll
   for (int j = 0; j < CB; ++j) {
-    if (SWIGLU)
-      brow[j] = (j < HB) ? wn * HB * 32 + j * 32 : BN / 2 + wn * HB * 32 + (j - HB) * 32;
-    else
-      brow[j] = wn * WTN + j * 32;
+    const int br = SWIGLU ? ((j < HB) ? wn * HB * 32 + j * 32 : BN / 2 + wn * HB * 32 + (j - HB) * 32)
+                          : wn * WTN + j * 32;
+    b_row[j] = SLOT_A + br * ROWB;
   }
-  const int frag_col = (lane >> 5) * 8;
-  int a_frag[NAc], b_frag[CB];  // LDS element offsets of this lane's fragments
-#pragma unroll
-  for (int i = 0; i < NAc; ++i)
-    a_frag[i] = ((i * WAVES_M + wm) * 32 + (lane & 31)) * LDS_STRIDE + frag_col;
-#pragma unroll
-  for (int j = 0; j < CB; ++j) b_frag[j] = (brow[j] + (lane & 31)) * LDS_STRIDE + frag_col;
 
   f32x16_t acc[NAc][CB];
 #pragma unroll
@@ -151,101 +208,85 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
     for (int j = 0; j < CB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  // Two register sets stage global loads two k-steps ahead (set k & 1 holds
-  // k-step k); the k loop is unrolled by two so the set index is static (the
-  // arrays must stay in registers: no lambdas, no dynamic indexing).
-  u32x4_t ra[A_LD], rb[B_LD];
   bf16x8_t fa[2][NAc], fb[2][CB];
 
-#define MOEZC_GLOAD_A(kt)                                                            \
+  // issue the direct loads of stage kt into ring slot `slot`
+#define MOEZC_DMA(kt, slot)                                                          \
   {                                                                                  \
-    const char* a_k = A_tile + (((kt) * BK) % p.a_kwrap) * 2;                        \
-    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) ra[i] =                         \
-        *reinterpret_cast<const u32x4_t*>(a_k + a_off[i]);                           \
+    const char* a_k = A_tile + (((kt) * BKS) % p.a_kwrap) * 2;                       \
+    const char* bg_k = B_gate + (kt) * BKS * 2;                                      \
+    const char* bu_k = SWIGLU ? B_up + (kt) * BKS * 2 : bg_k;                        \
+    char* sl_ = smem + (slot) * SLOT;                                                \
+    _Pragma("unroll") for (int t = 0; t < DA; ++t) __builtin_amdgcn_global_load_lds( \
+        (glb_void_t*)(a_k + a_src[t]), (lds_void_t*)(sl_ + a_dst[t]), 16, 0, 0);     \
+    _Pragma("unroll") for (int t = 0; t < DB; ++t) __builtin_amdgcn_global_load_lds( \
+        (glb_void_t*)((b_up[t] ? bu_k : bg_k) + b_src[t]),                           \
+        (lds_void_t*)(sl_ + b_dst[t]), 16, 0, 0);                                    \
   }
-#define MOEZC_GLOAD_B(RB, kt)                                                        \
+  // fragments of substep ks (0 or 1) of the stage in ring slot `slot`
+#define MOEZC_LOADF(fs, slot, ks)                                                    \
   {                                                                                  \
-    const char* bg_k = B_gate + (kt) * BK * 2;                                       \
-    const char* bu_k = SWIGLU ? B_up + (kt) * BK * 2 : bg_k;                         \
-    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) RB[i] =                         \
-        *reinterpret_cast<const u32x4_t*>(((SWIGLU && i >= B_GATE_LD) ? bu_k : bg_k) + \
-                                          b_off[i]);                                 \
+    const char* sl_ = smem + (slot) * SLOT;                                          \
+    const int fo_ = fr[ks];                                                          \
+    _Pragma("unroll") for (int i = 0; i < NAc; ++i) fa[fs][i] =                      \
+        *reinterpret_cast<const bf16x8_t*>(sl_ + a_row[i] + fo_);                    \
+    _Pragma("unroll") for (int j = 0; j < CB; ++j) fb[fs][j] =                       \
+        *reinterpret_cast<const bf16x8_t*>(sl_ + b_row[j] + fo_);                    \
   }
-#define MOEZC_LSTORE(RB, buf)                                                    \
-  {                                                                                  \
-    bf16_t* as_w = As + (buf) * STAGE_A;                                             \
-    bf16_t* bs_w = Bs + (buf) * STAGE_B;                                             \
-    _Pragma("unroll") for (int i = 0; i < A_LD; ++i)                                 \
-        *reinterpret_cast<u32x4_t*>(&as_w[(lrow + ROWS_PER_LD * i) * LDS_STRIDE + lc]) = \
-        ra[i];                                                                       \
-    _Pragma("unroll") for (int i = 0; i < B_LD; ++i)                                 \
-        *reinterpret_cast<u32x4_t*>(&bs_w[(lrow + ROWS_PER_LD * i) * LDS_STRIDE + lc]) = \
-        RB[i];                                                                       \
-  }
-  // this lane's MFMA fragments of substep ks (16 k) into register slot sl
-#define MOEZC_LOADF(sl, as_r, bs_r, ks)                                              \
-  {                                                                                  \
-    _Pragma("unroll") for (int i = 0; i < NAc; ++i) fa[sl][i] =                      \
-        *reinterpret_cast<const bf16x8_t*>(&(as_r)[a_frag[i] + (ks) * 16]);          \
-    _Pragma("unroll") for (int j = 0; j < CB; ++j) fb[sl][j] =                       \
-        *reinterpret_cast<const bf16x8_t*>(&(bs_r)[b_frag[j] + (ks) * 16]);          \
-  }
-#define MOEZC_MMA(sl)                                                                \
+#define MOEZC_MMA(fs)                                                                \
   {                                                                                  \
     _Pragma("unroll") for (int i = 0; i < NAc; ++i)                                  \
         _Pragma("unroll") for (int j = 0; j < CB; ++j) acc[i][j] =                   \
-        __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[sl][i], fb[sl][j], acc[i][j], 0, 0, 0); \
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fs][i], fb[fs][j], acc[i][j], 0, 0, 0); \
   }
-  // One k-step.  The global loads of k-step kt+1 are issued first; substep
-  // ks then issues the fragment reads of ks+1 and its own MFMAs, so LDS
-  // latency hides under MFMA work.  Before the last substep the data of kt+1
-  // goes to the other LDS stage and the workgroup meets at its one barrier;
-  // the last substep's MFMAs then cover the first fragment reads of kt+1.
-#define MOEZC_KSTEP(kt)                                                              \
+  // Stage kt lives in slot kt % NSLOT.  Its first-substep fragments were read
+  // at the end of the previous stage.  Substep ks reads the fragments of
+  // ks+1, then runs its MFMAs.  Before the last substep the wavefront waits
+  // until its own direct loads of stage kt+1 have landed (later stages may
+  // stay in flight) and meets the others at the barrier: stage kt+1 is then
+  // complete in LDS and every wavefront is done with slot kt, which is
+  // refilled with stage kt+NSLOT.  The last substep's MFMAs then cover the
+  // first fragment reads of kt+1.
+#define MOEZC_STAGE(kt, slot)                                                        \
   {                                                                                  \
-    const int buf_ = (kt) & 1;                                                       \
-    const bf16_t* as_r = As + buf_ * STAGE_A;                                        \
-    const bf16_t* bs_r = Bs + buf_ * STAGE_B;                                        \
-    if ((kt) + 1 < nk) {                                                             \
-      MOEZC_GLOAD_B(rb, (kt) + 1);                                                   \
-      MOEZC_GLOAD_A((kt) + 1);                                                       \
-    }                                                                                \
     _Pragma("unroll") for (int ks = 0; ks + 1 < KS; ++ks) {                          \
       if (NA > 0) {                                                                  \
-        MOEZC_LOADF((ks + 1) & 1, as_r, bs_r, ks + 1);                               \
+        MOEZC_LOADF((ks + 1) & 1, slot, ks + 1);                                     \
         __builtin_amdgcn_sched_barrier(0);                                           \
         MOEZC_MMA(ks & 1);                                                           \
         __builtin_amdgcn_sched_barrier(0);                                           \
       }                                                                              \
     }                                                                                \
-    if ((kt) + 1 < nk) MOEZC_LSTORE(rb, buf_ ^ 1);                                   \
-    __syncthreads();                                                                 \
+    if (NSLOT >= 3 && (kt) + 3 < nk) ring_barrier<(NSLOT >= 3 ? (NSLOT - 2) * DPS : 0)>(); \
+    else ring_barrier<0>();                                                          \
+    if ((kt) + NSLOT < nk) MOEZC_DMA((kt) + NSLOT, slot);                            \
     if (NA > 0) {                                                                    \
-      if ((kt) + 1 < nk) MOEZC_LOADF(0, As + (buf_ ^ 1) * STAGE_A,                   \
-                                     Bs + (buf_ ^ 1) * STAGE_B, 0);                  \
+      if ((kt) + 1 < nk) MOEZC_LOADF(0, ((slot) + 1) % NSLOT, 0);                    \
       __builtin_amdgcn_sched_barrier(0);                                             \
       MOEZC_MMA((KS - 1) & 1);                                                       \
       __builtin_amdgcn_sched_barrier(0);                                             \
     }                                                                                \
   }
 
-  constexpr int KS = BK / 16;  // MFMA substeps per k-step (even)
   static_assert(KS % 2 == 0, "fragment slots alternate");
-  const int nk = p.K / BK;
-  MOEZC_GLOAD_A(0);
-  MOEZC_GLOAD_B(rb, 0);
-  MOEZC_LSTORE(rb, 0);
-  __syncthreads();
-  if (NA > 0) MOEZC_LOADF(0, As, Bs, 0);
-  for (int kt = 0; kt < nk; ++kt) MOEZC_KSTEP(kt);
-#undef MOEZC_GLOAD_A
-#undef MOEZC_GLOAD_B
-#undef MOEZC_LSTORE
+  static_assert(NSLOT == 2, "ring waits below are written for two slots");
+  const int nk = p.K / BKS;
+  MOEZC_DMA(0, 0);
+  if (nk > 1) MOEZC_DMA(1, 1);
+  if (nk > 1) ring_barrier<DPS>();
+  else ring_barrier<0>();
+  if (NA > 0) MOEZC_LOADF(0, 0, 0);
+  // unrolled by the ring depth so every slot index is a constant
+  for (int kt = 0; kt < nk; kt += NSLOT) {
+    MOEZC_STAGE(kt, 0);
+    if (kt + 1 < nk) MOEZC_STAGE(kt + 1, 1);
+  }
+#undef MOEZC_DMA
 #undef MOEZC_LOADF
 #undef MOEZC_MMA
-#undef MOEZC_KSTEP
+#undef MOEZC_STAGE
   if (NA == 0) return;
+  ring_barrier<0>();  // every wavefront is done reading the ring before it is reused
 
   // epilogue: D[i][j] of a 32x32 block sits in lane j + 32*((i/4)%2),
   // register 4*(i/8) + i%4
@@ -267,22 +308,22 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
       }
     return;
   }
-  // bf16 outputs go through a wavefront-private LDS tile so that global
-  // stores are whole 16-byte row pieces (the main loop is done with LDS:
-  // every wavefront passed the last barrier before its final MFMAs)
+  // bf16 outputs go through a wavefront-private LDS tile, one 32-row block at
+  // a time, so that global stores are whole 16-byte row pieces (every
+  // wavefront passed the barrier above, so the ring is free)
   constexpr int OC = SWIGLU ? HB * 32 : CB * 32;  // output columns of this wavefront
-  constexpr int OS = OC + 8;                      // padded LDS row
-  constexpr int RBmax = BM / WAVES_M / 32;          // same stride for every wavefront
-  bf16_t* ot = As + wave * (RBmax * 32 * OS);         // As and Bs are one LDS block
-  static_assert(WAVES_M * WAVES_N * RBmax * 32 * OS <= 2 * BM * LDS_STRIDE + 2 * BN * LDS_STRIDE,
-                "output staging must fit in the LDS stages");
+  constexpr int OS = OC + 8;                      // padded LDS row (elements)
+  bf16_t* ot = reinterpret_cast<bf16_t*>(smem) + wave * (32 * OS);
+  const int gcol0 = c.n0 + (SWIGLU ? wn * HB * 32 : wn * WTN);
+  bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.C);
+  constexpr int CH = OC / 8;  // 16-byte pieces per row
 #pragma unroll
-  for (int i = 0; i < NAc; ++i)
+  for (int i = 0; i < NAc; ++i) {
 #pragma unroll
     for (int j = 0; j < OC / 32; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = i * 32 + 8 * (v >> 2) + lrow4 + (v & 3);
+        const int r = 8 * (v >> 2) + lrow4 + (v & 3);
         float val;
         if (SWIGLU) {
           const float a = acc[i][j][v];
@@ -291,23 +332,21 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
           val = acc[i][j][v];
         }
         ot[r * OS + j * 32 + lcol] = f32_to_bf16(val);
-        // one 32x32 block at a time keeps the epilogue's live registers small
-        if (v == 15) __builtin_amdgcn_sched_barrier(0);
       }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this lane's LDS writes landed
-  __builtin_amdgcn_wave_barrier();
-  const int gcol0 = c.n0 + (SWIGLU ? wn * HB * 32 : wn * WTN);
-  bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.C);
-  constexpr int CH = OC / 8;  // 16-byte pieces per row
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS writes landed
+    __builtin_amdgcn_wave_barrier();
+    const int grow0 = c.m0 + (i * WAVES_M + wm) * 32;
 #pragma unroll
-  for (int q = lane; q < NAc * 32 * CH; q += 64) {
-    const int r = q / CH, ch = q - r * CH;
-    const int i = r >> 5;
-    const int grow = c.m0 + (i * WAVES_M + wm) * 32 + (r & 31);
-    const int gcol = gcol0 + ch * 8;
-    if (grow < c.m_end && gcol < p.Nout)
-      *reinterpret_cast<u32x4_t*>(&Cout[(int64_t)grow * p.ldc + gcol]) =
-          *reinterpret_cast<const u32x4_t*>(&ot[r * OS + ch * 8]);
+    for (int q = lane; q < 32 * CH; q += 64) {
+      const int r = q / CH, ch = q - r * CH;
+      const int grow = grow0 + r;
+      const int gcol = gcol0 + ch * 8;
+      if (grow < c.m_end && gcol < p.Nout)
+        *reinterpret_cast<u32x4_t*>(&Cout[(int64_t)grow * p.ldc + gcol]) =
+            *reinterpret_cast<const u32x4_t*>(&ot[r * OS + ch * 8]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -320,10 +359,8 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void mfma_gemm_kernel(Ge
   constexpr bool SWIGLU = (EPI == kSwiGLU_BF16);
   static_assert((BM / WAVES_M) % 32 == 0 && (BN / WAVES_N) % 32 == 0, "wave tile");
   static_assert(!SWIGLU || ((BN / WAVES_N) / 32) % 2 == 0, "SwiGLU needs gate and up blocks");
-  // one LDS block: two A stages, then two B stages (the epilogue reuses all)
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2 * (BM + BN) * LDS_STRIDE];
-  bf16_t* As = smem;
-  bf16_t* Bs = smem + 2 * BM * LDS_STRIDE;
+  // one LDS block: the ring of stages, reused by the epilogue
+  __shared__ __attribute__((aligned(16))) char smem[smem_bytes<BM, BN, WAVES_M, WAVES_N>()];
 
   // XCD-aware order: workgroup b runs on XCD b % 8; XCD x takes the logical
   // range [x * per, (x + 1) * per) of the live tiles
@@ -342,17 +379,18 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void mfma_gemm_kernel(Ge
   int na = (nb - wm + WAVES_M - 1) / WAVES_M;
   na = na < 0 ? 0 : (na > RB ? RB : na);
   switch (na) {
-    case 0: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, 0>(p, c, As, Bs); break;
-    case 1: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 1 ? 1 : 0)>(p, c, As, Bs); break;
-    case 2: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 2 ? 2 : 0)>(p, c, As, Bs); break;
-    case 3: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 3 ? 3 : 0)>(p, c, As, Bs); break;
-    default: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 4 ? 4 : 0)>(p, c, As, Bs); break;
+    case 0: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, 0>(p, c, smem); break;
+    case 1: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 1 ? 1 : 0)>(p, c, smem); break;
+    case 2: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 2 ? 2 : 0)>(p, c, smem); break;
+    case 3: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 3 ? 3 : 0)>(p, c, smem); break;
+    case 4: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 4 ? 4 : 0)>(p, c, smem); break;
+    default: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 5 ? 5 : 0)>(p, c, smem); break;
   }
 }
 
 template <int EPI, int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(const GemmProblem& p, int64_t max_rows, hipStream_t s) {
-  static_assert(BM / WM / 32 <= 4, "at most four row blocks per wavefront");
+  static_assert(BM / WM / 32 <= 5, "at most five row blocks per wavefront");
   const int n_tiles = (EPI == kSwiGLU_BF16) ? p.Nout / (BN / 2) : (p.Nout + BN - 1) / BN;
   int64_t mt_bound;
   if (p.tile_prefix) {
@@ -385,13 +423,14 @@ hipError_t launch_epi(const GemmProblem& p, int epi, int64_t max_rows, hipStream
 int mfma_tile_rows(int64_t expected_rows_per_group) {
   if (expected_rows_per_group < 48) return 32;
   if (expected_rows_per_group < 160) return 128;
-  return 256;
+  return 320;
 }
 
 hipError_t launch_mfma_gemm(const GemmProblem& p, int epilogue, int tile_rows, int64_t max_rows,
                             hipStream_t s) {
-  if (p.K % BK != 0 || p.a_kwrap % BK != 0) return hipErrorInvalidValue;
+  if (p.K % BKS != 0 || p.a_kwrap % BKS != 0) return hipErrorInvalidValue;
   if (epilogue == kSwiGLU_BF16 && tile_rows != 32 && p.Nout % 128 != 0) return hipErrorInvalidValue;
+  if (tile_rows == 320) return launch_epi<320, 256, 2, 4>(p, epilogue, max_rows, s);
   if (tile_rows == 256) return launch_epi<256, 256, 2, 4>(p, epilogue, max_rows, s);
   if (tile_rows == 128) return launch_epi<128, 256, 2, 4>(p, epilogue, max_rows, s);
   if (tile_rows == 32) return launch_epi<32, 256, 1, 4>(p, epilogue, max_rows, s);
