@@ -13,21 +13,24 @@
 //
 // Prefill shape (about 256 rows per expert, K = 6144 or 2048): a 256 x 256
 // tile per workgroup, so one workgroup holds every row of a typical expert and
-// each weight panel is streamed from HBM once while it is used 256 times; four
-// wavefronts each own a 128 x 128 block (16 MFMA blocks, 256 accumulators).
-// An expert with more rows than the tile is split into equal parts whose
-// workgroups run side by side on one XCD and so share the panel in L2.
-// Row blocks of 32 that hold no rows are skipped by the wavefront that owns
-// them (the K loop is instantiated per count of live row blocks).
+// each weight panel is streamed from HBM once while it is used 256 times.
+// Eight wavefronts in a 2 x 4 grid each own up to four 32-row blocks by two
+// 32-column MFMA blocks (128 fp32 accumulators).  An expert with more rows
+// than the tile is split into equal parts whose workgroups run side by side
+// on one XCD and so share the weight panel in L2.  Row blocks of 32 that hold
+// no rows are skipped by the wavefront that owns them (the K loop is
+// instantiated per count of live row blocks).  Decode shape (a few rows per
+// expert): 32-row tiles, one row block per wavefront.
 //
 // Tile order: expert, then weight panel, then row part.  Consecutive
 // workgroups land on different XCDs (round robin), so each XCD is handed a
 // contiguous range of this order: the workgroups of one expert run together
 // on one XCD and share its L2 for the expert's activation rows.
 //
-// Pipeline: two LDS stages of BK = 64; the global loads of step k+1 are
-// issued into registers before the MFMAs of step k.  LDS rows are padded to
-// 72 bf16 so the 16-byte fragment reads of a wavefront hit distinct banks.
+// Pipeline: stages of 64 k move from global memory straight into LDS rings
+// (direct loads, no register staging): two activation slots and up to three
+// weight slots, so up to two weight stages stream from HBM while the MFMAs
+// of the current stage run.
 #include "kernels.hpp"
 
 namespace moezc {
@@ -106,16 +109,24 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 // land at base + 16 l), so no registers stage it.  Whole-line row pieces
 // matter: half-line (64-byte) pieces stream several times slower from L2.
 constexpr int BKS = 64;
-constexpr int NSLOT = 2;       // ring slots: one stage in flight ahead of use
 constexpr int ROWB = BKS * 2;  // bytes per LDS row
 constexpr int CPR = ROWB / 16; // 16-byte chunks per row
 constexpr int RPI = 64 / CPR;  // rows filled by one direct load instruction
+constexpr int LDS_MAX = 160 * 1024;
 
-// LDS bytes of one workgroup: the ring, or the bf16 output staging of the
-// epilogue (one padded tile per wavefront), whichever is larger.
+// Two ring slots hold activation (A) stages; the weight (B) ring is as deep
+// as the LDS allows (at most three slots), so weights streamed from HBM get
+// two stages in flight where the tile leaves room.
+template <int BM, int BN>
+constexpr int b_slots() {
+  return (2 * BM + 3 * BN) * ROWB <= LDS_MAX ? 3 : 2;
+}
+
+// LDS bytes of one workgroup: the rings, or the bf16 output staging of the
+// epilogue (one padded 32-row block per wavefront), whichever is larger.
 template <int BM, int BN, int WAVES_M, int WAVES_N>
 constexpr int smem_bytes() {
-  constexpr int ring = NSLOT * (BM + BN) * ROWB;
+  constexpr int ring = (2 * BM + b_slots<BM, BN>() * BN) * ROWB;
   constexpr int epi = WAVES_M * WAVES_N * 32 * (BN / WAVES_N + 8) * 2;
   return ring > epi ? ring : epi;
 }
@@ -130,7 +141,9 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
   constexpr int HB = CB / 2;
   constexpr int NAc = NA > 0 ? NA : 1;
   constexpr int SLOT_A = BM * ROWB, SLOT_B = BN * ROWB;  // bytes per stage
-  constexpr int SLOT = SLOT_A + SLOT_B;
+  constexpr int NSA = 2, NSB = b_slots<BM, BN>();         // ring slots
+  char* const ringA = smem;
+  char* const ringB = smem + NSA * SLOT_A;
   constexpr int IA = BM / RPI, IB = BN / RPI;  // direct loads per stage
   constexpr int DA = (IA + NW - 1) / NW;      // per wavefront (a few may repeat: same bytes)
   constexpr int DB = (IB + NW - 1) / NW;
@@ -181,7 +194,7 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
       n = min(c.n0 + r, p.Nout - 1) - c.n0;
     }
     b_src[t] = (uint32_t)(n * (int)p.ldb * 2 + lc * 16);
-    b_dst[t] = SLOT_A + RPI * j * ROWB;
+    b_dst[t] = RPI * j * ROWB;
   }
 
   // ---- fragment addresses (bytes within a slot) -------------------------
@@ -198,7 +211,7 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
   for (int j = 0; j < CB; ++j) {
     const int br = SWIGLU ? ((j < HB) ? wn * HB * 32 + j * 32 : BN / 2 + wn * HB * 32 + (j - HB) * 32)
                           : wn * WTN + j * 32;
-    b_row[j] = SLOT_A + br * ROWB;
+    b_row[j] = br * ROWB;
   }
 
   f32x16_t acc[NAc][CB];
@@ -210,28 +223,34 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   bf16x8_t fa[2][NAc], fb[2][CB];
 
-  // issue the direct loads of stage kt into ring slot `slot`
-#define MOEZC_DMA(kt, slot)                                                          \
+  // issue the direct loads of stage kt: activations into A slot sa, weights
+  // into B slot sb
+#define MOEZC_DMA_A(kt, sa)                                                          \
   {                                                                                  \
     const char* a_k = A_tile + (((kt) * BKS) % p.a_kwrap) * 2;                       \
-    const char* bg_k = B_gate + (kt) * BKS * 2;                                      \
-    const char* bu_k = SWIGLU ? B_up + (kt) * BKS * 2 : bg_k;                        \
-    char* sl_ = smem + (slot) * SLOT;                                                \
+    char* sl_ = ringA + (sa) * SLOT_A;                                               \
     _Pragma("unroll") for (int t = 0; t < DA; ++t) __builtin_amdgcn_global_load_lds( \
         (glb_void_t*)(a_k + a_src[t]), (lds_void_t*)(sl_ + a_dst[t]), 16, 0, 0);     \
+  }
+#define MOEZC_DMA_B(kt, sb)                                                          \
+  {                                                                                  \
+    const char* bg_k = B_gate + (kt) * BKS * 2;                                      \
+    const char* bu_k = SWIGLU ? B_up + (kt) * BKS * 2 : bg_k;                        \
+    char* sl_ = ringB + (sb) * SLOT_B;                                               \
     _Pragma("unroll") for (int t = 0; t < DB; ++t) __builtin_amdgcn_global_load_lds( \
         (glb_void_t*)((b_up[t] ? bu_k : bg_k) + b_src[t]),                           \
         (lds_void_t*)(sl_ + b_dst[t]), 16, 0, 0);                                    \
   }
-  // fragments of substep ks (0 or 1) of the stage in ring slot `slot`
-#define MOEZC_LOADF(fs, slot, ks)                                                    \
+  // fragments of substep ks of the stage in A slot sa / B slot sb
+#define MOEZC_LOADF(fs, sa, sb, ks)                                                  \
   {                                                                                  \
-    const char* sl_ = smem + (slot) * SLOT;                                          \
+    const char* la_ = ringA + (sa) * SLOT_A;                                         \
+    const char* lb_ = ringB + (sb) * SLOT_B;                                         \
     const int fo_ = fr[ks];                                                          \
     _Pragma("unroll") for (int i = 0; i < NAc; ++i) fa[fs][i] =                      \
-        *reinterpret_cast<const bf16x8_t*>(sl_ + a_row[i] + fo_);                    \
+        *reinterpret_cast<const bf16x8_t*>(la_ + a_row[i] + fo_);                    \
     _Pragma("unroll") for (int j = 0; j < CB; ++j) fb[fs][j] =                       \
-        *reinterpret_cast<const bf16x8_t*>(sl_ + b_row[j] + fo_);                    \
+        *reinterpret_cast<const bf16x8_t*>(lb_ + b_row[j] + fo_);                    \
   }
 #define MOEZC_MMA(fs)                                                                \
   {                                                                                  \
@@ -239,29 +258,32 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
         _Pragma("unroll") for (int j = 0; j < CB; ++j) acc[i][j] =                   \
         __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fs][i], fb[fs][j], acc[i][j], 0, 0, 0); \
   }
-  // Stage kt lives in slot kt % NSLOT.  Its first-substep fragments were read
-  // at the end of the previous stage.  Substep ks reads the fragments of
-  // ks+1, then runs its MFMAs.  Before the last substep the wavefront waits
-  // until its own direct loads of stage kt+1 have landed (later stages may
-  // stay in flight) and meets the others at the barrier: stage kt+1 is then
-  // complete in LDS and every wavefront is done with slot kt, which is
-  // refilled with stage kt+NSLOT.  The last substep's MFMAs then cover the
-  // first fragment reads of kt+1.
-#define MOEZC_STAGE(kt, slot)                                                        \
+  // Stage kt lives in A slot kt % NSA and B slot kt % NSB.  Its first-substep
+  // fragments were read at the end of the previous stage.  Substep ks reads
+  // the fragments of ks+1, then runs its MFMAs.  Before the last substep the
+  // wavefront waits until its own loads of stage kt+1 have landed and meets
+  // the others at the barrier: stage kt+1 is then complete in LDS and every
+  // wavefront is done with stage kt's slots, which are refilled (A with stage
+  // kt+NSA, then B with stage kt+NSB; loads of a stage are issued in that
+  // order, so with a three-slot B ring the weights of stage kt+2 - issued
+  // after the activations of kt+1 - may stay in flight across the wait).  The
+  // last substep's MFMAs then cover the first fragment reads of kt+1.
+#define MOEZC_STAGE(kt, sa, sb)                                                      \
   {                                                                                  \
     _Pragma("unroll") for (int ks = 0; ks + 1 < KS; ++ks) {                          \
       if (NA > 0) {                                                                  \
-        MOEZC_LOADF((ks + 1) & 1, slot, ks + 1);                                     \
+        MOEZC_LOADF((ks + 1) & 1, sa, sb, ks + 1);                                   \
         __builtin_amdgcn_sched_barrier(0);                                           \
         MOEZC_MMA(ks & 1);                                                           \
         __builtin_amdgcn_sched_barrier(0);                                           \
       }                                                                              \
     }                                                                                \
-    if (NSLOT >= 3 && (kt) + 3 < nk) ring_barrier<(NSLOT >= 3 ? (NSLOT - 2) * DPS : 0)>(); \
+    if (NSB > NSA && (kt) + 2 < nk) ring_barrier<(NSB > NSA ? DB : 0)>();            \
     else ring_barrier<0>();                                                          \
-    if ((kt) + NSLOT < nk) MOEZC_DMA((kt) + NSLOT, slot);                            \
+    if ((kt) + NSA < nk) MOEZC_DMA_A((kt) + NSA, sa);                                \
+    if ((kt) + NSB < nk) MOEZC_DMA_B((kt) + NSB, sb);                                \
     if (NA > 0) {                                                                    \
-      if ((kt) + 1 < nk) MOEZC_LOADF(0, ((slot) + 1) % NSLOT, 0);                    \
+      if ((kt) + 1 < nk) MOEZC_LOADF(0, ((sa) + 1) % NSA, ((sb) + 1) % NSB, 0);      \
       __builtin_amdgcn_sched_barrier(0);                                             \
       MOEZC_MMA((KS - 1) & 1);                                                       \
       __builtin_amdgcn_sched_barrier(0);                                             \
@@ -269,19 +291,30 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
   }
 
   static_assert(KS % 2 == 0, "fragment slots alternate");
-  static_assert(NSLOT == 2, "ring waits below are written for two slots");
+  static_assert(NSA == 2 && (NSB == 2 || NSB == 3), "ring waits are written for these depths");
   const int nk = p.K / BKS;
-  MOEZC_DMA(0, 0);
-  if (nk > 1) MOEZC_DMA(1, 1);
-  if (nk > 1) ring_barrier<DPS>();
-  else ring_barrier<0>();
-  if (NA > 0) MOEZC_LOADF(0, 0, 0);
-  // unrolled by the ring depth so every slot index is a constant
-  for (int kt = 0; kt < nk; kt += NSLOT) {
-    MOEZC_STAGE(kt, 0);
-    if (kt + 1 < nk) MOEZC_STAGE(kt + 1, 1);
+  // prologue, in issue order A(0) B(0) A(1) B(1) [B(2)]
+  MOEZC_DMA_A(0, 0);
+  MOEZC_DMA_B(0, 0);
+  if (nk > 1) {
+    MOEZC_DMA_A(1, 1);
+    MOEZC_DMA_B(1, 1);
   }
-#undef MOEZC_DMA
+  if (NSB == 3 && nk > 2) MOEZC_DMA_B(2, 2);
+  // stage 0 landed; everything issued after it may stay in flight
+  if (NSB == 3 && nk > 2) ring_barrier<DA + 2 * DB>();
+  else if (nk > 1) ring_barrier<DA + DB>();
+  else ring_barrier<0>();
+  if (NA > 0) MOEZC_LOADF(0, 0, 0, 0);
+  // unrolled over lcm(NSA, NSB) stages so every slot index is a constant
+  constexpr int UNR = (NSB == 3) ? 6 : 2;
+  for (int kt = 0; kt < nk; kt += UNR) {
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+      if (kt + u < nk) MOEZC_STAGE(kt + u, u % NSA, u % NSB);
+  }
+#undef MOEZC_DMA_A
+#undef MOEZC_DMA_B
 #undef MOEZC_LOADF
 #undef MOEZC_MMA
 #undef MOEZC_STAGE
@@ -383,14 +416,13 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void mfma_gemm_kernel(Ge
     case 1: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 1 ? 1 : 0)>(p, c, smem); break;
     case 2: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 2 ? 2 : 0)>(p, c, smem); break;
     case 3: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 3 ? 3 : 0)>(p, c, smem); break;
-    case 4: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 4 ? 4 : 0)>(p, c, smem); break;
-    default: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 5 ? 5 : 0)>(p, c, smem); break;
+    default: run_tile<EPI, BM, BN, WAVES_M, WAVES_N, (RB >= 4 ? 4 : 0)>(p, c, smem); break;
   }
 }
 
 template <int EPI, int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(const GemmProblem& p, int64_t max_rows, hipStream_t s) {
-  static_assert(BM / WM / 32 <= 5, "at most five row blocks per wavefront");
+  static_assert(BM / WM / 32 <= 4, "at most four row blocks per wavefront");
   const int n_tiles = (EPI == kSwiGLU_BF16) ? p.Nout / (BN / 2) : (p.Nout + BN - 1) / BN;
   int64_t mt_bound;
   if (p.tile_prefix) {
@@ -423,14 +455,13 @@ hipError_t launch_epi(const GemmProblem& p, int epi, int64_t max_rows, hipStream
 int mfma_tile_rows(int64_t expected_rows_per_group) {
   if (expected_rows_per_group < 48) return 32;
   if (expected_rows_per_group < 160) return 128;
-  return 320;
+  return 256;
 }
 
 hipError_t launch_mfma_gemm(const GemmProblem& p, int epilogue, int tile_rows, int64_t max_rows,
                             hipStream_t s) {
   if (p.K % BKS != 0 || p.a_kwrap % BKS != 0) return hipErrorInvalidValue;
   if (epilogue == kSwiGLU_BF16 && tile_rows != 32 && p.Nout % 128 != 0) return hipErrorInvalidValue;
-  if (tile_rows == 320) return launch_epi<320, 256, 2, 4>(p, epilogue, max_rows, s);
   if (tile_rows == 256) return launch_epi<256, 256, 2, 4>(p, epilogue, max_rows, s);
   if (tile_rows == 128) return launch_epi<128, 256, 2, 4>(p, epilogue, max_rows, s);
   if (tile_rows == 32) return launch_epi<32, 256, 1, 4>(p, epilogue, max_rows, s);
