@@ -1,10 +1,13 @@
 """Benchmark of the MoE layer with zero-computation experts on one MI355X.
 
-One step = one moe_zc_forward (router GEMM, softmax + bias top-K, histogram,
-scan, permute, grouped GEMM gate/up + SwiGLU, grouped GEMM down, combine with
-the identity experts and the residual) followed by one moe_zc_bias_update
-(PID step toward uniform load) on the same stream.  Inputs are seeded and
-synthetic, resident in HBM before the timed region.
+One step = one forward of the layer (router GEMM, softmax + bias top-K,
+histogram, scan, permute, grouped GEMM gate/up + SwiGLU, grouped GEMM down,
+combine with the identity experts and the residual) followed by one
+moe_zc_bias_update (PID step toward uniform load) on the same stream.  Inputs
+are seeded and synthetic, resident in HBM before the timed region.  bf16
+expert weights are packed once at setup (moe_zc_pack_expert_weights, as at
+model load) and the step calls moe_zc_forward_packed; --layout rowmajor
+times moe_zc_forward on the row-major weights instead.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload prefill]
 
@@ -34,6 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill",
                     choices=["tiny", "mid", "decode", "prefill", "skew"])
+    ap.add_argument("--layout", default="packed", choices=["packed", "rowmajor"],
+                    help="expert weight layout of the bf16 forward")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=24,
                     help="experts the CPU-baseline sample evaluates")
@@ -43,7 +48,7 @@ def parse():
 
 
 COUNTERS_MD = os.path.join(ROOT, "profiles", "gemm_gate_up_prefill_counters.md")
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_bias_amd", "csrc", "gemm_mfma.hip")
+GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_bias_amd", "csrc", "gemm_packed.hip")
 
 
 def source_sha(path):
@@ -103,10 +108,10 @@ def algorithmic(w, S, touched, es):
     }
 
 
-def cpu_baseline(w, inp, n_experts):
+def cpu_baseline(w, inp, n_experts, weights):
     """The fp64 oracle on the host cores: routing of every token, the SwiGLU
-    experts 0..n_experts-1 with all their rows (scaled to all touched
-    experts), and the combine of every token."""
+    experts 0..n_experts-1 (``weights``: their host copies) with all their
+    rows (scaled to all touched experts), and the combine of every token."""
     import numpy as np
     import oracle
     try:
@@ -119,9 +124,7 @@ def cpu_baseline(w, inp, n_experts):
     wr = inp["w_router"].cpu()
     b = inp["bias"].cpu().numpy()
     res = inp["residual"].cpu() if inp["residual"] is not None else None
-    n_exp = min(n_experts, w.N)
-    weights = [(inp["w_gate"][e].cpu(), inp["w_up"][e].cpu(), inp["w_down"][e].cpu())
-               for e in range(n_exp)]
+    n_exp = min(n_experts, w.N, len(weights))
     t0 = time.perf_counter()
     l64 = oracle.router_logits(x, wr)
     rt = oracle.route(l64.astype(np.float32), b, w.K, w.N)
@@ -178,11 +181,27 @@ def main():
     bias = inp["bias"].clone()
     pid = m.PidState(w.E, dev, kp=0.5, ki=0.5, kd=0.0)
     target = torch.full((w.E,), w.T * w.K / w.E, dtype=torch.float32, device=dev)
+    # host copies of the experts the CPU baseline evaluates
+    n_cpu = 0 if args.no_cpu_baseline else min(args.cpu_experts, w.N)
+    cpu_weights = [(inp["w_gate"][e].cpu(), inp["w_up"][e].cpu(), inp["w_down"][e].cpu())
+                   for e in range(n_cpu)]
+    packed = args.layout == "packed" and w.dtype == "bf16"
+    if packed:
+        gu, dn = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+        torch.cuda.synchronize()
+        for k in ("w_gate", "w_up", "w_down"):
+            inp[k] = None
+        torch.cuda.empty_cache()
 
     def step(events=None):
-        m.moe_zc_forward(inp["x"], inp["w_router"], bias, inp["w_gate"], inp["w_up"],
-                         inp["w_down"], w.N, w.Z, w.K, residual=inp["residual"], out=y,
-                         aux=aux, workspace=ws, events=events)
+        if packed:
+            m.moe_zc_forward_packed(inp["x"], inp["w_router"], bias, gu, dn, w.N, w.Z, w.K, w.I,
+                                    residual=inp["residual"], out=y, aux=aux, workspace=ws,
+                                    events=events)
+        else:
+            m.moe_zc_forward(inp["x"], inp["w_router"], bias, inp["w_gate"], inp["w_up"],
+                             inp["w_down"], w.N, w.Z, w.K, residual=inp["residual"], out=y,
+                             aux=aux, workspace=ws, events=events)
         m.moe_zc_bias_update(aux["loads"], target, bias, pid)
 
     for _ in range(args.warmup):
@@ -241,7 +260,7 @@ def main():
     for k in ("chunk_hist", "scan"):
         stage_roof[k] = {"ms": round(stage[k], 4)}
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_experts)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_experts, cpu_weights)
     ffn_per_token = S / w.T
     out = {
         "metric": METRIC,
@@ -258,7 +277,10 @@ def main():
         "data": "synthetic (seeded Gaussian inputs, random-init expert weights)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "I": w.I, "N": w.N, "Z": w.Z,
                    "K": w.K, "expert_ffn": "SwiGLU", "residual": True,
-                   "step": "moe_zc_forward + moe_zc_bias_update", "parallelism": "none (1 GPU)"},
+                   "step": ("moe_zc_forward_packed" if packed else "moe_zc_forward")
+                   + " + moe_zc_bias_update",
+                   "expert_weights": "packed" if packed else "row-major",
+                   "parallelism": "none (1 GPU)"},
         "activated_tflops": flop_act / t_step / 1e12,
         "activated_mfma_frac": flop_act / t_step / PEAK_BF16,
         "grouped_gemm_mfma_frac": mfma_frac,

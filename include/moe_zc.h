@@ -67,7 +67,7 @@ typedef enum {
 /* Limits of this implementation (else MOE_ZC_ERR_UNSUPPORTED):
  *   E = N + Z in [1, 2048]; K in [1, min(E, 32)];
  *   bf16: d a multiple of 64 and I of 128;  f32: d and I multiples of 32;
- *   d * I < 2^31, 2 * d * E < 2^31, T * min(K, N) < 2^31 and
+ *   d, I < 2^20, d * I < 2^31, 2 * d * E < 2^31, T * min(K, N) < 2^31 and
  *   T * max(d, I, E) < 2^40. */
 #define MOE_ZC_MAX_EXPERTS 2048
 #define MOE_ZC_MAX_TOPK 32
@@ -136,6 +136,53 @@ moe_zc_status moe_zc_forward(const void* x, const float* w_router,
                              int32_t K, moe_zc_dtype dt, moe_zc_aux* aux,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/* ---- packed expert weights (bf16) ------------------------------------------
+ * The bf16 expert GEMMs stream every expert's weights from HBM once per
+ * forward; they run fastest when those weights sit in the order the matrix
+ * cores consume them.  Pack them once, when the model is loaded, with
+ * moe_zc_pack_expert_weights, then call moe_zc_forward_packed: it computes
+ * exactly what moe_zc_forward computes on the row-major weights (bitwise
+ * equal outputs), only faster.  The packed layout is opaque; its size per
+ * expert comes from moe_zc_packed_expert_bytes.  Expert e's packed weights
+ * start at byte e * gate_up_bytes (resp. e * down_bytes), so a model can be
+ * packed expert by expert into offset pointers. */
+
+/* Bytes of ONE expert's packed weights: *gate_up_bytes for the gate and up
+ * projections together (4 d I), *down_bytes for the down projection
+ * (2 I * d rounded up to a multiple of 256 rows).  dt must be MOE_ZC_BF16
+ * (MOE_ZC_ERR_UNSUPPORTED for MOE_ZC_F32); d and I follow the limits of
+ * moe_zc_forward.  Host only. */
+moe_zc_status moe_zc_packed_expert_bytes(int64_t d, int64_t I, moe_zc_dtype dt,
+                                         size_t* gate_up_bytes,
+                                         size_t* down_bytes);
+
+/* Pack n_experts experts (device pointers, bf16, row-major as taken by
+ * moe_zc_forward):
+ *   w_gate, w_up [n_experts, I, d],  w_down [n_experts, d, I]
+ * into gate_up_packed (n_experts * gate_up_bytes) and down_packed
+ * (n_experts * down_bytes), all 16-byte aligned and owned by the caller.
+ * Enqueued on `stream`; reads the inputs once.  n_experts = 0 does nothing. */
+moe_zc_status moe_zc_pack_expert_weights(const void* w_gate, const void* w_up,
+                                         const void* w_down, int32_t n_experts,
+                                         int64_t d, int64_t I, moe_zc_dtype dt,
+                                         void* gate_up_packed, void* down_packed,
+                                         hipStream_t stream);
+
+/* moe_zc_forward with the FFN expert weights packed by
+ * moe_zc_pack_expert_weights (gate_up_packed, down_packed: N experts each;
+ * NULL allowed when N = 0).  bf16 only (MOE_ZC_ERR_UNSUPPORTED otherwise);
+ * every other argument, the workspace size and the outputs are those of
+ * moe_zc_forward. */
+moe_zc_status moe_zc_forward_packed(const void* x, const float* w_router,
+                                    const float* bias,
+                                    const void* gate_up_packed,
+                                    const void* down_packed,
+                                    const void* residual, void* y, int64_t T,
+                                    int64_t d, int64_t I, int32_t N, int32_t Z,
+                                    int32_t K, moe_zc_dtype dt, moe_zc_aux* aux,
+                                    void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
 
 /* Routing alone, from given fp32 logits [T, E] and bias [E]: the softmax,
  * bias key and top-K step of the forward, bit for bit.

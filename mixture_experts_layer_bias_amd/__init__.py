@@ -6,7 +6,7 @@ package is its thin Python binding.
 """
 from .api import (  # noqa: F401
     AUX_KEYS, MoeZcError, PidState, StageEvents, alloc_aux, moe_zc_abi_version,
-    moe_zc_bias_update, moe_zc_forward, moe_zc_route, moe_zc_status_string,
-    moe_zc_workspace_size,
+    moe_zc_bias_update, moe_zc_forward, moe_zc_forward_packed, moe_zc_pack_expert_weights,
+    moe_zc_packed_expert_bytes, moe_zc_route, moe_zc_status_string, moe_zc_workspace_size,
 )
 from ._lib import LIB_PATH, STAGE_NAMES  # noqa: F401

@@ -20,7 +20,8 @@ STAGE_NAMES = ("router_gemm", "softmax_topk", "chunk_hist", "scan", "permute",
                "gemm_gate_up_swiglu", "gemm_down", "combine")
 
 # every symbol include/moe_zc.h declares
-EXPORTS = ("moe_zc_workspace_size", "moe_zc_forward", "moe_zc_route",
+EXPORTS = ("moe_zc_workspace_size", "moe_zc_forward", "moe_zc_packed_expert_bytes",
+           "moe_zc_pack_expert_weights", "moe_zc_forward_packed", "moe_zc_route",
            "moe_zc_bias_update", "moe_zc_status_string", "moe_zc_abi_version")
 
 
@@ -56,6 +57,15 @@ def load() -> ctypes.CDLL:
     lib.moe_zc_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
                                    i32, ctypes.c_int, ctypes.POINTER(MoeZcAux), vp, sz, vp]
     lib.moe_zc_forward.restype = ctypes.c_int
+    lib.moe_zc_packed_expert_bytes.argtypes = [i64, i64, ctypes.c_int, ctypes.POINTER(sz),
+                                               ctypes.POINTER(sz)]
+    lib.moe_zc_packed_expert_bytes.restype = ctypes.c_int
+    lib.moe_zc_pack_expert_weights.argtypes = [vp, vp, vp, i32, i64, i64, ctypes.c_int, vp, vp,
+                                               vp]
+    lib.moe_zc_pack_expert_weights.restype = ctypes.c_int
+    lib.moe_zc_forward_packed.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
+                                          i32, ctypes.c_int, ctypes.POINTER(MoeZcAux), vp, sz, vp]
+    lib.moe_zc_forward_packed.restype = ctypes.c_int
     lib.moe_zc_route.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
     lib.moe_zc_route.restype = ctypes.c_int
     lib.moe_zc_bias_update.argtypes = [vp, vp, vp, ctypes.POINTER(MoeZcPid), i32, vp]

@@ -119,46 +119,29 @@ class StageEvents:
             pass
 
 
-def moe_zc_forward(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
-                   w_gate: Optional[torch.Tensor], w_up: Optional[torch.Tensor],
-                   w_down: Optional[torch.Tensor], N: int, Z: int, K: int,
-                   residual: Optional[torch.Tensor] = None,
-                   out: Optional[torch.Tensor] = None,
-                   aux: Optional[Dict[str, torch.Tensor]] = None,
-                   workspace: Optional[torch.Tensor] = None,
-                   events: Optional[StageEvents] = None) -> torch.Tensor:
-    """y = MoE-ZC(x) (+ residual); see include/moe_zc.h for the definition."""
+def _forward(name: str, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
+             weights, N: int, Z: int, K: int, I: int, residual, out, aux, workspace, events):
+    """Shared marshalling of moe_zc_forward and moe_zc_forward_packed;
+    ``weights`` are the already checked weight tensors (or None)."""
     lib = _lib.load()
-    if x.dim() != 2:
-        raise ValueError("x must be [T, d]")
     T, d = x.shape
     dev = x.device
-    if dev.type != "cuda":
-        raise ValueError("x must be a GPU tensor")
     dt = x.dtype
-    if dt not in _DT:
-        raise ValueError(f"unsupported dtype {dt}")
     E = N + Z
-    _need(x, "x", dt, (T, d), dev)
     _need(w_router, "w_router", torch.float32, (E, d), dev)
     _need(bias, "bias", torch.float32, (E,), dev)
-    if N > 0:
-        I = w_gate.shape[1]
-        _need(w_gate, "w_gate", dt, (N, I, d), dev)
-        _need(w_up, "w_up", dt, (N, I, d), dev)
-        _need(w_down, "w_down", dt, (N, d, I), dev)
-    else:
-        I = w_gate.shape[1] if w_gate is not None else 64
     if residual is not None:
         _need(residual, "residual", dt, (T, d), dev)
     if out is None:
         out = torch.empty(T, d, dtype=dt, device=dev)
     _need(out, "out", dt, (T, d), dev)
+    fn = getattr(lib, name)
+    nulls = [None] * len(weights)
     need = moe_zc_workspace_size(T, d, I, N, Z, K, dt)
     if need == 0:
-        code = lib.moe_zc_forward(None, None, None, None, None, None, None, None, T, d, I, N, Z,
-                                  K, _DT[dt], None, None, 0, None)
-        raise MoeZcError(code, "moe_zc_forward")
+        code = fn(None, None, None, *nulls, None, None, T, d, I, N, Z, K, _DT[dt], None, None, 0,
+                  None)
+        raise MoeZcError(code, name)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
@@ -173,14 +156,109 @@ def moe_zc_forward(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
             setattr(a, k, t.data_ptr())
     if events is not None:
         a.stage_events = ctypes.cast(events.array, ctypes.c_void_p).value
-    code = lib.moe_zc_forward(
-        _ptr(x), _ptr(w_router), _ptr(bias), _ptr(w_gate) if N > 0 else None,
-        _ptr(w_up) if N > 0 else None, _ptr(w_down) if N > 0 else None, _ptr(residual),
-        _ptr(out), T, d, I, N, Z, K, _DT[dt], ctypes.byref(a), _ptr(workspace),
-        workspace.numel(), _stream(dev))
+    code = fn(_ptr(x), _ptr(w_router), _ptr(bias), *[_ptr(w) for w in weights], _ptr(residual),
+              _ptr(out), T, d, I, N, Z, K, _DT[dt], ctypes.byref(a), _ptr(workspace),
+              workspace.numel(), _stream(dev))
     if code != _lib.MOE_ZC_OK:
-        raise MoeZcError(code, "moe_zc_forward")
+        raise MoeZcError(code, name)
     return out
+
+
+def _check_x(x: torch.Tensor):
+    if x.dim() != 2:
+        raise ValueError("x must be [T, d]")
+    if x.device.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    if x.dtype not in _DT:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    _need(x, "x", x.dtype, tuple(x.shape), x.device)
+
+
+def moe_zc_forward(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
+                   w_gate: Optional[torch.Tensor], w_up: Optional[torch.Tensor],
+                   w_down: Optional[torch.Tensor], N: int, Z: int, K: int,
+                   residual: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None,
+                   aux: Optional[Dict[str, torch.Tensor]] = None,
+                   workspace: Optional[torch.Tensor] = None,
+                   events: Optional[StageEvents] = None) -> torch.Tensor:
+    """y = MoE-ZC(x) (+ residual); see include/moe_zc.h for the definition."""
+    _check_x(x)
+    T, d = x.shape
+    dev, dt = x.device, x.dtype
+    if N > 0:
+        I = w_gate.shape[1]
+        _need(w_gate, "w_gate", dt, (N, I, d), dev)
+        _need(w_up, "w_up", dt, (N, I, d), dev)
+        _need(w_down, "w_down", dt, (N, d, I), dev)
+        weights = (w_gate, w_up, w_down)
+    else:
+        I = w_gate.shape[1] if w_gate is not None else 128
+        weights = (None, None, None)
+    return _forward("moe_zc_forward", x, w_router, bias, weights, N, Z, K, I, residual, out, aux,
+                    workspace, events)
+
+
+def moe_zc_packed_expert_bytes(d: int, I: int, dtype=torch.bfloat16):
+    """(gate_up_bytes, down_bytes) of one expert's packed weights."""
+    gu, dn = ctypes.c_size_t(), ctypes.c_size_t()
+    code = _lib.load().moe_zc_packed_expert_bytes(d, I, _dtype_code(dtype), ctypes.byref(gu),
+                                                  ctypes.byref(dn))
+    if code != _lib.MOE_ZC_OK:
+        raise MoeZcError(code, "moe_zc_packed_expert_bytes")
+    return int(gu.value), int(dn.value)
+
+
+def moe_zc_pack_expert_weights(w_gate: torch.Tensor, w_up: torch.Tensor, w_down: torch.Tensor,
+                               gate_up_packed: Optional[torch.Tensor] = None,
+                               down_packed: Optional[torch.Tensor] = None):
+    """Pack row-major bf16 expert weights ([n, I, d], [n, I, d], [n, d, I]) for
+    moe_zc_forward_packed; returns (gate_up_packed, down_packed), uint8
+    tensors of n * gate_up_bytes and n * down_bytes."""
+    lib = _lib.load()
+    n, I, d = w_gate.shape
+    dev, dt = w_gate.device, w_gate.dtype
+    if dev.type != "cuda":
+        raise ValueError("weights must be GPU tensors")
+    _need(w_gate, "w_gate", torch.bfloat16, (n, I, d), dev)
+    _need(w_up, "w_up", torch.bfloat16, (n, I, d), dev)
+    _need(w_down, "w_down", torch.bfloat16, (n, d, I), dev)
+    gu, dn = moe_zc_packed_expert_bytes(d, I, dt)
+    if gate_up_packed is None:
+        gate_up_packed = torch.empty(n * gu, dtype=torch.uint8, device=dev)
+    if down_packed is None:
+        down_packed = torch.empty(n * dn, dtype=torch.uint8, device=dev)
+    _need(gate_up_packed, "gate_up_packed", torch.uint8, (n * gu,), dev)
+    _need(down_packed, "down_packed", torch.uint8, (n * dn,), dev)
+    code = lib.moe_zc_pack_expert_weights(_ptr(w_gate), _ptr(w_up), _ptr(w_down), n, d, I,
+                                          _DT[dt], _ptr(gate_up_packed), _ptr(down_packed),
+                                          _stream(dev))
+    if code != _lib.MOE_ZC_OK:
+        raise MoeZcError(code, "moe_zc_pack_expert_weights")
+    return gate_up_packed, down_packed
+
+
+def moe_zc_forward_packed(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
+                          gate_up_packed: Optional[torch.Tensor],
+                          down_packed: Optional[torch.Tensor], N: int, Z: int, K: int, I: int,
+                          residual: Optional[torch.Tensor] = None,
+                          out: Optional[torch.Tensor] = None,
+                          aux: Optional[Dict[str, torch.Tensor]] = None,
+                          workspace: Optional[torch.Tensor] = None,
+                          events: Optional[StageEvents] = None) -> torch.Tensor:
+    """moe_zc_forward on weights packed by moe_zc_pack_expert_weights (bf16)."""
+    _check_x(x)
+    T, d = x.shape
+    dev = x.device
+    if N > 0:
+        gu, dn = moe_zc_packed_expert_bytes(d, I, x.dtype)
+        _need(gate_up_packed, "gate_up_packed", torch.uint8, (N * gu,), dev)
+        _need(down_packed, "down_packed", torch.uint8, (N * dn,), dev)
+        weights = (gate_up_packed, down_packed)
+    else:
+        weights = (None, None)
+    return _forward("moe_zc_forward_packed", x, w_router, bias, weights, N, Z, K, I, residual,
+                    out, aux, workspace, events)
 
 
 def moe_zc_route(logits: torch.Tensor, bias: torch.Tensor, K: int,

@@ -46,7 +46,8 @@ moe_zc_status check_shape(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z,
     return MOE_ZC_ERR_UNSUPPORTED;
   const int64_t widest = std::max<int64_t>(std::max<int64_t>(d, I), E);
   if (T > 0 && widest > (int64_t(1) << 40) / T) return MOE_ZC_ERR_UNSUPPORTED;
-  if (d >= (int64_t(1) << 24) || I >= (int64_t(1) << 24)) return MOE_ZC_ERR_UNSUPPORTED;
+  // 32-bit byte offsets of up to 256 rows inside a GEMM tile
+  if (d >= (int64_t(1) << 20) || I >= (int64_t(1) << 20)) return MOE_ZC_ERR_UNSUPPORTED;
   s->T = T; s->d = d; s->I = I; s->N = N; s->Z = Z; s->K = K; s->E = (int32_t)E; s->dt = dt;
   s->smax = smax;
   s->chunks = (T + kChunk - 1) / kChunk;
@@ -81,7 +82,7 @@ Plan make_plan(const Shape& s) {
   p.perm = take((size_t)std::max<int64_t>(s.smax, 1) * 4);
   p.counts = take((size_t)s.chunks * s.E * 4);
   p.tiles = take((size_t)(s.N + 1) * 4);
-  p.wr2 = take(s.dt == MOE_ZC_BF16 ? (size_t)s.E * 2 * s.d * 2 : 0);
+  p.wr2 = take(s.dt == MOE_ZC_BF16 ? (size_t)packed_bytes(s.E, 2 * s.d, false) : 0);
   p.xp = take((size_t)s.smax * s.d * s.es);
   p.h = take((size_t)s.smax * s.I * s.es);
   p.o = take((size_t)s.smax * s.d * s.es);
@@ -94,44 +95,34 @@ Plan make_plan(const Shape& s) {
     if ((expr) != hipSuccess) return MOE_ZC_ERR_HIP; \
   } while (0)
 
-}  // namespace
-
-extern "C" {
-
-int32_t moe_zc_abi_version(void) { return MOE_ZC_ABI_VERSION; }
-
-const char* moe_zc_status_string(moe_zc_status s) {
-  switch (s) {
-    case MOE_ZC_OK: return "ok";
-    case MOE_ZC_ERR_INVALID: return "invalid argument";
-    case MOE_ZC_ERR_WORKSPACE: return "workspace missing or too small";
-    case MOE_ZC_ERR_UNSUPPORTED: return "sizes outside what the kernels support";
-    case MOE_ZC_ERR_HIP: return "HIP launch or runtime error";
-  }
-  return "unknown status";
+// Rows per router tile: enough tiles to cover the 256 CUs once where T allows
+// (the router is one group of T rows by E columns in 256-column panels).
+int router_tile_rows(int64_t T, int E) {
+  const int64_t panels = (E + kPackedPanel - 1) / kPackedPanel;
+  const int64_t tiles_m = std::max<int64_t>(1, 256 / panels);
+  int64_t rows = (T + tiles_m - 1) / tiles_m;
+  rows = (rows + 31) / 32 * 32;
+  return (int)std::min<int64_t>(std::max<int64_t>(rows, 32), kPackedMaxTileRows);
 }
 
-size_t moe_zc_workspace_size(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z, int32_t K,
-                             moe_zc_dtype dt) {
-  Shape s;
-  if (check_shape(T, d, I, N, Z, K, dt, &s) != MOE_ZC_OK) return 0;
-  return make_plan(s).total;
-}
-
-moe_zc_status moe_zc_forward(const void* x, const float* w_router, const float* bias,
-                             const void* w_gate, const void* w_up, const void* w_down,
-                             const void* residual, void* y, int64_t T, int64_t d, int64_t I,
-                             int32_t N, int32_t Z, int32_t K, moe_zc_dtype dt, moe_zc_aux* aux,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// The forward on either weight layout (packed: bf16 expert weights as
+// written by moe_zc_pack_expert_weights; gate_up and down then point there).
+moe_zc_status forward_impl(const void* x, const float* w_router, const float* bias,
+                           const void* w_gate, const void* w_up, const void* w_down,
+                           bool packed, const void* residual, void* y, int64_t T, int64_t d,
+                           int64_t I, int32_t N, int32_t Z, int32_t K, moe_zc_dtype dt,
+                           moe_zc_aux* aux, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
   Shape s;
   const moe_zc_status st = check_shape(T, d, I, N, Z, K, dt, &s);
   if (st != MOE_ZC_OK) return st;
+  if (packed && dt != MOE_ZC_BF16) return MOE_ZC_ERR_UNSUPPORTED;
   if (T == 0) return MOE_ZC_OK;
   if (!x || !w_router || !bias || !y) return MOE_ZC_ERR_INVALID;
-  if (N > 0 && (!w_gate || !w_up || !w_down)) return MOE_ZC_ERR_INVALID;
+  if (N > 0 && (!w_gate || !w_down || (!packed && !w_up))) return MOE_ZC_ERR_INVALID;
   if (!aligned16(x) || !aligned16(y) || !aligned16(w_router) || (residual && !aligned16(residual)))
     return MOE_ZC_ERR_INVALID;
-  if (N > 0 && (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down)))
+  if (N > 0 && (!aligned16(w_gate) || !aligned16(w_down) || (!packed && !aligned16(w_up))))
     return MOE_ZC_ERR_INVALID;
   const Plan pl = make_plan(s);
   if (!workspace || workspace_bytes < pl.total) return MOE_ZC_ERR_WORKSPACE;
@@ -166,9 +157,9 @@ moe_zc_status moe_zc_forward(const void* x, const float* w_router, const float* 
     p.G = 1; p.M = (int)T;
     if (bf) {
       bf16_t* wr2 = reinterpret_cast<bf16_t*>(ws + pl.wr2);
-      MOE_ZC_TRY(launch_split_router(w_router, wr2, E, (int)d, stream));
-      p.B0 = wr2; p.ldb = 2 * d; p.K = (int)(2 * d);
-      MOE_ZC_TRY(launch_mfma_gemm(p, kStoreF32, 128, T, stream));
+      MOE_ZC_TRY(launch_split_router_packed(w_router, wr2, E, (int)d, stream));
+      p.B0 = wr2; p.K = (int)(2 * d);
+      MOE_ZC_TRY(launch_packed_gemm(p, kStoreF32, router_tile_rows(T, E), T, stream));
     } else {
       p.B0 = w_router; p.ldb = d; p.K = (int)d;
       MOE_ZC_TRY(launch_simt_gemm(p, kStoreF32, T, stream));
@@ -200,7 +191,9 @@ moe_zc_status moe_zc_forward(const void* x, const float* w_router, const float* 
     p.B0 = w_gate; p.B1 = w_up; p.ldb = d; p.b_group_stride = I * d;
     p.C = h; p.ldc = I; p.Nout = (int)I;
     p.row_offsets = offsets; p.tile_prefix = tiles; p.G = N; p.M = 0;
-    if (bf)
+    if (packed)
+      MOE_ZC_TRY(launch_packed_gemm(p, kSwiGLU_BF16, s.ffn_tile_rows, s.smax, stream));
+    else if (bf)
       MOE_ZC_TRY(launch_mfma_gemm(p, kSwiGLU_BF16, s.ffn_tile_rows, s.smax, stream));
     else
       MOE_ZC_TRY(launch_simt_gemm(p, kSwiGLU_F32, s.smax, stream));
@@ -212,7 +205,9 @@ moe_zc_status moe_zc_forward(const void* x, const float* w_router, const float* 
     p.B0 = w_down; p.ldb = I; p.b_group_stride = d * I;
     p.C = o; p.ldc = d; p.Nout = (int)d;
     p.row_offsets = offsets; p.tile_prefix = tiles; p.G = N; p.M = 0;
-    if (bf)
+    if (packed)
+      MOE_ZC_TRY(launch_packed_gemm(p, kStoreBF16, s.ffn_tile_rows, s.smax, stream));
+    else if (bf)
       MOE_ZC_TRY(launch_mfma_gemm(p, kStoreBF16, s.ffn_tile_rows, s.smax, stream));
     else
       MOE_ZC_TRY(launch_simt_gemm(p, kStoreF32, s.smax, stream));
@@ -228,6 +223,90 @@ moe_zc_status moe_zc_forward(const void* x, const float* w_router, const float* 
                                      static_cast<const float*>(residual), idx, gate, pos,
                                      static_cast<float*>(y), T, (int)d, K, N, stream));
   MOE_ZC_TRY(mark(8));
+  return MOE_ZC_OK;
+}
+
+// Shape checks of the packing entry points (bf16 only; the forward's limits).
+moe_zc_status check_pack_shape(int64_t d, int64_t I, moe_zc_dtype dt) {
+  if (dt != MOE_ZC_F32 && dt != MOE_ZC_BF16) return MOE_ZC_ERR_INVALID;
+  if (d <= 0 || I <= 0) return MOE_ZC_ERR_INVALID;
+  if (dt != MOE_ZC_BF16) return MOE_ZC_ERR_UNSUPPORTED;
+  Shape s;
+  return check_shape(0, d, I, 1, 0, 1, dt, &s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_zc_abi_version(void) { return MOE_ZC_ABI_VERSION; }
+
+const char* moe_zc_status_string(moe_zc_status s) {
+  switch (s) {
+    case MOE_ZC_OK: return "ok";
+    case MOE_ZC_ERR_INVALID: return "invalid argument";
+    case MOE_ZC_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ZC_ERR_UNSUPPORTED: return "sizes outside what the kernels support";
+    case MOE_ZC_ERR_HIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+size_t moe_zc_workspace_size(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z, int32_t K,
+                             moe_zc_dtype dt) {
+  Shape s;
+  if (check_shape(T, d, I, N, Z, K, dt, &s) != MOE_ZC_OK) return 0;
+  return make_plan(s).total;
+}
+
+moe_zc_status moe_zc_forward(const void* x, const float* w_router, const float* bias,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             const void* residual, void* y, int64_t T, int64_t d, int64_t I,
+                             int32_t N, int32_t Z, int32_t K, moe_zc_dtype dt, moe_zc_aux* aux,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return forward_impl(x, w_router, bias, w_gate, w_up, w_down, false, residual, y, T, d, I, N, Z,
+                      K, dt, aux, workspace, workspace_bytes, stream);
+}
+
+moe_zc_status moe_zc_forward_packed(const void* x, const float* w_router, const float* bias,
+                                    const void* gate_up_packed, const void* down_packed,
+                                    const void* residual, void* y, int64_t T, int64_t d,
+                                    int64_t I, int32_t N, int32_t Z, int32_t K, moe_zc_dtype dt,
+                                    moe_zc_aux* aux, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  return forward_impl(x, w_router, bias, gate_up_packed, nullptr, down_packed, true, residual, y,
+                      T, d, I, N, Z, K, dt, aux, workspace, workspace_bytes, stream);
+}
+
+moe_zc_status moe_zc_packed_expert_bytes(int64_t d, int64_t I, moe_zc_dtype dt,
+                                         size_t* gate_up_bytes, size_t* down_bytes) {
+  if (!gate_up_bytes || !down_bytes) return MOE_ZC_ERR_INVALID;
+  const moe_zc_status st = check_pack_shape(d, I, dt);
+  if (st != MOE_ZC_OK) return st;
+  *gate_up_bytes = (size_t)packed_bytes(I, d, true);
+  *down_bytes = (size_t)packed_bytes(d, I, false);
+  return MOE_ZC_OK;
+}
+
+moe_zc_status moe_zc_pack_expert_weights(const void* w_gate, const void* w_up,
+                                         const void* w_down, int32_t n_experts, int64_t d,
+                                         int64_t I, moe_zc_dtype dt, void* gate_up_packed,
+                                         void* down_packed, hipStream_t stream) {
+  const moe_zc_status st = check_pack_shape(d, I, dt);
+  if (st != MOE_ZC_OK) return st;
+  if (n_experts < 0) return MOE_ZC_ERR_INVALID;
+  if (n_experts == 0) return MOE_ZC_OK;
+  if (!w_gate || !w_up || !w_down || !gate_up_packed || !down_packed) return MOE_ZC_ERR_INVALID;
+  if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(gate_up_packed) ||
+      !aligned16(down_packed))
+    return MOE_ZC_ERR_INVALID;
+  MOE_ZC_TRY(launch_pack_weights(static_cast<const bf16_t*>(w_gate),
+                                 static_cast<const bf16_t*>(w_up),
+                                 static_cast<bf16_t*>(gate_up_packed), n_experts, (int)I, (int)d,
+                                 true, stream));
+  MOE_ZC_TRY(launch_pack_weights(static_cast<const bf16_t*>(w_down), nullptr,
+                                 static_cast<bf16_t*>(down_packed), n_experts, (int)d, (int)I,
+                                 false, stream));
   return MOE_ZC_OK;
 }
 

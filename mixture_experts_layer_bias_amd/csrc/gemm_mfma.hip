@@ -31,75 +31,11 @@
 // (direct loads, no register staging): two activation slots and up to three
 // weight slots, so up to two weight stages stream from HBM while the MFMAs
 // of the current stage run.
-#include "kernels.hpp"
+#include "gemm_tile.hpp"
 
 namespace moezc {
 
 namespace {
-
-
-struct TileCoord {
-  int g, m0, m_end, n0;
-};
-
-// Logical tile -> (group, rows, output columns).  Returns false past the end.
-template <int BM, int BN, bool SWIGLU>
-__device__ __forceinline__ bool map_tile(const GemmProblem& p, int n_tiles, int logical,
-                                         TileCoord& c) {
-  if (p.tile_prefix) {
-    const int total = p.tile_prefix[p.G] * n_tiles;
-    if (logical >= total) return false;
-    const int mt_all = logical / n_tiles;  // only to find the group
-    int lo = 0, hi = p.G;  // tile_prefix[lo] <= mt_all < tile_prefix[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.tile_prefix[mid] <= mt_all) lo = mid; else hi = mid;
-    }
-    const int g = lo;
-    const int mtc = p.tile_prefix[g + 1] - p.tile_prefix[g];
-    const int local = logical - p.tile_prefix[g] * n_tiles;
-    const int nt = local / mtc;
-    const int mt = local - nt * mtc;
-    const int r0 = p.row_offsets[g], r1 = p.row_offsets[g + 1];
-    const int rpt = (r1 - r0 + mtc - 1) / mtc;  // equal parts
-    c.g = g;
-    c.m0 = r0 + mt * rpt;
-    c.m_end = min(c.m0 + rpt, r1);
-    c.n0 = SWIGLU ? nt * (BN / 2) : nt * BN;
-  } else {
-    const int mtiles = (p.M + BM - 1) / BM;
-    if (logical >= mtiles * n_tiles) return false;
-    const int nt = logical / mtiles;
-    const int mt = logical - nt * mtiles;
-    c.g = 0;
-    c.m0 = mt * BM;
-    c.m_end = min(c.m0 + BM, p.M);
-    c.n0 = SWIGLU ? nt * (BN / 2) : nt * BN;
-  }
-  return true;
-}
-
-// s_waitcnt immediate that waits until at most n vector-memory operations of
-// this wavefront are outstanding (gfx9 encoding; other counters unchanged).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | 0x0F70 | (n & 15));
-}
-
-// Workgroup barrier for the LDS ring: this wavefront's direct loads older
-// than the newest n have landed in LDS and all its LDS reads are complete
-// (s_waitcnt vmcnt(n) lgkmcnt(0)), then s_barrier.  No memory fence: a fence
-// would wait for every load in flight and empty the ring.
-template <int n>
-__device__ __forceinline__ void ring_barrier() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | 0x0070 | (n & 15));
-  __builtin_amdgcn_s_barrier();
-}
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
 
 // Stage geometry of the LDS ring: BKS = 64 k per stage, rows of 128 bytes
 // (eight 16-byte chunks, one full cache line per row) with no padding; chunk c
@@ -395,15 +331,10 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void mfma_gemm_kernel(Ge
   // one LDS block: the ring of stages, reused by the epilogue
   __shared__ __attribute__((aligned(16))) char smem[smem_bytes<BM, BN, WAVES_M, WAVES_N>()];
 
-  // XCD-aware order: workgroup b runs on XCD b % 8; XCD x takes the logical
-  // range [x * per, (x + 1) * per) of the live tiles
-  const int total = p.tile_prefix ? p.tile_prefix[p.G] * n_tiles : total_bound;
-  const int per = (total + 7) >> 3;
-  const int jx = blockIdx.x >> 3;
-  if (jx >= per) return;
-  const int logical = (blockIdx.x & 7) * per + jx;
+  const int logical = xcd_logical_tile(p.tile_prefix ? p.tile_prefix[p.G] * n_tiles : total_bound);
+  if (logical < 0) return;
   TileCoord c;
-  if (!map_tile<BM, BN, SWIGLU>(p, n_tiles, logical, c)) return;
+  if (!map_tile<BN, SWIGLU>(p, n_tiles, logical, BM, c)) return;
 
   // live 32-row blocks of the tile, and how many of them this wavefront owns
   // (row block i of wavefront row wm is tile block i * WAVES_M + wm)

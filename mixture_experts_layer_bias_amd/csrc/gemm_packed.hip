@@ -1,0 +1,454 @@
+// Grouped GEMM on bf16 MFMA (gfx950 v_mfma_f32_32x32x16_bf16, fp32 accumulate)
+// with the weights in a packed, fragment-ordered layout:
+//
+//   C[rows of group g, :] = A[rows, :] * B_g^T        (router, expert down)
+//   H[rows of group g, :] = silu(A B_gate_g^T) * (A B_up_g^T)   (expert gate/up)
+//
+// Same products, tile schedule and per-element accumulation order (k in
+// stages of 64, MFMA substeps of 16) as the row-major kernel, so the two give
+// bitwise equal results; only the way operands reach the matrix cores differs.
+//
+// Packed layout.  The weights of one group are cut into panels of 256 weight
+// rows (output columns; for SwiGLU 128 gate rows and the 128 up rows of the
+// same hidden units) and each panel into stages of 64 k.  One (group, panel,
+// stage) block is 32 KB: four 8 KB quarters, one per wavefront w; quarter w
+// holds eight 1 KB pieces q = 2 ks + j (MFMA substep ks, column block j), and
+// piece q holds for lane l the 16 bytes that lane feeds to the MFMA:
+//   B[row][64 stage + 16 ks + 8 (l / 32) + 0..7],   row = r(w, j, l % 32),
+//   r = panel * 256 + 64 w + 32 j + c             (plain; zero past the end)
+//   r = gate (j = 0) or up (j = 1) row panel * 128 + 32 w + c   (SwiGLU).
+// Blocks are ordered group, panel, stage, so a tile streams one contiguous
+// range and every load instruction reads 1 KB of consecutive bytes.
+//
+// Kernel.  A 256-thread workgroup (one wavefront per SIMD) computes up to 256
+// rows by one 256-column panel; wavefront w owns columns [64 w, 64 w + 64) of
+// every row (up to 8 x 2 MFMA blocks, 256 accumulators).  Weights go from
+// global memory straight into registers: each wavefront loads only its own
+// quarter, nothing is loaded twice and nothing passes through LDS.
+// Activations, which all four wavefronts share, stream into a four-slot LDS
+// ring by direct loads.  Both operands run three stages ahead of the MFMAs,
+// which keeps about 190 KB of loads in flight per CU.
+#include "gemm_tile.hpp"
+
+namespace moezc {
+
+namespace {
+
+constexpr int PK_WAVES = 4;                          // one wavefront per SIMD
+constexpr int PK_BKS = 64;                           // k per stage
+constexpr int PK_ROWB = PK_BKS * 2;                  // LDS bytes of one activation row
+constexpr int PK_MAXRB = kPackedMaxTileRows / 32;    // 32-row blocks per tile
+constexpr int PK_DEPTH = 4;                          // stages in the pipeline
+constexpr int PK_SLOT = PK_MAXRB * 32 * PK_ROWB;     // 32 KB per activation stage
+constexpr int PK_BLOCK = kPackedPanel * PK_BKS * 2;  // 32 KB of weights per stage
+constexpr int PK_QUARTER = PK_BLOCK / PK_WAVES;      // one wavefront's share
+static_assert(PK_QUARTER == 8 * 1024, "eight 1 KB pieces per wavefront");
+
+// NA = live 32-row blocks of the tile (1..8).
+template <int EPI, int NA>
+__device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord& c,
+                                           int n_tiles, char* __restrict__ smem) {
+  constexpr bool SWIGLU = (EPI == kSwiGLU_BF16);
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int nk = p.K / PK_BKS;
+  const int rows = c.m_end - c.m0;
+
+  // ---- activation direct loads: LDS rows of 128 bytes, chunk c of row r at
+  // position c ^ ((r >> 1) & 7) (conflict-free fragment reads).  Instruction
+  // t of wavefront w fills rows 8 (w + 4 t) .. + 7 (lane l: row + l / 8,
+  // position l % 8); rows past the tile repeat its last row (their products
+  // reach accumulator rows that are never stored).  These are buffer loads
+  // with the LDS bit (MUBUF), not global_load_lds: the compiler treats a
+  // FLAT-encoded load that writes LDS as making both wait counters unordered
+  // while it is in flight, and would then turn every wait it needs into a
+  // full drain of the pipeline.
+  // k-blocked A (a_plane != 0): stage kt of the tile is rows m0.. of plane kt,
+  // one contiguous block of 128-byte rows; row-major A: 128 bytes of each
+  // row, rows lda apart.
+  const bool kblk = p.a_plane != 0;
+  const char* A_tile = static_cast<const char*>(p.A) +
+                       (int64_t)c.m0 * (kblk ? (int64_t)PK_ROWB : p.lda * 2);
+  const int a_row_bytes = kblk ? PK_ROWB : (int)p.lda * 2;
+  uint32_t a_src[NA];
+#pragma unroll
+  for (int t = 0; t < NA; ++t) {
+    const int r = 8 * (wave + PK_WAVES * t) + (lane >> 3);
+    const int lc = (lane & 7) ^ ((r >> 1) & 7);
+    a_src[t] = (uint32_t)(min(r, rows - 1) * a_row_bytes + lc * 16);
+  }
+  char* const a_dst = smem + wave * 1024;  // + slot + 4096 t
+
+  // ---- this wavefront's quarter of each weight block of the panel
+  const char* B_pan = static_cast<const char*>(p.B0) +
+                      ((int64_t)c.g * n_tiles + c.nt) * (int64_t)nk * PK_BLOCK;
+  const uint32_t b_off = (uint32_t)(wave * PK_QUARTER + lane * 16);
+
+  // ---- fragment reads: lane l reads row 32 i + l % 32, logical chunk
+  // 2 ks + l / 32 (the swizzle depends on the lane only)
+  const int swz = ((lane & 31) >> 1) & 7;
+  int fr[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) fr[ks] = (lane & 31) * PK_ROWB + ((2 * ks + (lane >> 5)) ^ swz) * 16;
+
+  f32x16_t acc[NA][2];
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  bf16x8_t fa[2][NA];
+  bf16x8_t fb[PK_DEPTH][8];
+
+#define PK_LOAD_B(kt, u)                                                              \
+  {                                                                                   \
+    const char* b_ = B_pan + (int64_t)(kt) * PK_BLOCK + b_off;                        \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) fb[u][q] =                          \
+        *reinterpret_cast<const bf16x8_t*>(b_ + q * 1024);                            \
+  }
+#define PK_DMA_A(kt, u)                                                               \
+  {                                                                                   \
+    const char* a_ = A_tile + (kblk ? (int64_t)(kt) * p.a_plane                      \
+                                    : (int64_t)((((kt) * PK_BKS) % p.a_kwrap) * 2));  \
+    const __amdgpu_buffer_rsrc_t r_ =                                                 \
+        __builtin_amdgcn_make_buffer_rsrc((void*)a_, 0, 0x7fffffff, 0x00020000);      \
+    _Pragma("unroll") for (int t = 0; t < NA; ++t)                                    \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                     \
+            r_, (lds_void_t*)(a_dst + (u) * PK_SLOT + t * 4096), 16, a_src[t], 0, 0, 0); \
+  }
+#define PK_LOADF(fs, u, ks)                                                           \
+  {                                                                                   \
+    const char* l_ = smem + (u) * PK_SLOT + fr[ks];                                   \
+    _Pragma("unroll") for (int i = 0; i < NA; ++i) fa[fs][i] =                        \
+        *reinterpret_cast<const bf16x8_t*>(l_ + i * 4096);                            \
+  }
+#define PK_MMA(fs, u, ks)                                                             \
+  {                                                                                   \
+    _Pragma("unroll") for (int i = 0; i < NA; ++i)                                    \
+        _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] =                     \
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fs][i], fb[u][2 * (ks) + j],       \
+                                                acc[i][j], 0, 0, 0);                  \
+  }
+  // Stage kt uses slot and register set u = kt % 4.  It refills the set of
+  // stage kt-1 (all wavefronts finished reading that slot before the last
+  // barrier) with stage kt+3: weights during substep 0, activations during
+  // substep 1.  Substep ks reads the activation fragments of ks+1 and runs
+  // the MFMAs of ks, interleaved (two MFMAs, one LDS read, a share of the
+  // vector-memory reads): one wavefront per SIMD has no other wavefront to
+  // cover a burst of memory instructions, so they are spread between MFMAs.
+  // Before the last substep the wavefront waits for its own loads of stage
+  // kt+1 - loads complete in issue order, and the two later stages' loads
+  // stay in flight - and meets the others, so stage kt+1 is whole in LDS and
+  // in registers; the last substep's MFMAs then cover the first fragment
+  // reads of kt+1.  FULL: stage kt+3 exists (the steady state; no branches).
+  // NA groups of (2 MFMAs, 1 LDS read, VM vector-memory reads): keeps the
+  // matrix pipe fed while the memory instructions issue
+#define PK_INTERLEAVE(VM)                                                             \
+  _Pragma("unroll") for (int g_ = 0; g_ < NA; ++g_) {                                 \
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                \
+    if ((VM) > 0) __builtin_amdgcn_sched_group_barrier(0x020, (VM), 0);               \
+  }
+#define PK_STAGE(kt, u, FULL)                                                         \
+  {                                                                                   \
+    const bool refill_ = FULL || (kt) + 3 < nk;                                       \
+    if (refill_) PK_LOAD_B((kt) + 3, ((u) + 3) % PK_DEPTH);                           \
+    PK_LOADF(1, u, 1);                                                                \
+    PK_MMA(0, u, 0);                                                                  \
+    PK_INTERLEAVE((8 + NA - 1) / NA);                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+    if (refill_) PK_DMA_A((kt) + 3, ((u) + 3) % PK_DEPTH);                            \
+    PK_LOADF(0, u, 2);                                                                \
+    PK_MMA(1, u, 1);                                                                  \
+    PK_INTERLEAVE(1);                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+    PK_LOADF(1, u, 3);                                                                \
+    PK_MMA(0, u, 2);                                                                  \
+    PK_INTERLEAVE(0);                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+    if (FULL || (kt) + 3 < nk) ring_barrier<2 * (8 + NA)>();                          \
+    else if ((kt) + 2 < nk) ring_barrier<8 + NA>();                                   \
+    else ring_barrier<0>();                                                           \
+    if (FULL || (kt) + 1 < nk) PK_LOADF(0, ((u) + 1) % PK_DEPTH, 0);                  \
+    PK_MMA(1, u, 3);                                                                  \
+    PK_INTERLEAVE(0);                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+  }
+
+  // prologue: stages 0..2 in issue order B(0) A(0) B(1) A(1) B(2) A(2); wait
+  // for stage 0 only
+  PK_LOAD_B(0, 0);
+  PK_DMA_A(0, 0);
+  if (nk > 1) {
+    PK_LOAD_B(1, 1);
+    PK_DMA_A(1, 1);
+  }
+  if (nk > 2) {
+    PK_LOAD_B(2, 2);
+    PK_DMA_A(2, 2);
+  }
+  if (nk > 2) ring_barrier<2 * (8 + NA)>();
+  else if (nk > 1) ring_barrier<8 + NA>();
+  else ring_barrier<0>();
+  PK_LOADF(0, 0, 0);
+  // steady state: four stages per trip, every one refilling; straight-line
+  // code, so the compiler sees that the barrier waits cover the weight
+  // registers and adds no wait of its own
+  int kt = 0;
+  for (; kt + PK_DEPTH + 3 <= nk; kt += PK_DEPTH) {
+    PK_STAGE(kt, 0, true);
+    PK_STAGE(kt + 1, 1, true);
+    PK_STAGE(kt + 2, 2, true);
+    PK_STAGE(kt + 3, 3, true);
+  }
+  // the last stages (at most six)
+#pragma unroll
+  for (int u = 0; u < PK_DEPTH; ++u)
+    if (kt + u < nk) PK_STAGE(kt + u, u, false);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (kt + PK_DEPTH + u < nk) PK_STAGE(kt + PK_DEPTH + u, u, false);
+#undef PK_LOAD_B
+#undef PK_DMA_A
+#undef PK_LOADF
+#undef PK_MMA
+#undef PK_STAGE
+#undef PK_INTERLEAVE
+  ring_barrier<0>();  // every wavefront is done reading the ring before it is reused
+
+  // ---- epilogue: D[i][j] of a 32 x 32 block sits in lane j + 32 ((i / 4) % 2),
+  // register 4 (i / 8) + i % 4
+  const int lrow4 = 4 * (lane >> 5);
+  const int lcol = lane & 31;
+  if (EPI == kStoreF32) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int gcol = c.n0 + wave * 64 + j * 32 + lcol;
+        if (gcol >= p.Nout) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int grow = c.m0 + i * 32 + 8 * (v >> 2) + lrow4 + (v & 3);
+          if (grow < c.m_end) static_cast<float*>(p.C)[(int64_t)grow * p.ldc + gcol] = acc[i][j][v];
+        }
+      }
+    return;
+  }
+  // bf16 outputs go through a wavefront-private LDS tile, one 32-row block at
+  // a time, so that global stores are whole 16-byte row pieces
+  constexpr int OC = SWIGLU ? 32 : 64;  // output columns of this wavefront
+  constexpr int OS = OC + 8;            // padded LDS row (elements)
+  constexpr int CH = OC / 8;            // 16-byte pieces per row
+  bf16_t* ot = reinterpret_cast<bf16_t*>(smem) + wave * (32 * OS);
+  const int gcol0 = c.n0 + wave * OC;
+  bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.C);
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+#pragma unroll
+    for (int jj = 0; jj < OC / 32; ++jj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + lrow4 + (v & 3);
+        float val;
+        if (SWIGLU) {
+          const float a = acc[i][0][v];
+          val = a / (1.0f + __expf(-a)) * acc[i][1][v];
+        } else {
+          val = acc[i][jj][v];
+        }
+        ot[r * OS + jj * 32 + lcol] = f32_to_bf16(val);
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS writes landed
+    __builtin_amdgcn_wave_barrier();
+    const int grow0 = c.m0 + i * 32;
+#pragma unroll
+    for (int q = lane; q < 32 * CH; q += 64) {
+      const int r = q / CH, ch = q - r * CH;
+      const int grow = grow0 + r;
+      const int gcol = gcol0 + ch * 8;
+      if (grow < c.m_end && gcol < p.Nout)
+        *reinterpret_cast<u32x4_t*>(&Cout[(int64_t)grow * p.ldc + gcol]) =
+            *reinterpret_cast<const u32x4_t*>(&ot[r * OS + ch * 8]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(64 * PK_WAVES, 1) void packed_gemm_kernel(GemmProblem p, int n_tiles,
+                                                                      int total_bound,
+                                                                      int tile_rows) {
+  constexpr bool SWIGLU = (EPI == kSwiGLU_BF16);
+  __shared__ __attribute__((aligned(16))) char smem[PK_DEPTH * PK_SLOT];
+  const int logical =
+      xcd_logical_tile(p.tile_prefix ? p.tile_prefix[p.G] * n_tiles : total_bound);
+  if (logical < 0) return;
+  TileCoord c;
+  if (!map_tile<kPackedPanel, SWIGLU>(p, n_tiles, logical, tile_rows, c)) return;
+  const int nb = (c.m_end - c.m0 + 31) / 32;  // at most 8: tiles hold at most 256 rows
+  switch (nb) {
+    case 0: return;
+    case 1: run_packed<EPI, 1>(p, c, n_tiles, smem); break;
+    case 2: run_packed<EPI, 2>(p, c, n_tiles, smem); break;
+    case 3: run_packed<EPI, 3>(p, c, n_tiles, smem); break;
+    case 4: run_packed<EPI, 4>(p, c, n_tiles, smem); break;
+    case 5: run_packed<EPI, 5>(p, c, n_tiles, smem); break;
+    case 6: run_packed<EPI, 6>(p, c, n_tiles, smem); break;
+    case 7: run_packed<EPI, 7>(p, c, n_tiles, smem); break;
+    default: run_packed<EPI, 8>(p, c, n_tiles, smem); break;
+  }
+}
+
+// ---- packing ------------------------------------------------------------------
+// Byte offset o (multiple of 16) inside a 32 KB block -> the weight row and
+// first k (relative to the block's panel and stage) of its 16 bytes.
+__device__ __forceinline__ void packed_piece(int o, bool swiglu, int& row, int& k, bool& up) {
+  const int w = o >> 13;         // 8 KB quarter: wavefront
+  const int q = (o >> 10) & 7;   // 1 KB piece: 2 ks + j
+  const int l = (o >> 4) & 63;   // lane
+  const int ks = q >> 1, j = q & 1, cc = l & 31;
+  k = 16 * ks + 8 * (l >> 5);
+  if (swiglu) {
+    row = 32 * w + cc;  // within the 128 hidden units of the panel
+    up = (j == 1);
+  } else {
+    row = 64 * w + 32 * j + cc;  // within the 256 rows of the panel
+    up = false;
+  }
+}
+
+// One workgroup per 32 KB block (group, panel, stage), 2048 pieces of 16 bytes;
+// consecutive threads write consecutive pieces.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const bf16_t* __restrict__ w0,
+                                                           const bf16_t* __restrict__ w1,
+                                                           bf16_t* __restrict__ out, int rows,
+                                                           int K, int n_panels,
+                                                           int64_t group_stride, int swiglu) {
+  const int nk = K / PK_BKS;
+  const int64_t b = blockIdx.x;
+  const int64_t per_group = (int64_t)n_panels * nk;
+  const int64_t g = b / per_group;
+  const int rem = (int)(b - g * per_group);
+  const int nt = rem / nk, kt = rem - nt * nk;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int o = (threadIdx.x + 256 * i) * 16;
+    int row, k;
+    bool up;
+    packed_piece(o, swiglu != 0, row, k, up);
+    row += swiglu ? nt * (kPackedPanel / 2) : nt * kPackedPanel;
+    k += kt * PK_BKS;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (row < rows) {
+      const bf16_t* src = (up ? w1 : w0) + g * group_stride + (int64_t)row * K + k;
+      v = *reinterpret_cast<const u32x4_t*>(src);
+    }
+    *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(out) + b * PK_BLOCK + o) = v;
+  }
+}
+
+// fp32 W_router [E, d] -> packed [E, 2d] bf16 split: k < d holds bf16(w),
+// k >= d holds bf16(w - bf16(w)) of column k - d; rows past E are zero.
+// w = hi + lo + r with |r| <= 2^-17 |w|, so x (bf16) times [hi | lo] on MFMA
+// with fp32 accumulation (A columns wrap at d) gives the fp32 logits to about
+// 1e-5 absolute at d = 6144 (one bf16 term alone: about 1e-3).
+__global__ __launch_bounds__(256) void split_router_packed_kernel(const float* __restrict__ w,
+                                                                  bf16_t* __restrict__ out,
+                                                                  int E, int d) {
+  const int nk = 2 * d / PK_BKS;
+  const int b = blockIdx.x;
+  const int nt = b / nk, kt = b - nt * nk;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int o = (threadIdx.x + 256 * i) * 16;
+    int row, k;
+    bool up;
+    packed_piece(o, false, row, k, up);
+    row += nt * kPackedPanel;
+    k += kt * PK_BKS;
+    uint32_t h[4] = {0u, 0u, 0u, 0u};
+    if (row < E) {
+      const bool lo = k >= d;
+      const float* src = w + (int64_t)row * d + (lo ? k - d : k);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = src[e];
+        const bf16_t hi = f32_to_bf16(v);
+        const bf16_t r = lo ? f32_to_bf16(v - bf16_to_f32(hi)) : hi;
+        h[e >> 1] |= (uint32_t)r << (16 * (e & 1));
+      }
+    }
+    const u32x4_t v = {h[0], h[1], h[2], h[3]};
+    *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(out) + (int64_t)b * PK_BLOCK + o) = v;
+  }
+}
+
+}  // namespace
+
+int64_t packed_bytes(int64_t rows, int64_t K, bool swiglu) {
+  // SwiGLU: `rows` hidden units, gate and up together
+  const int64_t panels = swiglu ? rows / (kPackedPanel / 2)
+                                : (rows + kPackedPanel - 1) / kPackedPanel;
+  return panels * (K / PK_BKS) * (int64_t)PK_BLOCK;
+}
+
+hipError_t launch_pack_weights(const bf16_t* w0, const bf16_t* w1, bf16_t* out, int groups,
+                               int rows, int K, bool swiglu, hipStream_t s) {
+  if (K % PK_BKS != 0 || (swiglu && rows % (kPackedPanel / 2) != 0)) return hipErrorInvalidValue;
+  const int n_panels = swiglu ? rows / (kPackedPanel / 2) : (rows + kPackedPanel - 1) / kPackedPanel;
+  const int64_t blocks = (int64_t)groups * n_panels * (K / PK_BKS);
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w0, w1, out,
+                     rows, K, n_panels, (int64_t)rows * K, swiglu ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_router_packed(const float* w, bf16_t* out, int E, int d, hipStream_t s) {
+  if ((2 * d) % PK_BKS != 0) return hipErrorInvalidValue;
+  const int n_panels = (E + kPackedPanel - 1) / kPackedPanel;
+  const int blocks = n_panels * (2 * d / PK_BKS);
+  hipLaunchKernelGGL(split_router_packed_kernel, dim3(blocks), dim3(256), 0, s, w, out, E, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_packed_gemm(const GemmProblem& p, int epilogue, int tile_rows, int64_t max_rows,
+                              hipStream_t s) {
+  if (p.K % PK_BKS != 0 || p.a_kwrap % PK_BKS != 0) return hipErrorInvalidValue;
+  if (tile_rows < 32 || tile_rows > kPackedMaxTileRows || tile_rows % 32 != 0)
+    return hipErrorInvalidValue;
+  const bool swiglu = (epilogue == kSwiGLU_BF16);
+  if (swiglu && p.Nout % (kPackedPanel / 2) != 0) return hipErrorInvalidValue;
+  const int n_tiles = swiglu ? p.Nout / (kPackedPanel / 2) : (p.Nout + kPackedPanel - 1) / kPackedPanel;
+  int64_t mt_bound;
+  if (p.tile_prefix) {
+    mt_bound = (max_rows + (int64_t)p.G * (tile_rows - 1)) / tile_rows;
+    if (mt_bound > max_rows) mt_bound = max_rows;
+  } else {
+    mt_bound = (p.M + tile_rows - 1) / tile_rows;
+  }
+  int64_t blocks = mt_bound * n_tiles;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7ffffff0) return hipErrorInvalidValue;
+  blocks = (blocks + 7) / 8 * 8;
+  const dim3 grid((unsigned)blocks), block(64 * PK_WAVES);
+  const int total = (int)(mt_bound * n_tiles);
+  switch (epilogue) {
+    case kStoreF32:
+      hipLaunchKernelGGL(packed_gemm_kernel<kStoreF32>, grid, block, 0, s, p, n_tiles, total, tile_rows);
+      break;
+    case kStoreBF16:
+      hipLaunchKernelGGL(packed_gemm_kernel<kStoreBF16>, grid, block, 0, s, p, n_tiles, total, tile_rows);
+      break;
+    case kSwiGLU_BF16:
+      hipLaunchKernelGGL(packed_gemm_kernel<kSwiGLU_BF16>, grid, block, 0, s, p, n_tiles, total, tile_rows);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moezc

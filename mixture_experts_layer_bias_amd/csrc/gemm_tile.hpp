@@ -1,0 +1,84 @@
+// Tile scheduling and LDS-ring helpers shared by the grouped GEMM kernels.
+#pragma once
+
+#include "kernels.hpp"
+
+namespace moezc {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+struct TileCoord {
+  int g;      // group (expert)
+  int m0;     // first row of the tile
+  int m_end;  // one past its last row
+  int n0;     // first output column (SwiGLU: first hidden unit)
+  int nt;     // weight panel index
+};
+
+// Logical tile -> (group, rows, output columns).  Returns false past the end.
+// Grouped problems (tile_prefix set): tiles run expert by expert, then weight
+// panel, then row part; an expert whose rows need several tiles is cut into
+// equal parts.  One group (tile_prefix null): `tile_rows` rows per tile.
+// A panel is BN weight rows (SwiGLU: BN / 2 gate rows and as many up rows).
+template <int BN, bool SWIGLU>
+__device__ __forceinline__ bool map_tile(const GemmProblem& p, int n_tiles, int logical,
+                                         int tile_rows, TileCoord& c) {
+  if (p.tile_prefix) {
+    const int total = p.tile_prefix[p.G] * n_tiles;
+    if (logical >= total) return false;
+    const int mt_all = logical / n_tiles;  // only to find the group
+    int lo = 0, hi = p.G;  // tile_prefix[lo] <= mt_all < tile_prefix[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.tile_prefix[mid] <= mt_all) lo = mid; else hi = mid;
+    }
+    const int g = lo;
+    const int mtc = p.tile_prefix[g + 1] - p.tile_prefix[g];
+    const int local = logical - p.tile_prefix[g] * n_tiles;
+    const int nt = local / mtc;
+    const int mt = local - nt * mtc;
+    const int r0 = p.row_offsets[g], r1 = p.row_offsets[g + 1];
+    const int rpt = (r1 - r0 + mtc - 1) / mtc;  // equal parts
+    c.g = g;
+    c.m0 = r0 + mt * rpt;
+    c.m_end = min(c.m0 + rpt, r1);
+    c.nt = nt;
+  } else {
+    const int mtiles = (p.M + tile_rows - 1) / tile_rows;
+    if (logical >= mtiles * n_tiles) return false;
+    const int nt = logical / mtiles;
+    const int mt = logical - nt * mtiles;
+    c.g = 0;
+    c.m0 = mt * tile_rows;
+    c.m_end = min(c.m0 + tile_rows, p.M);
+    c.nt = nt;
+  }
+  c.n0 = SWIGLU ? c.nt * (BN / 2) : c.nt * BN;
+  return true;
+}
+
+// XCD-aware order: workgroup b runs on XCD b % 8, and XCD x takes the logical
+// range [x * per, (x + 1) * per) of the `total` live tiles, so neighbouring
+// tiles (one expert's panels and row parts) share one XCD's L2.  Returns -1
+// for a workgroup past the end.
+__device__ __forceinline__ int xcd_logical_tile(int total) {
+  const int per = (total + 7) >> 3;
+  const int jx = blockIdx.x >> 3;
+  if (jx >= per) return -1;
+  return (blockIdx.x & 7) * per + jx;
+}
+
+// Workgroup barrier for an LDS ring filled by direct loads: this wavefront's
+// vector-memory operations older than the newest n have completed (loads
+// return in issue order) and all its LDS operations are done (s_waitcnt
+// vmcnt(n) lgkmcnt(0), gfx9 encoding), then s_barrier.  No memory fence: a
+// fence would wait for every load in flight and empty the ring.
+template <int n>
+__device__ __forceinline__ void ring_barrier() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(((n >> 4) << 14) | 0x0070 | (n & 15));
+  __builtin_amdgcn_s_barrier();
+}
+
+}  // namespace moezc

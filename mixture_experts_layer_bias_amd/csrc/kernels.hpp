@@ -14,9 +14,6 @@ constexpr int kMaxExperts = 2048;
 constexpr int kMaxTopK = 32;
 
 // ---- routing (route.hip) ----------------------------------------------------
-// W_router fp32 [E, d] -> [E, 2d] bf16: columns [0, d) = bf16(w),
-// columns [d, 2d) = bf16(w - bf16(w)).
-hipError_t launch_split_router(const float* w, bf16_t* w2, int E, int d, hipStream_t s);
 // fp64 softmax, fp32 bias key, top-K with lowest-index tie-break.
 hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int K,
                        int32_t* idx, float* gate, hipStream_t s);
@@ -45,9 +42,11 @@ hipError_t launch_pid(const int32_t* loads, const float* target, float* bias, fl
 // C[rows of group g, :] = A[rows, :K] * B_g[:, :K]^T.  Groups are the FFN
 // experts (rows = their grouped slots) or one group of M rows (router).
 struct GemmProblem {
-  const void* A;           // [rows, K] (row stride lda)
+  const void* A;           // [rows, K] (row stride lda), or k-blocked (a_plane)
   int64_t lda;
   int a_kwrap;             // A column = k % a_kwrap (router: d; else K)
+  int64_t a_plane;         // k-blocked A: bytes between planes of 64 k, each
+                           // [rows][64] (row stride 128 B); 0 = row-major A
   const void* B0;          // [G][Nout or I][K] weights (gate or plain)
   const void* B1;          // up weights for SwiGLU, else null
   int64_t ldb;             // row stride of B
@@ -69,6 +68,24 @@ enum Epilogue { kStoreF32 = 0, kStoreBF16 = 1, kSwiGLU_BF16 = 2, kSwiGLU_F32 = 3
 hipError_t launch_mfma_gemm(const GemmProblem& p, int epilogue, int tile_rows,
                             int64_t max_rows, hipStream_t s);
 int mfma_tile_rows(int64_t expected_rows_per_group);
+
+// bf16 MFMA path on packed weights (gemm_packed.hip).  Panels of
+// kPackedPanel weight rows (SwiGLU: half gate, half up rows), stages of 64 k,
+// one 32 KB block per (group, panel, stage); tiles of at most
+// kPackedMaxTileRows rows, any multiple of 32.
+constexpr int kPackedPanel = 256;
+constexpr int kPackedMaxTileRows = 256;
+// Bytes of one group's packed weights: `rows` weight rows (SwiGLU: hidden
+// units, gate and up together) by K.
+int64_t packed_bytes(int64_t rows, int64_t K, bool swiglu);
+// Row-major [groups][rows][K] (gate w0 and up w1 for SwiGLU) -> packed.
+hipError_t launch_pack_weights(const bf16_t* w0, const bf16_t* w1, bf16_t* out, int groups,
+                               int rows, int K, bool swiglu, hipStream_t s);
+// W_router fp32 [E, d] -> packed two-term bf16 split [E, 2d].
+hipError_t launch_split_router_packed(const float* w, bf16_t* out, int E, int d, hipStream_t s);
+// B0 = packed weights; B1, ldb and b_group_stride are unused.
+hipError_t launch_packed_gemm(const GemmProblem& p, int epilogue, int tile_rows,
+                              int64_t max_rows, hipStream_t s);
 
 // fp32 FMA path (gemm_simt.hip).
 hipError_t launch_simt_gemm(const GemmProblem& p, int epilogue, int64_t max_rows,

@@ -1,6 +1,6 @@
 // Routing-side kernels of the MoE layer with zero-computation experts (gfx950):
-// router-weight split, softmax + bias key + top-K, expert histogram, scan,
-// grouping permutation, combine and the PID bias update.
+// softmax + bias key + top-K, expert histogram, scan, grouping permutation,
+// combine and the PID bias update.
 //
 // Layer definition: LongCat-Flash pages, 『衝上熱搜！美團大模型，靠「快」火了』,
 // section 零計算專家 (softmax router over N FFN + Z identity experts, bias b_i
@@ -10,33 +10,6 @@
 #include "kernels.hpp"
 
 namespace moezc {
-
-// ---------------------------------------------------------------------------
-// Router weight split: w = hi + lo + r with |r| <= 2^-17 |w|, hi, lo in bf16.
-// x (bf16) times [hi | lo] on MFMA with fp32 accumulation then gives the fp32
-// logits to about 1e-5 absolute at d = 6144 (one bf16 term alone: ~1e-3).
-__global__ __launch_bounds__(256) void split_router_kernel(const float* __restrict__ w,
-                                                           bf16_t* __restrict__ w2,
-                                                           int E, int d) {
-  const int64_t n = (int64_t)E * d;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e = i / d, k = i - e * d;
-    const float v = w[i];
-    const bf16_t hi = f32_to_bf16(v);
-    const bf16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
-    w2[e * 2 * d + k] = hi;
-    w2[e * 2 * d + d + k] = lo;
-  }
-}
-
-hipError_t launch_split_router(const float* w, bf16_t* w2, int E, int d, hipStream_t s) {
-  const int64_t n = (int64_t)E * d;
-  int blocks = (int)((n + 255) / 256);
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(split_router_kernel, dim3(blocks), dim3(256), 0, s, w, w2, E, d);
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------
 // Softmax + bias key + top-K.  One wavefront per token; lane l holds experts

@@ -27,13 +27,20 @@ LOGIT_TOL = 1e-4
 Y_TOL = {"bf16": 1e-2, "f32": 1e-5}
 
 
-def run_gpu(w, inp, residual=True, workspace=None, events=None):
+def run_gpu(w, inp, residual=True, workspace=None, events=None, packed=None):
+    """One forward through the C ABI; ``packed`` = (gate_up, down) from
+    moe_zc_pack_expert_weights selects moe_zc_forward_packed."""
     dev = inp["x"].device
     aux = m.alloc_aux(w.T, w.N, w.Z, w.K, dev)
-    y = m.moe_zc_forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
-                         inp["w_down"], w.N, w.Z, w.K,
-                         residual=inp["residual"] if residual else None, aux=aux,
-                         workspace=workspace, events=events)
+    res = inp["residual"] if residual else None
+    if packed is None:
+        y = m.moe_zc_forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
+                             inp["w_down"], w.N, w.Z, w.K, residual=res, aux=aux,
+                             workspace=workspace, events=events)
+    else:
+        y = m.moe_zc_forward_packed(inp["x"], inp["w_router"], inp["bias"], packed[0], packed[1],
+                                    w.N, w.Z, w.K, w.I, residual=res, aux=aux,
+                                    workspace=workspace, events=events)
     torch.cuda.synchronize()
     out = {k: v.cpu().numpy() for k, v in aux.items()}
     out["y_t"] = y

@@ -86,6 +86,40 @@ def test_forward_validation(lib):
     assert _fwd(lib, x=ctypes.c_void_p((1 << 20) + 2)) == INVALID       # not 16-aligned
 
 
+def test_packed_sizes_and_validation(lib):
+    gu, dn = ctypes.c_size_t(), ctypes.c_size_t()
+    sz = lambda d, I, dt: lib.moe_zc_packed_expert_bytes(d, I, dt, ctypes.byref(gu),
+                                                         ctypes.byref(dn))
+    assert sz(6144, 2048, BF16) == OK
+    assert (gu.value, dn.value) == (4 * 6144 * 2048, 2 * 2048 * 6144)
+    assert sz(192, 256, BF16) == OK                  # down rows padded to 256
+    assert (gu.value, dn.value) == (4 * 192 * 256, 2 * 256 * 256)
+    assert sz(6144, 2048, F32) == UNSUPPORTED        # packing is a bf16 layout
+    assert sz(100, 256, BF16) == UNSUPPORTED
+    assert sz(0, 256, BF16) == INVALID
+    assert lib.moe_zc_packed_expert_bytes(64, 128, BF16, None, ctypes.byref(dn)) == INVALID
+    pk = lib.moe_zc_pack_expert_weights
+    assert pk(FAKE, FAKE, FAKE, 0, 64, 128, BF16, FAKE, FAKE, None) == OK   # nothing to pack
+    assert pk(FAKE, FAKE, FAKE, -1, 64, 128, BF16, FAKE, FAKE, None) == INVALID
+    assert pk(None, FAKE, FAKE, 2, 64, 128, BF16, FAKE, FAKE, None) == INVALID
+    assert pk(FAKE, FAKE, FAKE, 2, 64, 128, BF16, None, FAKE, None) == INVALID
+    assert pk(FAKE, FAKE, FAKE, 2, 64, 128, F32, FAKE, FAKE, None) == UNSUPPORTED
+    assert pk(FAKE, FAKE, FAKE, 2, 64, 100, BF16, FAKE, FAKE, None) == UNSUPPORTED
+    assert pk(FAKE, ctypes.c_void_p((1 << 20) + 8), FAKE, 2, 64, 128, BF16, FAKE, FAKE,
+              None) == INVALID
+    fp = lib.moe_zc_forward_packed
+    T, d, I, N, Z, K = 64, 128, 128, 8, 4, 3
+    nb = lib.moe_zc_workspace_size(T, d, I, N, Z, K, BF16)
+    args = lambda **o: [o.get("x", FAKE), FAKE, FAKE, o.get("gu", FAKE), o.get("dn", FAKE), None,
+                        FAKE, o.get("T", T), d, I, o.get("N", N), Z, K, o.get("dt", BF16), None,
+                        FAKE, nb, None]
+    assert fp(*args(T=0)) == OK
+    assert fp(*args(dt=F32)) == UNSUPPORTED
+    assert fp(*args(gu=None)) == INVALID
+    assert fp(*args(dn=None)) == INVALID
+    assert fp(*args(x=None)) == INVALID
+
+
 def test_route_and_bias_update_validation(lib):
     r = lib.moe_zc_route
     assert r(FAKE, FAKE, 0, 12, 3, FAKE, FAKE, None) == OK

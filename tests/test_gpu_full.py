@@ -1,8 +1,9 @@
 """GPU parity at the full sizes of the decode, prefill and skewed workloads, in
-the launch configuration the benchmark times (same entry point, same sizes,
-same library).  Routing and grouping are checked for every token; the layer
-output on a seeded sample of tokens that the oracle evaluates one by one
-(tokens are independent, so a sample is exact)."""
+the launch configuration the benchmark times (moe_zc_forward_packed on packed
+expert weights, same sizes, same library), plus bitwise equality with the
+row-major moe_zc_forward.  Routing and grouping are checked for every token;
+the layer output on a seeded sample of tokens that the oracle evaluates one
+by one (tokens are independent, so a sample is exact)."""
 import numpy as np
 import pytest
 import torch
@@ -21,7 +22,11 @@ def test_full_size_layer(name, n_sample):
     w = get_workload(name)
     print(f"[{name}] generating inputs", flush=True)
     inp = make_inputs(w, device=DEV)
-    g = run_gpu(w, inp)
+    packed = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    g = run_gpu(w, inp, packed=packed)
+    y_rowmajor = run_gpu(w, inp)["y_t"]
+    assert torch.equal(g["y_t"], y_rowmajor), "packed and row-major forwards differ"
+    del y_rowmajor
     sample = np.sort(np.random.default_rng(1).choice(w.T, n_sample, replace=False))
     print(f"[{name}] checking against the oracle, tokens {sample.tolist()}", flush=True)
     rep = check_forward(w, inp, g, y_tokens=sample, get_expert=gpu_expert_getter(inp))
