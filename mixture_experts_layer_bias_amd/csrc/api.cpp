@@ -28,6 +28,9 @@ struct Shape {
   int64_t chunks;
   size_t es;     // element size of dt
   int ffn_tile_rows;
+  // the bf16 expert GEMMs gather their rows of x through perm (byte offsets
+  // into x below 2^31); otherwise the permute stage copies them into xp
+  bool gather;
 };
 
 // Host-side shape validation shared by every entry point that takes sizes.
@@ -52,6 +55,7 @@ moe_zc_status check_shape(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z,
   s->smax = smax;
   s->chunks = (T + kChunk - 1) / kChunk;
   s->es = (dt == MOE_ZC_BF16) ? 2 : 4;
+  s->gather = (dt == MOE_ZC_BF16) && T * d * 2 < (int64_t(1) << 31);
   if (dt == MOE_ZC_BF16) {
     const int64_t expected = (N > 0) ? (T * K) / E : 0;  // rows per expert, symmetric routing
     s->ffn_tile_rows = mfma_tile_rows(expected);
@@ -83,7 +87,7 @@ Plan make_plan(const Shape& s) {
   p.counts = take((size_t)s.chunks * s.E * 4);
   p.tiles = take((size_t)(s.N + 1) * 4);
   p.wr2 = take(s.dt == MOE_ZC_BF16 ? (size_t)packed_bytes(s.E, 2 * s.d, false) : 0);
-  p.xp = take((size_t)s.smax * s.d * s.es);
+  p.xp = take(s.gather ? 0 : (size_t)s.smax * s.d * s.es);
   p.h = take((size_t)s.smax * s.I * s.es);
   p.o = take((size_t)s.smax * s.d * s.es);
   p.total = at;
@@ -143,6 +147,7 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
 
   const bool bf = (dt == MOE_ZC_BF16);
+  const bool gather = s.gather;
   void* xp = ws + pl.xp;
   void* h = ws + pl.h;
   void* o = ws + pl.o;
@@ -179,7 +184,8 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
   MOE_ZC_TRY(mark(4));
   if (bf)
     MOE_ZC_TRY(launch_permute<bf16_t>(static_cast<const bf16_t*>(x), idx, counts, offsets, pos,
-                                      perm, static_cast<bf16_t*>(xp), T, (int)d, K, E, N, stream));
+                                      perm, gather ? nullptr : static_cast<bf16_t*>(xp), T,
+                                      (int)d, K, E, N, stream));
   else
     MOE_ZC_TRY(launch_permute<float>(static_cast<const float*>(x), idx, counts, offsets, pos,
                                      perm, static_cast<float*>(xp), T, (int)d, K, E, N, stream));
@@ -187,7 +193,8 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
   MOE_ZC_TRY(mark(5));
   if (N > 0) {
     GemmProblem p{};
-    p.A = xp; p.lda = d; p.a_kwrap = (int)d; p.K = (int)d;
+    p.A = gather ? x : xp; p.lda = d; p.a_kwrap = (int)d; p.K = (int)d;
+    p.a_rows = gather ? perm : nullptr;
     p.B0 = w_gate; p.B1 = w_up; p.ldb = d; p.b_group_stride = I * d;
     p.C = h; p.ldc = I; p.Nout = (int)I;
     p.row_offsets = offsets; p.tile_prefix = tiles; p.G = N; p.M = 0;

@@ -91,7 +91,8 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
       static_cast<const bf16_t*>(p.B0) + (int64_t)c.g * p.b_group_stride;
   const bf16_t* __restrict__ B1 =
       SWIGLU ? static_cast<const bf16_t*>(p.B1) + (int64_t)c.g * p.b_group_stride : nullptr;
-  const char* A_tile = reinterpret_cast<const char*>(A + (int64_t)c.m0 * p.lda);
+  // gathered A (a_rows): offsets are taken from the start of A
+  const char* A_tile = reinterpret_cast<const char*>(A + (p.a_rows ? 0 : (int64_t)c.m0 * p.lda));
   const char* B_gate = reinterpret_cast<const char*>(B0 + (int64_t)c.n0 * p.ldb);
   const char* B_up = SWIGLU ? reinterpret_cast<const char*>(B1 + (int64_t)c.n0 * p.ldb) : nullptr;
 
@@ -113,7 +114,8 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
     const int r = RPI * j + lane / CPR;
     const int lc = (lane % CPR) ^ ((r >> 1) & 7);
     const int rr = min(r, c.m_end - 1 - c.m0);
-    a_src[t] = (uint32_t)(rr * (int)p.lda * 2 + lc * 16);
+    const uint32_t arow = p.a_rows ? (uint32_t)p.a_rows[c.m0 + rr] : (uint32_t)rr;
+    a_src[t] = arow * (uint32_t)(p.lda * 2) + (uint32_t)(lc * 16);
     a_dst[t] = RPI * j * ROWB;
   }
 #pragma unroll

@@ -26,8 +26,8 @@
 // global memory straight into registers: each wavefront loads only its own
 // quarter, nothing is loaded twice and nothing passes through LDS.
 // Activations, which all four wavefronts share, stream into a four-slot LDS
-// ring by direct loads.  Both operands run three stages ahead of the MFMAs,
-// which keeps about 190 KB of loads in flight per CU.
+// ring by direct loads.  Both operands are loaded PK_DIST stages ahead of the
+// MFMAs (three: up to about 190 KB of loads in flight per CU).
 #include "gemm_tile.hpp"
 
 namespace moezc {
@@ -38,11 +38,24 @@ constexpr int PK_WAVES = 4;                          // one wavefront per SIMD
 constexpr int PK_BKS = 64;                           // k per stage
 constexpr int PK_ROWB = PK_BKS * 2;                  // LDS bytes of one activation row
 constexpr int PK_MAXRB = kPackedMaxTileRows / 32;    // 32-row blocks per tile
-constexpr int PK_DEPTH = 4;                          // stages in the pipeline
+constexpr int PK_DEPTH = 3;                          // stages in the pipeline
+constexpr int PK_DIST = PK_DEPTH - 1;                // stages loaded ahead of use
 constexpr int PK_SLOT = PK_MAXRB * 32 * PK_ROWB;     // 32 KB per activation stage
 constexpr int PK_BLOCK = kPackedPanel * PK_BKS * 2;  // 32 KB of weights per stage
 constexpr int PK_QUARTER = PK_BLOCK / PK_WAVES;      // one wavefront's share
 static_assert(PK_QUARTER == 8 * 1024, "eight 1 KB pieces per wavefront");
+
+// Ring barrier that lets the newest c stages of STEP loads each stay in
+// flight (c = 1 .. 3; otherwise none).
+template <int STEP>
+__device__ __forceinline__ void barrier_in_flight(int c) {
+  switch (c) {
+    case 1: ring_barrier<STEP>(); break;
+    case 2: ring_barrier<2 * STEP>(); break;
+    case 3: ring_barrier<3 * STEP>(); break;
+    default: ring_barrier<0>(); break;  // c <= 0: nothing may stay in flight
+  }
+}
 
 // NA = live 32-row blocks of the tile (1..8).
 template <int EPI, int NA>
@@ -50,7 +63,10 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
                                            int n_tiles, char* __restrict__ smem) {
   constexpr bool SWIGLU = (EPI == kSwiGLU_BF16);
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // the wavefront index is uniform: keep it in a scalar register, so LDS
+  // destinations of the direct loads (M0) need no per-load readfirstlane
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int nk = p.K / PK_BKS;
   const int rows = c.m_end - c.m0;
 
@@ -67,15 +83,25 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
   // one contiguous block of 128-byte rows; row-major A: 128 bytes of each
   // row, rows lda apart.
   const bool kblk = p.a_plane != 0;
+  // gathered A (a_rows): GEMM row s reads row a_rows[s] of A, so offsets are
+  // taken from the start of A; otherwise from the tile's first row
+  const int32_t* __restrict__ a_rows = p.a_rows;
   const char* A_tile = static_cast<const char*>(p.A) +
-                       (int64_t)c.m0 * (kblk ? (int64_t)PK_ROWB : p.lda * 2);
+                       (a_rows ? (int64_t)0
+                               : (int64_t)c.m0 * (kblk ? (int64_t)PK_ROWB : p.lda * 2));
   const int a_row_bytes = kblk ? PK_ROWB : (int)p.lda * 2;
+  // bytes from one stage to the next, and the stage at which the A column
+  // wraps back to 0 (router: A = x is read twice, once per weight term)
+  const int64_t a_step = kblk ? p.a_plane : (int64_t)PK_ROWB;
+  const int a_wrap = kblk ? nk : p.a_kwrap / PK_BKS;
   uint32_t a_src[NA];
 #pragma unroll
   for (int t = 0; t < NA; ++t) {
-    const int r = 8 * (wave + PK_WAVES * t) + (lane >> 3);
+    const int r = 8 * (wave + PK_WAVES * t) + (lane >> 3);  // LDS row filled
     const int lc = (lane & 7) ^ ((r >> 1) & 7);
-    a_src[t] = (uint32_t)(min(r, rows - 1) * a_row_bytes + lc * 16);
+    const int rs = min(r, rows - 1);                          // tile row read
+    const uint32_t arow = a_rows ? (uint32_t)a_rows[c.m0 + rs] : (uint32_t)rs;
+    a_src[t] = arow * (uint32_t)a_row_bytes + (uint32_t)(lc * 16);
   }
   char* const a_dst = smem + wave * 1024;  // + slot + 4096 t
 
@@ -109,8 +135,8 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
   }
 #define PK_DMA_A(kt, u)                                                               \
   {                                                                                   \
-    const char* a_ = A_tile + (kblk ? (int64_t)(kt) * p.a_plane                      \
-                                    : (int64_t)((((kt) * PK_BKS) % p.a_kwrap) * 2));  \
+    const int ks_ = (kt) >= a_wrap ? (kt) - a_wrap : (kt);                            \
+    const char* a_ = A_tile + (int64_t)ks_ * a_step;                                  \
     const __amdgpu_buffer_rsrc_t r_ =                                                 \
         __builtin_amdgcn_make_buffer_rsrc((void*)a_, 0, 0x7fffffff, 0x00020000);      \
     _Pragma("unroll") for (int t = 0; t < NA; ++t)                                    \
@@ -130,18 +156,19 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
         __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fs][i], fb[u][2 * (ks) + j],       \
                                                 acc[i][j], 0, 0, 0);                  \
   }
-  // Stage kt uses slot and register set u = kt % 4.  It refills the set of
-  // stage kt-1 (all wavefronts finished reading that slot before the last
-  // barrier) with stage kt+3: weights during substep 0, activations during
+  // Stage kt uses slot and register set u = kt % PK_DEPTH.  It refills the
+  // set of stage kt-1 (all wavefronts finished reading that slot before the
+  // last barrier) with stage kt+PK_DIST: weights during substep 0, activations during
   // substep 1.  Substep ks reads the activation fragments of ks+1 and runs
   // the MFMAs of ks, interleaved (two MFMAs, one LDS read, a share of the
   // vector-memory reads): one wavefront per SIMD has no other wavefront to
   // cover a burst of memory instructions, so they are spread between MFMAs.
   // Before the last substep the wavefront waits for its own loads of stage
-  // kt+1 - loads complete in issue order, and the two later stages' loads
-  // stay in flight - and meets the others, so stage kt+1 is whole in LDS and
+  // kt+1 - loads complete in issue order, and the later stages' loads stay
+  // in flight - and meets the others, so stage kt+1 is whole in LDS and
   // in registers; the last substep's MFMAs then cover the first fragment
-  // reads of kt+1.  FULL: stage kt+3 exists (the steady state; no branches).
+  // reads of kt+1.  FULL: stage kt+PK_DIST exists (the steady state; no
+  // branches).
   // NA groups of (2 MFMAs, 1 LDS read, VM vector-memory reads): keeps the
   // matrix pipe fed while the memory instructions issue
 #define PK_INTERLEAVE(VM)                                                             \
@@ -152,13 +179,13 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
   }
 #define PK_STAGE(kt, u, FULL)                                                         \
   {                                                                                   \
-    const bool refill_ = FULL || (kt) + 3 < nk;                                       \
-    if (refill_) PK_LOAD_B((kt) + 3, ((u) + 3) % PK_DEPTH);                           \
+    const bool refill_ = FULL || (kt) + PK_DIST < nk;                                 \
+    if (refill_) PK_LOAD_B((kt) + PK_DIST, ((u) + PK_DIST) % PK_DEPTH);               \
     PK_LOADF(1, u, 1);                                                                \
     PK_MMA(0, u, 0);                                                                  \
     PK_INTERLEAVE((8 + NA - 1) / NA);                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                \
-    if (refill_) PK_DMA_A((kt) + 3, ((u) + 3) % PK_DEPTH);                            \
+    if (refill_) PK_DMA_A((kt) + PK_DIST, ((u) + PK_DIST) % PK_DEPTH);                \
     PK_LOADF(0, u, 2);                                                                \
     PK_MMA(1, u, 1);                                                                  \
     PK_INTERLEAVE(1);                                                                 \
@@ -167,47 +194,49 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
     PK_MMA(0, u, 2);                                                                  \
     PK_INTERLEAVE(0);                                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                \
-    if (FULL || (kt) + 3 < nk) ring_barrier<2 * (8 + NA)>();                          \
-    else if ((kt) + 2 < nk) ring_barrier<8 + NA>();                                   \
-    else ring_barrier<0>();                                                           \
+    if (FULL) ring_barrier<(PK_DIST - 1) * (8 + NA)>();                               \
+    else barrier_in_flight<8 + NA>(min(nk - 1, (kt) + PK_DIST) - ((kt) + 1));         \
     if (FULL || (kt) + 1 < nk) PK_LOADF(0, ((u) + 1) % PK_DEPTH, 0);                  \
     PK_MMA(1, u, 3);                                                                  \
     PK_INTERLEAVE(0);                                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                \
   }
 
-  // prologue: stages 0..2 in issue order B(0) A(0) B(1) A(1) B(2) A(2); wait
-  // for stage 0 only
-  PK_LOAD_B(0, 0);
-  PK_DMA_A(0, 0);
-  if (nk > 1) {
-    PK_LOAD_B(1, 1);
-    PK_DMA_A(1, 1);
-  }
-  if (nk > 2) {
-    PK_LOAD_B(2, 2);
-    PK_DMA_A(2, 2);
-  }
-  if (nk > 2) ring_barrier<2 * (8 + NA)>();
-  else if (nk > 1) ring_barrier<8 + NA>();
-  else ring_barrier<0>();
-  PK_LOADF(0, 0, 0);
-  // steady state: four stages per trip, every one refilling; straight-line
-  // code, so the compiler sees that the barrier waits cover the weight
-  // registers and adds no wait of its own
+  // prologue: stages 0 .. PK_DIST-1, weights then activations of each; wait
+  // for stage 0 only.  Where the steady-state loop runs, the prologue is
+  // straight-line code, so the compiler enters the loop knowing which loads
+  // are still in flight and adds no wait of its own at the loop top.
   int kt = 0;
-  for (; kt + PK_DEPTH + 3 <= nk; kt += PK_DEPTH) {
-    PK_STAGE(kt, 0, true);
-    PK_STAGE(kt + 1, 1, true);
-    PK_STAGE(kt + 2, 2, true);
-    PK_STAGE(kt + 3, 3, true);
+  if (nk >= PK_DEPTH + PK_DIST) {
+#pragma unroll
+    for (int u = 0; u < PK_DIST; ++u) {
+      PK_LOAD_B(u, u);
+      PK_DMA_A(u, u);
+    }
+    ring_barrier<(PK_DIST - 1) * (8 + NA)>();
+    PK_LOADF(0, 0, 0);
+    // steady state: PK_DEPTH stages per trip, every one refilling
+    do {
+#pragma unroll
+      for (int u = 0; u < PK_DEPTH; ++u) PK_STAGE(kt + u, u, true);
+      kt += PK_DEPTH;
+    } while (kt + PK_DEPTH + PK_DIST <= nk);
+  } else {
+#pragma unroll
+    for (int u = 0; u < PK_DIST; ++u)
+      if (u < nk) {
+        PK_LOAD_B(u, u);
+        PK_DMA_A(u, u);
+      }
+    barrier_in_flight<8 + NA>(min(nk, PK_DIST) - 1);
+    PK_LOADF(0, 0, 0);
   }
-  // the last stages (at most six)
+  // the last stages (fewer than PK_DEPTH + PK_DIST)
 #pragma unroll
   for (int u = 0; u < PK_DEPTH; ++u)
     if (kt + u < nk) PK_STAGE(kt + u, u, false);
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
+  for (int u = 0; u + 1 < PK_DIST; ++u)
     if (kt + PK_DEPTH + u < nk) PK_STAGE(kt + PK_DEPTH + u, u, false);
 #undef PK_LOAD_B
 #undef PK_DMA_A

@@ -25,7 +25,8 @@ hipError_t launch_chunk_hist(const int32_t* idx, int64_t T, int K, int E, int N,
 // offsets [N+1]; m-tile prefix [N+1] for tiles of `bm` rows.
 hipError_t launch_scan(int32_t* counts, int C, int E, int N, int32_t* loads,
                        int32_t* offsets, int bm, int32_t* tile_prefix, hipStream_t s);
-// Grouped rows: pos (rank -> row), perm, and xp[row] = x[token].
+// Grouped rows: pos (rank -> row), perm, and xp[row] = x[token] (the row
+// copy only when xp is not null).
 template <typename T>
 hipError_t launch_permute(const T* x, const int32_t* idx, const int32_t* chunk_base,
                           const int32_t* offsets, int32_t* pos, int32_t* perm, T* xp,
@@ -47,6 +48,8 @@ struct GemmProblem {
   int a_kwrap;             // A column = k % a_kwrap (router: d; else K)
   int64_t a_plane;         // k-blocked A: bytes between planes of 64 k, each
                            // [rows][64] (row stride 128 B); 0 = row-major A
+  const int32_t* a_rows;   // row-major A only: GEMM row s reads A row
+                           // a_rows[s] (gather), or null: A row s
   const void* B0;          // [G][Nout or I][K] weights (gate or plain)
   const void* B1;          // up weights for SwiGLU, else null
   int64_t ldb;             // row stride of B

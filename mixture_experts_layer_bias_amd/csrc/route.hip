@@ -282,12 +282,38 @@ __global__ __launch_bounds__(256) void permute_kernel(const T* __restrict__ x,
   }
 }
 
+// Grouping without the row copy (the grouped GEMM gathers rows of x through
+// perm itself): one thread per slot (t, k).
+__global__ __launch_bounds__(256) void group_rows_kernel(const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ base,
+                                                         const int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ pos,
+                                                         int32_t* __restrict__ perm,
+                                                         int64_t TK, int K, int E, int N) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= TK) return;
+  const int64_t t = i / K;
+  const int e = idx[i];
+  int row = -1;
+  if (e < N) {
+    row = offsets[e] + base[(t / kChunk) * E + e] + pos[i];
+    perm[row] = (int32_t)t;
+  }
+  pos[i] = row;
+}
+
 template <typename T>
 hipError_t launch_permute(const T* x, const int32_t* idx, const int32_t* chunk_base,
                           const int32_t* offsets, int32_t* pos, int32_t* perm, T* xp,
                           int64_t Tn, int d, int K, int E, int N, hipStream_t s) {
-  hipLaunchKernelGGL(permute_kernel<T>, dim3((unsigned)Tn), dim3(256), 0, s, x, idx, chunk_base,
-                     offsets, pos, perm, xp, d, K, E, N);
+  if (xp) {
+    hipLaunchKernelGGL(permute_kernel<T>, dim3((unsigned)Tn), dim3(256), 0, s, x, idx,
+                       chunk_base, offsets, pos, perm, xp, d, K, E, N);
+  } else {
+    const int64_t TK = Tn * K;
+    hipLaunchKernelGGL(group_rows_kernel, dim3((unsigned)((TK + 255) / 256)), dim3(256), 0, s,
+                       idx, chunk_base, offsets, pos, perm, TK, K, E, N);
+  }
   return hipGetLastError();
 }
 template hipError_t launch_permute<float>(const float*, const int32_t*, const int32_t*,

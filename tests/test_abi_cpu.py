@@ -46,7 +46,13 @@ def test_version_and_status_strings(lib):
 def test_workspace_size_rules(lib):
     ws = lib.moe_zc_workspace_size
     assert ws(64, 128, 256, 8, 4, 3, F32) > 0
-    assert ws(16384, 6144, 2048, 512, 256, 12, BF16) > 5 * 10**9
+    # bf16 prefill: hidden and output rows (S <= T*min(K, N) rows of I and d)
+    # plus routing scratch; the GEMMs gather x rows, so no grouped copy of x
+    rows = 16384 * 12
+    big = ws(16384, 6144, 2048, 512, 256, 12, BF16)
+    assert rows * (2048 + 6144) * 2 < big < rows * (2048 + 6144) * 2 + 2 * 10**8
+    # fp32 keeps the grouped copy of x
+    assert ws(1024, 128, 256, 8, 4, 3, F32) > 1024 * 3 * (128 + 256 + 128) * 4
     assert ws(0, 128, 256, 8, 4, 3, F32) > 0          # T = 0 is valid
     assert ws(64, 100, 256, 8, 4, 3, BF16) == 0        # d not a multiple of 64
     assert ws(64, 128, 256, 8, 4, 13, BF16) == 0       # K > E
