@@ -93,15 +93,19 @@ def calibrate_copy():
 
 def algorithmic(w, S, touched, es):
     """Algorithmic bytes / FLOPs per launch of each stage (inputs read once,
-    outputs written once)."""
+    outputs written once).  bf16: the gate/up GEMM gathers its rows from x,
+    so its input is x itself and the grouping stage moves only indices."""
     T, d, I, N, E, K = w.T, w.d, w.I, w.N, w.E, w.K
+    gathered = es == 2 and T * d * es < 2**31
     return {
         "router_gemm": {"flop": 2.0 * T * d * E,
                         "bytes": T * d * es + E * d * 4 + T * E * 4},
         "softmax_topk": {"bytes": T * E * 4 + E * 4 + T * K * 8},
-        "permute": {"bytes": T * d * es + S * d * es + T * K * 4 * 3},
+        "permute": {"bytes": T * K * 4 * 4 if gathered else
+                    T * d * es + S * d * es + T * K * 4 * 3},
         "gemm_gate_up_swiglu": {"flop": 4.0 * d * I * S,
-                                "bytes": touched * 2 * I * d * es + S * d * es + S * I * es},
+                                "bytes": touched * 2 * I * d * es
+                                + (T if gathered else S) * d * es + S * I * es},
         "gemm_down": {"flop": 2.0 * d * I * S,
                       "bytes": touched * d * I * es + S * I * es + S * d * es},
         "combine": {"bytes": S * d * es + 3 * T * d * es + T * K * 12},
