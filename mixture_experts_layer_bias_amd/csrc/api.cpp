@@ -66,7 +66,7 @@ moe_zc_status check_shape(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z,
 }
 
 struct Plan {
-  size_t logits, idx, gate, pos, loads, offsets, perm, counts, tiles, wr2, xp, h, o, total;
+  size_t logits, idx, gate, pos, loads, offsets, perm, counts, tiles, tiles2, wr2, xp, h, o, total;
 };
 
 Plan make_plan(const Shape& s) {
@@ -86,6 +86,7 @@ Plan make_plan(const Shape& s) {
   p.perm = take((size_t)std::max<int64_t>(s.smax, 1) * 4);
   p.counts = take((size_t)s.chunks * s.E * 4);
   p.tiles = take((size_t)(s.N + 1) * 4);
+  p.tiles2 = take((size_t)(s.N + 1) * 4);
   p.wr2 = take(s.dt == MOE_ZC_BF16 ? (size_t)packed_bytes(s.E, 2 * s.d, false) : 0);
   p.xp = take(s.gather ? 0 : (size_t)s.smax * s.d * s.es);
   p.h = take((size_t)s.smax * s.I * s.es);
@@ -143,6 +144,9 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
   int32_t* perm = (aux && aux->perm) ? aux->perm : reinterpret_cast<int32_t*>(ws + pl.perm);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + pl.counts);
   int32_t* tiles = reinterpret_cast<int32_t*>(ws + pl.tiles);
+  // the packed down GEMM runs shorter row tiles, with a schedule of its own
+  int32_t* tiles2 = packed ? reinterpret_cast<int32_t*>(ws + pl.tiles2) : nullptr;
+  const int down_rows = packed ? packed_down_tile_rows(s.ffn_tile_rows) : s.ffn_tile_rows;
   hipEvent_t* ev = (aux && aux->stage_events) ? aux->stage_events : nullptr;
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
 
@@ -179,7 +183,7 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
   // stage 3: loads, offsets, tile schedule
   MOE_ZC_TRY(mark(3));
   MOE_ZC_TRY(launch_scan(counts, (int)s.chunks, E, N, loads, offsets, s.ffn_tile_rows, tiles,
-                         stream));
+                         down_rows, tiles2, stream));
   // stage 4: grouping permutation and row gather
   MOE_ZC_TRY(mark(4));
   if (bf)
@@ -211,9 +215,9 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
     p.A = h; p.lda = I; p.a_kwrap = (int)I; p.K = (int)I;
     p.B0 = w_down; p.ldb = I; p.b_group_stride = d * I;
     p.C = o; p.ldc = d; p.Nout = (int)d;
-    p.row_offsets = offsets; p.tile_prefix = tiles; p.G = N; p.M = 0;
+    p.row_offsets = offsets; p.tile_prefix = packed ? tiles2 : tiles; p.G = N; p.M = 0;
     if (packed)
-      MOE_ZC_TRY(launch_packed_gemm(p, kStoreBF16, s.ffn_tile_rows, s.smax, stream));
+      MOE_ZC_TRY(launch_packed_gemm(p, kStoreBF16, down_rows, s.smax, stream));
     else if (bf)
       MOE_ZC_TRY(launch_mfma_gemm(p, kStoreBF16, s.ffn_tile_rows, s.smax, stream));
     else

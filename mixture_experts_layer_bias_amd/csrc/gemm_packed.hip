@@ -37,10 +37,6 @@ namespace {
 constexpr int PK_WAVES = 4;                          // one wavefront per SIMD
 constexpr int PK_BKS = 64;                           // k per stage
 constexpr int PK_ROWB = PK_BKS * 2;                  // LDS bytes of one activation row
-constexpr int PK_MAXRB = kPackedMaxTileRows / 32;    // 32-row blocks per tile
-constexpr int PK_DEPTH = 3;                          // stages in the pipeline
-constexpr int PK_DIST = PK_DEPTH - 1;                // stages loaded ahead of use
-constexpr int PK_SLOT = PK_MAXRB * 32 * PK_ROWB;     // 32 KB per activation stage
 constexpr int PK_BLOCK = kPackedPanel * PK_BKS * 2;  // 32 KB of weights per stage
 constexpr int PK_QUARTER = PK_BLOCK / PK_WAVES;      // one wavefront's share
 static_assert(PK_QUARTER == 8 * 1024, "eight 1 KB pieces per wavefront");
@@ -57,10 +53,27 @@ __device__ __forceinline__ void barrier_in_flight(int c) {
   }
 }
 
-// NA = live 32-row blocks of the tile (1..8).
-template <int EPI, int NA>
+// Kernel configuration: MAXRB = most 32-row blocks per tile, DEPTH = stages
+// in the pipeline (DEPTH - 1 loaded ahead of use), OCC = workgroups per CU.
+//   gate/up, router: 256-row tiles, three stages, one workgroup per CU (256
+//     accumulators per wavefront leave room for no second workgroup);
+//   down: 128-row tiles, two stages, two workgroups per CU - its tiles are
+//     short (K = I), and a second workgroup covers each tile's pipeline fill
+//     and epilogue.
+template <int MAXRB_, int DEPTH_, int OCC_>
+struct PkCfg {
+  static constexpr int MAXRB = MAXRB_, DEPTH = DEPTH_, OCC = OCC_;
+  static constexpr int DIST = DEPTH - 1;
+  static constexpr int SLOT = MAXRB * 32 * PK_ROWB;  // bytes of one activation stage
+};
+using PkWide = PkCfg<kPackedMaxTileRows / 32, 3, 1>;
+using PkHalf = PkCfg<kPackedMaxTileRows / 64, 2, 2>;
+
+// NA = live 32-row blocks of the tile (1..CFG::MAXRB).
+template <typename CFG, int EPI, int NA>
 __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord& c,
                                            int n_tiles, char* __restrict__ smem) {
+  constexpr int PK_DEPTH = CFG::DEPTH, PK_DIST = CFG::DIST, PK_SLOT = CFG::SLOT;
   constexpr bool SWIGLU = (EPI == kSwiGLU_BF16);
   const int tid = threadIdx.x;
   // the wavefront index is uniform: keep it in a scalar register, so LDS
@@ -306,28 +319,31 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
   }
 }
 
-template <int EPI>
-__global__ __launch_bounds__(64 * PK_WAVES, 1) void packed_gemm_kernel(GemmProblem p, int n_tiles,
-                                                                      int total_bound,
-                                                                      int tile_rows) {
+template <typename CFG, int EPI>
+__global__ __launch_bounds__(64 * PK_WAVES, CFG::OCC) void packed_gemm_kernel(GemmProblem p,
+                                                                             int n_tiles,
+                                                                             int total_bound,
+                                                                             int tile_rows) {
   constexpr bool SWIGLU = (EPI == kSwiGLU_BF16);
-  __shared__ __attribute__((aligned(16))) char smem[PK_DEPTH * PK_SLOT];
+  __shared__ __attribute__((aligned(16))) char smem[CFG::DEPTH * CFG::SLOT];
   const int logical =
       xcd_logical_tile(p.tile_prefix ? p.tile_prefix[p.G] * n_tiles : total_bound);
   if (logical < 0) return;
   TileCoord c;
   if (!map_tile<kPackedPanel, SWIGLU>(p, n_tiles, logical, tile_rows, c)) return;
-  const int nb = (c.m_end - c.m0 + 31) / 32;  // at most 8: tiles hold at most 256 rows
+  // at most CFG::MAXRB: the host checks tile_rows against the configuration
+  const int nb = (c.m_end - c.m0 + 31) / 32;
+  if (nb <= 0) return;
+  constexpr int M = CFG::MAXRB;
   switch (nb) {
-    case 0: return;
-    case 1: run_packed<EPI, 1>(p, c, n_tiles, smem); break;
-    case 2: run_packed<EPI, 2>(p, c, n_tiles, smem); break;
-    case 3: run_packed<EPI, 3>(p, c, n_tiles, smem); break;
-    case 4: run_packed<EPI, 4>(p, c, n_tiles, smem); break;
-    case 5: run_packed<EPI, 5>(p, c, n_tiles, smem); break;
-    case 6: run_packed<EPI, 6>(p, c, n_tiles, smem); break;
-    case 7: run_packed<EPI, 7>(p, c, n_tiles, smem); break;
-    default: run_packed<EPI, 8>(p, c, n_tiles, smem); break;
+    case 1: run_packed<CFG, EPI, 1>(p, c, n_tiles, smem); break;
+    case 2: run_packed<CFG, EPI, (M >= 2 ? 2 : M)>(p, c, n_tiles, smem); break;
+    case 3: run_packed<CFG, EPI, (M >= 3 ? 3 : M)>(p, c, n_tiles, smem); break;
+    case 4: run_packed<CFG, EPI, (M >= 4 ? 4 : M)>(p, c, n_tiles, smem); break;
+    case 5: run_packed<CFG, EPI, (M >= 5 ? 5 : M)>(p, c, n_tiles, smem); break;
+    case 6: run_packed<CFG, EPI, (M >= 6 ? 6 : M)>(p, c, n_tiles, smem); break;
+    case 7: run_packed<CFG, EPI, (M >= 7 ? 7 : M)>(p, c, n_tiles, smem); break;
+    default: run_packed<CFG, EPI, M>(p, c, n_tiles, smem); break;
   }
 }
 
@@ -444,6 +460,10 @@ hipError_t launch_split_router_packed(const float* w, bf16_t* out, int E, int d,
   return hipGetLastError();
 }
 
+int packed_down_tile_rows(int ffn_tile_rows) {
+  return ffn_tile_rows < 32 * PkHalf::MAXRB ? ffn_tile_rows : 32 * PkHalf::MAXRB;
+}
+
 hipError_t launch_packed_gemm(const GemmProblem& p, int epilogue, int tile_rows, int64_t max_rows,
                               hipStream_t s) {
   if (p.K % PK_BKS != 0 || p.a_kwrap % PK_BKS != 0) return hipErrorInvalidValue;
@@ -452,6 +472,9 @@ hipError_t launch_packed_gemm(const GemmProblem& p, int epilogue, int tile_rows,
   const bool swiglu = (epilogue == kSwiGLU_BF16);
   if (swiglu && p.Nout % (kPackedPanel / 2) != 0) return hipErrorInvalidValue;
   const int n_tiles = swiglu ? p.Nout / (kPackedPanel / 2) : (p.Nout + kPackedPanel - 1) / kPackedPanel;
+  // the down GEMM runs the two-workgroups-per-CU configuration
+  const bool half_cfg = (epilogue == kStoreBF16);
+  if (tile_rows > 32 * (half_cfg ? PkHalf::MAXRB : PkWide::MAXRB)) return hipErrorInvalidValue;
   int64_t mt_bound;
   if (p.tile_prefix) {
     mt_bound = (max_rows + (int64_t)p.G * (tile_rows - 1)) / tile_rows;
@@ -467,13 +490,16 @@ hipError_t launch_packed_gemm(const GemmProblem& p, int epilogue, int tile_rows,
   const int total = (int)(mt_bound * n_tiles);
   switch (epilogue) {
     case kStoreF32:
-      hipLaunchKernelGGL(packed_gemm_kernel<kStoreF32>, grid, block, 0, s, p, n_tiles, total, tile_rows);
+      hipLaunchKernelGGL((packed_gemm_kernel<PkWide, kStoreF32>), grid, block, 0, s, p, n_tiles,
+                         total, tile_rows);
       break;
     case kStoreBF16:
-      hipLaunchKernelGGL(packed_gemm_kernel<kStoreBF16>, grid, block, 0, s, p, n_tiles, total, tile_rows);
+      hipLaunchKernelGGL((packed_gemm_kernel<PkHalf, kStoreBF16>), grid, block, 0, s, p, n_tiles,
+                         total, tile_rows);
       break;
     case kSwiGLU_BF16:
-      hipLaunchKernelGGL(packed_gemm_kernel<kSwiGLU_BF16>, grid, block, 0, s, p, n_tiles, total, tile_rows);
+      hipLaunchKernelGGL((packed_gemm_kernel<PkWide, kSwiGLU_BF16>), grid, block, 0, s, p, n_tiles,
+                         total, tile_rows);
       break;
     default: return hipErrorInvalidValue;
   }

@@ -22,9 +22,11 @@ hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E,
 hipError_t launch_chunk_hist(const int32_t* idx, int64_t T, int K, int E, int N,
                              int32_t* counts, int32_t* rank, hipStream_t s);
 // counts [C, E] -> exclusive per-expert chunk bases (in place); loads [E];
-// offsets [N+1]; m-tile prefix [N+1] for tiles of `bm` rows.
+// offsets [N+1]; m-tile prefix [N+1] for tiles of `bm` rows, and another for
+// tiles of `bm2` rows when tile_prefix2 is not null.
 hipError_t launch_scan(int32_t* counts, int C, int E, int N, int32_t* loads,
-                       int32_t* offsets, int bm, int32_t* tile_prefix, hipStream_t s);
+                       int32_t* offsets, int bm, int32_t* tile_prefix, int bm2,
+                       int32_t* tile_prefix2, hipStream_t s);
 // Grouped rows: pos (rank -> row), perm, and xp[row] = x[token] (the row
 // copy only when xp is not null).
 template <typename T>
@@ -86,9 +88,11 @@ hipError_t launch_pack_weights(const bf16_t* w0, const bf16_t* w1, bf16_t* out, 
                                int rows, int K, bool swiglu, hipStream_t s);
 // W_router fp32 [E, d] -> packed two-term bf16 split [E, 2d].
 hipError_t launch_split_router_packed(const float* w, bf16_t* out, int E, int d, hipStream_t s);
-// B0 = packed weights; B1, ldb and b_group_stride are unused.
+// B0 = packed weights; B1, ldb and b_group_stride are unused.  The down GEMM
+// (kStoreBF16) runs tiles of at most packed_down_tile_rows() rows.
 hipError_t launch_packed_gemm(const GemmProblem& p, int epilogue, int tile_rows,
                               int64_t max_rows, hipStream_t s);
+int packed_down_tile_rows(int ffn_tile_rows);
 
 // fp32 FMA path (gemm_simt.hip).
 hipError_t launch_simt_gemm(const GemmProblem& p, int epilogue, int64_t max_rows,

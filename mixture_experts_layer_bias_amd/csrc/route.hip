@@ -165,12 +165,14 @@ hipError_t launch_chunk_hist(const int32_t* idx, int64_t T, int K, int E, int N,
 //   loads[e]      = sum_c counts[c][e]
 //   offsets[e]    = sum_{e' < e, e' < N} loads[e']            (offsets[N] = S)
 //   tile_prefix[e] = sum_{e' < e} ceil(loads[e'] / bm)        (FFN experts)
+//   tile_prefix2: the same for tiles of bm2 rows (optional)
 // Wave w owns the chunk range [C*w/16, C*(w+1)/16); all sums are integer.
 constexpr int kScanWaves = 16;
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts, int C, int E,
                                                     int N, int32_t* __restrict__ loads,
                                                     int32_t* __restrict__ offsets, int bm,
-                                                    int32_t* __restrict__ tile_prefix) {
+                                                    int32_t* __restrict__ tile_prefix, int bm2,
+                                                    int32_t* __restrict__ tile_prefix2) {
   __shared__ int32_t part[kScanWaves][kMaxExperts];
   __shared__ int32_t tot[kMaxExperts];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -207,38 +209,44 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts
     const int seg = (N + 63) / 64;
     const int e0 = lane * seg;
     const int e1 = min(N, e0 + seg);
-    int sr = 0, st = 0;
+    int sr = 0, st = 0, st2 = 0;
     for (int e = e0; e < e1; ++e) {
       sr += tot[e];
       st += (tot[e] + bm - 1) / bm;
+      st2 += (tot[e] + bm2 - 1) / bm2;
     }
-    int ir = sr, it = st;  // inclusive scan over lanes
+    int ir = sr, it = st, it2 = st2;  // inclusive scan over lanes
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int a = __shfl_up(ir, off), b = __shfl_up(it, off);
+      const int a = __shfl_up(ir, off), b = __shfl_up(it, off), b2 = __shfl_up(it2, off);
       if (lane >= off) {
         ir += a;
         it += b;
+        it2 += b2;
       }
     }
-    int rr = ir - sr, rt = it - st;
+    int rr = ir - sr, rt = it - st, rt2 = it2 - st2;
     for (int e = e0; e < e1; ++e) {
       offsets[e] = rr;
       tile_prefix[e] = rt;
+      if (tile_prefix2) tile_prefix2[e] = rt2;
       rr += tot[e];
       rt += (tot[e] + bm - 1) / bm;
+      rt2 += (tot[e] + bm2 - 1) / bm2;
     }
     if (lane == 63) {
       offsets[N] = ir;
       tile_prefix[N] = it;
+      if (tile_prefix2) tile_prefix2[N] = it2;
     }
   }
 }
 
 hipError_t launch_scan(int32_t* counts, int C, int E, int N, int32_t* loads, int32_t* offsets,
-                       int bm, int32_t* tile_prefix, hipStream_t s) {
+                       int bm, int32_t* tile_prefix, int bm2, int32_t* tile_prefix2,
+                       hipStream_t s) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, counts, C, E, N, loads, offsets, bm,
-                     tile_prefix);
+                     tile_prefix, bm2, tile_prefix2);
   return hipGetLastError();
 }
 
