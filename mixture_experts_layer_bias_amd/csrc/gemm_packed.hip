@@ -146,6 +146,13 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
     _Pragma("unroll") for (int q = 0; q < 8; ++q) fb[u][q] =                          \
         *reinterpret_cast<const bf16x8_t*>(b_ + q * 1024);                            \
   }
+  // half h of the eight weight pieces of stage kt
+#define PK_LOAD_BH(kt, u, h)                                                          \
+  {                                                                                   \
+    const char* b_ = B_pan + (int64_t)(kt) * PK_BLOCK + b_off;                        \
+    _Pragma("unroll") for (int q = 4 * (h); q < 4 * (h) + 4; ++q) fb[u][q] =          \
+        *reinterpret_cast<const bf16x8_t*>(b_ + q * 1024);                            \
+  }
 #define PK_DMA_A(kt, u)                                                               \
   {                                                                                   \
     const int ks_ = (kt) >= a_wrap ? (kt) - a_wrap : (kt);                            \
@@ -171,41 +178,34 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
   }
   // Stage kt uses slot and register set u = kt % PK_DEPTH.  It refills the
   // set of stage kt-1 (all wavefronts finished reading that slot before the
-  // last barrier) with stage kt+PK_DIST: weights during substep 0, activations during
-  // substep 1.  Substep ks reads the activation fragments of ks+1 and runs
-  // the MFMAs of ks, interleaved (two MFMAs, one LDS read, a share of the
-  // vector-memory reads): one wavefront per SIMD has no other wavefront to
-  // cover a burst of memory instructions, so they are spread between MFMAs.
-  // Before the last substep the wavefront waits for its own loads of stage
-  // kt+1 - loads complete in issue order, and the later stages' loads stay
-  // in flight - and meets the others, so stage kt+1 is whole in LDS and
-  // in registers; the last substep's MFMAs then cover the first fragment
-  // reads of kt+1.  FULL: stage kt+PK_DIST exists (the steady state; no
-  // branches).
-  // NA groups of (2 MFMAs, 1 LDS read, VM vector-memory reads): keeps the
-  // matrix pipe fed while the memory instructions issue
-#define PK_INTERLEAVE(VM)                                                             \
-  _Pragma("unroll") for (int g_ = 0; g_ < NA; ++g_) {                                 \
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                \
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                \
-    if ((VM) > 0) __builtin_amdgcn_sched_group_barrier(0x020, (VM), 0);               \
-  }
+  // last barrier) with stage kt+PK_DIST: half of the weights during substep
+  // 0, the other half during substep 1, the activations during substep 2.
+  // Substep ks reads the activation fragments of ks+1 and runs the MFMAs of
+  // ks, interleaved (two MFMAs, one LDS read, a share of the vector-memory
+  // reads): one wavefront per SIMD has no other wavefront to cover a burst of
+  // memory instructions, so they are spread between MFMAs.  Before the last
+  // substep the wavefront waits for its own loads of stage kt+1 - loads
+  // complete in issue order, and the later stages' loads stay in flight - and
+  // meets the others, so stage kt+1 is whole in LDS and in registers; the
+  // last substep's MFMAs then cover the first fragment reads of kt+1.
+  // FULL: stage kt+PK_DIST exists (the steady state; no branches).
 #define PK_STAGE(kt, u, FULL)                                                         \
   {                                                                                   \
     const bool refill_ = FULL || (kt) + PK_DIST < nk;                                 \
-    if (refill_) PK_LOAD_B((kt) + PK_DIST, ((u) + PK_DIST) % PK_DEPTH);               \
+    if (refill_) PK_LOAD_BH((kt) + PK_DIST, ((u) + PK_DIST) % PK_DEPTH, 0);           \
     PK_LOADF(1, u, 1);                                                                \
     PK_MMA(0, u, 0);                                                                  \
-    PK_INTERLEAVE((8 + NA - 1) / NA);                                                 \
+    PK_INTERLEAVE((4 + NA - 1) / NA);                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                \
-    if (refill_) PK_DMA_A((kt) + PK_DIST, ((u) + PK_DIST) % PK_DEPTH);                \
+    if (refill_) PK_LOAD_BH((kt) + PK_DIST, ((u) + PK_DIST) % PK_DEPTH, 1);           \
     PK_LOADF(0, u, 2);                                                                \
     PK_MMA(1, u, 1);                                                                  \
-    PK_INTERLEAVE(1);                                                                 \
+    PK_INTERLEAVE((4 + NA - 1) / NA);                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                \
+    if (refill_) PK_DMA_A((kt) + PK_DIST, ((u) + PK_DIST) % PK_DEPTH);                \
     PK_LOADF(1, u, 3);                                                                \
     PK_MMA(0, u, 2);                                                                  \
-    PK_INTERLEAVE(0);                                                                 \
+    PK_INTERLEAVE(1);                                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                \
     if (FULL) ring_barrier<(PK_DIST - 1) * (8 + NA)>();                               \
     else barrier_in_flight<8 + NA>(min(nk - 1, (kt) + PK_DIST) - ((kt) + 1));         \
@@ -252,6 +252,7 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
   for (int u = 0; u + 1 < PK_DIST; ++u)
     if (kt + PK_DEPTH + u < nk) PK_STAGE(kt + PK_DEPTH + u, u, false);
 #undef PK_LOAD_B
+#undef PK_LOAD_BH
 #undef PK_DMA_A
 #undef PK_LOADF
 #undef PK_MMA
