@@ -189,6 +189,13 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
   // meets the others, so stage kt+1 is whole in LDS and in registers; the
   // last substep's MFMAs then cover the first fragment reads of kt+1.
   // FULL: stage kt+PK_DIST exists (the steady state; no branches).
+  // NA groups of (2 MFMAs, 1 LDS read, VM vector-memory reads)
+#define PK_INTERLEAVE(VM)                                                             \
+  _Pragma("unroll") for (int g_ = 0; g_ < NA; ++g_) {                                 \
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                \
+    if ((VM) > 0) __builtin_amdgcn_sched_group_barrier(0x020, (VM), 0);               \
+  }
 #define PK_STAGE(kt, u, FULL)                                                         \
   {                                                                                   \
     const bool refill_ = FULL || (kt) + PK_DIST < nk;                                 \
