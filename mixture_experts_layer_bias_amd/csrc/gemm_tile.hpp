@@ -19,7 +19,8 @@ struct TileCoord {
 // Logical tile -> (group, rows, output columns).  Returns false past the end.
 // Grouped problems (tile_prefix set): tiles run expert by expert, then weight
 // panel, then row part; an expert whose rows need several tiles is cut into
-// equal parts.  One group (tile_prefix null): `tile_rows` rows per tile.
+// near-equal parts of whole 32-row blocks (only the last part is ragged), so
+// a split costs no more padded MFMA rows than an unsplit expert.  One group (tile_prefix null): `tile_rows` rows per tile.
 // A panel is BN weight rows (SwiGLU: BN / 2 gate rows and as many up rows).
 template <int BN, bool SWIGLU>
 __device__ __forceinline__ bool map_tile(const GemmProblem& p, int n_tiles, int logical,
@@ -39,7 +40,7 @@ __device__ __forceinline__ bool map_tile(const GemmProblem& p, int n_tiles, int 
     const int nt = local / mtc;
     const int mt = local - nt * mtc;
     const int r0 = p.row_offsets[g], r1 = p.row_offsets[g + 1];
-    const int rpt = (r1 - r0 + mtc - 1) / mtc;  // equal parts
+    const int rpt = ((r1 - r0 + mtc - 1) / mtc + 31) / 32 * 32;  // parts of whole 32-row blocks
     c.g = g;
     c.m0 = r0 + mt * rpt;
     c.m_end = min(c.m0 + rpt, r1);
