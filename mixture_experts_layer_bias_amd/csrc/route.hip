@@ -160,43 +160,43 @@ hipError_t launch_chunk_hist(const int32_t* idx, int64_t T, int K, int E, int N,
 }
 
 // ---------------------------------------------------------------------------
-// One workgroup of 16 wavefronts turns the chunk counts into:
-//   counts[c][e] <- sum_{c' < c} counts[c'][e]   (exclusive, in place)
-//   loads[e]      = sum_c counts[c][e]
-//   offsets[e]    = sum_{e' < e, e' < N} loads[e']            (offsets[N] = S)
-//   tile_prefix[e] = sum_{e' < e} ceil(loads[e'] / bm)        (FFN experts)
-//   tile_prefix2: the same for tiles of bm2 rows (optional)
-// Wave w owns the chunk range [C*w/16, C*(w+1)/16); all sums are integer.
+// Scan of the chunk counts, in two launches (all sums are integer):
+//   scan_chunks: counts[c][e] <- sum_{c' < c} counts[c'][e]  (exclusive, in
+//     place) and loads[e] = sum_c counts[c][e].  One workgroup of 16
+//     wavefronts per 64 experts (lane = expert); wave w owns the chunk range
+//     [C*w/16, C*(w+1)/16).
+//   scan_experts: offsets[e] = sum_{e' < e} loads[e'] over the N FFN experts
+//     (offsets[N] = S), tile_prefix[e] = sum_{e' < e} ceil(loads[e'] / bm),
+//     and tile_prefix2 the same for tiles of bm2 rows (optional).  One
+//     wavefront; lane l owns a contiguous segment of experts.
 constexpr int kScanWaves = 16;
-__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts, int C, int E,
-                                                    int N, int32_t* __restrict__ loads,
-                                                    int32_t* __restrict__ offsets, int bm,
-                                                    int32_t* __restrict__ tile_prefix, int bm2,
-                                                    int32_t* __restrict__ tile_prefix2) {
-  __shared__ int32_t part[kScanWaves][kMaxExperts];
-  __shared__ int32_t tot[kMaxExperts];
+__global__ __launch_bounds__(64 * kScanWaves) void scan_chunks_kernel(
+    int32_t* __restrict__ counts, int C, int E, int32_t* __restrict__ loads) {
+  __shared__ int32_t part[kScanWaves][64];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int e = blockIdx.x * 64 + lane;
+  const bool live = e < E;
   const int c0 = (int)(((int64_t)C * w) / kScanWaves);
   const int c1 = (int)(((int64_t)C * (w + 1)) / kScanWaves);
-  for (int e = lane; e < E; e += 64) {
-    int s = 0;
+  int s = 0;
+  if (live) {
+#pragma unroll 8
     for (int c = c0; c < c1; ++c) s += counts[(int64_t)c * E + e];
-    part[w][e] = s;
   }
+  part[w][lane] = s;
   __syncthreads();
-  for (int e = tid; e < E; e += 1024) {
+  if (w == 0) {
     int run = 0;
     for (int v = 0; v < kScanWaves; ++v) {
-      const int x = part[v][e];
-      part[v][e] = run;
+      const int x = part[v][lane];
+      part[v][lane] = run;
       run += x;
     }
-    tot[e] = run;
-    loads[e] = run;
+    if (live) loads[e] = run;
   }
   __syncthreads();
-  for (int e = lane; e < E; e += 64) {
-    int run = part[w][e];
+  if (live) {
+    int run = part[w][lane];
     for (int c = c0; c < c1; ++c) {
       const int64_t q = (int64_t)c * E + e;
       const int x = counts[q];
@@ -204,48 +204,57 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts
       run += x;
     }
   }
-  if (w == 0) {
-    // lane owns the contiguous expert segment [lane*seg, lane*seg + seg)
-    const int seg = (N + 63) / 64;
-    const int e0 = lane * seg;
-    const int e1 = min(N, e0 + seg);
-    int sr = 0, st = 0, st2 = 0;
-    for (int e = e0; e < e1; ++e) {
-      sr += tot[e];
-      st += (tot[e] + bm - 1) / bm;
-      st2 += (tot[e] + bm2 - 1) / bm2;
-    }
-    int ir = sr, it = st, it2 = st2;  // inclusive scan over lanes
+}
+
+__global__ __launch_bounds__(64) void scan_experts_kernel(const int32_t* __restrict__ loads,
+                                                          int N, int32_t* __restrict__ offsets,
+                                                          int bm, int32_t* __restrict__ tile_prefix,
+                                                          int bm2,
+                                                          int32_t* __restrict__ tile_prefix2) {
+  const int lane = threadIdx.x;
+  const int seg = (N + 63) / 64;
+  const int e0 = lane * seg;
+  const int e1 = min(N, e0 + seg);
+  int sr = 0, st = 0, st2 = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int l = loads[e];
+    sr += l;
+    st += (l + bm - 1) / bm;
+    st2 += (l + bm2 - 1) / bm2;
+  }
+  int ir = sr, it = st, it2 = st2;  // inclusive scan over lanes
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int a = __shfl_up(ir, off), b = __shfl_up(it, off), b2 = __shfl_up(it2, off);
-      if (lane >= off) {
-        ir += a;
-        it += b;
-        it2 += b2;
-      }
+  for (int off = 1; off < 64; off <<= 1) {
+    const int a = __shfl_up(ir, off), b = __shfl_up(it, off), b2 = __shfl_up(it2, off);
+    if (lane >= off) {
+      ir += a;
+      it += b;
+      it2 += b2;
     }
-    int rr = ir - sr, rt = it - st, rt2 = it2 - st2;
-    for (int e = e0; e < e1; ++e) {
-      offsets[e] = rr;
-      tile_prefix[e] = rt;
-      if (tile_prefix2) tile_prefix2[e] = rt2;
-      rr += tot[e];
-      rt += (tot[e] + bm - 1) / bm;
-      rt2 += (tot[e] + bm2 - 1) / bm2;
-    }
-    if (lane == 63) {
-      offsets[N] = ir;
-      tile_prefix[N] = it;
-      if (tile_prefix2) tile_prefix2[N] = it2;
-    }
+  }
+  int rr = ir - sr, rt = it - st, rt2 = it2 - st2;
+  for (int e = e0; e < e1; ++e) {
+    const int l = loads[e];
+    offsets[e] = rr;
+    tile_prefix[e] = rt;
+    if (tile_prefix2) tile_prefix2[e] = rt2;
+    rr += l;
+    rt += (l + bm - 1) / bm;
+    rt2 += (l + bm2 - 1) / bm2;
+  }
+  if (lane == 63) {
+    offsets[N] = ir;
+    tile_prefix[N] = it;
+    if (tile_prefix2) tile_prefix2[N] = it2;
   }
 }
 
 hipError_t launch_scan(int32_t* counts, int C, int E, int N, int32_t* loads, int32_t* offsets,
                        int bm, int32_t* tile_prefix, int bm2, int32_t* tile_prefix2,
                        hipStream_t s) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, counts, C, E, N, loads, offsets, bm,
+  hipLaunchKernelGGL(scan_chunks_kernel, dim3((unsigned)((E + 63) / 64)), dim3(64 * kScanWaves),
+                     0, s, counts, C, E, loads);
+  hipLaunchKernelGGL(scan_experts_kernel, dim3(1), dim3(64), 0, s, loads, N, offsets, bm,
                      tile_prefix, bm2, tile_prefix2);
   return hipGetLastError();
 }
