@@ -25,9 +25,8 @@
 // every row (up to 8 x 2 MFMA blocks, 256 accumulators).  Weights go from
 // global memory straight into registers: each wavefront loads only its own
 // quarter, nothing is loaded twice and nothing passes through LDS.
-// Activations, which all four wavefronts share, stream into a four-slot LDS
-// ring by direct loads.  Both operands are loaded PK_DIST stages ahead of the
-// MFMAs (three: up to about 190 KB of loads in flight per CU).
+// Activations, which all four wavefronts share, stream into an LDS ring by
+// direct loads.  Both operands are loaded CFG::DIST stages ahead of the MFMAs.
 #include "gemm_tile.hpp"
 
 namespace moezc {
@@ -40,18 +39,6 @@ constexpr int PK_ROWB = PK_BKS * 2;                  // LDS bytes of one activat
 constexpr int PK_BLOCK = kPackedPanel * PK_BKS * 2;  // 32 KB of weights per stage
 constexpr int PK_QUARTER = PK_BLOCK / PK_WAVES;      // one wavefront's share
 static_assert(PK_QUARTER == 8 * 1024, "eight 1 KB pieces per wavefront");
-
-// Ring barrier that lets the newest c stages of STEP loads each stay in
-// flight (c = 1 .. 3; otherwise none).
-template <int STEP>
-__device__ __forceinline__ void barrier_in_flight(int c) {
-  switch (c) {
-    case 1: ring_barrier<STEP>(); break;
-    case 2: ring_barrier<2 * STEP>(); break;
-    case 3: ring_barrier<3 * STEP>(); break;
-    default: ring_barrier<0>(); break;  // c <= 0: nothing may stay in flight
-  }
-}
 
 // Kernel configuration: MAXRB = most 32-row blocks per tile, DEPTH = stages
 // in the pipeline (DEPTH - 1 loaded ahead of use), OCC = workgroups per CU.
@@ -146,13 +133,6 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
     _Pragma("unroll") for (int q = 0; q < 8; ++q) fb[u][q] =                          \
         *reinterpret_cast<const bf16x8_t*>(b_ + q * 1024);                            \
   }
-  // half h of the eight weight pieces of stage kt
-#define PK_LOAD_BH(kt, u, h)                                                          \
-  {                                                                                   \
-    const char* b_ = B_pan + (int64_t)(kt) * PK_BLOCK + b_off;                        \
-    _Pragma("unroll") for (int q = 4 * (h); q < 4 * (h) + 4; ++q) fb[u][q] =          \
-        *reinterpret_cast<const bf16x8_t*>(b_ + q * 1024);                            \
-  }
 #define PK_DMA_A(kt, u)                                                               \
   {                                                                                   \
     const int ks_ = (kt) >= a_wrap ? (kt) - a_wrap : (kt);                            \
@@ -169,102 +149,89 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
     _Pragma("unroll") for (int i = 0; i < NA; ++i) fa[fs][i] =                        \
         *reinterpret_cast<const bf16x8_t*>(l_ + i * 4096);                            \
   }
-#define PK_MMA(fs, u, ks)                                                             \
-  {                                                                                   \
-    _Pragma("unroll") for (int i = 0; i < NA; ++i)                                    \
-        _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] =                     \
-        __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fs][i], fb[u][2 * (ks) + j],       \
-                                                acc[i][j], 0, 0, 0);                  \
-  }
-  // Stage kt uses slot and register set u = kt % PK_DEPTH.  It refills the
-  // set of stage kt-1 (all wavefronts finished reading that slot before the
-  // last barrier) with stage kt+PK_DIST: half of the weights during substep
-  // 0, the other half during substep 1, the activations during substep 2.
-  // Substep ks reads the activation fragments of ks+1 and runs the MFMAs of
-  // ks, interleaved (two MFMAs, one LDS read, a share of the vector-memory
-  // reads): one wavefront per SIMD has no other wavefront to cover a burst of
-  // memory instructions, so they are spread between MFMAs.  Before the last
-  // substep the wavefront waits for its own loads of stage kt+1 - loads
-  // complete in issue order, and the later stages' loads stay in flight - and
-  // meets the others, so stage kt+1 is whole in LDS and in registers; the
-  // last substep's MFMAs then cover the first fragment reads of kt+1.
-  // FULL: stage kt+PK_DIST exists (the steady state; no branches).
-  // NA groups of (2 MFMAs, 1 LDS read, VM vector-memory reads)
-#define PK_INTERLEAVE(VM)                                                             \
+  // One substep ks of stage slot/register set u.  For each live row block g:
+  // the LDS read of block g's fragment for the next substep (fragment set
+  // 1 - fs, slot nu, substep nks; skipped when NEXT is false), the two MFMAs
+  // of block g, and block g's share of the refill of stage KN into set NU
+  // (VMK 1 / 2: weight pieces 0-3 / 4-7, spread over the blocks; VMK 3: the
+  // activation rows of block g; VMK 0: none).  One wavefront per SIMD has no
+  // other wavefront to cover a burst of memory instructions, so they are
+  // spread between MFMAs; a scheduling fence after each group keeps that
+  // order through both scheduler passes (without it, register reuse in the
+  // second pass let the LDS reads and direct loads bunch up and the MFMAs
+  // wait on them).
+#define PK_SUB(fs, u, ks, NEXT, nu, nks, VMK, KN, NU)                                 \
   _Pragma("unroll") for (int g_ = 0; g_ < NA; ++g_) {                                 \
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                \
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                \
-    if ((VM) > 0) __builtin_amdgcn_sched_group_barrier(0x020, (VM), 0);               \
+    if (NEXT) fa[1 - (fs)][g_] = *reinterpret_cast<const bf16x8_t*>(                  \
+        smem + (nu) * PK_SLOT + fr[nks] + g_ * 4096);                                 \
+    acc[g_][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fs][g_], fb[u][2 * (ks)], \
+                                                         acc[g_][0], 0, 0, 0);        \
+    acc[g_][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[fs][g_], fb[u][2 * (ks) + 1], \
+                                                         acc[g_][1], 0, 0, 0);        \
+    if ((VMK) == 1 || (VMK) == 2) {                                                   \
+      const char* b_ = B_pan + (int64_t)(KN) * PK_BLOCK + b_off;                      \
+      _Pragma("unroll") for (int q = 4 * ((VMK) - 1) + (g_ * 4) / NA;                 \
+                             q < 4 * ((VMK) - 1) + ((g_ + 1) * 4) / NA; ++q)          \
+          fb[NU][q] = *reinterpret_cast<const bf16x8_t*>(b_ + q * 1024);              \
+    } else if ((VMK) == 3) {                                                          \
+      const int ks_ = (KN) >= a_wrap ? (KN) - a_wrap : (KN);                          \
+      const char* a_ = A_tile + (int64_t)ks_ * a_step;                                \
+      const __amdgpu_buffer_rsrc_t r_ =                                               \
+          __builtin_amdgcn_make_buffer_rsrc((void*)a_, 0, 0x7fffffff, 0x00020000);    \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(                                       \
+          r_, (lds_void_t*)(a_dst + (NU) * PK_SLOT + g_ * 4096), 16, a_src[g_], 0, 0, 0); \
+    }                                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                \
   }
-#define PK_STAGE(kt, u, FULL)                                                         \
+  // Stage kt uses slot and register set u = kt % PK_DEPTH and refills the set
+  // of stage kt-1 (every wavefront finished reading that slot before the last
+  // barrier) with stage kt+PK_DIST: weight halves in substeps 0 and 1, the
+  // activations in substep 2.  Before the last substep the wavefront waits for
+  // its own loads of stage kt+1 (loads complete in issue order; the refill of
+  // kt+PK_DIST stays in flight) and meets the others, so stage kt+1 is whole
+  // in LDS and in registers; the last substep's MFMAs cover the first
+  // fragment reads of kt+1.  In the steady loop, a refill past the last stage
+  // repeats the last stage's addresses (those slots and registers are never
+  // read), so every stage there keeps the same count of loads in flight and
+  // the loop has no branches.  The stages after the loop (fewer than
+  // PK_DEPTH) would only refill past the end, so they issue no loads and wait
+  // for all of them: the compiler drops register loads whose results are
+  // never read, and a dummy refill there would not be issued at all, leaving
+  // a count-based wait short.
+#define PK_STAGE(kt, u, REFILL)                                                       \
   {                                                                                   \
-    const bool refill_ = FULL || (kt) + PK_DIST < nk;                                 \
-    if (refill_) PK_LOAD_BH((kt) + PK_DIST, ((u) + PK_DIST) % PK_DEPTH, 0);           \
-    PK_LOADF(1, u, 1);                                                                \
-    PK_MMA(0, u, 0);                                                                  \
-    PK_INTERLEAVE((4 + NA - 1) / NA);                                                 \
+    const int kn_ = min((kt) + PK_DIST, nk - 1);                                      \
+    const int un_ = ((u) + PK_DIST) % PK_DEPTH;                                       \
+    PK_SUB(0, u, 0, true, u, 1, (REFILL) ? 1 : 0, kn_, un_);                          \
+    PK_SUB(1, u, 1, true, u, 2, (REFILL) ? 2 : 0, kn_, un_);                          \
+    PK_SUB(0, u, 2, true, u, 3, (REFILL) ? 3 : 0, kn_, un_);                          \
+    ring_barrier<(REFILL) ? (PK_DIST - 1) * (8 + NA) : 0>();                          \
     __builtin_amdgcn_sched_barrier(0);                                                \
-    if (refill_) PK_LOAD_BH((kt) + PK_DIST, ((u) + PK_DIST) % PK_DEPTH, 1);           \
-    PK_LOADF(0, u, 2);                                                                \
-    PK_MMA(1, u, 1);                                                                  \
-    PK_INTERLEAVE((4 + NA - 1) / NA);                                                 \
-    __builtin_amdgcn_sched_barrier(0);                                                \
-    if (refill_) PK_DMA_A((kt) + PK_DIST, ((u) + PK_DIST) % PK_DEPTH);                \
-    PK_LOADF(1, u, 3);                                                                \
-    PK_MMA(0, u, 2);                                                                  \
-    PK_INTERLEAVE(1);                                                                 \
-    __builtin_amdgcn_sched_barrier(0);                                                \
-    if (FULL) ring_barrier<(PK_DIST - 1) * (8 + NA)>();                               \
-    else barrier_in_flight<8 + NA>(min(nk - 1, (kt) + PK_DIST) - ((kt) + 1));         \
-    if (FULL || (kt) + 1 < nk) PK_LOADF(0, ((u) + 1) % PK_DEPTH, 0);                  \
-    PK_MMA(1, u, 3);                                                                  \
-    PK_INTERLEAVE(0);                                                                 \
-    __builtin_amdgcn_sched_barrier(0);                                                \
+    PK_SUB(1, u, 3, true, ((u) + 1) % PK_DEPTH, 0, 0, 0, 0);                          \
   }
 
-  // prologue: stages 0 .. PK_DIST-1, weights then activations of each; wait
-  // for stage 0 only.  Where the steady-state loop runs, the prologue is
-  // straight-line code, so the compiler enters the loop knowing which loads
-  // are still in flight and adds no wait of its own at the loop top.
-  int kt = 0;
-  if (nk >= PK_DEPTH + PK_DIST) {
+  // prologue: stages 0 .. PK_DIST-1 (repeating the last stage where nk is
+  // smaller), weights then activations of each; wait for stage 0 only
 #pragma unroll
-    for (int u = 0; u < PK_DIST; ++u) {
-      PK_LOAD_B(u, u);
-      PK_DMA_A(u, u);
-    }
-    ring_barrier<(PK_DIST - 1) * (8 + NA)>();
-    PK_LOADF(0, 0, 0);
-    // steady state: PK_DEPTH stages per trip, every one refilling
-    do {
-#pragma unroll
-      for (int u = 0; u < PK_DEPTH; ++u) PK_STAGE(kt + u, u, true);
-      kt += PK_DEPTH;
-    } while (kt + PK_DEPTH + PK_DIST <= nk);
-  } else {
-#pragma unroll
-    for (int u = 0; u < PK_DIST; ++u)
-      if (u < nk) {
-        PK_LOAD_B(u, u);
-        PK_DMA_A(u, u);
-      }
-    barrier_in_flight<8 + NA>(min(nk, PK_DIST) - 1);
-    PK_LOADF(0, 0, 0);
+  for (int u = 0; u < PK_DIST; ++u) {
+    PK_LOAD_B(min(u, nk - 1), u);
+    PK_DMA_A(min(u, nk - 1), u);
   }
-  // the last stages (fewer than PK_DEPTH + PK_DIST)
+  ring_barrier<(PK_DIST - 1) * (8 + NA)>();
+  PK_LOADF(0, 0, 0);
+  int kt = 0;
+  for (; kt + PK_DEPTH <= nk; kt += PK_DEPTH) {
 #pragma unroll
-  for (int u = 0; u < PK_DEPTH; ++u)
+    for (int u = 0; u < PK_DEPTH; ++u) PK_STAGE(kt + u, u, true);
+  }
+#pragma unroll
+  for (int u = 0; u + 1 < PK_DEPTH; ++u)
     if (kt + u < nk) PK_STAGE(kt + u, u, false);
-#pragma unroll
-  for (int u = 0; u + 1 < PK_DIST; ++u)
-    if (kt + PK_DEPTH + u < nk) PK_STAGE(kt + PK_DEPTH + u, u, false);
 #undef PK_LOAD_B
-#undef PK_LOAD_BH
 #undef PK_DMA_A
 #undef PK_LOADF
-#undef PK_MMA
 #undef PK_STAGE
-#undef PK_INTERLEAVE
+#undef PK_SUB
   ring_barrier<0>();  // every wavefront is done reading the ring before it is reused
 
   // ---- epilogue: D[i][j] of a 32 x 32 block sits in lane j + 32 ((i / 4) % 2),
@@ -474,7 +441,7 @@ int packed_down_tile_rows(int ffn_tile_rows) {
 
 hipError_t launch_packed_gemm(const GemmProblem& p, int epilogue, int tile_rows, int64_t max_rows,
                               hipStream_t s) {
-  if (p.K % PK_BKS != 0 || p.a_kwrap % PK_BKS != 0) return hipErrorInvalidValue;
+  if (p.K < PK_BKS || p.K % PK_BKS != 0 || p.a_kwrap % PK_BKS != 0) return hipErrorInvalidValue;
   if (tile_rows < 32 || tile_rows > kPackedMaxTileRows || tile_rows % 32 != 0)
     return hipErrorInvalidValue;
   const bool swiglu = (epilogue == kSwiGLU_BF16);

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import mixture_experts_layer_bias_amd as m
-from gpu_check import check_forward, run_gpu
+from gpu_check import LOGIT_TOL, check_forward, run_gpu
 from workloads import Workload, get_workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -118,3 +118,20 @@ def test_packed_mid_vs_oracle():
     g = run_gpu(w, inp, packed=packed)
     sample = np.sort(np.random.default_rng(0).choice(w.T, 384, replace=False))
     print("mid packed", check_forward(w, inp, g, y_tokens=sample), flush=True)
+
+
+# The router is one group of T rows in 256 tiles of 32 * na rows (E <= 256:
+# one weight panel) over 2 d / 64 k-stages.  The grouped GEMM runs its stages
+# three at a time and the last one or two after the loop, so every remainder
+# of the stage count by three is taken with several row-block counts.
+@pytest.mark.parametrize("d", [1216, 1280, 1344])   # 38, 40, 42 router k-stages
+@pytest.mark.parametrize("na", [1, 2, 3, 8])
+def test_router_logits_stage_remainders(d, na):
+    w = _edge(T=8192 * na, d=d, I=128, N=8, Z=4, K=2)
+    print(f"[router tails] d={d} na={na} {w.describe()}", flush=True)
+    inp = make_inputs(w, device=DEV)
+    g = run_gpu(w, inp)
+    x = inp["x"].float().cpu().double().numpy()
+    ref = x @ inp["w_router"].cpu().double().numpy().T
+    err = np.abs(g["logits"].astype(np.float64) - ref).max()
+    assert err <= LOGIT_TOL, f"router logits off by {err}"
