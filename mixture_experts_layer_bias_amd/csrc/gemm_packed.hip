@@ -44,9 +44,10 @@ static_assert(PK_QUARTER == 8 * 1024, "eight 1 KB pieces per wavefront");
 // in the pipeline (DEPTH - 1 loaded ahead of use), OCC = workgroups per CU.
 //   gate/up, router: 256-row tiles, three stages, one workgroup per CU (256
 //     accumulators per wavefront leave room for no second workgroup);
-//   down: 128-row tiles, two stages, two workgroups per CU - its tiles are
+//   down: 128-row tiles, three stages, two workgroups per CU - its tiles are
 //     short (K = I), and a second workgroup covers each tile's pipeline fill
-//     and epilogue.
+//     and epilogue (128 accumulators and three weight register sets fit the
+//     256 registers each of two wavefronts per SIMD may hold).
 template <int MAXRB_, int DEPTH_, int OCC_>
 struct PkCfg {
   static constexpr int MAXRB = MAXRB_, DEPTH = DEPTH_, OCC = OCC_;
@@ -54,7 +55,7 @@ struct PkCfg {
   static constexpr int SLOT = MAXRB * 32 * PK_ROWB;  // bytes of one activation stage
 };
 using PkWide = PkCfg<kPackedMaxTileRows / 32, 3, 1>;
-using PkHalf = PkCfg<kPackedMaxTileRows / 64, 2, 2>;
+using PkHalf = PkCfg<kPackedMaxTileRows / 64, 3, 2>;
 
 // NA = live 32-row blocks of the tile (1..CFG::MAXRB).
 template <typename CFG, int EPI, int NA>
