@@ -208,8 +208,16 @@ def main():
                              aux=aux, workspace=ws, events=events)
         m.moe_zc_bias_update(aux["loads"], target, bias, pid)
 
-    for _ in range(args.warmup):
+    def ffn_stats(ld):
+        f = ld[: w.N].astype(np.float64)
+        return {"ffn_per_token": float(f.sum() / w.T),
+                "max_over_mean_ffn_load": float(f.max() / f.mean()) if f.sum() > 0 else None}
+
+    first_pid = None
+    for i in range(args.warmup):
         step()
+        if i == 0:  # closed-loop statistics of the first step (untimed)
+            first_pid = ffn_stats(aux["loads"].cpu().numpy())
     events = [m.StageEvents() for _ in range(args.steps)]
     S_list, touched_list = [], []
     torch.cuda.synchronize()
@@ -229,6 +237,10 @@ def main():
     loads = aux["loads"].cpu().numpy()
     S = int(aux["offsets"][w.N].item())
     touched = int((loads[: w.N] > 0).sum())
+    last_pid = ffn_stats(loads)
+    pid_report = {"gains": [pid.kp, pid.ki, pid.kd], "target": "uniform T*K/E",
+                  "steps_applied": args.warmup + args.steps,
+                  "first_step": first_pid, "last_step": last_pid}
     alg = algorithmic(w, S, touched, es)
     flop_act = 2.0 * w.T * w.d * w.E + 6.0 * w.d * w.I * S
     t_step = ms_per_step / 1e3
@@ -292,6 +304,7 @@ def main():
         "ffn_experts_per_token": ffn_per_token,
         "touched_experts": touched,
         "stages": stage_roof,
+        "pid_closed_loop": pid_report,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

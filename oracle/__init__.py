@@ -21,11 +21,13 @@ MoE module was an image and did not survive on the page that introduces it):
     its Figure 3 caption: about 8 activated experts per token on average.
 
 Pinned functions and their pins are listed in ``moe_zc.py``; the PID gains and
-their convergence are parity unpinned (the pages give no values).
+the convergence rate on a real model are parity unpinned (the pages give no
+values).
 """
 from .moe_zc import (  # noqa: F401
     router_logits, softmax_fp64, selection_keys, select_topk, gates_of,
     expert_loads, ffn_offsets, permutation, unpermute, silu, swiglu_ffn,
     combine, route, forward, forward_tokens, pid_step, ffn_count_per_token,
+    budget_target, closed_loop,
 )
 from . import bruteforce  # noqa: F401

@@ -24,8 +24,8 @@ For each token t independently:
 Experts are numbered FFN first (0..N-1), then the zero-computation experts
 (N..E-1), following the page's wording that the Z experts extend the pool.
 
-Pins (tests/test_oracle_pins.py, tests/test_oracle_golden.py,
-tests/test_oracle_mutations.py):
+Pins (tests/test_oracle_pins.py with the checks in tests/pins.py, the
+fixtures in tests/golden, and tests/test_oracle_mutations.py):
   router_logits   brute-force fsum loops; hand example in tests/golden
   softmax_fp64    sums to 1; brute force with math.exp; hand example
   select_topk     enumeration of all C(E,K) subsets; tie cases by hand
@@ -37,6 +37,12 @@ tests/test_oracle_mutations.py):
                   (independent of b); brute-force loops; per-token independence
   pid_step        closed-form first and second steps; zero error is a no-op;
                   sum of updates is zero when totals match; sign
+  budget_target   closed-form sums (T f FFN slots, T (K - f) identity slots)
+  closed_loop     a routing that meets the target is a fixed point; the bias
+                  sum is conserved; velocity steps accumulate to the positional
+                  form over the recorded loads; integral control of a one-FFN,
+                  one-identity layer settles on the target (textbook, monotone
+                  plant)
   ffn counts      hypergeometric law of the FFN count under exchangeable logits
 PID gains and convergence: parity unpinned (no values on the pages).
 """
@@ -257,3 +263,56 @@ def pid_step(loads, target, bias, e_prev, e_prev2, kp, ki, kd):
     e2 = np.asarray(e_prev2, dtype=np.float64)
     db = kp * (e - e1) + ki * e + kd * (e - 2.0 * e1 + e2)
     return np.asarray(bias, dtype=np.float64) + db, e, e1
+
+
+def budget_target(T: int, K: int, N: int, Z: int, ffn_per_token: float) -> np.ndarray:
+    """Per-expert load target [E] for a chosen number f of FFN experts per token.
+
+    The pages give the controller's purpose as a compute budget: it keeps the
+    compute activated per token near a set amount (about 27B of 560B
+    parameters, 『美团的 LongCat-Flash：用 27B 激活算力跑起一个 560B 模型』,
+    section 关键要点), which comes to about 8 FFN experts per token
+    (『美团LongCat-Flash：算力调度新纪元』, Figure 3 caption).  Reading: the T*K
+    slots of a batch split into T*f FFN slots and T*(K-f) identity slots, each
+    share spread evenly over its experts.  Routing that meets this target
+    averages exactly f FFN experts per token.
+    """
+    if not 0.0 <= ffn_per_token <= K:
+        raise ValueError("ffn_per_token outside [0, K]")
+    if (N == 0 and ffn_per_token > 0) or (Z == 0 and ffn_per_token < K):
+        raise ValueError("budget needs experts of the kind it assigns slots to")
+    t = np.zeros(N + Z, dtype=np.float64)
+    if N:
+        t[:N] = T * ffn_per_token / N
+    if Z:
+        t[N:] = T * (K - ffn_per_token) / Z
+    return t
+
+
+def closed_loop(logits32_batches, bias0, target, K: int, N: int, kp, ki, kd):
+    """The bias controller over a sequence of batches.
+
+    The bias is tuned in real time from recent expert usage
+    (『衝上熱搜！美團大模型，靠「快」火了』, section 零計算專家).  Reading: batch s
+    is routed with the current bias b_s, its loads drive one pid_step, and
+    b_{s+1} routes batch s+1.  Between steps the controller state (bias and the
+    two error histories) is held in fp32, as a device stores it; the step
+    itself is evaluated in fp64.
+
+    Returns dict: bias [S+1, E] fp32 (bias[0] = bias0), loads [S, E],
+    ffn_per_token [S] (mean over the batch's tokens).
+    """
+    b = np.asarray(bias0, dtype=np.float32).copy()
+    E = b.shape[0]
+    e1 = np.zeros(E, dtype=np.float32)
+    e2 = np.zeros(E, dtype=np.float32)
+    tgt = np.asarray(target, dtype=np.float32)
+    biases, loads, ffn = [b.copy()], [], []
+    for l32 in logits32_batches:
+        rt = route(l32, b, K, N)
+        loads.append(rt["loads"])
+        ffn.append(float(ffn_count_per_token(rt["idx"], N).mean()))
+        nb, ne1, ne2 = pid_step(rt["loads"], tgt, b, e1, e2, kp, ki, kd)
+        b, e1, e2 = nb.astype(np.float32), ne1.astype(np.float32), ne2.astype(np.float32)
+        biases.append(b.copy())
+    return {"bias": np.array(biases), "loads": np.array(loads), "ffn_per_token": np.array(ffn)}

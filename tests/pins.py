@@ -285,11 +285,91 @@ def check_pid_properties(E=64, seed=12):
     assert np.allclose(b, pos_form, rtol=0, atol=1e-14)
 
 
+# ------------------------------------------------------ closed-loop PID -----
+def check_budget_target():
+    T, K, N, Z = 96, 12, 512, 256
+    for f in (0.0, 3.5, 8.0, 12.0):
+        if (f == 0.0 and N == 0) or (f == 12.0 and Z == 0):
+            continue
+        t = om.budget_target(T, K, N, Z, f)
+        assert t.shape == (N + Z,)
+        assert abs(t[:N].sum() - T * f) < 1e-9 and abs(t[N:].sum() - T * (K - f)) < 1e-9
+        assert np.ptp(t[:N]) == 0 and np.ptp(t[N:]) == 0
+    for bad in (-0.5, 12.5):
+        try:
+            om.budget_target(T, K, N, Z, bad)
+        except ValueError:
+            continue
+        raise AssertionError("budget outside [0, K] accepted")
+
+
+def check_closed_loop_fixed_point(S=5):
+    # E = 4 (2 FFN, 2 identity), K = 2: token t strongly prefers experts t and
+    # t+1 (mod 4), so every expert gets 2 slots; the budget of one FFN expert
+    # per token asks for exactly that, so the bias must never move
+    T, N, Z, K = 4, 2, 2, 2
+    l32 = np.zeros((T, N + Z), np.float32)
+    for t in range(T):
+        l32[t, t % 4], l32[t, (t + 1) % 4] = 5.0, 4.0
+    b0 = np.array([0.01, -0.02, 0.005, -0.01], np.float32)
+    tgt = om.budget_target(T, K, N, Z, 1.0)
+    out = om.closed_loop([l32] * S, b0, tgt, K, N, 0.7, 0.3, 0.2)
+    assert np.array_equal(out["bias"], np.broadcast_to(b0, (S + 1, 4)))
+    assert (out["loads"] == 2).all() and np.allclose(out["ffn_per_token"], 1.0)
+
+
+def _skewed_logits(r, T, N, Z, s=1.1, c=0.0):
+    l = r.standard_normal((T, N + Z)) * 0.5
+    ranks = r.permutation(N) + 1
+    l[:, :N] += -s * np.log(ranks) + c
+    return l.astype(np.float32)
+
+
+def check_closed_loop_conservation_and_positional_form(S=8, seed=13):
+    r = _rng(seed)
+    T, N, Z, K = 600, 16, 8, 4
+    kp, ki, kd = 0.4, 0.5, 0.2
+    batches = [_skewed_logits(r, T, N, Z, c=0.8) for _ in range(S)]
+    b0 = r.uniform(-0.01, 0.01, N + Z).astype(np.float32)
+    tgt = om.budget_target(T, K, N, Z, 2.5)
+    out = om.closed_loop(batches, b0, tgt, K, N, kp, ki, kd)
+    # the target and the loads both sum to T K: the bias sum is conserved
+    # (to fp32 rounding of the stored state)
+    sums = out["bias"].astype(np.float64).sum(axis=1)
+    assert np.abs(sums - sums[0]).max() < 1e-5, sums
+    # the velocity-form steps add up to the positional PID over the recorded
+    # loads: b_S = b_0 + kp e_S + ki sum(e) + kd (e_S - e_{S-1})
+    e = (tgt[None, :] - out["loads"]) / tgt.sum()
+    pos = b0 + kp * e[-1] + ki * e.sum(axis=0) + kd * (e[-1] - e[-2])
+    assert np.abs(out["bias"][-1] - pos).max() < 1e-5
+    # the skew comes down: the busiest FFN expert carries less at the end
+    ld = out["loads"][:, :N].astype(np.float64)
+    assert ld[-1].max() / ld[-1].mean() < ld[0].max() / ld[0].mean()
+
+
+def check_closed_loop_integral_settles(seed=14, S=60):
+    # one FFN and one identity expert, K = 1: expert 0 wins token t when
+    # p0 + b0 > p1 + b1, so its load falls monotonically as b1 - b0 grows; an
+    # integral controller on such a plant settles where the load meets the
+    # target (to the granularity of one token)
+    r = _rng(seed)
+    T = 400
+    a = r.normal(1.0, 1.0, T)
+    l32 = np.stack([a, np.zeros(T)], axis=1).astype(np.float32)
+    tgt = om.budget_target(T, 1, 1, 1, 0.25)          # 100 FFN slots, 300 identity
+    out = om.closed_loop([l32] * S, np.zeros(2, np.float32), tgt, 1, 1, 0.0, 0.5, 0.0)
+    assert out["loads"][0, 0] > 250                     # the skew it starts from
+    assert np.abs(out["loads"][-10:, 0] - 100).max() <= 3, out["loads"][-10:, 0]
+    assert abs(out["ffn_per_token"][-1] - 0.25) <= 3 / T
+
+
 ALL_CHECKS = [
     check_hand_example, check_pid_golden, check_bruteforce_tiny,
     check_topk_ties_enumeration, check_softmax_bruteforce,
     check_single_forced_ffn, check_all_identity, check_k_equals_e,
     check_z_zero_textbook_moe, check_permutation_invariants,
     check_token_independence, check_ffn_count_hypergeometric,
-    check_pid_properties,
+    check_pid_properties, check_budget_target, check_closed_loop_fixed_point,
+    check_closed_loop_conservation_and_positional_form,
+    check_closed_loop_integral_settles,
 ]

@@ -13,7 +13,8 @@ from oracle import moe_zc as om
 
 _orig = {name: getattr(om, name) for name in (
     "softmax_fp64", "selection_keys", "select_topk", "gates_of", "expert_loads",
-    "ffn_offsets", "permutation", "silu", "swiglu_ffn", "combine", "pid_step")}
+    "ffn_offsets", "permutation", "silu", "swiglu_ffn", "combine", "pid_step",
+    "route", "closed_loop", "budget_target")}
 
 
 def m_bias_in_gate(mp):
@@ -164,12 +165,35 @@ def m_pid_no_derivative(mp):
     mp.setattr(om, "pid_step", pid)
 
 
+def m_loop_without_feedback(mp):
+    # every batch routed with the starting bias: the controller never acts
+    def route(l32, bias, K, N):
+        return _orig["route"](l32, np.zeros_like(np.asarray(bias)), K, N)
+    mp.setattr(om, "route", route)
+
+
+def m_loop_history_reset(mp):
+    # the error histories are dropped between batches
+    def pid(loads, target, bias, e_prev, e_prev2, kp, ki, kd):
+        return _orig["pid_step"](loads, target, bias, np.zeros_like(e_prev),
+                                 np.zeros_like(e_prev2), kp, ki, kd)
+    mp.setattr(om, "pid_step", pid)
+
+
+def m_budget_swapped(mp):
+    # FFN and identity shares exchanged
+    def bt(T, K, N, Z, f):
+        return _orig["budget_target"](T, K, N, Z, K - f)
+    mp.setattr(om, "budget_target", bt)
+
+
 MUTATIONS = [
     m_bias_in_gate, m_renormalised_gates, m_softmax_ffn_only, m_bias_on_logit,
     m_tie_to_higher_index, m_smallest_keys, m_drop_identity_term,
     m_drop_residual, m_transposed_down, m_gate_up_swapped, m_silu_sign,
     m_sigmoid_not_silu, m_loads_ffn_only, m_inclusive_offsets,
     m_unstable_permutation, m_pid_sign, m_pid_p_on_error, m_pid_no_derivative,
+    m_loop_without_feedback, m_loop_history_reset, m_budget_swapped,
 ]
 
 # the statistical check is slow and not needed to catch any of these
