@@ -31,3 +31,4 @@ from .moe_zc import (  # noqa: F401
     budget_target, closed_loop,
 )
 from . import bruteforce  # noqa: F401
+from . import mx  # noqa: F401

@@ -1,0 +1,148 @@
+"""FP8 block quantization for the mixed-precision expert path (fp64 oracle).
+
+TEST INFRASTRUCTURE: imported only by the tests, the smoke check and the
+benchmark's CPU-baseline leg.
+
+The pages say LongCat-Flash quantizes with the same fine-grained block scheme
+as DeepSeek-V3, mixed per layer: the down projection's input activations reach
+magnitudes near 1e6 and some expert layers show large block-FP8 error, so
+precision is chosen layer by layer
+(『衝上熱搜！美團大模型，靠「快」火了』, section on system-level optimisation,
+paragraph on quantization).
+
+Readings (the pages name the scheme but define no format):
+  * format: FP8 E4M3 elements (1 sign, 4 exponent bits with bias 7, 3
+    mantissa bits; exponent field 0 holds subnormals, code 0x7F is NaN, the
+    largest finite magnitude is 448), one power-of-two scale per block of 32
+    consecutive values along the reduction axis, stored as an 8-bit biased
+    exponent (E8M0, bias 127).  This is the block-scaled FP8 the MI355X matrix
+    cores consume;
+  * scale: the smallest power of two 2^s with amax <= 448 * 2^s, i.e.
+    DeepSeek-style amax scaling rounded up to a power of two, so no element
+    saturates; s is clamped to [-127, 127]; an all-zero block takes s = -127;
+  * rounding: round to nearest, ties to even, onto the E4M3 grid;
+  * mixed precision: the gate/up projection runs in FP8 (x quantized per
+    token per 32 channels, W_gate and W_up per output row per 32 inputs); the
+    down projection stays bf16, since its input is where the pages find the
+    extreme activations.
+
+Pins (tests/pins.py): every code decodes by the closed form of the format and
+re-encodes to itself; rounding of arbitrary values equals a brute-force
+nearest search over the 127 finite non-negative codes with ties to the even
+code; the scale is the minimal one (closed form); the quantization error is
+within half a step; quantization is lossless for values already on a block's
+grid, where the FP8 layer equals the bf16 layer exactly.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import moe_zc as _layer
+
+E4M3_MAX = 448.0
+BLOCK = 32
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of each E4M3 byte (NaN for 0x7F / 0xFF), by the format's closed form."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    mag = np.where((e == 0xF) & (m == 0x7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """Round-to-nearest-even onto the E4M3 grid; |y| must not exceed 448.
+    The sign bit is copied from y.
+
+    Subnormals (|y| < 2^-6) are multiples of 2^-9: code = rint(|y| 2^9), and a
+    result of 8 is exactly the first normal code.  A normal |y| = m 2^E
+    (1 <= m < 2) has code 8 (E + 7) + rint(8 (m - 1)); a mantissa that rounds
+    up to 8 carries into the exponent field, which is the next binade's first
+    code.  Both pieces are exact in fp64."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    if np.any(a > E4M3_MAX) or np.any(~np.isfinite(a)):
+        raise ValueError("value outside the E4M3 range")
+    sub = a < 2.0 ** -6
+    m, ex = np.frexp(np.where(sub, 1.0, a))          # a = m 2^ex, 0.5 <= m < 1
+    E = ex - 1                                       # a = (2m) 2^E, 1 <= 2m < 2
+    code_n = 8 * (E + 7) + np.rint(8.0 * (2.0 * m - 1.0))
+    code_s = np.rint(a * 2.0 ** 9)
+    code = np.where(sub, code_s, code_n).astype(np.int64)
+    # the sign bit is the input's, also for -0 and for values rounding to 0
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def mx_scale_exponent(amax) -> np.ndarray:
+    """Smallest integer s with amax <= 448 * 2^s, clamped to [-127, 127]
+    (amax = 0 gives -127).  With amax = f 2^E (1 <= f < 2): s = E - 8 when
+    f <= 1.75 and E - 7 otherwise, since 448 = 1.75 * 2^8."""
+    a = np.asarray(amax, dtype=np.float64)
+    m, ex = np.frexp(np.where(a > 0, a, 1.0))
+    E = ex - 1
+    s = E - 8 + (2.0 * m > 1.75)
+    s = np.where(a > 0, s, -127)
+    return np.clip(s, -127, 127).astype(np.int64)
+
+
+def mx_quantize(v, axis=-1):
+    """Block quantization along ``axis`` in blocks of 32 (the axis length must
+    be a multiple of 32).  Returns (codes uint8, same shape as v; scales uint8
+    E8M0 = s + 127, shape with that axis divided by 32)."""
+    v = np.moveaxis(np.asarray(v, dtype=np.float64), axis, -1)
+    n = v.shape[-1]
+    if n % BLOCK:
+        raise ValueError("axis length must be a multiple of 32")
+    blk = v.reshape(v.shape[:-1] + (n // BLOCK, BLOCK))
+    s = mx_scale_exponent(np.abs(blk).max(axis=-1))
+    codes = e4m3_encode(blk * np.ldexp(1.0, -s)[..., None])
+    codes = np.moveaxis(codes.reshape(v.shape), -1, axis)
+    scales = np.moveaxis((s + 127).astype(np.uint8), -1, axis)
+    return codes, scales
+
+
+def mx_dequantize(codes, scales, axis=-1) -> np.ndarray:
+    c = np.moveaxis(np.asarray(codes), axis, -1)
+    sc = np.moveaxis(np.asarray(scales, dtype=np.int64), axis, -1)
+    vals = e4m3_decode(c).reshape(c.shape[:-1] + (c.shape[-1] // BLOCK, BLOCK))
+    out = vals * np.ldexp(1.0, sc - 127)[..., None]
+    return np.moveaxis(out.reshape(c.shape), -1, axis)
+
+
+def forward_fp8_gateup(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, K: int,
+                       residual=None, logits32=None):
+    """The layer with the gate/up projection in block FP8: x quantized per
+    token per 32 channels, W_gate and W_up per output row per 32 inputs, the
+    products taken exactly (fp64) from the dequantized values; router, down
+    projection and combine as in the bf16 layer.  Routing uses ``logits32``
+    when given (the router itself is not quantized)."""
+    x64 = np.asarray(x, dtype=np.float64)
+    xq, xs = mx_quantize(x64, axis=-1)
+    x_dq = mx_dequantize(xq, xs, axis=-1)
+
+    def get(e):
+        gq, gs = mx_quantize(np.asarray(w_gate[e], dtype=np.float64), axis=-1)
+        uq, us = mx_quantize(np.asarray(w_up[e], dtype=np.float64), axis=-1)
+        return mx_dequantize(gq, gs), mx_dequantize(uq, us), np.asarray(w_down[e], np.float64)
+
+    l64 = _layer.router_logits(x64, w_router)
+    if logits32 is None:
+        logits32 = l64.astype(np.float32)
+    rt = _layer.route(logits32, bias, K, N)
+    idx, g = rt["idx"], rt["gate"]
+    T = x64.shape[0]
+    rows = np.zeros((T, K, x64.shape[1]))
+    for e in np.unique(idx[idx < N]):
+        tt, kk = np.nonzero(idx == e)
+        wg, wu, wd = get(int(e))
+        # gate/up on the dequantized FP8 operands, down on the bf16 weights
+        rows[tt, kk] = _layer.swiglu_ffn(x_dq[tt], wg, wu, wd)
+    # identity experts pass the unquantized x (they compute nothing)
+    y = _layer.combine(x64, idx, g, rows, N, residual)
+    rt["logits64"] = l64
+    rt["y"] = y
+    return rt

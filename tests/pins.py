@@ -15,6 +15,7 @@ import torch
 import torch.nn.functional as F
 
 from oracle import moe_zc as om
+from oracle import mx as omx
 from oracle import bruteforce as bf
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -363,6 +364,108 @@ def check_closed_loop_integral_settles(seed=14, S=60):
     assert abs(out["ffn_per_token"][-1] - 0.25) <= 3 / T
 
 
+# ------------------------------------------------------- block FP8 (MX) -----
+def check_e4m3_codes():
+    c = np.arange(256, dtype=np.uint8)
+    v = omx.e4m3_decode(c)
+    nan = np.isnan(v)
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    # closed-form landmarks of the format
+    assert v[0x7E] == 448.0 and v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6
+    assert v[0x38] == 1.0 and v[0x3C] == 1.5 and v[0xB8] == -1.0
+    fin = ~nan
+    assert np.array_equal(omx.e4m3_encode(v[fin]), c[fin])        # incl. -0 -> 0x80
+    pos = v[:0x7F]
+    assert (np.diff(pos) > 0).all()                               # codes increase with value
+
+
+def check_e4m3_rounding_bruteforce(seed=15, n=4000):
+    r = _rng(seed)
+    grid = omx.e4m3_decode(np.arange(0x7F, dtype=np.uint8))      # 0 .. 448, increasing
+    mids = (grid[1:] + grid[:-1]) / 2.0
+    ys = np.concatenate([r.uniform(-448, 448, n), mids, -mids, grid,
+                         r.uniform(0, 2.0 ** -5, n // 4), [0.0, -0.0, 448.0, -448.0]])
+    got = omx.e4m3_encode(ys)
+    for y, g in zip(ys, got):
+        a = abs(y)
+        d = np.abs(grid - a)
+        best = np.flatnonzero(d == d.min())
+        code = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        want = code | (0x80 if np.signbit(y) else 0)
+        assert g == want, (y, g, want)
+    try:
+        omx.e4m3_encode(np.array([448.5]))
+    except ValueError:
+        return
+    raise AssertionError("out-of-range value accepted")
+
+
+def check_mx_scales_minimal(seed=16):
+    r = _rng(seed)
+    v = r.standard_normal((64, 256)) * np.ldexp(1.0, r.integers(-30, 30, (64, 1)))
+    v[3, 32:64] = 0.0                                             # an all-zero block
+    v[5, 0:32] = 0.0
+    v[5, 7] = 448.0 * 2.0 ** 3                                    # amax exactly on the range
+    codes, scales = omx.mx_quantize(v, axis=1)
+    assert codes.shape == v.shape and scales.shape == (64, 8)
+    s = scales.astype(np.int64) - 127
+    amax = np.abs(v.reshape(64, 8, 32)).max(axis=2)
+    live = amax > 0
+    assert (amax[live] <= 448.0 * np.ldexp(1.0, s[live])).all()
+    assert (amax[live] > 448.0 * np.ldexp(1.0, s[live] - 1)).all()   # the smallest such scale
+    assert s[3, 1] == -127 and not codes[3, 32:64].any()
+    assert s[5, 0] == 3 and codes[5, 7] == 0x7E
+    # error within half a grid step at the value's magnitude
+    dq = omx.mx_dequantize(codes, scales, axis=1)
+    y = np.abs(v) / np.repeat(np.ldexp(1.0, s), 32, axis=1)
+    E = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+    half = np.ldexp(1.0, (E - 4).astype(int)) * np.repeat(np.ldexp(1.0, s), 32, axis=1)
+    assert (np.abs(dq - v) <= half).all()
+
+
+def _on_block_grid(r, shape, axis_len):
+    """Values already on an FP8 block grid: every 32-block holds one element
+    of magnitude exactly 448 * 2^s, the rest are E4M3 values times 2^s."""
+    grid = omx.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    v = r.choice(grid, shape) * r.choice([-1.0, 1.0], shape)
+    nb = axis_len // 32
+    s = r.integers(-12, -4, shape[:-1] + (nb,))
+    v = v.reshape(shape[:-1] + (nb, 32))
+    v[..., 0] = 448.0 * r.choice([-1.0, 1.0], shape[:-1] + (nb,))
+    v = v * np.ldexp(1.0, s)[..., None]
+    return v.reshape(shape)
+
+
+def check_fp8_layer_lossless_on_grid(T=24, d=64, I=32, N=5, Z=3, K=3, seed=17):
+    r = _rng(seed)
+    x = _on_block_grid(r, (T, d), d) * 64.0
+    wr = r.standard_normal((N + Z, d)) / np.sqrt(d)
+    wg = _on_block_grid(r, (N, I, d), d)
+    wu = _on_block_grid(r, (N, I, d), d)
+    wd = r.standard_normal((N, d, I)) / np.sqrt(I)
+    b = r.uniform(-0.05, 0.05, N + Z)
+    res = r.standard_normal((T, d))
+    xq, xs = omx.mx_quantize(x)
+    assert np.array_equal(omx.mx_dequantize(xq, xs), x)
+    ref = om.forward(x, wr, b, wg, wu, wd, N, Z, K, residual=res)
+    got = omx.forward_fp8_gateup(x, wr, b, wg, wu, wd, N, Z, K, residual=res)
+    assert np.array_equal(got["idx"], ref["idx"]) and np.array_equal(got["y"], ref["y"])
+    # identity experts pass x itself, never its FP8 image: with every slot on
+    # an identity expert the two layers agree exactly off the grid too
+    x3 = r.standard_normal((T, d))
+    b3 = np.concatenate([np.full(N, -10.0), np.zeros(Z)])
+    a3 = om.forward(x3, wr, b3, wg, wu, wd, N, Z, K, residual=res)["y"]
+    c3 = omx.forward_fp8_gateup(x3, wr, b3, wg, wu, wd, N, Z, K, residual=res)["y"]
+    assert np.array_equal(a3, c3)
+    # off the grid the two differ, by about the FP8 rounding of the gate/up inputs
+    x2 = r.standard_normal((T, d))
+    wg2 = r.standard_normal((N, I, d)) / np.sqrt(d)
+    a = om.forward(x2, wr, b, wg2, wu, wd, N, Z, K)["y"]
+    c = omx.forward_fp8_gateup(x2, wr, b, wg2, wu, wd, N, Z, K)["y"]
+    rel = np.abs(a - c).max() / np.abs(a).max()
+    assert 1e-4 < rel < 0.1, rel
+
+
 ALL_CHECKS = [
     check_hand_example, check_pid_golden, check_bruteforce_tiny,
     check_topk_ties_enumeration, check_softmax_bruteforce,
@@ -371,5 +474,6 @@ ALL_CHECKS = [
     check_token_independence, check_ffn_count_hypergeometric,
     check_pid_properties, check_budget_target, check_closed_loop_fixed_point,
     check_closed_loop_conservation_and_positional_form,
-    check_closed_loop_integral_settles,
+    check_closed_loop_integral_settles, check_e4m3_codes, check_e4m3_rounding_bruteforce,
+    check_mx_scales_minimal, check_fp8_layer_lossless_on_grid,
 ]

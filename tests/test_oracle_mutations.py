@@ -10,6 +10,7 @@ import pytest
 
 import pins
 from oracle import moe_zc as om
+from oracle import mx as omx
 
 _orig = {name: getattr(om, name) for name in (
     "softmax_fp64", "selection_keys", "select_topk", "gates_of", "expert_loads",
@@ -187,6 +188,55 @@ def m_budget_swapped(mp):
     mp.setattr(om, "budget_target", bt)
 
 
+_mx = {name: getattr(omx, name) for name in (
+    "mx_scale_exponent", "e4m3_encode", "mx_quantize", "mx_dequantize", "forward_fp8_gateup")}
+
+
+def m_mx_floor_scale(mp):
+    # scale from floor(log2 amax) - 8 alone: the block maximum can overflow 448
+    def sc(amax):
+        a = np.asarray(amax, np.float64)
+        m, ex = np.frexp(np.where(a > 0, a, 1.0))
+        return np.clip(np.where(a > 0, ex - 1 - 8, -127), -127, 127).astype(np.int64)
+    mp.setattr(omx, "mx_scale_exponent", sc)
+
+
+def m_mx_truncate(mp):
+    # rounding toward zero instead of to nearest even
+    def enc(y):
+        y = np.asarray(y, np.float64)
+        a = np.abs(y)
+        grid = omx.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+        code = np.searchsorted(grid, a, side="right") - 1
+        return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+    mp.setattr(omx, "e4m3_encode", enc)
+
+
+def m_mx_scale_bias_128(mp):
+    def q(v, axis=-1):
+        c, sc = _mx["mx_quantize"](v, axis)
+        return c, (sc.astype(np.int64) + 1).astype(np.uint8)
+    def dq(c, sc, axis=-1):
+        return _mx["mx_dequantize"](c, (np.asarray(sc, np.int64) - 1).astype(np.uint8), axis)
+    mp.setattr(omx, "mx_quantize", q)
+    mp.setattr(omx, "mx_dequantize", dq)
+
+
+def m_mx_block16(mp):
+    mp.setattr(omx, "BLOCK", 16)
+
+
+def m_fp8_identity_quantized(mp):
+    # the identity experts fed the FP8 image of x
+    def fwd(x, w_router, bias, w_gate, w_up, w_down, N, Z, K, residual=None, logits32=None):
+        xq, xs = _mx["mx_quantize"](np.asarray(x, np.float64))
+        x_dq = _mx["mx_dequantize"](xq, xs)
+        rt = _mx["forward_fp8_gateup"](x_dq, w_router, bias, w_gate, w_up, w_down, N, Z, K,
+                                       residual, om.router_logits(x, w_router).astype(np.float32))
+        return rt
+    mp.setattr(omx, "forward_fp8_gateup", fwd)
+
+
 MUTATIONS = [
     m_bias_in_gate, m_renormalised_gates, m_softmax_ffn_only, m_bias_on_logit,
     m_tie_to_higher_index, m_smallest_keys, m_drop_identity_term,
@@ -194,6 +244,8 @@ MUTATIONS = [
     m_sigmoid_not_silu, m_loads_ffn_only, m_inclusive_offsets,
     m_unstable_permutation, m_pid_sign, m_pid_p_on_error, m_pid_no_derivative,
     m_loop_without_feedback, m_loop_history_reset, m_budget_swapped,
+    m_mx_floor_scale, m_mx_truncate, m_mx_scale_bias_128, m_mx_block16,
+    m_fp8_identity_quantized,
 ]
 
 # the statistical check is slow and not needed to catch any of these
