@@ -8,5 +8,7 @@ from .api import (  # noqa: F401
     AUX_KEYS, MoeZcError, PidState, StageEvents, alloc_aux, moe_zc_abi_version,
     moe_zc_bias_update, moe_zc_forward, moe_zc_forward_packed, moe_zc_pack_expert_weights,
     moe_zc_packed_expert_bytes, moe_zc_route, moe_zc_status_string, moe_zc_workspace_size,
+    moe_zc_forward_packed_fp8, moe_zc_pack_expert_weights_fp8, moe_zc_packed_fp8_expert_bytes,
+    moe_zc_quantize_mx, moe_zc_workspace_size_fp8,
 )
 from ._lib import LIB_PATH, STAGE_NAMES  # noqa: F401

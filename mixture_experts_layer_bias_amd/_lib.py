@@ -22,7 +22,9 @@ STAGE_NAMES = ("router_gemm", "softmax_topk", "chunk_hist", "scan", "permute",
 # every symbol include/moe_zc.h declares
 EXPORTS = ("moe_zc_workspace_size", "moe_zc_forward", "moe_zc_packed_expert_bytes",
            "moe_zc_pack_expert_weights", "moe_zc_forward_packed", "moe_zc_route",
-           "moe_zc_bias_update", "moe_zc_status_string", "moe_zc_abi_version")
+           "moe_zc_bias_update", "moe_zc_status_string", "moe_zc_abi_version",
+           "moe_zc_packed_fp8_expert_bytes", "moe_zc_pack_expert_weights_fp8",
+           "moe_zc_workspace_size_fp8", "moe_zc_forward_packed_fp8", "moe_zc_quantize_mx")
 
 
 class MoeZcAux(ctypes.Structure):
@@ -66,6 +68,17 @@ def load() -> ctypes.CDLL:
     lib.moe_zc_forward_packed.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
                                           i32, ctypes.c_int, ctypes.POINTER(MoeZcAux), vp, sz, vp]
     lib.moe_zc_forward_packed.restype = ctypes.c_int
+    lib.moe_zc_packed_fp8_expert_bytes.argtypes = [i64, i64, ctypes.POINTER(sz)]
+    lib.moe_zc_packed_fp8_expert_bytes.restype = ctypes.c_int
+    lib.moe_zc_pack_expert_weights_fp8.argtypes = [vp, vp, i32, i64, i64, vp, vp]
+    lib.moe_zc_pack_expert_weights_fp8.restype = ctypes.c_int
+    lib.moe_zc_workspace_size_fp8.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.moe_zc_workspace_size_fp8.restype = sz
+    lib.moe_zc_forward_packed_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32,
+                                              i32, i32, ctypes.POINTER(MoeZcAux), vp, sz, vp]
+    lib.moe_zc_forward_packed_fp8.restype = ctypes.c_int
+    lib.moe_zc_quantize_mx.argtypes = [vp, i64, i64, vp, vp, vp]
+    lib.moe_zc_quantize_mx.restype = ctypes.c_int
     lib.moe_zc_route.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
     lib.moe_zc_route.restype = ctypes.c_int
     lib.moe_zc_bias_update.argtypes = [vp, vp, vp, ctypes.POINTER(MoeZcPid), i32, vp]

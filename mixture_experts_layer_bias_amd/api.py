@@ -120,9 +120,11 @@ class StageEvents:
 
 
 def _forward(name: str, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
-             weights, N: int, Z: int, K: int, I: int, residual, out, aux, workspace, events):
-    """Shared marshalling of moe_zc_forward and moe_zc_forward_packed;
-    ``weights`` are the already checked weight tensors (or None)."""
+             weights, N: int, Z: int, K: int, I: int, residual, out, aux, workspace, events,
+             fp8: bool = False):
+    """Shared marshalling of the forward entry points; ``weights`` are the
+    already checked weight tensors (or None).  The block-FP8 forward takes no
+    dtype argument and has a workspace size of its own."""
     lib = _lib.load()
     T, d = x.shape
     dev = x.device
@@ -137,9 +139,11 @@ def _forward(name: str, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Ten
     _need(out, "out", dt, (T, d), dev)
     fn = getattr(lib, name)
     nulls = [None] * len(weights)
-    need = moe_zc_workspace_size(T, d, I, N, Z, K, dt)
+    dt_arg = [] if fp8 else [_DT[dt]]
+    need = (moe_zc_workspace_size_fp8(T, d, I, N, Z, K) if fp8
+            else moe_zc_workspace_size(T, d, I, N, Z, K, dt))
     if need == 0:
-        code = fn(None, None, None, *nulls, None, None, T, d, I, N, Z, K, _DT[dt], None, None, 0,
+        code = fn(None, None, None, *nulls, None, None, T, d, I, N, Z, K, *dt_arg, None, None, 0,
                   None)
         raise MoeZcError(code, name)
     if workspace is None:
@@ -157,7 +161,7 @@ def _forward(name: str, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Ten
     if events is not None:
         a.stage_events = ctypes.cast(events.array, ctypes.c_void_p).value
     code = fn(_ptr(x), _ptr(w_router), _ptr(bias), *[_ptr(w) for w in weights], _ptr(residual),
-              _ptr(out), T, d, I, N, Z, K, _DT[dt], ctypes.byref(a), _ptr(workspace),
+              _ptr(out), T, d, I, N, Z, K, *dt_arg, ctypes.byref(a), _ptr(workspace),
               workspace.numel(), _stream(dev))
     if code != _lib.MOE_ZC_OK:
         raise MoeZcError(code, name)
@@ -313,3 +317,88 @@ def moe_zc_bias_update(loads: torch.Tensor, target: torch.Tensor, bias: torch.Te
     if code != _lib.MOE_ZC_OK:
         raise MoeZcError(code, "moe_zc_bias_update")
     return bias
+
+
+# ---- block-FP8 gate/up projection --------------------------------------------
+def moe_zc_workspace_size_fp8(T: int, d: int, I: int, N: int, Z: int, K: int) -> int:
+    return int(_lib.load().moe_zc_workspace_size_fp8(T, d, I, N, Z, K))
+
+
+def moe_zc_packed_fp8_expert_bytes(d: int, I: int) -> int:
+    """Bytes of one expert's packed FP8 gate/up weights."""
+    gu = ctypes.c_size_t()
+    code = _lib.load().moe_zc_packed_fp8_expert_bytes(d, I, ctypes.byref(gu))
+    if code != _lib.MOE_ZC_OK:
+        raise MoeZcError(code, "moe_zc_packed_fp8_expert_bytes")
+    return int(gu.value)
+
+
+def moe_zc_pack_expert_weights_fp8(w_gate: torch.Tensor, w_up: torch.Tensor,
+                                   gate_up_fp8: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Quantize and pack bf16 gate/up weights ([n, I, d] each) for
+    moe_zc_forward_packed_fp8; returns a uint8 tensor of n * gate_up_bytes."""
+    lib = _lib.load()
+    n, I, d = w_gate.shape
+    dev = w_gate.device
+    if dev.type != "cuda":
+        raise ValueError("weights must be GPU tensors")
+    _need(w_gate, "w_gate", torch.bfloat16, (n, I, d), dev)
+    _need(w_up, "w_up", torch.bfloat16, (n, I, d), dev)
+    gu = moe_zc_packed_fp8_expert_bytes(d, I)
+    if gate_up_fp8 is None:
+        gate_up_fp8 = torch.empty(n * gu, dtype=torch.uint8, device=dev)
+    _need(gate_up_fp8, "gate_up_fp8", torch.uint8, (n * gu,), dev)
+    code = lib.moe_zc_pack_expert_weights_fp8(_ptr(w_gate), _ptr(w_up), n, d, I,
+                                              _ptr(gate_up_fp8), _stream(dev))
+    if code != _lib.MOE_ZC_OK:
+        raise MoeZcError(code, "moe_zc_pack_expert_weights_fp8")
+    return gate_up_fp8
+
+
+def moe_zc_forward_packed_fp8(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
+                              gate_up_fp8: Optional[torch.Tensor],
+                              down_packed: Optional[torch.Tensor], N: int, Z: int, K: int, I: int,
+                              residual: Optional[torch.Tensor] = None,
+                              out: Optional[torch.Tensor] = None,
+                              aux: Optional[Dict[str, torch.Tensor]] = None,
+                              workspace: Optional[torch.Tensor] = None,
+                              events: Optional[StageEvents] = None) -> torch.Tensor:
+    """moe_zc_forward (bf16) with the gate/up projection in block FP8:
+    gate_up_fp8 from moe_zc_pack_expert_weights_fp8, down_packed the down
+    half of moe_zc_pack_expert_weights."""
+    _check_x(x)
+    T, d = x.shape
+    dev = x.device
+    if x.dtype != torch.bfloat16:
+        raise ValueError("the block-FP8 forward takes bf16 x")
+    if N > 0:
+        gu = moe_zc_packed_fp8_expert_bytes(d, I)
+        _, dn = moe_zc_packed_expert_bytes(d, I, x.dtype)
+        _need(gate_up_fp8, "gate_up_fp8", torch.uint8, (N * gu,), dev)
+        _need(down_packed, "down_packed", torch.uint8, (N * dn,), dev)
+        weights = (gate_up_fp8, down_packed)
+    else:
+        weights = (None, None)
+    return _forward("moe_zc_forward_packed_fp8", x, w_router, bias, weights, N, Z, K, I,
+                    residual, out, aux, workspace, events, fp8=True)
+
+
+def moe_zc_quantize_mx(x: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                       scales: Optional[torch.Tensor] = None):
+    """Block-FP8 codes [rows, d] and scale bytes [rows, d / 32] of bf16 x."""
+    lib = _lib.load()
+    if x.dim() != 2 or x.device.type != "cuda":
+        raise ValueError("x must be a [rows, d] GPU tensor")
+    rows, d = x.shape
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (rows, d), dev)
+    if codes is None:
+        codes = torch.empty(rows, d, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(rows, max(d // 32, 1), dtype=torch.uint8, device=dev)
+    _need(codes, "codes", torch.uint8, (rows, d), dev)
+    _need(scales, "scales", torch.uint8, (rows, max(d // 32, 1)), dev)
+    code = lib.moe_zc_quantize_mx(_ptr(x), rows, d, _ptr(codes), _ptr(scales), _stream(dev))
+    if code != _lib.MOE_ZC_OK:
+        raise MoeZcError(code, "moe_zc_quantize_mx")
+    return codes, scales

@@ -65,11 +65,20 @@ moe_zc_status check_shape(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z,
   return MOE_ZC_OK;
 }
 
+// Extra conditions of the block-FP8 forward: bf16 data, stages of 128 k,
+// and byte offsets into the FP8 copy of x below 2^31 (rows are gathered).
+moe_zc_status check_fp8_shape(const Shape& s) {
+  if (s.dt != MOE_ZC_BF16) return MOE_ZC_ERR_UNSUPPORTED;
+  if (s.d % 128 != 0 || s.T * s.d >= (int64_t(1) << 31)) return MOE_ZC_ERR_UNSUPPORTED;
+  return MOE_ZC_OK;
+}
+
 struct Plan {
-  size_t logits, idx, gate, pos, loads, offsets, perm, counts, tiles, tiles2, wr2, xp, h, o, total;
+  size_t logits, idx, gate, pos, loads, offsets, perm, counts, tiles, tiles2, wr2, xp, h, o;
+  size_t xq, xs, total;  // FP8 codes and scales of x (block-FP8 forward only)
 };
 
-Plan make_plan(const Shape& s) {
+Plan make_plan(const Shape& s, bool fp8 = false) {
   Plan p{};
   size_t at = 0;
   auto take = [&](size_t bytes) {
@@ -91,6 +100,8 @@ Plan make_plan(const Shape& s) {
   p.xp = take(s.gather ? 0 : (size_t)s.smax * s.d * s.es);
   p.h = take((size_t)s.smax * s.I * s.es);
   p.o = take((size_t)s.smax * s.d * s.es);
+  p.xq = take(fp8 ? (size_t)s.T * s.d : 0);
+  p.xs = take(fp8 ? (size_t)s.T * (s.d / 32) : 0);
   p.total = at;
   return p;
 }
@@ -110,18 +121,28 @@ int router_tile_rows(int64_t T, int E) {
   return (int)std::min<int64_t>(std::max<int64_t>(rows, 32), kPackedMaxTileRows);
 }
 
-// The forward on either weight layout (packed: bf16 expert weights as
-// written by moe_zc_pack_expert_weights; gate_up and down then point there).
+enum Layout { kRowMajor = 0, kPacked = 1, kPackedFp8 = 2 };
+
+// The forward on one of the weight layouts.  kPacked: bf16 expert weights as
+// written by moe_zc_pack_expert_weights (gate_up and down point there);
+// kPackedFp8: the gate/up weights as written by moe_zc_pack_expert_weights_fp8
+// and the down weights packed bf16; x is quantized per forward.
 moe_zc_status forward_impl(const void* x, const float* w_router, const float* bias,
                            const void* w_gate, const void* w_up, const void* w_down,
-                           bool packed, const void* residual, void* y, int64_t T, int64_t d,
+                           Layout layout, const void* residual, void* y, int64_t T, int64_t d,
                            int64_t I, int32_t N, int32_t Z, int32_t K, moe_zc_dtype dt,
                            moe_zc_aux* aux, void* workspace, size_t workspace_bytes,
                            hipStream_t stream) {
   Shape s;
   const moe_zc_status st = check_shape(T, d, I, N, Z, K, dt, &s);
   if (st != MOE_ZC_OK) return st;
+  const bool packed = layout != kRowMajor;
+  const bool fp8 = layout == kPackedFp8;
   if (packed && dt != MOE_ZC_BF16) return MOE_ZC_ERR_UNSUPPORTED;
+  if (fp8) {
+    const moe_zc_status s8 = check_fp8_shape(s);
+    if (s8 != MOE_ZC_OK) return s8;
+  }
   if (T == 0) return MOE_ZC_OK;
   if (!x || !w_router || !bias || !y) return MOE_ZC_ERR_INVALID;
   if (N > 0 && (!w_gate || !w_down || (!packed && !w_up))) return MOE_ZC_ERR_INVALID;
@@ -129,7 +150,7 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
     return MOE_ZC_ERR_INVALID;
   if (N > 0 && (!aligned16(w_gate) || !aligned16(w_down) || (!packed && !aligned16(w_up))))
     return MOE_ZC_ERR_INVALID;
-  const Plan pl = make_plan(s);
+  const Plan pl = make_plan(s, fp8);
   if (!workspace || workspace_bytes < pl.total) return MOE_ZC_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ZC_ERR_WORKSPACE;
 
@@ -202,7 +223,15 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
     p.B0 = w_gate; p.B1 = w_up; p.ldb = d; p.b_group_stride = I * d;
     p.C = h; p.ldc = I; p.Nout = (int)I;
     p.row_offsets = offsets; p.tile_prefix = tiles; p.G = N; p.M = 0;
-    if (packed)
+    if (fp8) {
+      // block-FP8 gate/up: x quantized once, its code rows gathered through perm
+      uint8_t* xq = reinterpret_cast<uint8_t*>(ws + pl.xq);
+      uint8_t* xs = reinterpret_cast<uint8_t*>(ws + pl.xs);
+      MOE_ZC_TRY(launch_quantize_mx(static_cast<const bf16_t*>(x), xq, xs, T, d, stream));
+      p.A = xq; p.a_rows = perm;
+      p.a_scales = xs; p.a_scale_ld = d / 32;
+      MOE_ZC_TRY(launch_fp8_gemm(p, s.ffn_tile_rows, s.smax, stream));
+    } else if (packed)
       MOE_ZC_TRY(launch_packed_gemm(p, kSwiGLU_BF16, s.ffn_tile_rows, s.smax, stream));
     else if (bf)
       MOE_ZC_TRY(launch_mfma_gemm(p, kSwiGLU_BF16, s.ffn_tile_rows, s.smax, stream));
@@ -275,8 +304,8 @@ moe_zc_status moe_zc_forward(const void* x, const float* w_router, const float* 
                              const void* residual, void* y, int64_t T, int64_t d, int64_t I,
                              int32_t N, int32_t Z, int32_t K, moe_zc_dtype dt, moe_zc_aux* aux,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return forward_impl(x, w_router, bias, w_gate, w_up, w_down, false, residual, y, T, d, I, N, Z,
-                      K, dt, aux, workspace, workspace_bytes, stream);
+  return forward_impl(x, w_router, bias, w_gate, w_up, w_down, kRowMajor, residual, y, T, d, I,
+                      N, Z, K, dt, aux, workspace, workspace_bytes, stream);
 }
 
 moe_zc_status moe_zc_forward_packed(const void* x, const float* w_router, const float* bias,
@@ -285,8 +314,64 @@ moe_zc_status moe_zc_forward_packed(const void* x, const float* w_router, const 
                                     int64_t I, int32_t N, int32_t Z, int32_t K, moe_zc_dtype dt,
                                     moe_zc_aux* aux, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream) {
-  return forward_impl(x, w_router, bias, gate_up_packed, nullptr, down_packed, true, residual, y,
-                      T, d, I, N, Z, K, dt, aux, workspace, workspace_bytes, stream);
+  return forward_impl(x, w_router, bias, gate_up_packed, nullptr, down_packed, kPacked, residual,
+                      y, T, d, I, N, Z, K, dt, aux, workspace, workspace_bytes, stream);
+}
+
+size_t moe_zc_workspace_size_fp8(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z,
+                                 int32_t K) {
+  Shape s;
+  if (check_shape(T, d, I, N, Z, K, MOE_ZC_BF16, &s) != MOE_ZC_OK) return 0;
+  if (check_fp8_shape(s) != MOE_ZC_OK) return 0;
+  return make_plan(s, true).total;
+}
+
+moe_zc_status moe_zc_forward_packed_fp8(const void* x, const float* w_router, const float* bias,
+                                        const void* gate_up_fp8, const void* down_packed,
+                                        const void* residual, void* y, int64_t T, int64_t d,
+                                        int64_t I, int32_t N, int32_t Z, int32_t K,
+                                        moe_zc_aux* aux, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  return forward_impl(x, w_router, bias, gate_up_fp8, nullptr, down_packed, kPackedFp8, residual,
+                      y, T, d, I, N, Z, K, MOE_ZC_BF16, aux, workspace, workspace_bytes, stream);
+}
+
+moe_zc_status moe_zc_packed_fp8_expert_bytes(int64_t d, int64_t I, size_t* gate_up_bytes) {
+  if (!gate_up_bytes) return MOE_ZC_ERR_INVALID;
+  const moe_zc_status st = check_pack_shape(d, I, MOE_ZC_BF16);
+  if (st != MOE_ZC_OK) return st;
+  if (d % 128 != 0) return MOE_ZC_ERR_UNSUPPORTED;
+  *gate_up_bytes = (size_t)fp8_packed_bytes(I, d);
+  return MOE_ZC_OK;
+}
+
+moe_zc_status moe_zc_pack_expert_weights_fp8(const void* w_gate, const void* w_up,
+                                             int32_t n_experts, int64_t d, int64_t I,
+                                             void* gate_up_fp8, hipStream_t stream) {
+  const moe_zc_status st = check_pack_shape(d, I, MOE_ZC_BF16);
+  if (st != MOE_ZC_OK) return st;
+  if (d % 128 != 0) return MOE_ZC_ERR_UNSUPPORTED;
+  if (n_experts < 0) return MOE_ZC_ERR_INVALID;
+  if (n_experts == 0) return MOE_ZC_OK;
+  if (!w_gate || !w_up || !gate_up_fp8) return MOE_ZC_ERR_INVALID;
+  if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(gate_up_fp8)) return MOE_ZC_ERR_INVALID;
+  MOE_ZC_TRY(launch_pack_weights_fp8(static_cast<const bf16_t*>(w_gate),
+                                     static_cast<const bf16_t*>(w_up),
+                                     static_cast<uint8_t*>(gate_up_fp8), n_experts, (int)I,
+                                     (int)d, stream));
+  return MOE_ZC_OK;
+}
+
+moe_zc_status moe_zc_quantize_mx(const void* x, int64_t rows, int64_t d, void* codes,
+                                 void* scales, hipStream_t stream) {
+  if (rows < 0 || d <= 0) return MOE_ZC_ERR_INVALID;
+  if (d % 32 != 0 || rows * d >= (int64_t(1) << 40)) return MOE_ZC_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_ZC_OK;
+  if (!x || !codes || !scales) return MOE_ZC_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(codes)) return MOE_ZC_ERR_INVALID;
+  MOE_ZC_TRY(launch_quantize_mx(static_cast<const bf16_t*>(x), static_cast<uint8_t*>(codes),
+                                static_cast<uint8_t*>(scales), rows, d, stream));
+  return MOE_ZC_OK;
 }
 
 moe_zc_status moe_zc_packed_expert_bytes(int64_t d, int64_t I, moe_zc_dtype dt,

@@ -213,10 +213,13 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
 
   // prologue: stages 0 .. PK_DIST-1 (repeating the last stage where nk is
   // smaller), weights then activations of each; wait for stage 0 only
+  // (fenced, so that the loads are issued stage by stage, as the wait counts
+  // assume)
 #pragma unroll
   for (int u = 0; u < PK_DIST; ++u) {
     PK_LOAD_B(min(u, nk - 1), u);
     PK_DMA_A(min(u, nk - 1), u);
+    __builtin_amdgcn_sched_barrier(0);
   }
   ring_barrier<(PK_DIST - 1) * (8 + NA)>();
   PK_LOADF(0, 0, 0);
@@ -254,45 +257,7 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
       }
     return;
   }
-  // bf16 outputs go through a wavefront-private LDS tile, one 32-row block at
-  // a time, so that global stores are whole 16-byte row pieces
-  constexpr int OC = SWIGLU ? 32 : 64;  // output columns of this wavefront
-  constexpr int OS = OC + 8;            // padded LDS row (elements)
-  constexpr int CH = OC / 8;            // 16-byte pieces per row
-  bf16_t* ot = reinterpret_cast<bf16_t*>(smem) + wave * (32 * OS);
-  const int gcol0 = c.n0 + wave * OC;
-  bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.C);
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-#pragma unroll
-    for (int jj = 0; jj < OC / 32; ++jj)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + lrow4 + (v & 3);
-        float val;
-        if (SWIGLU) {
-          const float a = acc[i][0][v];
-          val = a / (1.0f + __expf(-a)) * acc[i][1][v];
-        } else {
-          val = acc[i][jj][v];
-        }
-        ot[r * OS + jj * 32 + lcol] = f32_to_bf16(val);
-      }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS writes landed
-    __builtin_amdgcn_wave_barrier();
-    const int grow0 = c.m0 + i * 32;
-#pragma unroll
-    for (int q = lane; q < 32 * CH; q += 64) {
-      const int r = q / CH, ch = q - r * CH;
-      const int grow = grow0 + r;
-      const int gcol = gcol0 + ch * 8;
-      if (grow < c.m_end && gcol < p.Nout)
-        *reinterpret_cast<u32x4_t*>(&Cout[(int64_t)grow * p.ldc + gcol]) =
-            *reinterpret_cast<const u32x4_t*>(&ot[r * OS + ch * 8]);
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
-    __builtin_amdgcn_wave_barrier();
-  }
+  store_bf16_tile<NA, SWIGLU>(acc, smem, wave, lane, c, p);
 }
 
 template <typename CFG, int EPI>

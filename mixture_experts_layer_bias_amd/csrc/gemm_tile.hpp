@@ -82,4 +82,57 @@ __device__ __forceinline__ void ring_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Epilogue of a 256-thread MFMA tile with bf16 output: wavefront `wave` holds
+// acc[i][j] for row block i and its column blocks j = 0, 1 of 32 columns; D of
+// a 32 x 32 block sits in lane j + 32 ((i / 4) % 2), register 4 (i / 8) + i % 4.
+// SwiGLU: column block 0 holds gate, 1 holds up of the same 32 hidden units,
+// and the output is silu(gate) * up (32 columns per wavefront); otherwise 64
+// columns.  Values go through a wavefront-private LDS tile (smem must hold
+// 4 x 32 rows of padded columns), one 32-row block at a time, so that global
+// stores are whole 16-byte row pieces.
+template <int NA, bool SWIGLU>
+__device__ __forceinline__ void store_bf16_tile(const f32x16_t (&acc)[NA][2], char* smem,
+                                                int wave, int lane, const TileCoord& c,
+                                                const GemmProblem& p) {
+  const int lrow4 = 4 * (lane >> 5);
+  const int lcol = lane & 31;
+  constexpr int OC = SWIGLU ? 32 : 64;  // output columns of this wavefront
+  constexpr int OS = OC + 8;            // padded LDS row (elements)
+  constexpr int CH = OC / 8;            // 16-byte pieces per row
+  bf16_t* ot = reinterpret_cast<bf16_t*>(smem) + wave * (32 * OS);
+  const int gcol0 = c.n0 + wave * OC;
+  bf16_t* __restrict__ Cout = static_cast<bf16_t*>(p.C);
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+#pragma unroll
+    for (int jj = 0; jj < OC / 32; ++jj)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + lrow4 + (v & 3);
+        float val;
+        if (SWIGLU) {
+          const float a = acc[i][0][v];
+          val = a / (1.0f + __expf(-a)) * acc[i][1][v];
+        } else {
+          val = acc[i][jj][v];
+        }
+        ot[r * OS + jj * 32 + lcol] = f32_to_bf16(val);
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS writes landed
+    __builtin_amdgcn_wave_barrier();
+    const int grow0 = c.m0 + i * 32;
+#pragma unroll
+    for (int q = lane; q < 32 * CH; q += 64) {
+      const int r = q / CH, ch = q - r * CH;
+      const int grow = grow0 + r;
+      const int gcol = gcol0 + ch * 8;
+      if (grow < c.m_end && gcol < p.Nout)
+        *reinterpret_cast<u32x4_t*>(&Cout[(int64_t)grow * p.ldc + gcol]) =
+            *reinterpret_cast<const u32x4_t*>(&ot[r * OS + ch * 8]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 }  // namespace moezc

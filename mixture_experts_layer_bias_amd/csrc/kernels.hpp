@@ -64,6 +64,8 @@ struct GemmProblem {
   const int32_t* tile_prefix;  // [G+1] device m-tile prefix, or null
   int G;
   int M;
+  const uint8_t* a_scales;  // block-FP8 A only: [rows][K / 32] scale bytes
+  int64_t a_scale_ld;       // scale bytes per A row (K / 32)
 };
 
 enum Epilogue { kStoreF32 = 0, kStoreBF16 = 1, kSwiGLU_BF16 = 2, kSwiGLU_F32 = 3 };
@@ -93,6 +95,21 @@ hipError_t launch_split_router_packed(const float* w, bf16_t* out, int E, int d,
 hipError_t launch_packed_gemm(const GemmProblem& p, int epilogue, int tile_rows,
                               int64_t max_rows, hipStream_t s);
 int packed_down_tile_rows(int ffn_tile_rows);
+
+// Block-FP8 gate/up path (gemm_fp8.hip): E4M3 codes with one power-of-two
+// scale per 32 values along k; the down projection stays bf16.
+// Bytes of one group's packed FP8 gate/up weights (I hidden units by d).
+int64_t fp8_packed_bytes(int64_t I, int64_t d);
+// x [rows][d] bf16 -> codes [rows][d] and scale bytes [rows][d / 32].
+hipError_t launch_quantize_mx(const bf16_t* x, uint8_t* xq, uint8_t* xs, int64_t rows, int64_t d,
+                              hipStream_t s);
+// W_gate, W_up [groups][I][d] bf16 -> packed FP8 gate/up blocks.
+hipError_t launch_pack_weights_fp8(const bf16_t* wg, const bf16_t* wu, uint8_t* out, int groups,
+                                   int I, int d, hipStream_t s);
+// SwiGLU gate/up GEMM: A = FP8 codes (row stride lda bytes, optional gather
+// a_rows), a_scales / a_scale_ld its scales, B0 = packed FP8 weights, C = h
+// bf16.  Tiles of at most kPackedMaxTileRows rows, as the bf16 packed path.
+hipError_t launch_fp8_gemm(const GemmProblem& p, int tile_rows, int64_t max_rows, hipStream_t s);
 
 // fp32 FMA path (gemm_simt.hip).
 hipError_t launch_simt_gemm(const GemmProblem& p, int epilogue, int64_t max_rows,

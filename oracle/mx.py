@@ -93,7 +93,7 @@ def mx_quantize(v, axis=-1):
     """Block quantization along ``axis`` in blocks of 32 (the axis length must
     be a multiple of 32).  Returns (codes uint8, same shape as v; scales uint8
     E8M0 = s + 127, shape with that axis divided by 32)."""
-    v = np.moveaxis(np.asarray(v, dtype=np.float64), axis, -1)
+    v = np.moveaxis(_layer._f64(v), axis, -1)
     n = v.shape[-1]
     if n % BLOCK:
         raise ValueError("axis length must be a multiple of 32")
@@ -113,36 +113,44 @@ def mx_dequantize(codes, scales, axis=-1) -> np.ndarray:
     return np.moveaxis(out.reshape(c.shape), -1, axis)
 
 
-def forward_fp8_gateup(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, K: int,
-                       residual=None, logits32=None):
-    """The layer with the gate/up projection in block FP8: x quantized per
-    token per 32 channels, W_gate and W_up per output row per 32 inputs, the
-    products taken exactly (fp64) from the dequantized values; router, down
-    projection and combine as in the bf16 layer.  Routing uses ``logits32``
-    when given (the router itself is not quantized)."""
-    x64 = np.asarray(x, dtype=np.float64)
+def forward_tokens_fp8(x_rows, logits32_rows, bias, get_expert, N: int, K: int,
+                       residual_rows=None):
+    """Layer output for a set of tokens with the gate/up projection in block
+    FP8, given their fp32 logits.  x is quantized per token, so any subset of
+    tokens can be evaluated alone; get_expert(e) returns the bf16 (W_gate[e],
+    W_up[e], W_down[e]), of which gate and up are quantized per output row.
+    The identity experts pass x itself (they compute nothing)."""
+    x64 = _layer._f64(x_rows)
     xq, xs = mx_quantize(x64, axis=-1)
     x_dq = mx_dequantize(xq, xs, axis=-1)
-
-    def get(e):
-        gq, gs = mx_quantize(np.asarray(w_gate[e], dtype=np.float64), axis=-1)
-        uq, us = mx_quantize(np.asarray(w_up[e], dtype=np.float64), axis=-1)
-        return mx_dequantize(gq, gs), mx_dequantize(uq, us), np.asarray(w_down[e], np.float64)
-
-    l64 = _layer.router_logits(x64, w_router)
-    if logits32 is None:
-        logits32 = l64.astype(np.float32)
-    rt = _layer.route(logits32, bias, K, N)
+    rt = _layer.route(logits32_rows, bias, K, N)
     idx, g = rt["idx"], rt["gate"]
     T = x64.shape[0]
     rows = np.zeros((T, K, x64.shape[1]))
     for e in np.unique(idx[idx < N]):
         tt, kk = np.nonzero(idx == e)
-        wg, wu, wd = get(int(e))
+        wg, wu, wd = (_layer._f64(w) for w in get_expert(int(e)))
+        wg = mx_dequantize(*mx_quantize(wg, axis=-1), axis=-1)
+        wu = mx_dequantize(*mx_quantize(wu, axis=-1), axis=-1)
         # gate/up on the dequantized FP8 operands, down on the bf16 weights
         rows[tt, kk] = _layer.swiglu_ffn(x_dq[tt], wg, wu, wd)
-    # identity experts pass the unquantized x (they compute nothing)
-    y = _layer.combine(x64, idx, g, rows, N, residual)
+    y = _layer.combine(x64, idx, g, rows, N, residual_rows)
+    return y, rt
+
+
+def forward_fp8_gateup(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, K: int,
+                       residual=None, logits32=None):
+    """The whole layer with the gate/up projection in block FP8 (see
+    forward_tokens_fp8); routing uses ``logits32`` when given, otherwise the
+    fp64 logits rounded once to fp32 (the router itself is not quantized)."""
+    l64 = _layer.router_logits(x, w_router)
+    if logits32 is None:
+        logits32 = l64.astype(np.float32)
+
+    def get(e):
+        return w_gate[e], w_up[e], w_down[e]
+
+    y, rt = forward_tokens_fp8(x, logits32, bias, get, N, K, residual)
     rt["logits64"] = l64
     rt["y"] = y
     return rt

@@ -27,13 +27,19 @@ LOGIT_TOL = 1e-4
 Y_TOL = {"bf16": 1e-2, "f32": 1e-5}
 
 
-def run_gpu(w, inp, residual=True, workspace=None, events=None, packed=None):
+def run_gpu(w, inp, residual=True, workspace=None, events=None, packed=None, fp8=False):
     """One forward through the C ABI; ``packed`` = (gate_up, down) from
-    moe_zc_pack_expert_weights selects moe_zc_forward_packed."""
+    moe_zc_pack_expert_weights selects moe_zc_forward_packed, and with ``fp8``
+    ``packed`` = (gate_up_fp8, down) selects moe_zc_forward_packed_fp8."""
     dev = inp["x"].device
     aux = m.alloc_aux(w.T, w.N, w.Z, w.K, dev)
     res = inp["residual"] if residual else None
-    if packed is None:
+    if fp8:
+        gu, dn = packed if packed is not None else (None, None)
+        y = m.moe_zc_forward_packed_fp8(inp["x"], inp["w_router"], inp["bias"], gu, dn,
+                                        w.N, w.Z, w.K, w.I, residual=res, aux=aux,
+                                        workspace=workspace, events=events)
+    elif packed is None:
         y = m.moe_zc_forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
                              inp["w_down"], w.N, w.Z, w.K, residual=res, aux=aux,
                              workspace=workspace, events=events)
@@ -78,8 +84,9 @@ def validate_grouping(idx, loads, offsets, perm, pos, N, E):
         assert (np.diff(blk) > 0).all(), f"expert {e}: tokens not ascending"
 
 
-def check_forward(w, inp, g, y_tokens=None, max_flip_frac=1e-3, get_expert=None):
-    """Compare a GPU forward (``g`` from run_gpu) with the oracle."""
+def check_forward(w, inp, g, y_tokens=None, max_flip_frac=1e-3, get_expert=None, fp8=False):
+    """Compare a GPU forward (``g`` from run_gpu) with the oracle (with the
+    gate/up projection in block FP8 when ``fp8``)."""
     T, N, K, E = w.T, w.N, w.K, w.E
     x = inp["x"].cpu()
     wr = inp["w_router"].cpu()
@@ -128,8 +135,8 @@ def check_forward(w, inp, g, y_tokens=None, max_flip_frac=1e-3, get_expert=None)
 
         def get_expert(e):
             return wg[e], wu[e], wd[e]
-    y_ref, _ = oracle.forward_tokens(x[toks], l32[toks], b, get_expert, N, K,
-                                     None if res is None else res[toks])
+    fwd = oracle.mx.forward_tokens_fp8 if fp8 else oracle.forward_tokens
+    y_ref, _ = fwd(x[toks], l32[toks], b, get_expert, N, K, None if res is None else res[toks])
     scale = max(np.abs(y_ref).max(), 1e-30)
     err = np.abs(g["y"][toks] - y_ref).max() if len(toks) else 0.0
     tol = Y_TOL[w.dtype] * scale
