@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s + activated TFLOP/s (% of bf16 MFMA peak) on 1 MI355X"
 PEAK_BF16 = 2.5e15      # dense bf16 MFMA, FLOP/s
+PEAK_FP8 = 5.0e15       # dense fp8 MFMA, FLOP/s
 PEAK_HBM = 8.0e12       # HBM3E, B/s
 
 
@@ -39,6 +40,9 @@ def parse():
                     choices=["tiny", "mid", "decode", "prefill", "skew"])
     ap.add_argument("--layout", default="packed", choices=["packed", "rowmajor"],
                     help="expert weight layout of the bf16 forward")
+    ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8"],
+                    help="fp8: gate/up projection in block FP8 (moe_zc_forward_packed_fp8); "
+                         "the down projection stays bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=24,
                     help="experts the CPU-baseline sample evaluates")
@@ -91,12 +95,16 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}))
 
 
-def algorithmic(w, S, touched, es):
+def algorithmic(w, S, touched, es, fp8=False):
     """Algorithmic bytes / FLOPs per launch of each stage (inputs read once,
     outputs written once).  bf16: the gate/up GEMM gathers its rows from x,
-    so its input is x itself and the grouping stage moves only indices."""
+    so its input is x itself and the grouping stage moves only indices.
+    fp8: the gate/up weights are one byte per value plus one scale byte per
+    32, and x (bf16) is read once to be quantized; the FP8 copy of x that the
+    GEMM gathers is internal traffic and not counted."""
     T, d, I, N, E, K = w.T, w.d, w.I, w.N, w.E, w.K
     gathered = es == 2 and T * d * es < 2**31
+    w_gu = touched * 2 * I * d * ((1.0 + 1.0 / 32.0) if fp8 else es)
     return {
         "router_gemm": {"flop": 2.0 * T * d * E,
                         "bytes": T * d * es + E * d * 4 + T * E * 4},
@@ -104,8 +112,7 @@ def algorithmic(w, S, touched, es):
         "permute": {"bytes": T * K * 4 * 4 if gathered else
                     T * d * es + S * d * es + T * K * 4 * 3},
         "gemm_gate_up_swiglu": {"flop": 4.0 * d * I * S,
-                                "bytes": touched * 2 * I * d * es
-                                + (T if gathered else S) * d * es + S * I * es},
+                                "bytes": w_gu + (T if gathered else S) * d * es + S * I * es},
         "gemm_down": {"flop": 2.0 * d * I * S,
                       "bytes": touched * d * I * es + S * I * es + S * d * es},
         "combine": {"bytes": S * d * es + 3 * T * d * es + T * K * 12},
@@ -178,7 +185,12 @@ def main():
     inp = make_inputs(w, device=dev)
     dt = inp["x"].dtype
     es = inp["x"].element_size()
-    need = m.moe_zc_workspace_size(w.T, w.d, w.I, w.N, w.Z, w.K, dt)
+    fp8 = args.precision == "fp8"
+    if fp8 and (w.dtype != "bf16" or args.layout != "packed"):
+        print("bench.py: --precision fp8 needs a bf16 workload and packed weights", file=sys.stderr)
+        sys.exit(2)
+    need = (m.moe_zc_workspace_size_fp8(w.T, w.d, w.I, w.N, w.Z, w.K) if fp8
+            else m.moe_zc_workspace_size(w.T, w.d, w.I, w.N, w.Z, w.K, dt))
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     aux = m.alloc_aux(w.T, w.N, w.Z, w.K, dev, keys=("loads", "offsets"))
     y = torch.empty(w.T, w.d, dtype=dt, device=dev)
@@ -192,13 +204,19 @@ def main():
     packed = args.layout == "packed" and w.dtype == "bf16"
     if packed:
         gu, dn = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+        if fp8:
+            gu = m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"])
         torch.cuda.synchronize()
         for k in ("w_gate", "w_up", "w_down"):
             inp[k] = None
         torch.cuda.empty_cache()
 
     def step(events=None):
-        if packed:
+        if fp8:
+            m.moe_zc_forward_packed_fp8(inp["x"], inp["w_router"], bias, gu, dn, w.N, w.Z, w.K,
+                                        w.I, residual=inp["residual"], out=y, aux=aux,
+                                        workspace=ws, events=events)
+        elif packed:
             m.moe_zc_forward_packed(inp["x"], inp["w_router"], bias, gu, dn, w.N, w.Z, w.K, w.I,
                                     residual=inp["residual"], out=y, aux=aux, workspace=ws,
                                     events=events)
@@ -241,24 +259,28 @@ def main():
     pid_report = {"gains": [pid.kp, pid.ki, pid.kd], "target": "uniform T*K/E",
                   "steps_applied": args.warmup + args.steps,
                   "first_step": first_pid, "last_step": last_pid}
-    alg = algorithmic(w, S, touched, es)
+    alg = algorithmic(w, S, touched, es, fp8)
     flop_act = 2.0 * w.T * w.d * w.E + 6.0 * w.d * w.I * S
     t_step = ms_per_step / 1e3
     gemm_s = (stage["gemm_gate_up_swiglu"] + stage["gemm_down"]) / 1e3
-    mfma_frac = 6.0 * w.d * w.I * S / gemm_s / PEAK_BF16 if gemm_s > 0 else None
+    # ideal MFMA time of both expert GEMMs at their dtypes' peaks over the measured time
+    t_ideal = 4.0 * w.d * w.I * S / (PEAK_FP8 if fp8 else PEAK_BF16) + 2.0 * w.d * w.I * S / PEAK_BF16
+    mfma_frac = t_ideal / gemm_s if gemm_s > 0 else None
 
     dom = "gemm_gate_up_swiglu"
     a = alg[dom]
     t_dom = stage[dom] / 1e3
-    t_b, t_f = a["bytes"] / PEAK_HBM, a["flop"] / PEAK_BF16
+    peak_dom = PEAK_FP8 if fp8 else PEAK_BF16   # a contraction against its own dtype's peak
+    t_b, t_f = a["bytes"] / PEAK_HBM, a["flop"] / peak_dom
     if t_b >= t_f:
         roof = {"bound": "hbm", "achieved": a["bytes"] / t_dom / 1e9, "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s"}
     else:
-        roof = {"bound": "mfma", "achieved": a["flop"] / t_dom / 1e12, "peak": PEAK_BF16 / 1e12,
+        roof = {"bound": "mfma", "achieved": a["flop"] / t_dom / 1e12, "peak": peak_dom / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = counter_traffic()
+    # the committed counter summary covers the bf16 kernel only
+    roof["traffic"] = None if fp8 else counter_traffic()
     roof["kernel"] = dom
     roof["avg_launch_ms"] = stage[dom]
 
@@ -270,8 +292,9 @@ def main():
         entry = {"ms": round(stage[k], 4), "GB/s": round(v["bytes"] / ts / 1e9, 1),
                  "hbm_frac": round(v["bytes"] / ts / PEAK_HBM, 4)}
         if "flop" in v:
+            pk = PEAK_FP8 if (fp8 and k == "gemm_gate_up_swiglu") else PEAK_BF16
             entry["TFLOP/s"] = round(v["flop"] / ts / 1e12, 1)
-            entry["mfma_frac"] = round(v["flop"] / ts / PEAK_BF16, 4)
+            entry["mfma_frac"] = round(v["flop"] / ts / pk, 4)
         stage_roof[k] = entry
     for k in ("chunk_hist", "scan"):
         stage_roof[k] = {"ms": round(stage[k], 4)}
@@ -289,12 +312,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": ("fp8-e4m3 block-scaled gate/up + bf16" if fp8
+                  else ("bf16" if w.dtype == "bf16" else "f32")),
         "data": "synthetic (seeded Gaussian inputs, random-init expert weights)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "I": w.I, "N": w.N, "Z": w.Z,
                    "K": w.K, "expert_ffn": "SwiGLU", "residual": True,
-                   "step": ("moe_zc_forward_packed" if packed else "moe_zc_forward")
+                   "step": ("moe_zc_forward_packed_fp8" if fp8 else
+                            "moe_zc_forward_packed" if packed else "moe_zc_forward")
                    + " + moe_zc_bias_update",
+                   "precision": ("gate/up block FP8 (E4M3, power-of-two scale per 32 k); "
+                                 "router, down, combine bf16/fp32" if fp8 else "bf16"),
                    "expert_weights": "packed" if packed else "row-major",
                    "parallelism": "none (1 GPU)"},
         "activated_tflops": flop_act / t_step / 1e12,
