@@ -32,3 +32,4 @@ from .moe_zc import (  # noqa: F401
 )
 from . import bruteforce  # noqa: F401
 from . import mx  # noqa: F401
+from . import backward  # noqa: F401

@@ -16,6 +16,7 @@ import torch.nn.functional as F
 
 from oracle import moe_zc as om
 from oracle import mx as omx
+from oracle import backward as obw
 from oracle import bruteforce as bf
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -466,6 +467,93 @@ def check_fp8_layer_lossless_on_grid(T=24, d=64, I=32, N=5, Z=3, K=3, seed=17):
     assert 1e-4 < rel < 0.1, rel
 
 
+# ------------------------------------------------------------- backward -----
+def _loss(x, wr, b, wg, wu, wd, N, Z, K, dy):
+    rt = om.forward(x, wr, b, wg, wu, wd, N, Z, K)
+    return float((rt["y"] * dy).sum()), rt["idx"]
+
+
+def check_backward_finite_differences(T=6, d=8, I=5, N=3, Z=2, K=2, seed=18, h=1e-3):
+    r = _rng(seed)
+    x = r.standard_normal((T, d))
+    wr = r.standard_normal((N + Z, d)) / np.sqrt(d)
+    wg = r.standard_normal((N, I, d)) / np.sqrt(d)
+    wu = r.standard_normal((N, I, d)) / np.sqrt(d)
+    wd = r.standard_normal((N, d, I)) / np.sqrt(I)
+    b = r.uniform(-0.05, 0.05, N + Z)
+    dy = r.standard_normal((T, d))
+    g = obw.backward(x, wr, b, wg, wu, wd, N, Z, K, dy)
+    _, idx0 = _loss(x, wr, b, wg, wu, wd, N, Z, K, dy)
+    params = {"dx": x, "dw_router": wr, "dw_gate": wg, "dw_up": wu, "dw_down": wd}
+    checked = 0
+    for name, P in params.items():
+        an = g[name]
+        fd = np.full(P.shape, np.nan)
+        for i in np.ndindex(P.shape):
+            old = P[i]
+            P[i] = old + h
+            lp, ip = _loss(x, wr, b, wg, wu, wd, N, Z, K, dy)
+            P[i] = old - h
+            lm, im = _loss(x, wr, b, wg, wu, wd, N, Z, K, dy)
+            P[i] = old
+            if np.array_equal(ip, idx0) and np.array_equal(im, idx0):   # routing unchanged
+                fd[i] = (lp - lm) / (2 * h)
+        ok = ~np.isnan(fd)
+        assert ok.mean() > 0.9, (name, ok.mean())
+        err = np.abs(fd[ok] - an[ok]).max()
+        assert err <= 2e-3 * max(np.abs(an).max(), 1e-3), (name, err, np.abs(an).max())
+        checked += int(ok.sum())
+    assert checked > 400
+
+
+def check_backward_single_ffn_textbook(T=10, d=12, I=7, seed=19):
+    # one FFN expert, K = 1: p = 1, so y = FFN(x) + r and the router gets nothing
+    import torch
+    r = _rng(seed)
+    x = r.standard_normal((T, d))
+    wr = r.standard_normal((1, d))
+    wg = r.standard_normal((1, I, d)) / np.sqrt(d)
+    wu = r.standard_normal((1, I, d)) / np.sqrt(d)
+    wd = r.standard_normal((1, d, I)) / np.sqrt(I)
+    dy = r.standard_normal((T, d))
+    g = obw.backward(x, wr, np.zeros(1), wg, wu, wd, 1, 0, 1, dy)
+    tx, tg, tu, td = (torch.tensor(a, dtype=torch.float64, requires_grad=True)
+                      for a in (x, wg[0], wu[0], wd[0]))
+    y = (torch.nn.functional.silu(tx @ tg.T) * (tx @ tu.T)) @ td.T
+    (y * torch.tensor(dy)).sum().backward()
+    for name, t in (("dx", tx), ("dw_down", td)):
+        ref = t.grad.numpy()
+        got = g[name] if name == "dx" else g[name][0]
+        assert np.abs(got - ref).max() <= 1e-12 * max(np.abs(ref).max(), 1.0), name
+    assert np.abs(g["dw_gate"][0] - tg.grad.numpy()).max() <= 1e-12 * max(np.abs(tg.grad.numpy()).max(), 1.0)
+    assert np.abs(g["dw_up"][0] - tu.grad.numpy()).max() <= 1e-12 * max(np.abs(tu.grad.numpy()).max(), 1.0)
+    assert not g["dw_router"].any()
+
+
+def check_backward_identity_closed_form(T=20, d=9, Z=5, K=3, seed=20):
+    # identity experts only: y_t = (sum over chosen p) x_t + r_t
+    r = _rng(seed)
+    x = r.standard_normal((T, d))
+    wr = r.standard_normal((Z, d)) / np.sqrt(d)
+    b = r.uniform(-0.05, 0.05, Z)
+    dy = r.standard_normal((T, d))
+    g = obw.backward(x, wr, b, np.zeros((0, 1, d)), np.zeros((0, 1, d)), np.zeros((0, d, 1)),
+                     0, Z, K, dy)
+    rt = g["route"]
+    p, idx = rt["p64"], rt["idx"]
+    chosen = np.zeros_like(p)
+    np.put_along_axis(chosen, idx, 1.0, axis=1)
+    sel = (p * chosen).sum(axis=1)                   # sum of the chosen gates
+    xy = (x * dy).sum(axis=1)
+    # d/dl_j of sum_{i chosen} p_i = p_j ([j chosen] - sel)
+    dl = xy[:, None] * p * (chosen - sel[:, None])
+    assert np.allclose(g["dlogits"], dl, rtol=1e-12, atol=1e-14)
+    # the direct path multiplies x by the gates as stored (fl32 of p)
+    gsum = rt["gate"].astype(np.float64).sum(axis=1)
+    assert np.allclose(g["dx"], gsum[:, None] * dy + dl @ wr, rtol=1e-12, atol=1e-12)
+    assert np.allclose(g["dw_router"], dl.T @ x, rtol=1e-12, atol=1e-12)
+
+
 ALL_CHECKS = [
     check_hand_example, check_pid_golden, check_bruteforce_tiny,
     check_topk_ties_enumeration, check_softmax_bruteforce,
@@ -476,4 +564,6 @@ ALL_CHECKS = [
     check_closed_loop_conservation_and_positional_form,
     check_closed_loop_integral_settles, check_e4m3_codes, check_e4m3_rounding_bruteforce,
     check_mx_scales_minimal, check_fp8_layer_lossless_on_grid,
+    check_backward_finite_differences, check_backward_single_ffn_textbook,
+    check_backward_identity_closed_form,
 ]

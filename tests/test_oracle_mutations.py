@@ -237,6 +237,58 @@ def m_fp8_identity_quantized(mp):
     mp.setattr(omx, "forward_fp8_gateup", fwd)
 
 
+from oracle import backward as obw
+_bw = obw.backward
+
+
+def _bw_variant(**flags):
+    """The oracle backward with one planted slip (re-implemented here)."""
+    def bw(x, w_router, bias, w_gate, w_up, w_down, N, Z, K, dy, logits32=None):
+        out = _bw(x, w_router, bias, w_gate, w_up, w_down, N, Z, K, dy, logits32)
+        wr = np.asarray(w_router, np.float64)
+        if flags.get("drop_router"):
+            out["dx"] = out["dx"] - out["dlogits"] @ wr
+        return out
+    return bw
+
+
+def m_bwd_no_router_term(mp):
+    mp.setattr(obw, "backward", _bw_variant(drop_router=True))
+
+
+def m_bwd_silu_derivative_sigmoid(mp):
+    # d silu / da taken as sigmoid(a) alone
+    src = __import__("inspect").getsource(_bw)
+    src = src.replace("s * (1.0 + a * (1.0 - s))", "s")
+    ns = dict(obw.__dict__)
+    exec(compile(src, "mutant", "exec"), ns)
+    mp.setattr(obw, "backward", ns["backward"])
+
+
+def m_bwd_gate_not_applied(mp):
+    src = __import__("inspect").getsource(_bw).replace("dE = g[:, None] * dy64[tt]", "dE = dy64[tt]")
+    ns = dict(obw.__dict__)
+    exec(compile(src, "mutant", "exec"), ns)
+    mp.setattr(obw, "backward", ns["backward"])
+
+
+def m_bwd_identity_dx_dropped(mp):
+    src = __import__("inspect").getsource(_bw).replace(
+        "np.add.at(dx, tz, gate[tz, kz][:, None] * dy64[tz])", "pass")
+    ns = dict(obw.__dict__)
+    exec(compile(src, "mutant", "exec"), ns)
+    mp.setattr(obw, "backward", ns["backward"])
+
+
+def m_bwd_softmax_jacobian_wrong(mp):
+    # dl = p * dp, without the centring term
+    src = __import__("inspect").getsource(_bw).replace(
+        "dl = p * (dp - (p * dp).sum(axis=1, keepdims=True))", "dl = p * dp")
+    ns = dict(obw.__dict__)
+    exec(compile(src, "mutant", "exec"), ns)
+    mp.setattr(obw, "backward", ns["backward"])
+
+
 MUTATIONS = [
     m_bias_in_gate, m_renormalised_gates, m_softmax_ffn_only, m_bias_on_logit,
     m_tie_to_higher_index, m_smallest_keys, m_drop_identity_term,
@@ -245,7 +297,8 @@ MUTATIONS = [
     m_unstable_permutation, m_pid_sign, m_pid_p_on_error, m_pid_no_derivative,
     m_loop_without_feedback, m_loop_history_reset, m_budget_swapped,
     m_mx_floor_scale, m_mx_truncate, m_mx_scale_bias_128, m_mx_block16,
-    m_fp8_identity_quantized,
+    m_fp8_identity_quantized, m_bwd_no_router_term, m_bwd_silu_derivative_sigmoid,
+    m_bwd_gate_not_applied, m_bwd_identity_dx_dropped, m_bwd_softmax_jacobian_wrong,
 ]
 
 # the statistical check is slow and not needed to catch any of these
