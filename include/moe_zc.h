@@ -249,6 +249,76 @@ moe_zc_status moe_zc_forward_packed_fp8(const void* x, const float* w_router,
 moe_zc_status moe_zc_quantize_mx(const void* x, int64_t rows, int64_t d,
                                  void* codes, void* scales, hipStream_t stream);
 
+/* ---- backward (training) --------------------------------------------------
+ * The pages count fully deterministic computation among LongCat-Flash's
+ * training techniques: runs reproduce bit for bit, which also exposes silent
+ * data corruption (『衝上熱搜！美團大模型，靠「快」火了』, section
+ * 模型擴展策略與多階段訓練, its fourth point).  This is the layer's backward
+ * with that property: no atomics, every reduction in a fixed order.
+ * Given the upstream gradient dy = dL/dy and the routing the forward saved in
+ * its moe_zc_aux (routing is piecewise constant and passes no gradient; the
+ * selection bias receives none; the gate is the probability itself):
+ *   slot (t,k) on FFN expert e, a = W_gate x_t, u = W_up x_t, s = sigmoid(a),
+ *   h = silu(a) u, o = W_down h, q = W_down^T dy_t:
+ *     gate gradient  <dy_t, o> = <q, h>
+ *     da = g q u s (1 + a (1 - s)),  du = g q silu(a)
+ *     dx_t += W_gate^T da + W_up^T du
+ *     dW_down[e] += (g dy_t) h^T,  dW_gate[e] += da x_t^T,  dW_up[e] += du x_t^T
+ *   slot (t,k) on a zero expert: gate gradient <dy_t, x_t>, dx_t += g dy_t
+ *   router: dl_t = p_t * (dp_t - <p_t, dp_t>), dp_t = gate gradients at the
+ *   chosen experts (0 elsewhere), p = softmax(l_t);
+ *     dx_t += W_router^T dl_t,  dW_router += dl_t x_t^T
+ *   The residual's gradient is dy itself and is not returned.
+ * Precision: a, u and q are recomputed on bf16 MFMA with fp32 accumulation;
+ * da, du and h are rounded to bf16 as operands of the following products
+ * (fp32 accumulation); the router's dx term is fp32; dl is rounded to bf16
+ * for dW_router; dx is accumulated in fp32 and rounded once to bf16.
+ * Requires dt = bf16 and T * d < 2^31 (else MOE_ZC_ERR_UNSUPPORTED); other
+ * limits as moe_zc_forward. */
+
+/* Transposed copies of the expert weights the backward reads (device, bf16):
+ *   w_gate, w_up [n, I, d], w_down [n, d, I] (16-byte aligned)
+ *   -> w_gate_up_t [n, d, 2I]: row j is (W_gate[:, j], W_up[:, j]);
+ *      w_down_t    [n, I, d]:  w_down_t[e][i][j] = w_down[e][j][i].
+ * Outputs are caller-owned and 16-byte aligned.  Enqueued on `stream`;
+ * n_experts = 0 does nothing.  Shape rules of moe_zc_pack_expert_weights. */
+moe_zc_status moe_zc_transpose_expert_weights(const void* w_gate,
+                                              const void* w_up,
+                                              const void* w_down,
+                                              int32_t n_experts, int64_t d,
+                                              int64_t I, void* w_gate_up_t,
+                                              void* w_down_t,
+                                              hipStream_t stream);
+
+/* Workspace bytes of moe_zc_backward (0 for invalid or unsupported sizes).
+ * Host only. */
+size_t moe_zc_backward_workspace_size(int64_t T, int64_t d, int64_t I,
+                                      int32_t N, int32_t Z, int32_t K);
+
+/* Gradients of the layer (definition above), dt = bf16.
+ *   x, w_router, w_gate, w_up   the forward's inputs (w_router fp32)
+ *   w_gate_up_t, w_down_t       from moe_zc_transpose_expert_weights
+ *   fwd       the forward's aux with logits, topk_idx, topk_gate, offsets,
+ *             perm and pos filled (same x, w_router, bias, sizes); read only
+ *   dy        [T, d] bf16 upstream gradient
+ *   dx        [T, d] bf16 output
+ *   dw_router [E, d] fp32 output
+ *   dw_gate, dw_up [N, I, d], dw_down [N, d, I] fp32 outputs (every expert
+ *             written; experts no token chose get zeros)
+ *   workspace device buffer of moe_zc_backward_workspace_size(...) bytes,
+ *             256-byte aligned; contents on entry are ignored.
+ * Outputs overwrite (do not accumulate into) their buffers and may not alias
+ * inputs.  N = 0: the expert arguments may be NULL.  T = 0 returns MOE_ZC_OK
+ * and enqueues nothing (the weight gradients are then not written). */
+moe_zc_status moe_zc_backward(const void* x, const float* w_router,
+                              const void* w_gate, const void* w_up,
+                              const void* w_gate_up_t, const void* w_down_t,
+                              const moe_zc_aux* fwd, const void* dy, void* dx,
+                              float* dw_router, float* dw_gate, float* dw_up,
+                              float* dw_down, int64_t T, int64_t d, int64_t I,
+                              int32_t N, int32_t Z, int32_t K, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
 /* Routing alone, from given fp32 logits [T, E] and bias [E]: the softmax,
  * bias key and top-K step of the forward, bit for bit.
  *   topk_idx [T, K] int32 and topk_gate [T, K] fp32 outputs (device).

@@ -9,6 +9,7 @@ from .api import (  # noqa: F401
     moe_zc_bias_update, moe_zc_forward, moe_zc_forward_packed, moe_zc_pack_expert_weights,
     moe_zc_packed_expert_bytes, moe_zc_route, moe_zc_status_string, moe_zc_workspace_size,
     moe_zc_forward_packed_fp8, moe_zc_pack_expert_weights_fp8, moe_zc_packed_fp8_expert_bytes,
-    moe_zc_quantize_mx, moe_zc_workspace_size_fp8,
+    moe_zc_quantize_mx, moe_zc_workspace_size_fp8, BWD_AUX_KEYS, moe_zc_backward,
+    moe_zc_backward_workspace_size, moe_zc_transpose_expert_weights,
 )
 from ._lib import LIB_PATH, STAGE_NAMES  # noqa: F401

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_zc.so")
 SOURCES = ["route.hip", "gemm_mfma.hip", "gemm_packed.hip", "gemm_fp8.hip", "gemm_simt.hip",
-           "api.cpp"]
+           "backward.hip", "api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops stay off: hipcc would otherwise form them from
@@ -48,7 +48,7 @@ def build(verbose: bool = False) -> str:
     """Compile every source and link libmoe_zc.so; returns the library path."""
     hipcc = _hipcc()
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(7, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(hipcc, s), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]

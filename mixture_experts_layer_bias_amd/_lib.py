@@ -24,7 +24,9 @@ EXPORTS = ("moe_zc_workspace_size", "moe_zc_forward", "moe_zc_packed_expert_byte
            "moe_zc_pack_expert_weights", "moe_zc_forward_packed", "moe_zc_route",
            "moe_zc_bias_update", "moe_zc_status_string", "moe_zc_abi_version",
            "moe_zc_packed_fp8_expert_bytes", "moe_zc_pack_expert_weights_fp8",
-           "moe_zc_workspace_size_fp8", "moe_zc_forward_packed_fp8", "moe_zc_quantize_mx")
+           "moe_zc_workspace_size_fp8", "moe_zc_forward_packed_fp8", "moe_zc_quantize_mx",
+           "moe_zc_transpose_expert_weights", "moe_zc_backward_workspace_size",
+           "moe_zc_backward")
 
 
 class MoeZcAux(ctypes.Structure):
@@ -79,6 +81,13 @@ def load() -> ctypes.CDLL:
     lib.moe_zc_forward_packed_fp8.restype = ctypes.c_int
     lib.moe_zc_quantize_mx.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.moe_zc_quantize_mx.restype = ctypes.c_int
+    lib.moe_zc_transpose_expert_weights.argtypes = [vp, vp, vp, i32, i64, i64, vp, vp, vp]
+    lib.moe_zc_transpose_expert_weights.restype = ctypes.c_int
+    lib.moe_zc_backward_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
+    lib.moe_zc_backward_workspace_size.restype = sz
+    lib.moe_zc_backward.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(MoeZcAux), vp, vp, vp,
+                                    vp, vp, vp, i64, i64, i64, i32, i32, i32, vp, sz, vp]
+    lib.moe_zc_backward.restype = ctypes.c_int
     lib.moe_zc_route.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
     lib.moe_zc_route.restype = ctypes.c_int
     lib.moe_zc_bias_update.argtypes = [vp, vp, vp, ctypes.POINTER(MoeZcPid), i32, vp]

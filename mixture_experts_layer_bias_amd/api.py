@@ -402,3 +402,99 @@ def moe_zc_quantize_mx(x: torch.Tensor, codes: Optional[torch.Tensor] = None,
     if code != _lib.MOE_ZC_OK:
         raise MoeZcError(code, "moe_zc_quantize_mx")
     return codes, scales
+
+
+# ---- backward ------------------------------------------------------------------
+BWD_AUX_KEYS = ("logits", "topk_idx", "topk_gate", "offsets", "perm", "pos")
+
+
+def moe_zc_backward_workspace_size(T: int, d: int, I: int, N: int, Z: int, K: int) -> int:
+    return int(_lib.load().moe_zc_backward_workspace_size(T, d, I, N, Z, K))
+
+
+def moe_zc_transpose_expert_weights(w_gate: torch.Tensor, w_up: torch.Tensor,
+                                    w_down: torch.Tensor,
+                                    w_gate_up_t: Optional[torch.Tensor] = None,
+                                    w_down_t: Optional[torch.Tensor] = None):
+    """Transposed bf16 expert weights for moe_zc_backward: returns
+    (w_gate_up_t [n, d, 2I], w_down_t [n, I, d])."""
+    lib = _lib.load()
+    n, I, d = w_gate.shape
+    dev = w_gate.device
+    if dev.type != "cuda":
+        raise ValueError("weights must be GPU tensors")
+    _need(w_gate, "w_gate", torch.bfloat16, (n, I, d), dev)
+    _need(w_up, "w_up", torch.bfloat16, (n, I, d), dev)
+    _need(w_down, "w_down", torch.bfloat16, (n, d, I), dev)
+    if w_gate_up_t is None:
+        w_gate_up_t = torch.empty(n, d, 2 * I, dtype=torch.bfloat16, device=dev)
+    if w_down_t is None:
+        w_down_t = torch.empty(n, I, d, dtype=torch.bfloat16, device=dev)
+    _need(w_gate_up_t, "w_gate_up_t", torch.bfloat16, (n, d, 2 * I), dev)
+    _need(w_down_t, "w_down_t", torch.bfloat16, (n, I, d), dev)
+    code = lib.moe_zc_transpose_expert_weights(_ptr(w_gate), _ptr(w_up), _ptr(w_down), n, d, I,
+                                               _ptr(w_gate_up_t), _ptr(w_down_t), _stream(dev))
+    if code != _lib.MOE_ZC_OK:
+        raise MoeZcError(code, "moe_zc_transpose_expert_weights")
+    return w_gate_up_t, w_down_t
+
+
+def moe_zc_backward(x: torch.Tensor, w_router: torch.Tensor, w_gate: Optional[torch.Tensor],
+                    w_up: Optional[torch.Tensor], transposed, aux: Dict[str, torch.Tensor],
+                    dy: torch.Tensor, N: int, Z: int, K: int, I: int,
+                    out: Optional[Dict[str, torch.Tensor]] = None,
+                    workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Gradients of the layer for upstream gradient dy, replaying the routing
+    the forward saved in ``aux`` (keys BWD_AUX_KEYS); ``transposed`` is the
+    pair from moe_zc_transpose_expert_weights (or None when N = 0).  Returns
+    dx (bf16) and dw_router, dw_gate, dw_up, dw_down (fp32)."""
+    lib = _lib.load()
+    _check_x(x)
+    T, d = x.shape
+    dev = x.device
+    E = N + Z
+    if x.dtype != torch.bfloat16:
+        raise ValueError("the backward takes bf16 x")
+    _need(w_router, "w_router", torch.float32, (E, d), dev)
+    _need(dy, "dy", torch.bfloat16, (T, d), dev)
+    spec = _aux_spec(T, N, Z, K)
+    for k in BWD_AUX_KEYS:
+        if k not in aux:
+            raise ValueError(f"aux lacks {k!r}")
+        _need(aux[k], f"aux[{k!r}]", spec[k][1], spec[k][0], dev)
+    shapes = {"dx": ((T, d), torch.bfloat16), "dw_router": ((E, d), torch.float32),
+              "dw_gate": ((N, I, d), torch.float32), "dw_up": ((N, I, d), torch.float32),
+              "dw_down": ((N, d, I), torch.float32)}
+    out = dict(out or {})
+    for k, (shp, dt) in shapes.items():
+        if k not in out:
+            out[k] = torch.empty(*shp, dtype=dt, device=dev)
+        _need(out[k], k, dt, shp, dev)
+    if N > 0:
+        _need(w_gate, "w_gate", torch.bfloat16, (N, I, d), dev)
+        _need(w_up, "w_up", torch.bfloat16, (N, I, d), dev)
+        gut, dnt = transposed
+        _need(gut, "w_gate_up_t", torch.bfloat16, (N, d, 2 * I), dev)
+        _need(dnt, "w_down_t", torch.bfloat16, (N, I, d), dev)
+        weights = (w_gate, w_up, gut, dnt)
+    else:
+        weights = (None, None, None, None)
+    need = moe_zc_backward_workspace_size(T, d, I, N, Z, K)
+    a = _lib.MoeZcAux()
+    for k in BWD_AUX_KEYS:
+        setattr(a, k, aux[k].data_ptr())
+    if need == 0:
+        code = lib.moe_zc_backward(None, None, None, None, None, None, ctypes.byref(a), None, None,
+                                   None, None, None, None, T, d, I, N, Z, K, None, 0, None)
+        raise MoeZcError(code, "moe_zc_backward")
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on x's device")
+    code = lib.moe_zc_backward(_ptr(x), _ptr(w_router), *[_ptr(w) for w in weights],
+                               ctypes.byref(a), _ptr(dy), _ptr(out["dx"]), _ptr(out["dw_router"]),
+                               _ptr(out["dw_gate"]), _ptr(out["dw_up"]), _ptr(out["dw_down"]),
+                               T, d, I, N, Z, K, _ptr(workspace), workspace.numel(), _stream(dev))
+    if code != _lib.MOE_ZC_OK:
+        raise MoeZcError(code, "moe_zc_backward")
+    return out

@@ -266,6 +266,73 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
   return MOE_ZC_OK;
 }
 
+// ---- backward -------------------------------------------------------------------
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+struct BwdPlan {
+  int64_t Sp, T64, E16;  // padded grouped columns, padded tokens, padded experts
+  size_t tiles, kofs, kofs_r, colrow, row_gate, row_dg, A, U, Q, dau, H, dxg, XT, ET, DAT, DUT,
+      HT, dl, dlT, xT, wrT, dx_acc, dx_r, total;
+};
+
+BwdPlan make_bwd_plan(const Shape& s) {
+  BwdPlan p{};
+  p.Sp = round_up(s.smax + 64 * (int64_t)s.N, 64);
+  p.T64 = round_up(s.T, 64);
+  p.E16 = round_up(s.E, 16);
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t here = at;
+    at += align_up(bytes);
+    return here;
+  };
+  const size_t S = (size_t)std::max<int64_t>(s.smax, 1), I = (size_t)s.I, d = (size_t)s.d;
+  p.tiles = take((size_t)(s.N + 1) * 4);
+  p.kofs = take((size_t)(s.N + 1) * 4);
+  p.kofs_r = take(2 * 4);
+  p.colrow = take((size_t)p.Sp * 4);
+  p.row_gate = take(S * 4);
+  p.row_dg = take(S * 4);
+  p.A = take(S * I * 4);
+  p.U = take(S * I * 4);
+  p.Q = take(S * I * 4);
+  p.dau = take(S * 2 * I * 2);
+  p.H = take(S * I * 2);
+  p.dxg = take(S * d * 4);
+  p.XT = take(d * (size_t)p.Sp * 2);
+  p.ET = take(d * (size_t)p.Sp * 2);
+  p.DAT = take(I * (size_t)p.Sp * 2);
+  p.DUT = take(I * (size_t)p.Sp * 2);
+  p.HT = take(I * (size_t)p.Sp * 2);
+  p.dl = take((size_t)s.T * p.E16 * 4);
+  p.dlT = take((size_t)s.E * p.T64 * 2);
+  p.xT = take(d * (size_t)p.T64 * 2);
+  p.wrT = take(d * (size_t)p.E16 * 4);
+  p.dx_acc = take((size_t)s.T * d * 4);
+  p.dx_r = take((size_t)s.T * d * 4);
+  p.total = at;
+  return p;
+}
+
+// Conditions of the backward beyond the forward's: bf16, grouped rows of x and
+// dy gathered with 32-bit byte offsets, padded group columns below 2^31.
+moe_zc_status check_bwd_shape(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z, int32_t K,
+                              Shape* s) {
+  const moe_zc_status st = check_shape(T, d, I, N, Z, K, MOE_ZC_BF16, s);
+  if (st != MOE_ZC_OK) return st;
+  if (!s->gather) return MOE_ZC_ERR_UNSUPPORTED;
+  if (round_up(s->smax + 64 * (int64_t)N, 64) >= (int64_t(1) << 31)) return MOE_ZC_ERR_UNSUPPORTED;
+  return MOE_ZC_OK;
+}
+
+TrArgsHost tr(const void* src, int64_t src_ld, void* dst, int64_t dst_ld, int dim, int64_t ncols,
+              int64_t ncols_valid, bool src_f32 = false, bool dst_f32 = false) {
+  TrArgsHost a{};
+  a.src = src; a.src_ld = src_ld; a.dst = dst; a.dst_ld = dst_ld; a.dim = dim; a.ncols = ncols;
+  a.ncols_valid = ncols_valid; a.batch = 1; a.src_f32 = src_f32; a.dst_f32 = dst_f32;
+  return a;
+}
+
 // Shape checks of the packing entry points (bf16 only; the forward's limits).
 moe_zc_status check_pack_shape(int64_t d, int64_t I, moe_zc_dtype dt) {
   if (dt != MOE_ZC_F32 && dt != MOE_ZC_BF16) return MOE_ZC_ERR_INVALID;
@@ -403,6 +470,153 @@ moe_zc_status moe_zc_pack_expert_weights(const void* w_gate, const void* w_up,
   MOE_ZC_TRY(launch_pack_weights(static_cast<const bf16_t*>(w_down), nullptr,
                                  static_cast<bf16_t*>(down_packed), n_experts, (int)d, (int)I,
                                  false, stream));
+  return MOE_ZC_OK;
+}
+
+size_t moe_zc_backward_workspace_size(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z,
+                                      int32_t K) {
+  Shape s;
+  if (check_bwd_shape(T, d, I, N, Z, K, &s) != MOE_ZC_OK) return 0;
+  return make_bwd_plan(s).total;
+}
+
+moe_zc_status moe_zc_transpose_expert_weights(const void* w_gate, const void* w_up,
+                                              const void* w_down, int32_t n_experts, int64_t d,
+                                              int64_t I, void* w_gate_up_t, void* w_down_t,
+                                              hipStream_t stream) {
+  const moe_zc_status st = check_pack_shape(d, I, MOE_ZC_BF16);
+  if (st != MOE_ZC_OK) return st;
+  if (n_experts < 0) return MOE_ZC_ERR_INVALID;
+  if (n_experts == 0) return MOE_ZC_OK;
+  if (!w_gate || !w_up || !w_down || !w_gate_up_t || !w_down_t) return MOE_ZC_ERR_INVALID;
+  // w_gate_up_t[e][j][i] = w_gate[e][i][j] (i < I), w_up[e][i - I][j] (i >= I)
+  for (int half = 0; half < 2; ++half) {
+    TrArgsHost a = tr(half ? w_up : w_gate, d, w_gate_up_t, 2 * I, (int)d, I, I);
+    a.src_bstride = I * d;
+    a.dst_bstride = d * 2 * I;
+    a.dst_col0 = half * I;
+    a.batch = n_experts;
+    MOE_ZC_TRY(launch_transpose(a, stream));
+  }
+  // w_down_t[e][i][j] = w_down[e][j][i]
+  TrArgsHost a = tr(w_down, I, w_down_t, d, (int)I, d, d);
+  a.src_bstride = d * I;
+  a.dst_bstride = I * d;
+  a.batch = n_experts;
+  MOE_ZC_TRY(launch_transpose(a, stream));
+  return MOE_ZC_OK;
+}
+
+moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* w_gate,
+                              const void* w_up, const void* w_gate_up_t, const void* w_down_t,
+                              const moe_zc_aux* fwd, const void* dy, void* dx, float* dw_router,
+                              float* dw_gate, float* dw_up, float* dw_down, int64_t T, int64_t d,
+                              int64_t I, int32_t N, int32_t Z, int32_t K, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  const moe_zc_status st = check_bwd_shape(T, d, I, N, Z, K, &s);
+  if (st != MOE_ZC_OK) return st;
+  if (T == 0) return MOE_ZC_OK;
+  if (!x || !w_router || !dy || !dx || !dw_router || !fwd) return MOE_ZC_ERR_INVALID;
+  if (!fwd->logits || !fwd->topk_idx || !fwd->topk_gate || !fwd->pos || !fwd->perm ||
+      !fwd->offsets)
+    return MOE_ZC_ERR_INVALID;
+  if (N > 0 && (!w_gate || !w_up || !w_gate_up_t || !w_down_t || !dw_gate || !dw_up || !dw_down))
+    return MOE_ZC_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(w_router) ||
+      (N > 0 && (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_gate_up_t) ||
+                 !aligned16(w_down_t))))
+    return MOE_ZC_ERR_INVALID;
+  const BwdPlan pl = make_bwd_plan(s);
+  if (!workspace || workspace_bytes < pl.total) return MOE_ZC_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ZC_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  auto F = [&](size_t o) { return reinterpret_cast<float*>(ws + o); };
+  auto B = [&](size_t o) { return reinterpret_cast<bf16_t*>(ws + o); };
+  auto Ix = [&](size_t o) { return reinterpret_cast<int32_t*>(ws + o); };
+  const int E = s.E;
+  const int32_t* offsets = fwd->offsets;
+  const int32_t* perm = fwd->perm;
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  const bf16_t* dyb = static_cast<const bf16_t*>(dy);
+  float* dxg = F(pl.dxg);
+  float* row_dg = F(pl.row_dg);
+
+  if (N > 0) {
+    int32_t* tiles = Ix(pl.tiles);
+    int32_t* kofs = Ix(pl.kofs);
+    int32_t* colrow = Ix(pl.colrow);
+    float* row_gate = F(pl.row_gate);
+    MOE_ZC_TRY(launch_bwd_prefix(offsets, N, s.ffn_tile_rows, tiles, kofs, stream));
+    MOE_ZC_TRY(launch_bwd_colrow(offsets, kofs, N, colrow, (int)pl.Sp, stream));
+    MOE_ZC_TRY(launch_bwd_rowgate(fwd->pos, fwd->topk_gate, T * K, row_gate, stream));
+    // a = W_gate x and u = W_up x of every grouped row (fp32), q = W_down^T dy
+    GemmProblem p{};
+    p.A = x; p.lda = d; p.a_kwrap = (int)d; p.K = (int)d; p.a_rows = perm;
+    p.ldb = d; p.b_group_stride = I * d;
+    p.ldc = I; p.Nout = (int)I;
+    p.row_offsets = offsets; p.tile_prefix = tiles; p.G = N; p.M = 0;
+    p.B0 = w_gate; p.C = F(pl.A);
+    MOE_ZC_TRY(launch_mfma_gemm(p, kStoreF32, s.ffn_tile_rows, s.smax, stream));
+    p.B0 = w_up; p.C = F(pl.U);
+    MOE_ZC_TRY(launch_mfma_gemm(p, kStoreF32, s.ffn_tile_rows, s.smax, stream));
+    p.A = dy; p.B0 = w_down_t; p.C = F(pl.Q);
+    MOE_ZC_TRY(launch_mfma_gemm(p, kStoreF32, s.ffn_tile_rows, s.smax, stream));
+    // SwiGLU backward: da | du, h, and the gate gradient of every grouped row
+    MOE_ZC_TRY(launch_swiglu_bwd(F(pl.A), F(pl.U), F(pl.Q), row_gate, offsets, N, (int)I, s.smax,
+                                 B(pl.dau), B(pl.H), row_dg, stream));
+    // rows of dx from the experts: [da | du] [W_gate ; W_up]
+    GemmProblem q{};
+    q.A = B(pl.dau); q.lda = 2 * I; q.a_kwrap = (int)(2 * I); q.K = (int)(2 * I);
+    q.B0 = w_gate_up_t; q.ldb = 2 * I; q.b_group_stride = d * 2 * I;
+    q.C = dxg; q.ldc = d; q.Nout = (int)d;
+    q.row_offsets = offsets; q.tile_prefix = tiles; q.G = N; q.M = 0;
+    MOE_ZC_TRY(launch_mfma_gemm(q, kStoreF32, s.ffn_tile_rows, s.smax, stream));
+    // weight gradients: operands transposed into [dim][padded grouped rows]
+    TrArgsHost a = tr(x, d, B(pl.XT), pl.Sp, (int)d, pl.Sp, 0);
+    a.colrow = colrow; a.rowidx = perm;
+    MOE_ZC_TRY(launch_transpose(a, stream));
+    a = tr(dy, d, B(pl.ET), pl.Sp, (int)d, pl.Sp, 0);
+    a.colrow = colrow; a.rowidx = perm; a.rowscale = row_gate;
+    MOE_ZC_TRY(launch_transpose(a, stream));
+    a = tr(B(pl.dau), 2 * I, B(pl.DAT), pl.Sp, (int)I, pl.Sp, 0);
+    a.colrow = colrow;
+    MOE_ZC_TRY(launch_transpose(a, stream));
+    a.dst = B(pl.DUT); a.src_col0 = I;
+    MOE_ZC_TRY(launch_transpose(a, stream));
+    a = tr(B(pl.H), I, B(pl.HT), pl.Sp, (int)I, pl.Sp, 0);
+    a.colrow = colrow;
+    MOE_ZC_TRY(launch_transpose(a, stream));
+    MOE_ZC_TRY(launch_wgrad(B(pl.ET), pl.Sp, B(pl.HT), pl.Sp, kofs, N, (int)d, (int)I, dw_down,
+                            stream));
+    MOE_ZC_TRY(launch_wgrad(B(pl.DAT), pl.Sp, B(pl.XT), pl.Sp, kofs, N, (int)I, (int)d, dw_gate,
+                            stream));
+    MOE_ZC_TRY(launch_wgrad(B(pl.DUT), pl.Sp, B(pl.XT), pl.Sp, kofs, N, (int)I, (int)d, dw_up,
+                            stream));
+  }
+  // per token: gate gradients, router softmax backward, dx from expert rows and
+  // identity slots
+  float* dl = F(pl.dl);
+  MOE_ZC_TRY(launch_token_bwd(xb, dyb, fwd->logits, fwd->topk_idx, fwd->topk_gate, fwd->pos,
+                              row_dg, dxg, T, (int)d, E, K, N, dl, (int)pl.E16, F(pl.dx_acc),
+                              stream));
+  // router: dx += dl W_r (fp32), dW_r = dl^T x
+  TrArgsHost a = tr(w_router, d, F(pl.wrT), pl.E16, (int)d, pl.E16, E, true, true);
+  MOE_ZC_TRY(launch_transpose(a, stream));
+  GemmProblem r{};
+  r.A = dl; r.lda = pl.E16; r.a_kwrap = (int)pl.E16; r.K = (int)pl.E16;
+  r.B0 = F(pl.wrT); r.ldb = pl.E16;
+  r.C = F(pl.dx_r); r.ldc = d; r.Nout = (int)d; r.G = 1; r.M = (int)T;
+  MOE_ZC_TRY(launch_simt_gemm(r, kStoreF32, T, stream));
+  MOE_ZC_TRY(launch_dx_final(F(pl.dx_acc), F(pl.dx_r), static_cast<bf16_t*>(dx), T * d, stream));
+  a = tr(dl, pl.E16, B(pl.dlT), pl.T64, E, pl.T64, T, true, false);
+  MOE_ZC_TRY(launch_transpose(a, stream));
+  a = tr(x, d, B(pl.xT), pl.T64, (int)d, pl.T64, T);
+  MOE_ZC_TRY(launch_transpose(a, stream));
+  int32_t* kofs_r = Ix(pl.kofs_r);
+  MOE_ZC_TRY(launch_set_range(kofs_r, 0, (int)pl.T64, stream));
+  MOE_ZC_TRY(launch_wgrad(B(pl.dlT), pl.T64, B(pl.xT), pl.T64, kofs_r, 1, E, (int)d, dw_router,
+                          stream));
   return MOE_ZC_OK;
 }
 

@@ -1,0 +1,478 @@
+// Backward of the MoE layer with zero-computation experts (bf16 data, fp32
+// arithmetic, fixed reduction orders: two runs give identical bits).
+//
+// With routing fixed by the forward (top-K and gates), upstream gradient dy
+// and, for a slot (t, k) on FFN expert e, a = W_gate x, u = W_up x,
+// s = sigmoid(a), h = a s u, g the gate:
+//   q    = W_down^T dy_t            (so dh = g q and the gate's gradient is <q, h>)
+//   da   = g q u s (1 + a (1 - s)),  du = g q a s
+//   dx_t += W_gate^T da + W_up^T du
+//   dW_down += (g dy_t) h^T,  dW_gate += da x_t^T,  dW_up += du x_t^T
+// for a slot on an identity expert: gate gradient <dy_t, x_t>, dx_t += g dy_t;
+// router: dl_t = p_t * (dp_t - <p_t, dp_t>) with dp_t the gate gradients at the
+// chosen experts, dx_t += W_r^T dl_t, dW_r += dl_t x_t^T.
+//
+// Kernels here: bookkeeping (tile prefix, 64-padded group columns, column ->
+// row map, slot of each grouped row), a tiled transpose that gathers, scales
+// and zero-pads rows into [dim][padded rows] operands, the per-row SwiGLU
+// backward, the per-token combine / identity / router-softmax backward, and
+// the weight-gradient GEMM: groups (experts) with their own reduction range
+// over the padded rows, both operands K-contiguous, fp32 output.  The
+// products with the expert weights (recomputing a and u, q, the rows of dx)
+// run on the bf16 MFMA grouped GEMM; the two router products on the fp32
+// grouped GEMM.
+#include "gemm_tile.hpp"
+
+namespace moezc {
+
+namespace {
+
+// ---- bookkeeping --------------------------------------------------------------
+// tile_prefix[g] = sum over f < g of ceil(rows_f / bm); kofs[g] = sum over f < g
+// of rows_f rounded up to 64 (each group's reduction range in the padded
+// operands).  One thread: N is at most a few thousand.
+__global__ void bwd_prefix_kernel(const int32_t* __restrict__ offsets, int N, int bm,
+                                  int32_t* __restrict__ tile_prefix, int32_t* __restrict__ kofs) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int t = 0, k = 0;
+  for (int e = 0; e < N; ++e) {
+    tile_prefix[e] = t;
+    kofs[e] = k;
+    const int rows = offsets[e + 1] - offsets[e];
+    t += (rows + bm - 1) / bm;
+    k += (rows + 63) / 64 * 64;
+  }
+  tile_prefix[N] = t;
+  kofs[N] = k;
+}
+
+// colrow[c] = grouped row s held by padded column c, or -1 for padding and
+// for c >= kofs[N]
+__global__ __launch_bounds__(256) void bwd_colrow_kernel(const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ kofs, int N,
+                                                         int32_t* __restrict__ colrow, int ncols) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= ncols) return;
+  int r = -1;
+  if (N > 0 && c < kofs[N]) {
+    int lo = 0, hi = N;  // kofs[lo] <= c < kofs[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (kofs[mid] <= c) lo = mid; else hi = mid;
+    }
+    const int s = offsets[lo] + (c - kofs[lo]);
+    r = s < offsets[lo + 1] ? s : -1;
+  }
+  colrow[c] = r;
+}
+
+// the gate of each grouped row (slot (t, k) with pos[t, k] = s)
+__global__ __launch_bounds__(256) void bwd_rowgate_kernel(const int32_t* __restrict__ pos,
+                                                          const float* __restrict__ gate,
+                                                          int64_t slots,
+                                                          float* __restrict__ row_gate) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= slots) return;
+  const int s = pos[i];
+  if (s >= 0) row_gate[s] = gate[i];
+}
+
+// ---- transpose ----------------------------------------------------------------
+// dst[j][dst_col0 + c] = scale(s) * src[row(s)][src_col0 + j] for the 64 x 64
+// tile of (c, j); s = colrow ? colrow[c] : (c < ncols_valid ? c : -1), row(s) =
+// rowidx ? rowidx[s] : s, scale = rowscale ? rowscale[s] : 1; columns with s < 0
+// get zeros.  Batched over blockIdx.z with the given strides.
+struct TrArgs {
+  const void* src;
+  int64_t src_ld, src_col0, src_bstride;
+  const int32_t* rowidx;
+  const float* rowscale;
+  const int32_t* colrow;
+  int64_t ncols_valid;
+  void* dst;
+  int64_t dst_ld, dst_col0, dst_bstride;
+  int dim;        // destination rows (source columns)
+  int64_t ncols;  // destination columns (multiple of 64)
+};
+
+__device__ __forceinline__ float ld_elem(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+__device__ __forceinline__ float ld_elem(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ void st_elem(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+__device__ __forceinline__ void st_elem(float* p, int64_t i, float v) { p[i] = v; }
+
+template <typename SRC, typename DST>
+__global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
+  __shared__ float tile[64][65];
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  const int j0 = blockIdx.y * 64;
+  const SRC* src = static_cast<const SRC*>(a.src) + (int64_t)blockIdx.z * a.src_bstride;
+  DST* dst = static_cast<DST*>(a.dst) + (int64_t)blockIdx.z * a.dst_bstride;
+  const int tid = threadIdx.x;
+  {
+    const int cl = tid >> 2, jc = (tid & 3) * 16;  // column c0 + cl, 16 source columns
+    const int64_t c = c0 + cl;
+    int64_t s = -1;
+    if (c < a.ncols) s = a.colrow ? (int64_t)a.colrow[c] : (c < a.ncols_valid ? c : -1);
+    float sc = 0.f;
+    int64_t row = 0;
+    if (s >= 0) {
+      sc = a.rowscale ? a.rowscale[s] : 1.f;
+      row = a.rowidx ? (int64_t)a.rowidx[s] : s;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int j = j0 + jc + q;
+      float v = 0.f;
+      if (s >= 0 && j < a.dim) v = sc * ld_elem(src, row * a.src_ld + a.src_col0 + j);
+      tile[jc + q][cl] = v;
+    }
+  }
+  __syncthreads();
+  {
+    const int jl = tid >> 2, cc = (tid & 3) * 16;
+    const int j = j0 + jl;
+    if (j < a.dim) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t c = c0 + cc + q;
+        if (c < a.ncols) st_elem(dst, (int64_t)j * a.dst_ld + a.dst_col0 + c, tile[jl][cc + q]);
+      }
+    }
+  }
+}
+
+// ---- per-row SwiGLU backward --------------------------------------------------
+// Row s of expert rows: a, u, q [S][I] fp32 -> dau [S][2I] bf16 (da | du),
+// h [S][I] bf16, row_dg[s] = <q, h> (the gate gradient of the row's slot).
+// One workgroup of 256 threads per row; the dot product reduces in a fixed
+// tree.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ A,
+                                                         const float* __restrict__ U,
+                                                         const float* __restrict__ Q,
+                                                         const float* __restrict__ row_gate,
+                                                         const int32_t* __restrict__ offsets,
+                                                         int N, int I, bf16_t* __restrict__ dau,
+                                                         bf16_t* __restrict__ H,
+                                                         float* __restrict__ row_dg) {
+  __shared__ float red[256];
+  const int64_t s = blockIdx.x;
+  if (s >= offsets[N]) return;
+  const float g = row_gate[s];
+  float dot = 0.f;
+  for (int i = threadIdx.x; i < I; i += 256) {
+    const int64_t o = s * I + i;
+    const float a = A[o], u = U[o], q = Q[o];
+    const float sg = 1.0f / (1.0f + __expf(-a));
+    const float h = a * sg * u;
+    dot += q * h;
+    const float dh = g * q;
+    dau[s * 2 * I + i] = f32_to_bf16(dh * u * sg * (1.0f + a * (1.0f - sg)));
+    dau[s * 2 * I + I + i] = f32_to_bf16(dh * a * sg);
+    H[o] = f32_to_bf16(h);
+  }
+  red[threadIdx.x] = dot;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) row_dg[s] = red[0];
+}
+
+// ---- per-token backward ---------------------------------------------------------
+// Token t: gate gradients of its K slots (FFN: row_dg; identity: <dy_t, x_t>),
+// dl_t = p_t * (dp_t - <p_t, dp_t>) into dl [T][ldl] (p = softmax of the fp32
+// logits), and dx_acc_t = sum over FFN slots in slot order of dxg[pos] plus the
+// identity slots' g dy_t (fp32).  One workgroup of 256 threads per token.
+__global__ __launch_bounds__(256) void token_bwd_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ dy, const float* __restrict__ logits,
+    const int32_t* __restrict__ idx, const float* __restrict__ gate, const int32_t* __restrict__ pos,
+    const float* __restrict__ row_dg, const float* __restrict__ dxg, int d, int E, int K, int N,
+    float* __restrict__ dl, int ldl, float* __restrict__ dx_acc) {
+  __shared__ float red[256];
+  __shared__ float dg_s[64];
+  __shared__ float stat[2];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t* it = idx + t * K;
+  const float* gt = gate + t * K;
+  const int32_t* pt = pos + t * K;
+  // <dy_t, x_t> for the identity slots
+  float xy = 0.f;
+  for (int j = tid; j < d; j += 256) xy += bf16_to_f32(dy[t * d + j]) * bf16_to_f32(x[t * d + j]);
+  red[tid] = xy;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  const float xyt = red[0];
+  __syncthreads();
+  if (tid < K) dg_s[tid] = it[tid] < N ? row_dg[pt[tid]] : xyt;
+  // softmax statistics of the fp32 logits (max, then sum of exp), fixed trees
+  const float* lt = logits + t * E;
+  float mx = -INFINITY;
+  for (int i = tid; i < E; i += 256) mx = fmaxf(mx, lt[i]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  mx = red[0];
+  __syncthreads();
+  float se = 0.f;
+  for (int i = tid; i < E; i += 256) se += __expf(lt[i] - mx);
+  red[tid] = se;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const float inv = 1.0f / red[0];
+    float c = 0.f;  // <p, dp>: only the chosen experts have dp != 0
+    for (int k = 0; k < K; ++k) c += __expf(lt[it[k]] - mx) * inv * dg_s[k];
+    stat[0] = inv;
+    stat[1] = c;
+  }
+  __syncthreads();
+  const float inv = stat[0], c = stat[1];
+  for (int i = tid; i < ldl; i += 256) {  // padding columns E .. ldl - 1 get zeros
+    float v = 0.f;
+    if (i < E) {
+      float dp = 0.f;
+      for (int k = 0; k < K; ++k)
+        if (it[k] == i) dp = dg_s[k];
+      v = __expf(lt[i] - mx) * inv * (dp - c);
+    }
+    dl[t * ldl + i] = v;
+  }
+  // dx from the expert rows and the identity slots, slot order
+  for (int j = tid; j < d; j += 256) {
+    float acc = 0.f;
+    const float dyj = bf16_to_f32(dy[t * d + j]);
+    for (int k = 0; k < K; ++k) {
+      if (it[k] < N) acc += dxg[(int64_t)pt[k] * d + j];
+      else acc += gt[k] * dyj;
+    }
+    dx_acc[t * d + j] = acc;
+  }
+}
+
+// out[0] = a, out[1] = b (a one-group reduction range)
+__global__ void set_range_kernel(int32_t* out, int a, int b) {
+  if (threadIdx.x == 0) {
+    out[0] = a;
+    out[1] = b;
+  }
+}
+
+// dx = bf16(dx_acc + dx_router)
+__global__ __launch_bounds__(256) void dx_final_kernel(const float* __restrict__ a,
+                                                       const float* __restrict__ b,
+                                                       bf16_t* __restrict__ dx, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dx[i] = f32_to_bf16(a[i] + b[i]);
+}
+
+// ---- weight-gradient GEMM --------------------------------------------------------
+// C[g][m][n] = sum over k in [kofs[g], kofs[g+1]) of A[m][k] B[n][k]; A [M][lda],
+// B [N][ldb] bf16, C fp32 [G][M][N].  128 x 128 tiles, four wavefronts (2 x 2,
+// 64 x 64 each), stages of 64 k double-buffered in LDS by direct loads.
+constexpr int WG_BKS = 64, WG_ROWB = 128, WG_TILE = 128;
+constexpr int WG_SLOT = WG_TILE * WG_ROWB;  // 16 KB per operand and stage
+
+struct WgradProblem {
+  const bf16_t* A;
+  int64_t lda;
+  const bf16_t* B;
+  int64_t ldb;
+  const int32_t* kofs;
+  int G, M, N;
+  float* C;
+};
+
+__global__ __launch_bounds__(256) void wgrad_kernel(WgradProblem p, int mtiles, int ntiles) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * WG_SLOT];
+  const int tile = blockIdx.x;
+  const int per_g = mtiles * ntiles;
+  const int g = tile / per_g;
+  if (g >= p.G) return;
+  const int rem = tile - g * per_g;
+  const int m0 = (rem / ntiles) * WG_TILE, n0 = (rem % ntiles) * WG_TILE;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int k0 = p.kofs[g];
+  const int nk = (p.kofs[g + 1] - k0) / WG_BKS;
+  // direct loads: instruction t of wavefront w fills rows 8 (w + 4 t) .. + 7 of
+  // the tile (lane l: row + l / 8, position l % 8 holding chunk
+  // (l % 8) ^ ((row >> 1) & 7)); rows past M or N repeat the last one
+  const char* A_base = reinterpret_cast<const char*>(p.A + (int64_t)m0 * p.lda + k0);
+  const char* B_base = reinterpret_cast<const char*>(p.B + (int64_t)n0 * p.ldb + k0);
+  uint32_t a_src[4], b_src[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r = 8 * (wave + 4 * t) + (lane >> 3);
+    const int lc = (lane & 7) ^ ((r >> 1) & 7);
+    const int ra = min(r, p.M - 1 - m0), rb = min(r, p.N - 1 - n0);
+    a_src[t] = (uint32_t)((int64_t)ra * p.lda * 2) + (uint32_t)(lc * 16);
+    b_src[t] = (uint32_t)((int64_t)rb * p.ldb * 2) + (uint32_t)(lc * 16);
+  }
+  char* const dstA = smem + wave * 1024;
+  char* const dstB = smem + WG_SLOT + wave * 1024;
+  auto load_stage = [&](int kt, int slot) {
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(A_base + (int64_t)kt * WG_ROWB), 0, 0x7fffffff, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(B_base + (int64_t)kt * WG_ROWB), 0, 0x7fffffff, 0x00020000);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (lds_void_t*)(dstA + slot * 2 * WG_SLOT + t * 4096), 16, a_src[t], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (lds_void_t*)(dstB + slot * 2 * WG_SLOT + t * 4096), 16, b_src[t], 0, 0, 0);
+    }
+  };
+  const int swz = ((lane & 31) >> 1) & 7;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  if (nk > 0) load_stage(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int slot = kt & 1;
+    if (kt + 1 < nk) {
+      load_stage(kt + 1, slot ^ 1);
+      ring_barrier<8>();  // this stage's 8 loads are older than the next stage's 8
+    } else {
+      ring_barrier<0>();
+    }
+    const char* As = smem + slot * 2 * WG_SLOT;
+    const char* Bs = As + WG_SLOT;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ch = ((2 * ks + (lane >> 5)) ^ swz) * 16;
+      bf16x8_t fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + 32 * i + (lane & 31)) * WG_ROWB + ch);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * 64 + 32 * j + (lane & 31)) * WG_ROWB + ch);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    // every wavefront is done reading this slot before it is refilled (its LDS
+    // reads have landed; the next stage's loads may stay in flight)
+    ring_barrier<63>();
+  }
+  // D[i][j] of a 32 x 32 block: lane j + 32 ((i / 4) % 2), register 4 (i / 8) + i % 4
+  float* Cg = p.C + (int64_t)g * p.M * p.N;
+  const int lrow4 = 4 * (lane >> 5), lcol = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + 32 * j + lcol;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + lrow4 + (v & 3);
+        if (m < p.M) Cg[(int64_t)m * p.N + n] = acc[i][j][v];
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prefix(const int32_t* offsets, int N, int bm, int32_t* tile_prefix,
+                             int32_t* kofs, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_prefix_kernel, dim3(1), dim3(64), 0, s, offsets, N, bm, tile_prefix, kofs);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_colrow(const int32_t* offsets, const int32_t* kofs, int N, int32_t* colrow,
+                             int ncols, hipStream_t s) {
+  if (ncols <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_colrow_kernel, dim3((ncols + 255) / 256), dim3(256), 0, s, offsets, kofs,
+                     N, colrow, ncols);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_rowgate(const int32_t* pos, const float* gate, int64_t slots,
+                              float* row_gate, hipStream_t s) {
+  if (slots <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_rowgate_kernel, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, s,
+                     pos, gate, slots, row_gate);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const TrArgsHost& h, hipStream_t s) {
+  if (h.ncols <= 0 || h.dim <= 0 || h.batch <= 0) return hipSuccess;
+  TrArgs a{h.src, h.src_ld, h.src_col0, h.src_bstride, h.rowidx, h.rowscale, h.colrow,
+           h.ncols_valid, h.dst, h.dst_ld, h.dst_col0, h.dst_bstride, h.dim, h.ncols};
+  const dim3 grid((unsigned)((h.ncols + 63) / 64), (unsigned)((h.dim + 63) / 64), (unsigned)h.batch);
+  if (h.src_f32 && h.dst_f32)
+    hipLaunchKernelGGL((transpose_kernel<float, float>), grid, dim3(256), 0, s, a);
+  else if (h.src_f32)
+    hipLaunchKernelGGL((transpose_kernel<float, bf16_t>), grid, dim3(256), 0, s, a);
+  else if (h.dst_f32)
+    hipLaunchKernelGGL((transpose_kernel<bf16_t, float>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((transpose_kernel<bf16_t, bf16_t>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const float* A, const float* U, const float* Q, const float* row_gate,
+                             const int32_t* offsets, int N, int I, int64_t max_rows, bf16_t* dau,
+                             bf16_t* H, float* row_dg, hipStream_t s) {
+  if (max_rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)max_rows), dim3(256), 0, s, A, U, Q,
+                     row_gate, offsets, N, I, dau, H, row_dg);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_bwd(const bf16_t* x, const bf16_t* dy, const float* logits,
+                            const int32_t* idx, const float* gate, const int32_t* pos,
+                            const float* row_dg, const float* dxg, int64_t T, int d, int E, int K,
+                            int N, float* dl, int ldl, float* dx_acc, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (K > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(token_bwd_kernel, dim3((unsigned)T), dim3(256), 0, s, x, dy, logits, idx,
+                     gate, pos, row_dg, dxg, d, E, K, N, dl, ldl, dx_acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_range(int32_t* out, int a, int b, hipStream_t s) {
+  hipLaunchKernelGGL(set_range_kernel, dim3(1), dim3(64), 0, s, out, a, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_final(const float* a, const float* b, bf16_t* dx, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dx_final_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, b, dx, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb,
+                        const int32_t* kofs, int G, int M, int N, float* C, hipStream_t s) {
+  if (G <= 0 || M <= 0 || N <= 0) return hipSuccess;
+  if (lda % 8 != 0 || ldb % 8 != 0) return hipErrorInvalidValue;
+  const int mt = (M + WG_TILE - 1) / WG_TILE, nt = (N + WG_TILE - 1) / WG_TILE;
+  const int64_t tiles = (int64_t)G * mt * nt;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  WgradProblem p{A, lda, B, ldb, kofs, G, M, N, C};
+  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)tiles), dim3(256), 0, s, p, mt, nt);
+  return hipGetLastError();
+}
+
+}  // namespace moezc

@@ -111,6 +111,47 @@ hipError_t launch_pack_weights_fp8(const bf16_t* wg, const bf16_t* wu, uint8_t* 
 // bf16.  Tiles of at most kPackedMaxTileRows rows, as the bf16 packed path.
 hipError_t launch_fp8_gemm(const GemmProblem& p, int tile_rows, int64_t max_rows, hipStream_t s);
 
+// Backward (backward.hip).
+// tile_prefix (row tiles of bm) and kofs (rows rounded up to 64) of the groups.
+hipError_t launch_bwd_prefix(const int32_t* offsets, int N, int bm, int32_t* tile_prefix,
+                             int32_t* kofs, hipStream_t s);
+// colrow[c]: grouped row held by padded column c, or -1.
+hipError_t launch_bwd_colrow(const int32_t* offsets, const int32_t* kofs, int N, int32_t* colrow,
+                             int ncols, hipStream_t s);
+// row_gate[pos[i]] = gate[i] for the FFN slots.
+hipError_t launch_bwd_rowgate(const int32_t* pos, const float* gate, int64_t slots,
+                              float* row_gate, hipStream_t s);
+// Tiled transpose: dst[j][dst_col0 + c] = scale(s) src[row(s)][src_col0 + j],
+// s = colrow ? colrow[c] : (c < ncols_valid ? c : -1) (zeros where s < 0),
+// row(s) = rowidx ? rowidx[s] : s, scale = rowscale ? rowscale[s] : 1.
+struct TrArgsHost {
+  const void* src;
+  int64_t src_ld, src_col0, src_bstride;
+  const int32_t* rowidx;
+  const float* rowscale;
+  const int32_t* colrow;
+  int64_t ncols_valid;
+  void* dst;
+  int64_t dst_ld, dst_col0, dst_bstride;
+  int dim;
+  int64_t ncols;
+  int batch;
+  bool src_f32, dst_f32;
+};
+hipError_t launch_transpose(const TrArgsHost& a, hipStream_t s);
+hipError_t launch_swiglu_bwd(const float* A, const float* U, const float* Q, const float* row_gate,
+                             const int32_t* offsets, int N, int I, int64_t max_rows, bf16_t* dau,
+                             bf16_t* H, float* row_dg, hipStream_t s);
+hipError_t launch_token_bwd(const bf16_t* x, const bf16_t* dy, const float* logits,
+                            const int32_t* idx, const float* gate, const int32_t* pos,
+                            const float* row_dg, const float* dxg, int64_t T, int d, int E, int K,
+                            int N, float* dl, int ldl, float* dx_acc, hipStream_t s);
+hipError_t launch_set_range(int32_t* out, int a, int b, hipStream_t s);
+hipError_t launch_dx_final(const float* a, const float* b, bf16_t* dx, int64_t n, hipStream_t s);
+// C[g] = A[:, kofs[g]:kofs[g+1]] B[:, kofs[g]:kofs[g+1]]^T, fp32 [G][M][N].
+hipError_t launch_wgrad(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb,
+                        const int32_t* kofs, int G, int M, int N, float* C, hipStream_t s);
+
 // fp32 FMA path (gemm_simt.hip).
 hipError_t launch_simt_gemm(const GemmProblem& p, int epilogue, int64_t max_rows,
                             hipStream_t s);

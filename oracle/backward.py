@@ -58,7 +58,7 @@ def backward(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, K: int, dy
     rt = _layer.route(logits32, bias, K, N)
     idx, p = rt["idx"], rt["p64"]
     gate = rt["gate"].astype(np.float64)
-    I = np.asarray(w_gate).shape[1] if N > 0 else 0
+    I = w_gate.shape[1] if N > 0 else 0
     dx = np.zeros((T, d))
     dwg = np.zeros((N, I, d))
     dwu = np.zeros((N, I, d))

@@ -159,3 +159,41 @@ def test_product_path_never_imports_the_oracle():
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in txt and "from oracle" not in txt, f
                 assert "oracle/" not in txt, f
+
+
+def test_backward_sizes_and_validation(lib):
+    ws = lib.moe_zc_backward_workspace_size
+    assert ws(64, 128, 256, 8, 4, 3) > 0
+    assert ws(0, 128, 256, 8, 4, 3) > 0               # T = 0 is valid
+    assert ws(64, 128, 256, 0, 4, 3) > 0              # N = 0 allowed
+    assert ws(64, 100, 256, 8, 4, 3) == 0             # d not a multiple of 64
+    assert ws(64, 128, 256, 8, 4, 13) == 0            # K > E
+    assert ws(200000, 6144, 2048, 8, 4, 3) == 0       # T * d >= 2^31: rows not gatherable
+    # prefill: recomputed a, u, q and the rows of dx (fp32), transposed operands
+    rows = 16384 * 12
+    big = ws(16384, 6144, 2048, 512, 256, 12)
+    assert rows * (3 * 2048 * 4 + 6144 * 4) < big < 30 * 2**30
+    aux = _lib.MoeZcAux(*(1 << 20,) * 7, None)
+    bw = lib.moe_zc_backward
+    T, d, I, N, Z, K = 64, 128, 128, 8, 4, 3
+    nb = ws(T, d, I, N, Z, K)
+    args = lambda **o: [o.get("x", FAKE), FAKE, FAKE, FAKE, o.get("gut", FAKE), FAKE,
+                        o.get("aux", ctypes.byref(aux)), FAKE, o.get("dx", FAKE), FAKE,
+                        o.get("dwg", FAKE), FAKE, FAKE, o.get("T", T), d, I, o.get("N", N), Z, K,
+                        o.get("ws", FAKE), o.get("nb", nb), None]
+    assert bw(*args(T=0)) == OK
+    assert bw(*args(x=None)) == INVALID
+    assert bw(*args(dx=None)) == INVALID
+    assert bw(*args(gut=None)) == INVALID
+    assert bw(*args(dwg=None)) == INVALID
+    assert bw(*args(aux=None)) == INVALID
+    assert bw(*args(ws=None)) == WORKSPACE
+    assert bw(*args(nb=100)) == WORKSPACE
+    assert bw(*args(x=ctypes.c_void_p((1 << 20) + 2))) == INVALID
+    no_perm = _lib.MoeZcAux(*(1 << 20,) * 5, None, 1 << 20, None)
+    assert bw(*args(aux=ctypes.byref(no_perm))) == INVALID
+    tr = lib.moe_zc_transpose_expert_weights
+    assert tr(FAKE, FAKE, FAKE, 0, 128, 128, FAKE, FAKE, None) == OK
+    assert tr(FAKE, FAKE, FAKE, -1, 128, 128, FAKE, FAKE, None) == INVALID
+    assert tr(FAKE, FAKE, FAKE, 2, 128, 100, FAKE, FAKE, None) == UNSUPPORTED
+    assert tr(FAKE, FAKE, FAKE, 2, 128, 128, None, FAKE, None) == INVALID

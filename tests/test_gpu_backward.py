@@ -1,0 +1,142 @@
+"""Backward of the layer (moe_zc_transpose_expert_weights, moe_zc_backward)
+against the fp64 oracle's gradients (oracle.backward).
+
+The forward on the GPU saves its routing (fp32 logits, top-K, gates, grouping);
+the oracle routes from those same fp32 logits, so both differentiate the same
+piecewise-smooth function.  Tolerance, per output tensor:
+max |G - G_ref| <= 1e-2 * max |G_ref|, the forward's bf16 bar.  The GPU rounds
+da, du, h, g dy and dl to bf16 as operands of fp32-accumulated products (a
+relative 2^-9 per operand), and dx once at the end, so errors sit near 1e-3
+of the maximum.  Determinism is exact: two calls give the same bits."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_bias_amd as m
+from oracle import backward as obwd
+from workloads import Workload, get_workload, make_inputs, make_upstream_grad
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = 1e-2
+GRADS = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down")
+
+
+def _edge(T=200, d=128, I=128, N=8, Z=4, K=3, seed=5, bias=("uniform", 0.05)):
+    return Workload("edge", T=T, d=d, I=I, N=N, Z=Z, K=K, dtype="bf16", seed=seed, bias=bias)
+
+
+def gpu_forward_backward(w, inp, dy, repeat=1):
+    aux = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV)
+    m.moe_zc_forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
+                     inp["w_down"], w.N, w.Z, w.K, aux=aux)
+    tr = None
+    if w.N > 0:
+        tr = m.moe_zc_transpose_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    outs = []
+    for _ in range(repeat):
+        outs.append(m.moe_zc_backward(inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], tr,
+                                      aux, dy, w.N, w.Z, w.K, w.I))
+    torch.cuda.synchronize()
+    return aux, outs
+
+
+def compare(w, inp, dy, aux, g, dx_tokens=None):
+    """Every gradient against the oracle's; dx optionally on a token sample
+    (the weight gradients need every token)."""
+    l32 = aux["logits"].cpu().numpy()
+    ref = obwd.backward(inp["x"].cpu(), inp["w_router"].cpu(), inp["bias"].cpu().numpy(),
+                        inp["w_gate"].cpu(), inp["w_up"].cpu(), inp["w_down"].cpu(),
+                        w.N, w.Z, w.K, dy.cpu(), logits32=l32)
+    assert np.array_equal(aux["topk_idx"].cpu().numpy(), ref["route"]["idx"]), "routing"
+    rep = {}
+    for k in GRADS:
+        got = g[k].float().cpu().double().numpy()
+        want = ref[k]
+        if k == "dx" and dx_tokens is not None:
+            got, want = got[dx_tokens], want[dx_tokens]
+        scale = np.abs(want).max() if want.size else 0.0
+        err = np.abs(got - want).max() if want.size else 0.0
+        rep[k] = float(err / scale) if scale > 0 else float(err)
+        assert err <= TOL * scale + 1e-30, f"{k}: max|err| {err:.3e} > {TOL} * {scale:.3e}"
+    # experts no token chose have exactly zero weight gradients
+    if w.N > 0:
+        loads = np.bincount(ref["route"]["idx"].ravel(), minlength=w.E)[: w.N]
+        for k in ("dw_gate", "dw_up", "dw_down"):
+            assert not g[k][torch.from_numpy(loads == 0).to(DEV)].any(), k
+    return rep
+
+
+CASES = {
+    "T1": dict(T=1),
+    "T65_ragged": dict(T=65),
+    "Z0": dict(N=8, Z=0, K=2),
+    "K_eq_E": dict(N=5, Z=3, K=8),
+    "N0_all_identity": dict(N=0, Z=6, K=3),
+    "N1_single_expert": dict(N=1, Z=3, K=2),
+    "few_rows_32_tiles": dict(T=64, N=64, Z=32, K=8),
+    "rows_128_tiles": dict(T=512, N=24, Z=8, K=6),
+    "rows_256_tiles": dict(T=1100, N=8, Z=4, K=3, d=256, I=256),
+    "wide_d": dict(T=130, d=1344, I=384, N=6, Z=2, K=2),
+    "many_experts": dict(T=300, d=128, I=128, N=300, Z=20, K=12),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_vs_oracle(name):
+    w = _edge(**CASES[name])
+    print(f"[backward {name}] {w.describe()}", flush=True)
+    inp = make_inputs(w, device=DEV)
+    dy = make_upstream_grad(w, DEV)
+    aux, (g,) = gpu_forward_backward(w, inp, dy)
+    print(name, compare(w, inp, dy, aux, g), flush=True)
+
+
+def test_backward_mid_vs_oracle():
+    w = get_workload("mid")
+    print(f"[backward mid] {w.describe()}", flush=True)
+    inp = make_inputs(w, device=DEV)
+    dy = make_upstream_grad(w, DEV)
+    aux, (g,) = gpu_forward_backward(w, inp, dy)
+    print("mid", compare(w, inp, dy, aux, g), flush=True)
+
+
+def test_backward_is_deterministic():
+    """Bitwise-equal gradients on repeated calls (no atomics, fixed orders)."""
+    w = _edge(T=1500, d=256, I=256, N=16, Z=8, K=6)
+    inp = make_inputs(w, device=DEV)
+    dy = make_upstream_grad(w, DEV)
+    _, outs = gpu_forward_backward(w, inp, dy, repeat=3)
+    for k in GRADS:
+        for o in outs[1:]:
+            assert torch.equal(outs[0][k].view(torch.int16 if k == "dx" else torch.int32),
+                               o[k].view(torch.int16 if k == "dx" else torch.int32)), k
+
+
+@pytest.mark.parametrize("n,d,I", [(3, 128, 256), (2, 320, 128)])
+def test_transpose_expert_weights(n, d, I):
+    g = torch.Generator().manual_seed(7 * n + d)
+    wg, wu = (torch.randn(n, I, d, generator=g).to(torch.bfloat16) for _ in range(2))
+    wd = torch.randn(n, d, I, generator=g).to(torch.bfloat16)
+    gut, dnt = m.moe_zc_transpose_expert_weights(wg.to(DEV), wu.to(DEV), wd.to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(gut.cpu(), torch.cat([wg, wu], dim=1).transpose(1, 2))
+    assert torch.equal(dnt.cpu(), wd.transpose(1, 2))
+
+
+def test_backward_empty_batch():
+    w = _edge(T=0)
+    inp = make_inputs(w, device=DEV)
+    dy = make_upstream_grad(w, DEV)
+    aux, (g,) = gpu_forward_backward(w, inp, dy)
+    assert g["dx"].shape == (0, w.d)
+
+
+def test_backward_rejects_f32():
+    w = Workload("f32", T=16, d=128, I=256, N=4, Z=2, K=2, dtype="f32", seed=0,
+                 bias=("zero",))
+    inp = make_inputs(w, device=DEV)
+    aux = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV)
+    with pytest.raises(ValueError):
+        m.moe_zc_backward(inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], None, aux,
+                          inp["x"], w.N, w.Z, w.K, w.I)

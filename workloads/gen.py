@@ -6,6 +6,8 @@ round-to-nearest-even by torch's ``.to``):
   W_router   N(0, 1/d)  (std d**-0.5)      [E, d]   fp32, generated on the CPU
   bias       per the workload recipe       [E]      fp32, generated on the CPU
   residual   N(0, 1)                       [T, d]   generated on the CPU
+  dy         N(0, 1)                       [T, d]   upstream gradient of the
+                                                    backward, on the CPU
   W_gate     N(0, 1/d)                     [N, I, d]
   W_up       N(0, 1/d)                     [N, I, d]
   W_down     N(0, 1/d)                     [N, d, I]
@@ -26,7 +28,7 @@ import torch
 
 from .configs import Workload
 
-_TAG_X, _TAG_WR, _TAG_BIAS, _TAG_RES, _TAG_ZIPF = 1, 2, 3, 4, 5
+_TAG_X, _TAG_WR, _TAG_BIAS, _TAG_RES, _TAG_ZIPF, _TAG_DY = 1, 2, 3, 4, 5, 6
 
 
 def _seed(w: Workload, tag: int, sub: int = 0) -> int:
@@ -111,3 +113,9 @@ def make_inputs(w: Workload, device="cpu", ffn_device: Optional[str] = None,
         wd[e].copy_(d_)
     out.update(w_gate=wg, w_up=wu, w_down=wd)
     return out
+
+
+def make_upstream_grad(w: Workload, device="cpu") -> torch.Tensor:
+    """dy = dL/dy [T, d] for the backward, N(0, 1) in the workload dtype."""
+    dy = torch.randn(w.T, w.d, generator=_gen(_seed(w, _TAG_DY), "cpu"))
+    return dy.to(torch_dtype(w)).to(device)
