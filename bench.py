@@ -11,6 +11,11 @@ times moe_zc_forward on the row-major weights instead.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload prefill]
 
+--pass backward times a training step of the layer instead: moe_zc_forward
+(row-major weights, routing saved) followed by moe_zc_backward (dx, the router
+gradient and the fp32 expert weight gradients), with the backward also timed
+alone.
+
 Prints one JSON line.  Per-stage times come from HIP events that the library
 records on the launch stream at its stage boundaries.
 """
@@ -43,6 +48,8 @@ def parse():
     ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8"],
                     help="fp8: gate/up projection in block FP8 (moe_zc_forward_packed_fp8); "
                          "the down projection stays bf16")
+    ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"],
+                    help="backward: time forward + moe_zc_backward (a training step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-experts", type=int, default=24,
                     help="experts the CPU-baseline sample evaluates")
@@ -162,6 +169,83 @@ def cpu_baseline(w, inp, n_experts, weights):
             "seconds_measured": round(t3 - t0, 2)}
 
 
+def bench_backward(args, w, dev):
+    """Training step = forward (routing saved) + backward; also the backward
+    alone.  FLOPs of the backward's expert products: a and u recomputed
+    (4 d I S), q (2 d I S), the rows of dx (4 d I S), dW_down, dW_gate,
+    dW_up (6 d I S); router: dx term and dW_router (4 T d E)."""
+    import torch
+
+    import mixture_experts_layer_bias_amd as m
+    from workloads import make_inputs, make_upstream_grad
+
+    if w.dtype != "bf16":
+        print("bench.py: the backward takes a bf16 workload", file=sys.stderr)
+        sys.exit(2)
+    inp = make_inputs(w, device=dev, residual=False)
+    dy = make_upstream_grad(w, dev)
+    tr = m.moe_zc_transpose_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    aux = m.alloc_aux(w.T, w.N, w.Z, w.K, dev)
+    y = torch.empty(w.T, w.d, dtype=torch.bfloat16, device=dev)
+    ws_f = torch.empty(m.moe_zc_workspace_size(w.T, w.d, w.I, w.N, w.Z, w.K, torch.bfloat16),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(m.moe_zc_backward_workspace_size(w.T, w.d, w.I, w.N, w.Z, w.K),
+                       dtype=torch.uint8, device=dev)
+    grads = {"dx": torch.empty(w.T, w.d, dtype=torch.bfloat16, device=dev),
+             "dw_router": torch.empty(w.E, w.d, dtype=torch.float32, device=dev),
+             "dw_gate": torch.empty(w.N, w.I, w.d, dtype=torch.float32, device=dev),
+             "dw_up": torch.empty(w.N, w.I, w.d, dtype=torch.float32, device=dev),
+             "dw_down": torch.empty(w.N, w.d, w.I, dtype=torch.float32, device=dev)}
+
+    def fwd():
+        m.moe_zc_forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
+                         inp["w_down"], w.N, w.Z, w.K, out=y, aux=aux, workspace=ws_f)
+
+    def bwd():
+        m.moe_zc_backward(inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], tr, aux, dy,
+                          w.N, w.Z, w.K, w.I, out=grads, workspace=ws_b)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    ms_step = timed(lambda: (fwd(), bwd()))
+    ms_bwd = timed(bwd)
+    S = int(aux["offsets"][w.N].item())
+    flop_bwd = 16.0 * w.d * w.I * S + 4.0 * w.T * w.d * w.E
+    flop_fwd = 6.0 * w.d * w.I * S + 2.0 * w.T * w.d * w.E
+    out = {
+        "metric": "MoE-layer training step (forward + backward) tokens/s on 1 MI355X",
+        "value": w.T / (ms_step / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 (fp32 accumulation, fp32 weight gradients)",
+        "data": "synthetic (seeded Gaussian inputs and upstream gradient, random-init weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "I": w.I, "N": w.N, "Z": w.Z,
+                   "K": w.K, "step": "moe_zc_forward + moe_zc_backward",
+                   "parallelism": "none (1 GPU)"},
+        "backward_ms": ms_bwd,
+        "backward_tflops": flop_bwd / (ms_bwd / 1e3) / 1e12,
+        "backward_mfma_frac": flop_bwd / (ms_bwd / 1e3) / PEAK_BF16,
+        "step_tflops": (flop_fwd + flop_bwd) / (ms_step / 1e3) / 1e12,
+        "ffn_rows": S,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -182,6 +266,9 @@ def main():
     w = get_workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.which == "backward":
+        bench_backward(args, w, dev)
+        return
     inp = make_inputs(w, device=dev)
     dt = inp["x"].dtype
     es = inp["x"].element_size()

@@ -315,13 +315,17 @@ BwdPlan make_bwd_plan(const Shape& s) {
 }
 
 // Conditions of the backward beyond the forward's: bf16, grouped rows of x and
-// dy gathered with 32-bit byte offsets, padded group columns below 2^31.
+// dy gathered with 32-bit byte offsets, padded group columns below 2^31,
+// expert blocks addressed with 32-bit byte offsets.
 moe_zc_status check_bwd_shape(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z, int32_t K,
                               Shape* s) {
   const moe_zc_status st = check_shape(T, d, I, N, Z, K, MOE_ZC_BF16, s);
   if (st != MOE_ZC_OK) return st;
   if (!s->gather) return MOE_ZC_ERR_UNSUPPORTED;
   if (round_up(s->smax + 64 * (int64_t)N, 64) >= (int64_t(1) << 31)) return MOE_ZC_ERR_UNSUPPORTED;
+  // the weight-gradient GEMM addresses 128 rows of an expert block (at most
+  // T rounded up to 64 columns each) with 32-bit byte offsets
+  if (128 * round_up(T, 64) * 2 >= (int64_t(1) << 31)) return MOE_ZC_ERR_UNSUPPORTED;
   return MOE_ZC_OK;
 }
 
@@ -572,27 +576,31 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
     q.C = dxg; q.ldc = d; q.Nout = (int)d;
     q.row_offsets = offsets; q.tile_prefix = tiles; q.G = N; q.M = 0;
     MOE_ZC_TRY(launch_mfma_gemm(q, kStoreF32, s.ffn_tile_rows, s.smax, stream));
-    // weight gradients: operands transposed into [dim][padded grouped rows]
-    TrArgsHost a = tr(x, d, B(pl.XT), pl.Sp, (int)d, pl.Sp, 0);
-    a.colrow = colrow; a.rowidx = perm;
+    // weight gradients: operands transposed into expert-blocked [dim][rows_e
+    // rounded up to 64] blocks (zeros in the padding columns)
+    auto blocked = [&](const void* src, int64_t src_ld, void* dst, int64_t dim) {
+      TrArgsHost a = tr(src, src_ld, dst, 0, (int)dim, pl.Sp, 0);
+      a.colrow = colrow;
+      a.kofs = kofs;
+      a.ngroups = N;
+      return a;
+    };
+    TrArgsHost a = blocked(x, d, B(pl.XT), d);
+    a.rowidx = perm;
     MOE_ZC_TRY(launch_transpose(a, stream));
-    a = tr(dy, d, B(pl.ET), pl.Sp, (int)d, pl.Sp, 0);
-    a.colrow = colrow; a.rowidx = perm; a.rowscale = row_gate;
+    a = blocked(dy, d, B(pl.ET), d);
+    a.rowidx = perm; a.rowscale = row_gate;
     MOE_ZC_TRY(launch_transpose(a, stream));
-    a = tr(B(pl.dau), 2 * I, B(pl.DAT), pl.Sp, (int)I, pl.Sp, 0);
-    a.colrow = colrow;
+    a = blocked(B(pl.dau), 2 * I, B(pl.DAT), I);
     MOE_ZC_TRY(launch_transpose(a, stream));
     a.dst = B(pl.DUT); a.src_col0 = I;
     MOE_ZC_TRY(launch_transpose(a, stream));
-    a = tr(B(pl.H), I, B(pl.HT), pl.Sp, (int)I, pl.Sp, 0);
-    a.colrow = colrow;
+    a = blocked(B(pl.H), I, B(pl.HT), I);
     MOE_ZC_TRY(launch_transpose(a, stream));
-    MOE_ZC_TRY(launch_wgrad(B(pl.ET), pl.Sp, B(pl.HT), pl.Sp, kofs, N, (int)d, (int)I, dw_down,
-                            stream));
-    MOE_ZC_TRY(launch_wgrad(B(pl.DAT), pl.Sp, B(pl.XT), pl.Sp, kofs, N, (int)I, (int)d, dw_gate,
-                            stream));
-    MOE_ZC_TRY(launch_wgrad(B(pl.DUT), pl.Sp, B(pl.XT), pl.Sp, kofs, N, (int)I, (int)d, dw_up,
-                            stream));
+    const int64_t most = round_up(T, 64);  // rows of one expert: at most T
+    MOE_ZC_TRY(launch_wgrad(B(pl.ET), B(pl.HT), kofs, N, (int)d, (int)I, most, dw_down, stream));
+    MOE_ZC_TRY(launch_wgrad(B(pl.DAT), B(pl.XT), kofs, N, (int)I, (int)d, most, dw_gate, stream));
+    MOE_ZC_TRY(launch_wgrad(B(pl.DUT), B(pl.XT), kofs, N, (int)I, (int)d, most, dw_up, stream));
   }
   // per token: gate gradients, router softmax backward, dx from expert rows and
   // identity slots
@@ -615,8 +623,7 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
   MOE_ZC_TRY(launch_transpose(a, stream));
   int32_t* kofs_r = Ix(pl.kofs_r);
   MOE_ZC_TRY(launch_set_range(kofs_r, 0, (int)pl.T64, stream));
-  MOE_ZC_TRY(launch_wgrad(B(pl.dlT), pl.T64, B(pl.xT), pl.T64, kofs_r, 1, E, (int)d, dw_router,
-                          stream));
+  MOE_ZC_TRY(launch_wgrad(B(pl.dlT), B(pl.xT), kofs_r, 1, E, (int)d, pl.T64, dw_router, stream));
   return MOE_ZC_OK;
 }
 

@@ -93,6 +93,12 @@ struct TrArgs {
   int64_t dst_ld, dst_col0, dst_bstride;
   int dim;        // destination rows (source columns)
   int64_t ncols;  // destination columns (multiple of 64)
+  // non-null: expert-blocked destination.  Group g owns columns
+  // [kofs[g], kofs[g+1]) (multiples of 64) and stores them as a contiguous
+  // [dim][kofs[g+1] - kofs[g]] block at element offset kofs[g] * dim; columns
+  // at or past kofs[ngroups] are not written.
+  const int32_t* kofs;
+  int ngroups;
 };
 
 __device__ __forceinline__ float ld_elem(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
@@ -100,6 +106,48 @@ __device__ __forceinline__ float ld_elem(const float* p, int64_t i) { return p[i
 __device__ __forceinline__ void st_elem(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 __device__ __forceinline__ void st_elem(float* p, int64_t i, float v) { p[i] = v; }
 
+// 16 consecutive elements through 16-byte accesses (the address is 16-byte
+// aligned: every row stride and column offset is a multiple of 8 elements)
+__device__ __forceinline__ void ld16(const bf16_t* p, float (&v)[16]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint4 u = reinterpret_cast<const uint4*>(p)[h];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[8 * h + 2 * q] = __uint_as_float(w[q] << 16);
+      v[8 * h + 2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+  }
+}
+__device__ __forceinline__ void ld16(const float* p, float (&v)[16]) {
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float4 f = reinterpret_cast<const float4*>(p)[h];
+    v[4 * h] = f.x; v[4 * h + 1] = f.y; v[4 * h + 2] = f.z; v[4 * h + 3] = f.w;
+  }
+}
+__device__ __forceinline__ void st16(bf16_t* p, const float (&v)[16]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (uint32_t)f32_to_bf16(v[8 * h + 2 * q]) |
+             ((uint32_t)f32_to_bf16(v[8 * h + 2 * q + 1]) << 16);
+    reinterpret_cast<uint4*>(p)[h] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+__device__ __forceinline__ void st16(float* p, const float (&v)[16]) {
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+    reinterpret_cast<float4*>(p)[h] = make_float4(v[4 * h], v[4 * h + 1], v[4 * h + 2], v[4 * h + 3]);
+}
+
+// 64 x 64 tiles: thread (row, 16-element chunk) reads a source row segment
+// and writes a destination row segment with 16-byte accesses; the LDS tile
+// (padded rows) turns one into the other.  Partial chunks at the edges
+// (dim or ncols not a multiple of 16) go element by element.
 template <typename SRC, typename DST>
 __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
   __shared__ float tile[64][65];
@@ -107,35 +155,60 @@ __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
   const int j0 = blockIdx.y * 64;
   const SRC* src = static_cast<const SRC*>(a.src) + (int64_t)blockIdx.z * a.src_bstride;
   DST* dst = static_cast<DST*>(a.dst) + (int64_t)blockIdx.z * a.dst_bstride;
+  int64_t dst_ld = a.dst_ld, cbase = c0;  // destination row stride, tile column in it
+  if (a.kofs) {
+    if (c0 >= a.kofs[a.ngroups]) return;
+    int lo = 0, hi = a.ngroups;  // kofs[lo] <= c0 < kofs[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.kofs[mid] <= c0) lo = mid; else hi = mid;
+    }
+    const int64_t k0 = a.kofs[lo];
+    dst_ld = a.kofs[lo + 1] - k0;
+    dst += k0 * a.dim;
+    cbase = c0 - k0;
+  }
   const int tid = threadIdx.x;
   {
     const int cl = tid >> 2, jc = (tid & 3) * 16;  // column c0 + cl, 16 source columns
     const int64_t c = c0 + cl;
     int64_t s = -1;
     if (c < a.ncols) s = a.colrow ? (int64_t)a.colrow[c] : (c < a.ncols_valid ? c : -1);
-    float sc = 0.f;
-    int64_t row = 0;
-    if (s >= 0) {
-      sc = a.rowscale ? a.rowscale[s] : 1.f;
-      row = a.rowidx ? (int64_t)a.rowidx[s] : s;
+    float v[16];
+    if (s < 0) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = 0.f;
+    } else {
+      const float sc = a.rowscale ? a.rowscale[s] : 1.f;
+      const int64_t row = a.rowidx ? (int64_t)a.rowidx[s] : s;
+      const SRC* p = src + row * a.src_ld + a.src_col0 + j0 + jc;
+      if (j0 + jc + 16 <= a.dim) {
+        ld16(p, v);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = (j0 + jc + q < a.dim) ? ld_elem(p, q) : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] *= sc;
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int j = j0 + jc + q;
-      float v = 0.f;
-      if (s >= 0 && j < a.dim) v = sc * ld_elem(src, row * a.src_ld + a.src_col0 + j);
-      tile[jc + q][cl] = v;
-    }
+    for (int q = 0; q < 16; ++q) tile[jc + q][cl] = v[q];
   }
   __syncthreads();
   {
     const int jl = tid >> 2, cc = (tid & 3) * 16;
     const int j = j0 + jl;
     if (j < a.dim) {
+      float v[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t c = c0 + cc + q;
-        if (c < a.ncols) st_elem(dst, (int64_t)j * a.dst_ld + a.dst_col0 + c, tile[jl][cc + q]);
+      for (int q = 0; q < 16; ++q) v[q] = tile[jl][cc + q];
+      DST* p = dst + (int64_t)j * dst_ld + a.dst_col0 + cbase + cc;
+      if (c0 + cc + 16 <= a.ncols) {
+        st16(p, v);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (c0 + cc + q < a.ncols) st_elem(p, q, v[q]);
       }
     }
   }
@@ -277,49 +350,69 @@ __global__ __launch_bounds__(256) void dx_final_kernel(const float* __restrict__
 }
 
 // ---- weight-gradient GEMM --------------------------------------------------------
-// C[g][m][n] = sum over k in [kofs[g], kofs[g+1]) of A[m][k] B[n][k]; A [M][lda],
-// B [N][ldb] bf16, C fp32 [G][M][N].  128 x 128 tiles, four wavefronts (2 x 2,
-// 64 x 64 each), stages of 64 k double-buffered in LDS by direct loads.
-constexpr int WG_BKS = 64, WG_ROWB = 128, WG_TILE = 128;
-constexpr int WG_SLOT = WG_TILE * WG_ROWB;  // 16 KB per operand and stage
+// C[g][m][n] = sum over k < R_g of A_g[m][k] B_g[n][k], R_g = kofs[g+1] - kofs[g]
+// (a multiple of 64); A_g [M][R_g] and B_g [N][R_g] bf16 are the contiguous
+// blocks at element offsets kofs[g] * M and kofs[g] * N (the expert-blocked
+// layout of the transposes above); C fp32 [G][M][N].  128 x 128 tiles, four
+// wavefronts (2 x 2, 64 x 64 each), stages of 32 k double-buffered in LDS by
+// direct loads.
+constexpr int WG_BKS = 32, WG_ROWB = 64, WG_TILE = 128;
+constexpr int WG_SLOT = WG_TILE * WG_ROWB;  // 8 KB per operand and stage
+constexpr int WG_PITCH = WG_TILE;           // fp32 epilogue rows in LDS
 
 struct WgradProblem {
   const bf16_t* A;
-  int64_t lda;
   const bf16_t* B;
-  int64_t ldb;
   const int32_t* kofs;
   int G, M, N;
   float* C;
 };
 
-__global__ __launch_bounds__(256) void wgrad_kernel(WgradProblem p, int mtiles, int ntiles) {
+// Tile order.  With 8 or more groups, workgroup i (dispatched to XCD i % 8)
+// takes a tile of group (i % 8) + 8 j: each XCD owns whole groups, so a
+// group's operands are fetched into one L2 only.  Within a group the faster
+// index runs over the smaller operand's tiles (m_inner: over A's), which
+// keeps the tiles in flight on an XCD to a few of the larger operand's.
+// 32 KB of LDS (two stages of both operands, later half the fp32 tile) lets
+// five workgroups share a CU, so the loads of one hide behind the others.
+__global__ __launch_bounds__(256) void wgrad_kernel(WgradProblem p, int mtiles, int ntiles,
+                                                     int xcd_major, int m_inner) {
   __shared__ __attribute__((aligned(16))) char smem[2 * 2 * WG_SLOT];
-  const int tile = blockIdx.x;
+  static_assert(64 * WG_PITCH * 4 <= 2 * 2 * WG_SLOT, "epilogue half fits");
   const int per_g = mtiles * ntiles;
-  const int g = tile / per_g;
+  int g, rem;
+  if (xcd_major) {
+    const int q = blockIdx.x >> 3;
+    g = (blockIdx.x & 7) + 8 * (q / per_g);
+    rem = q % per_g;
+  } else {
+    g = blockIdx.x / per_g;
+    rem = blockIdx.x % per_g;
+  }
   if (g >= p.G) return;
-  const int rem = tile - g * per_g;
-  const int m0 = (rem / ntiles) * WG_TILE, n0 = (rem % ntiles) * WG_TILE;
+  const int mt = m_inner ? rem % mtiles : rem / ntiles;
+  const int nt = m_inner ? rem / mtiles : rem % ntiles;
+  const int m0 = mt * WG_TILE, n0 = nt * WG_TILE;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int wm = wave & 1, wn = wave >> 1;
-  const int k0 = p.kofs[g];
-  const int nk = (p.kofs[g + 1] - k0) / WG_BKS;
-  // direct loads: instruction t of wavefront w fills rows 8 (w + 4 t) .. + 7 of
-  // the tile (lane l: row + l / 8, position l % 8 holding chunk
-  // (l % 8) ^ ((row >> 1) & 7)); rows past M or N repeat the last one
-  const char* A_base = reinterpret_cast<const char*>(p.A + (int64_t)m0 * p.lda + k0);
-  const char* B_base = reinterpret_cast<const char*>(p.B + (int64_t)n0 * p.ldb + k0);
-  uint32_t a_src[4], b_src[4];
+  const int64_t k0 = p.kofs[g];
+  const int64_t ld = p.kofs[g + 1] - k0;  // row stride of both blocks
+  const int nk = (int)(ld / WG_BKS);
+  // direct loads: instruction t of wavefront w fills rows 16 (w + 4 t) .. + 15
+  // of the tile (lane l: row + l / 4, position l % 4 holding chunk
+  // (l % 4) ^ ((row >> 2) & 3)); rows past M or N repeat the last one
+  const char* A_base = reinterpret_cast<const char*>(p.A + k0 * p.M + (int64_t)m0 * ld);
+  const char* B_base = reinterpret_cast<const char*>(p.B + k0 * p.N + (int64_t)n0 * ld);
+  uint32_t a_src[2], b_src[2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int r = 8 * (wave + 4 * t) + (lane >> 3);
-    const int lc = (lane & 7) ^ ((r >> 1) & 7);
+  for (int t = 0; t < 2; ++t) {
+    const int r = 16 * (wave + 4 * t) + (lane >> 2);
+    const int lc = (lane & 3) ^ ((r >> 2) & 3);
     const int ra = min(r, p.M - 1 - m0), rb = min(r, p.N - 1 - n0);
-    a_src[t] = (uint32_t)((int64_t)ra * p.lda * 2) + (uint32_t)(lc * 16);
-    b_src[t] = (uint32_t)((int64_t)rb * p.ldb * 2) + (uint32_t)(lc * 16);
+    a_src[t] = (uint32_t)((int64_t)ra * ld * 2) + (uint32_t)(lc * 16);
+    b_src[t] = (uint32_t)((int64_t)rb * ld * 2) + (uint32_t)(lc * 16);
   }
   char* const dstA = smem + wave * 1024;
   char* const dstB = smem + WG_SLOT + wave * 1024;
@@ -329,14 +422,14 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradProblem p, int mtiles, 
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(B_base + (int64_t)kt * WG_ROWB), 0, 0x7fffffff, 0x00020000);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2; ++t) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           ra, (lds_void_t*)(dstA + slot * 2 * WG_SLOT + t * 4096), 16, a_src[t], 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rb, (lds_void_t*)(dstB + slot * 2 * WG_SLOT + t * 4096), 16, b_src[t], 0, 0, 0);
     }
   };
-  const int swz = ((lane & 31) >> 1) & 7;
+  const int swz = ((lane & 31) >> 2) & 3;
   f32x16_t acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -349,14 +442,14 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradProblem p, int mtiles, 
     const int slot = kt & 1;
     if (kt + 1 < nk) {
       load_stage(kt + 1, slot ^ 1);
-      ring_barrier<8>();  // this stage's 8 loads are older than the next stage's 8
+      ring_barrier<4>();  // this stage's 4 loads are older than the next stage's 4
     } else {
       ring_barrier<0>();
     }
     const char* As = smem + slot * 2 * WG_SLOT;
     const char* Bs = As + WG_SLOT;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < 2; ++ks) {
       const int ch = ((2 * ks + (lane >> 5)) ^ swz) * 16;
       bf16x8_t fa[2], fb[2];
 #pragma unroll
@@ -375,21 +468,39 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradProblem p, int mtiles, 
     // reads have landed; the next stage's loads may stay in flight)
     ring_barrier<63>();
   }
-  // D[i][j] of a 32 x 32 block: lane j + 32 ((i / 4) % 2), register 4 (i / 8) + i % 4
+  // D[i][j] of a 32 x 32 block: lane j + 32 ((i / 4) % 2), register 4 (i / 8) + i % 4.
+  // The tile leaves through LDS in two halves of 64 rows (the wavefronts with
+  // wm = h hold half h), as 16-byte stores of whole 512-byte row segments.
+  float* Cs = reinterpret_cast<float*>(smem);
   float* Cg = p.C + (int64_t)g * p.M * p.N;
   const int lrow4 = 4 * (lane >> 5), lcol = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int h = 0; h < 2; ++h) {
+    if (wm == h) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn * 64 + 32 * j + lcol;
-      if (n >= p.N) continue;
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * 64 + 32 * i + 8 * (v >> 2) + lrow4 + (v & 3);
-        if (m < p.M) Cg[(int64_t)m * p.N + n] = acc[i][j][v];
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int ml = 32 * i + 8 * (v >> 2) + lrow4 + (v & 3);
+            const int nl = wn * 64 + 32 * j + lcol;
+            Cs[ml * WG_PITCH + nl] = acc[i][j][v];
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int idx = q * 256 + tid;  // 32 chunks of 4 floats per row
+      const int ml = idx >> 5, nc = (idx & 31) * 4;
+      const int m = m0 + 64 * h + ml, n = n0 + nc;
+      if (m < p.M && n < p.N) {
+        const float4 val = *reinterpret_cast<const float4*>(Cs + ml * WG_PITCH + nc);
+        *reinterpret_cast<float4*>(Cg + (int64_t)m * p.N + n) = val;
       }
     }
+    __syncthreads();
+  }
 }
 
 }  // namespace
@@ -418,8 +529,17 @@ hipError_t launch_bwd_rowgate(const int32_t* pos, const float* gate, int64_t slo
 
 hipError_t launch_transpose(const TrArgsHost& h, hipStream_t s) {
   if (h.ncols <= 0 || h.dim <= 0 || h.batch <= 0) return hipSuccess;
+  // 16-byte accesses: strides and column offsets in multiples of 8 elements
+  // (of 4 for fp32 would do; 8 keeps one rule), bases 16-byte aligned
+  const bool ok = h.src_ld % 8 == 0 && h.src_col0 % 8 == 0 && h.src_bstride % 8 == 0 &&
+                  h.dst_ld % 8 == 0 && h.dst_col0 % 8 == 0 && h.dst_bstride % 8 == 0 &&
+                  (reinterpret_cast<uintptr_t>(h.src) & 15) == 0 &&
+                  (reinterpret_cast<uintptr_t>(h.dst) & 15) == 0;
+  if (!ok) return hipErrorInvalidValue;
+  if (h.kofs && (h.dst_col0 != 0 || h.batch != 1 || h.ngroups < 1)) return hipErrorInvalidValue;
   TrArgs a{h.src, h.src_ld, h.src_col0, h.src_bstride, h.rowidx, h.rowscale, h.colrow,
-           h.ncols_valid, h.dst, h.dst_ld, h.dst_col0, h.dst_bstride, h.dim, h.ncols};
+           h.ncols_valid, h.dst, h.dst_ld, h.dst_col0, h.dst_bstride, h.dim, h.ncols,
+           h.kofs, h.ngroups};
   const dim3 grid((unsigned)((h.ncols + 63) / 64), (unsigned)((h.dim + 63) / 64), (unsigned)h.batch);
   if (h.src_f32 && h.dst_f32)
     hipLaunchKernelGGL((transpose_kernel<float, float>), grid, dim3(256), 0, s, a);
@@ -463,15 +583,19 @@ hipError_t launch_dx_final(const float* a, const float* b, bf16_t* dx, int64_t n
   return hipGetLastError();
 }
 
-hipError_t launch_wgrad(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb,
-                        const int32_t* kofs, int G, int M, int N, float* C, hipStream_t s) {
+hipError_t launch_wgrad(const bf16_t* A, const bf16_t* B, const int32_t* kofs, int G, int M,
+                        int N, int64_t max_rows, float* C, hipStream_t s) {
   if (G <= 0 || M <= 0 || N <= 0) return hipSuccess;
-  if (lda % 8 != 0 || ldb % 8 != 0) return hipErrorInvalidValue;
+  if (N % 4 != 0) return hipErrorInvalidValue;  // 16-byte stores of C rows
+  // byte offsets of up to 128 rows of a block within the buffer descriptor
+  if ((int64_t)WG_TILE * max_rows * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const int mt = (M + WG_TILE - 1) / WG_TILE, nt = (N + WG_TILE - 1) / WG_TILE;
-  const int64_t tiles = (int64_t)G * mt * nt;
+  const int xcd_major = G >= 8;
+  const int64_t tiles = (int64_t)(xcd_major ? (G + 7) / 8 * 8 : G) * mt * nt;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  WgradProblem p{A, lda, B, ldb, kofs, G, M, N, C};
-  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)tiles), dim3(256), 0, s, p, mt, nt);
+  WgradProblem p{A, B, kofs, G, M, N, C};
+  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)tiles), dim3(256), 0, s, p, mt, nt, xcd_major,
+                     (int)(M <= N));
   return hipGetLastError();
 }
 

@@ -137,6 +137,11 @@ struct TrArgsHost {
   int64_t ncols;
   int batch;
   bool src_f32, dst_f32;
+  // non-null: expert-blocked destination (group g's columns [kofs[g],
+  // kofs[g+1]) as a contiguous [dim][kofs[g+1] - kofs[g]] block at element
+  // offset kofs[g] * dim; dst_ld unused; batch 1, dst_col0 0)
+  const int32_t* kofs;
+  int ngroups;
 };
 hipError_t launch_transpose(const TrArgsHost& a, hipStream_t s);
 hipError_t launch_swiglu_bwd(const float* A, const float* U, const float* Q, const float* row_gate,
@@ -148,9 +153,10 @@ hipError_t launch_token_bwd(const bf16_t* x, const bf16_t* dy, const float* logi
                             int N, float* dl, int ldl, float* dx_acc, hipStream_t s);
 hipError_t launch_set_range(int32_t* out, int a, int b, hipStream_t s);
 hipError_t launch_dx_final(const float* a, const float* b, bf16_t* dx, int64_t n, hipStream_t s);
-// C[g] = A[:, kofs[g]:kofs[g+1]] B[:, kofs[g]:kofs[g+1]]^T, fp32 [G][M][N].
-hipError_t launch_wgrad(const bf16_t* A, int64_t lda, const bf16_t* B, int64_t ldb,
-                        const int32_t* kofs, int G, int M, int N, float* C, hipStream_t s);
+// C[g] = A_g B_g^T, fp32 [G][M][N], with A_g [M][R_g] and B_g [N][R_g] the
+// expert-blocked operands (R_g = kofs[g+1] - kofs[g] <= max_rows).
+hipError_t launch_wgrad(const bf16_t* A, const bf16_t* B, const int32_t* kofs, int G, int M,
+                        int N, int64_t max_rows, float* C, hipStream_t s);
 
 // fp32 FMA path (gemm_simt.hip).
 hipError_t launch_simt_gemm(const GemmProblem& p, int epilogue, int64_t max_rows,
