@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"],
                     help="backward: time forward + moe_zc_backward (a training step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peak-probe", action="store_true",
+                    help="skip measuring the box's stream bandwidths and dense GEMM rate")
     ap.add_argument("--cpu-experts", type=int, default=24,
                     help="experts the CPU-baseline sample evaluates")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -100,6 +102,46 @@ def calibrate_copy():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}))
+
+
+def measured_peaks(dev):
+    """What this machine reaches on plain streams and a dense GEMM, measured before
+    the inputs exist: a 8 GiB fill (writes), a 4 GiB copy (reads + writes),
+    row sums of an 8 GiB [65536, 32768] matrix (reads; a single full reduction
+    streams slower on this machine), and an 8192^3 bf16 matrix product from the
+    vendor BLAS.  The fractions of the spec peaks are what the roofline uses;
+    these put them in context."""
+    import torch
+
+    def timed(fn, n=5):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / 1e3 / n
+
+    out = {}
+    buf = torch.empty(2 << 30, dtype=torch.float32, device=dev)          # 8 GiB
+    out["hbm_write_GBps"] = buf.numel() * 4 / timed(lambda: buf.fill_(1.0)) / 1e9
+    rows = buf.view(65536, 32768)                                      # row sums: a read stream
+    out["hbm_read_GBps"] = buf.numel() * 4 / timed(lambda: rows.sum(dim=1)) / 1e9
+    del rows
+    del buf
+    src = torch.empty(1 << 30, dtype=torch.float32, device=dev).fill_(1.0)  # 4 GiB
+    dst = torch.empty_like(src)
+    out["hbm_copy_GBps"] = 2 * src.numel() * 4 / timed(lambda: dst.copy_(src)) / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    out["bf16_gemm_TFLOPs"] = 2.0 * n ** 3 / timed(lambda: torch.matmul(a, b)) / 1e12
+    del a, b
+    torch.cuda.empty_cache()
+    return {k: round(v, 1) for k, v in out.items()}
 
 
 def algorithmic(w, S, touched, es, fp8=False):
@@ -269,6 +311,7 @@ def main():
     if args.which == "backward":
         bench_backward(args, w, dev)
         return
+    peaks = None if args.no_peak_probe else measured_peaks(dev)
     inp = make_inputs(w, device=dev)
     dt = inp["x"].dtype
     es = inp["x"].element_size()
@@ -366,6 +409,10 @@ def main():
         roof = {"bound": "mfma", "achieved": a["flop"] / t_dom / 1e12, "peak": peak_dom / 1e12,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    if peaks:  # the same achieved rate against what the box reaches on a read stream / dense GEMM
+        ref = peaks["hbm_read_GBps"] if roof["bound"] == "hbm" else (
+            None if fp8 else peaks["bf16_gemm_TFLOPs"])
+        roof["frac_of_measured"] = roof["achieved"] / ref if ref else None
     # the committed counter summary covers the bf16 kernel only
     roof["traffic"] = None if fp8 else counter_traffic()
     roof["kernel"] = dom
@@ -419,6 +466,7 @@ def main():
         "touched_experts": touched,
         "stages": stage_roof,
         "pid_closed_loop": pid_report,
+        "measured_peaks": peaks,
         "roofline": roof,
         "cpu_baseline": cpu,
     }
