@@ -125,7 +125,9 @@ size_t moe_zc_workspace_size(int64_t T, int64_t d, int64_t I, int32_t N,
  * N may be 0 (every expert is a zero expert; the FFN weights may be NULL).
  * T = 0 returns MOE_ZC_OK and enqueues nothing.
  * Precision: router logits fp32 (bf16 path: x times a two-term bf16 split of
- * W_router on MFMA, fp32 accumulation); softmax in fp64; FFN on bf16 MFMA
+ * W_router on MFMA, fp32 accumulation; with few tokens the reduction is cut
+ * into equal parts whose fp32 partial sums are added in a fixed order);
+ * softmax in fp64; FFN on bf16 MFMA
  * with fp32 accumulation, SiLU in fp32, the hidden activation and expert
  * outputs stored in dt; combine accumulated in fp32 and rounded once. */
 moe_zc_status moe_zc_forward(const void* x, const float* w_router,

@@ -75,11 +75,18 @@ moe_zc_status check_fp8_shape(const Shape& s) {
 
 struct Plan {
   size_t logits, idx, gate, pos, loads, offsets, perm, counts, tiles, tiles2, wr2, xp, h, o;
-  size_t xq, xs, total;  // FP8 codes and scales of x (block-FP8 forward only)
+  size_t xq, xs;    // FP8 codes and scales of x (block-FP8 forward only)
+  size_t lsplit;    // partial router products of a split-K router
+  int splits;       // parts of the router's K range (1: not split)
+  size_t total;
 };
+
+int router_tile_rows(int64_t T, int E);
+int router_splits(int64_t T, int E, int64_t d);
 
 Plan make_plan(const Shape& s, bool fp8 = false) {
   Plan p{};
+  p.splits = (s.dt == MOE_ZC_BF16) ? router_splits(s.T, s.E, s.d) : 1;
   size_t at = 0;
   auto take = [&](size_t bytes) {
     const size_t here = at;
@@ -102,6 +109,7 @@ Plan make_plan(const Shape& s, bool fp8 = false) {
   p.o = take((size_t)s.smax * s.d * s.es);
   p.xq = take(fp8 ? (size_t)s.T * s.d : 0);
   p.xs = take(fp8 ? (size_t)s.T * (s.d / 32) : 0);
+  p.lsplit = take(p.splits > 1 ? (size_t)p.splits * s.T * s.E * 4 : 0);
   p.total = at;
   return p;
 }
@@ -119,6 +127,25 @@ int router_tile_rows(int64_t T, int E) {
   int64_t rows = (T + tiles_m - 1) / tiles_m;
   rows = (rows + 31) / 32 * 32;
   return (int)std::min<int64_t>(std::max<int64_t>(rows, 32), kPackedMaxTileRows);
+}
+
+// Parts of the bf16 router's K range (2d in stages of 64).  Few tokens give
+// few row tiles (T = 128: 12 tiles of 192 stages each, on 256 CUs), and each
+// tile then walks a long K range alone; splitting K into equal parts of at
+// least four stages brings the tile count near one per CU.  More than 128
+// row tiles are left whole.
+int router_splits(int64_t T, int E, int64_t d) {
+  if (T <= 0) return 1;
+  const int64_t panels = (E + kPackedPanel - 1) / kPackedPanel;
+  const int64_t rows = router_tile_rows(T, E);
+  const int64_t tiles = (T + rows - 1) / rows * panels;
+  if (tiles > 128) return 1;
+  const int64_t nk = 2 * d / 64;
+  const int64_t target = (256 + tiles - 1) / tiles;
+  int best = 1;
+  for (int64_t sp = 2; sp <= target; ++sp)
+    if (nk % sp == 0 && nk / sp >= 4) best = (int)sp;
+  return best;
 }
 
 enum Layout { kRowMajor = 0, kPacked = 1, kPackedFp8 = 2 };
@@ -189,6 +216,11 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
       bf16_t* wr2 = reinterpret_cast<bf16_t*>(ws + pl.wr2);
       MOE_ZC_TRY(launch_split_router_packed(w_router, wr2, E, (int)d, stream));
       p.B0 = wr2; p.K = (int)(2 * d);
+      if (pl.splits > 1) {  // partial products, summed by the top-K stage
+        p.C = ws + pl.lsplit;
+        p.k_splits = pl.splits;
+        p.c_split_stride = T * E;
+      }
       MOE_ZC_TRY(launch_packed_gemm(p, kStoreF32, router_tile_rows(T, E), T, stream));
     } else {
       p.B0 = w_router; p.ldb = d; p.K = (int)d;
@@ -197,7 +229,11 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
   }
   // stage 1: softmax, bias key, top-K
   MOE_ZC_TRY(mark(1));
-  MOE_ZC_TRY(launch_topk(logits, bias, T, E, K, idx, gate, stream));
+  if (bf && pl.splits > 1)
+    MOE_ZC_TRY(launch_topk(reinterpret_cast<const float*>(ws + pl.lsplit), bias, T, E, K, idx,
+                           gate, stream, pl.splits, T * E, logits));
+  else
+    MOE_ZC_TRY(launch_topk(logits, bias, T, E, K, idx, gate, stream));
   // stage 2: per-chunk histogram and in-chunk ranks (into pos)
   MOE_ZC_TRY(mark(2));
   MOE_ZC_TRY(launch_chunk_hist(idx, T, K, E, N, counts, pos, stream));

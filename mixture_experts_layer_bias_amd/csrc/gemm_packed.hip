@@ -60,7 +60,7 @@ using PkHalf = PkCfg<kPackedMaxTileRows / 64, 3, 2>;
 // NA = live 32-row blocks of the tile (1..CFG::MAXRB).
 template <typename CFG, int EPI, int NA>
 __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord& c,
-                                           int n_tiles, char* __restrict__ smem) {
+                                           int n_tiles, int split, char* __restrict__ smem) {
   constexpr int PK_DEPTH = CFG::DEPTH, PK_DIST = CFG::DIST, PK_SLOT = CFG::SLOT;
   constexpr bool SWIGLU = (EPI == kSwiGLU_BF16);
   const int tid = threadIdx.x;
@@ -68,7 +68,12 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
   // destinations of the direct loads (M0) need no per-load readfirstlane
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int nk = p.K / PK_BKS;
+  // split-K (fp32 output only): this tile covers stages [k_base, k_base + nk)
+  // of the nk_all of its panel; the other epilogues always take the whole range
+  const int nk_all = p.K / PK_BKS;
+  const int nsplit = (EPI == kStoreF32 && p.k_splits > 1) ? p.k_splits : 1;
+  const int nk = nk_all / nsplit;
+  const int k_base = (EPI == kStoreF32) ? split * nk : 0;
   const int rows = c.m_end - c.m0;
 
   // ---- activation direct loads: LDS rows of 128 bytes, chunk c of row r at
@@ -108,7 +113,7 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
 
   // ---- this wavefront's quarter of each weight block of the panel
   const char* B_pan = static_cast<const char*>(p.B0) +
-                      ((int64_t)c.g * n_tiles + c.nt) * (int64_t)nk * PK_BLOCK;
+                      (((int64_t)c.g * n_tiles + c.nt) * (int64_t)nk_all + k_base) * PK_BLOCK;
   const uint32_t b_off = (uint32_t)(wave * PK_QUARTER + lane * 16);
 
   // ---- fragment reads: lane l reads row 32 i + l % 32, logical chunk
@@ -136,7 +141,8 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
   }
 #define PK_DMA_A(kt, u)                                                               \
   {                                                                                   \
-    const int ks_ = (kt) >= a_wrap ? (kt) - a_wrap : (kt);                            \
+    const int ka_ = (kt) + k_base;                                                    \
+    const int ks_ = ka_ >= a_wrap ? ka_ - a_wrap : ka_;                               \
     const char* a_ = A_tile + (int64_t)ks_ * a_step;                                  \
     const __amdgpu_buffer_rsrc_t r_ =                                                 \
         __builtin_amdgcn_make_buffer_rsrc((void*)a_, 0, 0x7fffffff, 0x00020000);      \
@@ -175,7 +181,8 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
                              q < 4 * ((VMK) - 1) + ((g_ + 1) * 4) / NA; ++q)          \
           fb[NU][q] = *reinterpret_cast<const bf16x8_t*>(b_ + q * 1024);              \
     } else if ((VMK) == 3) {                                                          \
-      const int ks_ = (KN) >= a_wrap ? (KN) - a_wrap : (KN);                          \
+      const int ka_ = (KN) + k_base;                                                  \
+      const int ks_ = ka_ >= a_wrap ? ka_ - a_wrap : ka_;                             \
       const char* a_ = A_tile + (int64_t)ks_ * a_step;                                \
       const __amdgpu_buffer_rsrc_t r_ =                                               \
           __builtin_amdgcn_make_buffer_rsrc((void*)a_, 0, 0x7fffffff, 0x00020000);    \
@@ -252,7 +259,9 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int grow = c.m0 + i * 32 + 8 * (v >> 2) + lrow4 + (v & 3);
-          if (grow < c.m_end) static_cast<float*>(p.C)[(int64_t)grow * p.ldc + gcol] = acc[i][j][v];
+          if (grow < c.m_end)
+            static_cast<float*>(p.C)[split * p.c_split_stride + (int64_t)grow * p.ldc + gcol] =
+                acc[i][j][v];
         }
       }
     return;
@@ -267,9 +276,15 @@ __global__ __launch_bounds__(64 * PK_WAVES, CFG::OCC) void packed_gemm_kernel(Ge
                                                                              int tile_rows) {
   constexpr bool SWIGLU = (EPI == kSwiGLU_BF16);
   __shared__ __attribute__((aligned(16))) char smem[CFG::DEPTH * CFG::SLOT];
-  const int logical =
+  int logical =
       xcd_logical_tile(p.tile_prefix ? p.tile_prefix[p.G] * n_tiles : total_bound);
   if (logical < 0) return;
+  // split-K (fp32 output, one group): the parts of a tile are adjacent
+  int split = 0;
+  if (EPI == kStoreF32 && p.k_splits > 1) {
+    split = logical % p.k_splits;
+    logical /= p.k_splits;
+  }
   TileCoord c;
   if (!map_tile<kPackedPanel, SWIGLU>(p, n_tiles, logical, tile_rows, c)) return;
   // at most CFG::MAXRB: the host checks tile_rows against the configuration
@@ -277,14 +292,14 @@ __global__ __launch_bounds__(64 * PK_WAVES, CFG::OCC) void packed_gemm_kernel(Ge
   if (nb <= 0) return;
   constexpr int M = CFG::MAXRB;
   switch (nb) {
-    case 1: run_packed<CFG, EPI, 1>(p, c, n_tiles, smem); break;
-    case 2: run_packed<CFG, EPI, (M >= 2 ? 2 : M)>(p, c, n_tiles, smem); break;
-    case 3: run_packed<CFG, EPI, (M >= 3 ? 3 : M)>(p, c, n_tiles, smem); break;
-    case 4: run_packed<CFG, EPI, (M >= 4 ? 4 : M)>(p, c, n_tiles, smem); break;
-    case 5: run_packed<CFG, EPI, (M >= 5 ? 5 : M)>(p, c, n_tiles, smem); break;
-    case 6: run_packed<CFG, EPI, (M >= 6 ? 6 : M)>(p, c, n_tiles, smem); break;
-    case 7: run_packed<CFG, EPI, (M >= 7 ? 7 : M)>(p, c, n_tiles, smem); break;
-    default: run_packed<CFG, EPI, M>(p, c, n_tiles, smem); break;
+    case 1: run_packed<CFG, EPI, 1>(p, c, n_tiles, split, smem); break;
+    case 2: run_packed<CFG, EPI, (M >= 2 ? 2 : M)>(p, c, n_tiles, split, smem); break;
+    case 3: run_packed<CFG, EPI, (M >= 3 ? 3 : M)>(p, c, n_tiles, split, smem); break;
+    case 4: run_packed<CFG, EPI, (M >= 4 ? 4 : M)>(p, c, n_tiles, split, smem); break;
+    case 5: run_packed<CFG, EPI, (M >= 5 ? 5 : M)>(p, c, n_tiles, split, smem); break;
+    case 6: run_packed<CFG, EPI, (M >= 6 ? 6 : M)>(p, c, n_tiles, split, smem); break;
+    case 7: run_packed<CFG, EPI, (M >= 7 ? 7 : M)>(p, c, n_tiles, split, smem); break;
+    default: run_packed<CFG, EPI, M>(p, c, n_tiles, split, smem); break;
   }
 }
 
@@ -423,12 +438,16 @@ hipError_t launch_packed_gemm(const GemmProblem& p, int epilogue, int tile_rows,
   } else {
     mt_bound = (p.M + tile_rows - 1) / tile_rows;
   }
-  int64_t blocks = mt_bound * n_tiles;
+  // split-K: fp32 output of one group only, equal whole-stage parts
+  const int splits = std::max(1, p.k_splits);
+  if (splits > 1 && (epilogue != kStoreF32 || p.tile_prefix || (p.K / PK_BKS) % splits != 0))
+    return hipErrorInvalidValue;
+  int64_t blocks = mt_bound * n_tiles * splits;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7ffffff0) return hipErrorInvalidValue;
+  const int total = (int)blocks;
   blocks = (blocks + 7) / 8 * 8;
   const dim3 grid((unsigned)blocks), block(64 * PK_WAVES);
-  const int total = (int)(mt_bound * n_tiles);
   switch (epilogue) {
     case kStoreF32:
       hipLaunchKernelGGL((packed_gemm_kernel<PkWide, kStoreF32>), grid, block, 0, s, p, n_tiles,

@@ -14,9 +14,12 @@ constexpr int kMaxExperts = 2048;
 constexpr int kMaxTopK = 32;
 
 // ---- routing (route.hip) ----------------------------------------------------
-// fp64 softmax, fp32 bias key, top-K with lowest-index tie-break.
+// fp64 softmax, fp32 bias key, top-K with lowest-index tie-break.  With
+// nsplit > 1, `logits` holds nsplit partial products split_stride apart: the
+// logits are their sum in part order, written to logits_out.
 hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int K,
-                       int32_t* idx, float* gate, hipStream_t s);
+                       int32_t* idx, float* gate, hipStream_t s, int nsplit = 1,
+                       int64_t split_stride = 0, float* logits_out = nullptr);
 // Per 64-token chunk: expert counts [C, E] and each FFN slot's rank among the
 // chunk's earlier tokens (written to rank[T, K], -1 for zero experts).
 hipError_t launch_chunk_hist(const int32_t* idx, int64_t T, int K, int E, int N,
@@ -66,6 +69,11 @@ struct GemmProblem {
   int M;
   const uint8_t* a_scales;  // block-FP8 A only: [rows][K / 32] scale bytes
   int64_t a_scale_ld;       // scale bytes per A row (K / 32)
+  // packed fp32-output GEMM only (the router): the K range is cut into
+  // k_splits equal parts and part s writes its partial product to
+  // C + s * c_split_stride (0 or 1: one part, C itself)
+  int k_splits;
+  int64_t c_split_stride;
 };
 
 enum Epilogue { kStoreF32 = 0, kStoreBF16 = 1, kSwiGLU_BF16 = 2, kSwiGLU_F32 = 3 };

@@ -19,13 +19,17 @@ namespace moezc {
 // a time by a wavefront arg-max on (key descending, index ascending), so an
 // exact tie goes to the lower expert index and the output order is the key
 // order.  Reductions are xor butterflies: every lane ends with the same,
-// run-to-run reproducible value.
+// run-to-run reproducible value.  A split router product arrives as nsplit
+// partial logits; they are summed in part order (fixed, so reproducible) and
+// the sums are stored as the logits.
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
                                                    const float* __restrict__ bias,
                                                    int64_t T, int E, int K,
                                                    int32_t* __restrict__ idx_out,
-                                                   float* __restrict__ gate_out) {
+                                                   float* __restrict__ gate_out, int nsplit,
+                                                   int64_t split_stride,
+                                                   float* __restrict__ logits_out) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -36,7 +40,21 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int j = lane + 64 * i;
-    l[i] = (j < E) ? row[j] : -INFINITY;
+    float v = -INFINITY;
+    if (j < E) {
+      v = row[j];
+      int s = 1;
+      for (; s + 8 <= nsplit; s += 8) {  // eight loads in flight, added in part order
+        float q[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) q[r] = row[(s + r) * split_stride + j];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) v += q[r];
+      }
+      for (; s < nsplit; ++s) v += row[s * split_stride + j];
+      if (nsplit > 1) logits_out[t * E + j] = v;
+    }
+    l[i] = v;
     m = fmaxf(m, l[i]);
   }
 #pragma unroll
@@ -98,23 +116,32 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 }
 
 hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int K,
-                       int32_t* idx, float* gate, hipStream_t s) {
+                       int32_t* idx, float* gate, hipStream_t s, int nsplit,
+                       int64_t split_stride, float* logits_out) {
   const dim3 grid((unsigned)((T + 3) / 4)), block(256);
   const int epl = (E + 63) / 64;
+  if (nsplit < 1 || (nsplit > 1 && !logits_out)) return hipErrorInvalidValue;
   if (epl <= 1)
-    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
+                       nsplit, split_stride, logits_out);
   else if (epl <= 2)
-    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
+                       nsplit, split_stride, logits_out);
   else if (epl <= 4)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
+                       nsplit, split_stride, logits_out);
   else if (epl <= 8)
-    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
+                       nsplit, split_stride, logits_out);
   else if (epl <= 12)
-    hipLaunchKernelGGL(topk_kernel<12>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<12>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
+                       nsplit, split_stride, logits_out);
   else if (epl <= 16)
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
+                       nsplit, split_stride, logits_out);
   else if (epl <= 32)
-    hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, logits, bias, T, E, K, idx, gate);
+    hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
+                       nsplit, split_stride, logits_out);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -135,3 +135,20 @@ def test_router_logits_stage_remainders(d, na):
     ref = x @ inp["w_router"].cpu().double().numpy().T
     err = np.abs(g["logits"].astype(np.float64) - ref).max()
     assert err <= LOGIT_TOL, f"router logits off by {err}"
+
+
+# Few tokens: the bf16 router splits its K range (2d in stages of 64) into
+# equal parts whose partial logits the top-K stage sums in part order.  The
+# cases give 1 (T=1, d=128: 4 stages), several and many parts (e.g. T=128 at
+# d=6144, E=768: 12 row tiles, 16 parts of 12 stages).
+@pytest.mark.parametrize("T,d,N,Z", [(1, 128, 8, 4), (40, 2048, 64, 32), (128, 6144, 512, 256),
+                                     (300, 1344, 6, 2), (1000, 4096, 24, 8)])
+def test_router_split_k(T, d, N, Z):
+    w = _edge(T=T, d=d, I=128, N=N, Z=Z, K=min(12, N + Z))
+    print(f"[router split] {w.describe()}", flush=True)
+    inp = make_inputs(w, device=DEV)
+    g1 = run_gpu(w, inp)
+    g2 = run_gpu(w, inp)
+    assert np.array_equal(g1["logits"].view(np.uint32), g2["logits"].view(np.uint32)), \
+        "split router logits differ between runs"
+    print(check_forward(w, inp, g1), flush=True)
