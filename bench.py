@@ -11,10 +11,12 @@ times moe_zc_forward on the row-major weights instead.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload prefill]
 
---pass backward times a training step of the layer instead: moe_zc_forward
-(row-major weights, routing saved) followed by moe_zc_backward (dx, the router
-gradient and the fp32 expert weight gradients), with the backward also timed
-alone.
+--pass backward times a training step of the layer instead: the packed
+forward saving its routing and the expert pre-activations (aux.act), then
+moe_zc_backward (dx, the router gradient and the fp32 expert weight
+gradients) from them, with the backward also timed alone; --recompute uses
+the row-major forward without saved pre-activations, so the backward
+recomputes them.
 
 Prints one JSON line.  Per-stage times come from HIP events that the library
 records on the launch stream at its stage boundaries.
@@ -50,6 +52,8 @@ def parse():
                          "the down projection stays bf16")
     ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"],
                     help="backward: time forward + moe_zc_backward (a training step)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="--pass backward: row-major forward, pre-activations recomputed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peak-probe", action="store_true",
                     help="skip measuring the box's stream bandwidths and dense GEMM rate")
@@ -213,9 +217,9 @@ def cpu_baseline(w, inp, n_experts, weights):
 
 def bench_backward(args, w, dev):
     """Training step = forward (routing saved) + backward; also the backward
-    alone.  FLOPs of the backward's expert products: a and u recomputed
-    (4 d I S), q (2 d I S), the rows of dx (4 d I S), dW_down, dW_gate,
-    dW_up (6 d I S); router: dx term and dW_router (4 T d E)."""
+    alone.  FLOPs of the backward's expert products: q (2 d I S), the rows
+    of dx (4 d I S), dW_down, dW_gate, dW_up (6 d I S), and with --recompute
+    a and u again (4 d I S); router: dx term and dW_router (4 T d E)."""
     import torch
 
     import mixture_experts_layer_bias_amd as m
@@ -227,7 +231,15 @@ def bench_backward(args, w, dev):
     inp = make_inputs(w, device=dev, residual=False)
     dy = make_upstream_grad(w, dev)
     tr = m.moe_zc_transpose_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
-    aux = m.alloc_aux(w.T, w.N, w.Z, w.K, dev)
+    saved = not args.recompute
+    if saved:  # packed weights for the forward; the row-major copies are no longer read
+        gu, dn = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+        torch.cuda.synchronize()
+        for k in ("w_gate", "w_up", "w_down"):
+            inp[k] = None
+        torch.cuda.empty_cache()
+    aux = m.alloc_aux(w.T, w.N, w.Z, w.K, dev, keys=m.AUX_KEYS + (("act",) if saved else ()),
+                      I=w.I)
     y = torch.empty(w.T, w.d, dtype=torch.bfloat16, device=dev)
     ws_f = torch.empty(m.moe_zc_workspace_size(w.T, w.d, w.I, w.N, w.Z, w.K, torch.bfloat16),
                        dtype=torch.uint8, device=dev)
@@ -240,8 +252,12 @@ def bench_backward(args, w, dev):
              "dw_down": torch.empty(w.N, w.d, w.I, dtype=torch.float32, device=dev)}
 
     def fwd():
-        m.moe_zc_forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
-                         inp["w_down"], w.N, w.Z, w.K, out=y, aux=aux, workspace=ws_f)
+        if saved:
+            m.moe_zc_forward_packed(inp["x"], inp["w_router"], inp["bias"], gu, dn, w.N, w.Z,
+                                    w.K, w.I, out=y, aux=aux, workspace=ws_f)
+        else:
+            m.moe_zc_forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
+                             inp["w_down"], w.N, w.Z, w.K, out=y, aux=aux, workspace=ws_f)
 
     def bwd():
         m.moe_zc_backward(inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], tr, aux, dy,
@@ -260,7 +276,9 @@ def bench_backward(args, w, dev):
     ms_step = timed(lambda: (fwd(), bwd()))
     ms_bwd = timed(bwd)
     S = int(aux["offsets"][w.N].item())
-    flop_bwd = 16.0 * w.d * w.I * S + 4.0 * w.T * w.d * w.E
+    # expert products: q, rows of dx, three weight gradients (12 d I S), plus
+    # the recomputed a and u (4 d I S) unless the forward saved them
+    flop_bwd = (12.0 if saved else 16.0) * w.d * w.I * S + 4.0 * w.T * w.d * w.E
     flop_fwd = 6.0 * w.d * w.I * S + 2.0 * w.T * w.d * w.E
     out = {
         "metric": "MoE-layer training step (forward + backward) tokens/s on 1 MI355X",
@@ -276,7 +294,9 @@ def bench_backward(args, w, dev):
         "dtype": "bf16 (fp32 accumulation, fp32 weight gradients)",
         "data": "synthetic (seeded Gaussian inputs and upstream gradient, random-init weights)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "I": w.I, "N": w.N, "Z": w.Z,
-                   "K": w.K, "step": "moe_zc_forward + moe_zc_backward",
+                   "K": w.K,
+                   "step": ("moe_zc_forward_packed (saving a | u) + moe_zc_backward" if saved
+                            else "moe_zc_forward + moe_zc_backward (a, u recomputed)"),
                    "parallelism": "none (1 GPU)"},
         "backward_ms": ms_bwd,
         "backward_tflops": flop_bwd / (ms_bwd / 1e3) / 1e12,

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define MOE_ZC_ABI_VERSION 1
+#define MOE_ZC_ABI_VERSION 2
 
 typedef enum {
   MOE_ZC_OK = 0,
@@ -93,7 +93,14 @@ typedef enum {
  *                       rows are grouped by expert, tokens ascending
  *   pos         [T, K]  grouped row of slot (t,k), -1 for a zero expert
  *   stage_events [MOE_ZC_NUM_EVENTS] created HIP events, recorded on
- *                       `stream` at stage boundaries (for timing), or NULL */
+ *                       `stream` at stage boundaries (for timing), or NULL
+ *   act         [T * min(K, N), 2I] bf16 (16-byte aligned): the expert
+ *                       pre-activations of grouped row s, a = W_gate x in
+ *                       columns [0, I) and u = W_up x in [I, 2I), rounded
+ *                       once from the fp32 accumulators (first S rows valid).
+ *                       What moe_zc_backward reads instead of recomputing
+ *                       them.  dt = bf16 only (else MOE_ZC_ERR_UNSUPPORTED).
+ * (act was added in ABI version 2.) */
 typedef struct moe_zc_aux {
   float* logits;
   int32_t* topk_idx;
@@ -103,6 +110,7 @@ typedef struct moe_zc_aux {
   int32_t* perm;
   int32_t* pos;
   hipEvent_t* stage_events;
+  void* act;
 } moe_zc_aux;
 
 /* Bytes of device workspace moe_zc_forward needs for these sizes (0 if the
@@ -301,7 +309,9 @@ size_t moe_zc_backward_workspace_size(int64_t T, int64_t d, int64_t I,
  *   x, w_router, w_gate, w_up   the forward's inputs (w_router fp32)
  *   w_gate_up_t, w_down_t       from moe_zc_transpose_expert_weights
  *   fwd       the forward's aux with logits, topk_idx, topk_gate, offsets,
- *             perm and pos filled (same x, w_router, bias, sizes); read only
+ *             perm and pos filled (same x, w_router, bias, sizes); read only.
+ *             With fwd->act filled as well, a and u are taken from it
+ *             instead of being recomputed, and w_gate, w_up may be NULL.
  *   dy        [T, d] bf16 upstream gradient
  *   dx        [T, d] bf16 output
  *   dw_router [E, d] fp32 output

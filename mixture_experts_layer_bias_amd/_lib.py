@@ -33,7 +33,8 @@ class MoeZcAux(ctypes.Structure):
     _fields_ = [("logits", ctypes.c_void_p), ("topk_idx", ctypes.c_void_p),
                 ("topk_gate", ctypes.c_void_p), ("loads", ctypes.c_void_p),
                 ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p),
-                ("pos", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
+                ("pos", ctypes.c_void_p), ("stage_events", ctypes.c_void_p),
+                ("act", ctypes.c_void_p)]
 
 
 class MoeZcPid(ctypes.Structure):

@@ -66,17 +66,24 @@ def _need(t: torch.Tensor, name: str, dtype, shape, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _aux_spec(T: int, N: int, Z: int, K: int):
+def _aux_spec(T: int, N: int, Z: int, K: int, I: Optional[int] = None):
     E = N + Z
-    return {"logits": ((T, E), torch.float32), "topk_idx": ((T, K), torch.int32),
+    spec = {"logits": ((T, E), torch.float32), "topk_idx": ((T, K), torch.int32),
             "topk_gate": ((T, K), torch.float32), "loads": ((E,), torch.int32),
             "offsets": ((N + 1,), torch.int32),
             "perm": ((max(1, T * min(K, N)),), torch.int32), "pos": ((T, K), torch.int32)}
+    if I is not None:  # the saved pre-activations (a | u) of every grouped row
+        spec["act"] = ((max(1, T * min(K, N)), 2 * I), torch.bfloat16)
+    return spec
 
 
-def alloc_aux(T: int, N: int, Z: int, K: int, device, keys=AUX_KEYS) -> Dict[str, torch.Tensor]:
-    """Caller-owned tensors for the optional outputs of moe_zc_forward."""
-    spec = _aux_spec(T, N, Z, K)
+def alloc_aux(T: int, N: int, Z: int, K: int, device, keys=AUX_KEYS,
+              I: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Caller-owned tensors for the optional outputs of moe_zc_forward; the
+    key "act" (pre-activations, bf16 forwards) needs the hidden size I."""
+    spec = _aux_spec(T, N, Z, K, I)
+    if "act" in keys and I is None:
+        raise ValueError("aux key 'act' needs I")
     return {k: torch.empty(*spec[k][0], dtype=spec[k][1], device=device) for k in keys}
 
 
@@ -152,9 +159,9 @@ def _forward(name: str, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Ten
         raise ValueError("workspace must be a contiguous uint8 tensor on x's device")
     a = _lib.MoeZcAux()
     if aux:
-        spec = _aux_spec(T, N, Z, K)
+        spec = _aux_spec(T, N, Z, K, I)
         for k, t in aux.items():
-            if k not in AUX_KEYS:
+            if k not in spec:
                 raise ValueError(f"unknown aux key {k!r}")
             _need(t, f"aux[{k!r}]", spec[k][1], spec[k][0], dev)
             setattr(a, k, t.data_ptr())
@@ -445,9 +452,11 @@ def moe_zc_backward(x: torch.Tensor, w_router: torch.Tensor, w_gate: Optional[to
                     out: Optional[Dict[str, torch.Tensor]] = None,
                     workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """Gradients of the layer for upstream gradient dy, replaying the routing
-    the forward saved in ``aux`` (keys BWD_AUX_KEYS); ``transposed`` is the
-    pair from moe_zc_transpose_expert_weights (or None when N = 0).  Returns
-    dx (bf16) and dw_router, dw_gate, dw_up, dw_down (fp32)."""
+    the forward saved in ``aux`` (keys BWD_AUX_KEYS, plus "act" when the
+    forward saved the pre-activations: then w_gate and w_up may be None);
+    ``transposed`` is the pair from moe_zc_transpose_expert_weights (or None
+    when N = 0).  Returns dx (bf16) and dw_router, dw_gate, dw_up, dw_down
+    (fp32)."""
     lib = _lib.load()
     _check_x(x)
     T, d = x.shape
@@ -457,11 +466,14 @@ def moe_zc_backward(x: torch.Tensor, w_router: torch.Tensor, w_gate: Optional[to
         raise ValueError("the backward takes bf16 x")
     _need(w_router, "w_router", torch.float32, (E, d), dev)
     _need(dy, "dy", torch.bfloat16, (T, d), dev)
-    spec = _aux_spec(T, N, Z, K)
+    spec = _aux_spec(T, N, Z, K, I)
     for k in BWD_AUX_KEYS:
         if k not in aux:
             raise ValueError(f"aux lacks {k!r}")
         _need(aux[k], f"aux[{k!r}]", spec[k][1], spec[k][0], dev)
+    act = aux.get("act")
+    if act is not None:
+        _need(act, "aux['act']", spec["act"][1], spec["act"][0], dev)
     shapes = {"dx": ((T, d), torch.bfloat16), "dw_router": ((E, d), torch.float32),
               "dw_gate": ((N, I, d), torch.float32), "dw_up": ((N, I, d), torch.float32),
               "dw_down": ((N, d, I), torch.float32)}
@@ -471,8 +483,10 @@ def moe_zc_backward(x: torch.Tensor, w_router: torch.Tensor, w_gate: Optional[to
             out[k] = torch.empty(*shp, dtype=dt, device=dev)
         _need(out[k], k, dt, shp, dev)
     if N > 0:
-        _need(w_gate, "w_gate", torch.bfloat16, (N, I, d), dev)
-        _need(w_up, "w_up", torch.bfloat16, (N, I, d), dev)
+        if act is None or w_gate is not None:
+            _need(w_gate, "w_gate", torch.bfloat16, (N, I, d), dev)
+        if act is None or w_up is not None:
+            _need(w_up, "w_up", torch.bfloat16, (N, I, d), dev)
         gut, dnt = transposed
         _need(gut, "w_gate_up_t", torch.bfloat16, (N, d, 2 * I), dev)
         _need(dnt, "w_down_t", torch.bfloat16, (N, I, d), dev)
@@ -483,6 +497,8 @@ def moe_zc_backward(x: torch.Tensor, w_router: torch.Tensor, w_gate: Optional[to
     a = _lib.MoeZcAux()
     for k in BWD_AUX_KEYS:
         setattr(a, k, aux[k].data_ptr())
+    if act is not None:
+        a.act = act.data_ptr()
     if need == 0:
         code = lib.moe_zc_backward(None, None, None, None, None, None, ctypes.byref(a), None, None,
                                    None, None, None, None, T, d, I, N, Z, K, None, 0, None)

@@ -177,6 +177,9 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
     return MOE_ZC_ERR_INVALID;
   if (N > 0 && (!aligned16(w_gate) || !aligned16(w_down) || (!packed && !aligned16(w_up))))
     return MOE_ZC_ERR_INVALID;
+  void* act = aux ? aux->act : nullptr;  // pre-activations, saved for the backward
+  if (act && dt != MOE_ZC_BF16) return MOE_ZC_ERR_UNSUPPORTED;
+  if (act && !aligned16(act)) return MOE_ZC_ERR_INVALID;
   const Plan pl = make_plan(s, fp8);
   if (!workspace || workspace_bytes < pl.total) return MOE_ZC_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MOE_ZC_ERR_WORKSPACE;
@@ -259,6 +262,8 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
     p.B0 = w_gate; p.B1 = w_up; p.ldb = d; p.b_group_stride = I * d;
     p.C = h; p.ldc = I; p.Nout = (int)I;
     p.row_offsets = offsets; p.tile_prefix = tiles; p.G = N; p.M = 0;
+    p.C2 = act; p.ldc2 = 2 * I;
+    const int swiglu_epi = act ? kSwiGLU_BF16_ACT : kSwiGLU_BF16;
     if (fp8) {
       // block-FP8 gate/up: x quantized once, its code rows gathered through perm
       uint8_t* xq = reinterpret_cast<uint8_t*>(ws + pl.xq);
@@ -268,9 +273,9 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
       p.a_scales = xs; p.a_scale_ld = d / 32;
       MOE_ZC_TRY(launch_fp8_gemm(p, s.ffn_tile_rows, s.smax, stream));
     } else if (packed)
-      MOE_ZC_TRY(launch_packed_gemm(p, kSwiGLU_BF16, s.ffn_tile_rows, s.smax, stream));
+      MOE_ZC_TRY(launch_packed_gemm(p, swiglu_epi, s.ffn_tile_rows, s.smax, stream));
     else if (bf)
-      MOE_ZC_TRY(launch_mfma_gemm(p, kSwiGLU_BF16, s.ffn_tile_rows, s.smax, stream));
+      MOE_ZC_TRY(launch_mfma_gemm(p, swiglu_epi, s.ffn_tile_rows, s.smax, stream));
     else
       MOE_ZC_TRY(launch_simt_gemm(p, kSwiGLU_F32, s.smax, stream));
   }
@@ -561,11 +566,14 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
   if (!fwd->logits || !fwd->topk_idx || !fwd->topk_gate || !fwd->pos || !fwd->perm ||
       !fwd->offsets)
     return MOE_ZC_ERR_INVALID;
-  if (N > 0 && (!w_gate || !w_up || !w_gate_up_t || !w_down_t || !dw_gate || !dw_up || !dw_down))
+  // a and u: from the forward's saved pre-activations, else recomputed
+  const void* act = fwd->act;
+  if (N > 0 && (!w_gate_up_t || !w_down_t || !dw_gate || !dw_up || !dw_down))
     return MOE_ZC_ERR_INVALID;
+  if (N > 0 && !act && (!w_gate || !w_up)) return MOE_ZC_ERR_INVALID;
   if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(w_router) ||
-      (N > 0 && (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_gate_up_t) ||
-                 !aligned16(w_down_t))))
+      (N > 0 && (!aligned16(w_gate_up_t) || !aligned16(w_down_t))) ||
+      (N > 0 && (act ? !aligned16(act) : (!aligned16(w_gate) || !aligned16(w_up)))))
     return MOE_ZC_ERR_INVALID;
   const BwdPlan pl = make_bwd_plan(s);
   if (!workspace || workspace_bytes < pl.total) return MOE_ZC_ERR_WORKSPACE;
@@ -590,21 +598,29 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
     MOE_ZC_TRY(launch_bwd_prefix(offsets, N, s.ffn_tile_rows, tiles, kofs, stream));
     MOE_ZC_TRY(launch_bwd_colrow(offsets, kofs, N, colrow, (int)pl.Sp, stream));
     MOE_ZC_TRY(launch_bwd_rowgate(fwd->pos, fwd->topk_gate, T * K, row_gate, stream));
-    // a = W_gate x and u = W_up x of every grouped row (fp32), q = W_down^T dy
+    // a = W_gate x and u = W_up x of every grouped row (fp32; unless the
+    // forward saved them), q = W_down^T dy
     GemmProblem p{};
     p.A = x; p.lda = d; p.a_kwrap = (int)d; p.K = (int)d; p.a_rows = perm;
     p.ldb = d; p.b_group_stride = I * d;
     p.ldc = I; p.Nout = (int)I;
     p.row_offsets = offsets; p.tile_prefix = tiles; p.G = N; p.M = 0;
-    p.B0 = w_gate; p.C = F(pl.A);
-    MOE_ZC_TRY(launch_mfma_gemm(p, kStoreF32, s.ffn_tile_rows, s.smax, stream));
-    p.B0 = w_up; p.C = F(pl.U);
-    MOE_ZC_TRY(launch_mfma_gemm(p, kStoreF32, s.ffn_tile_rows, s.smax, stream));
+    if (!act) {
+      p.B0 = w_gate; p.C = F(pl.A);
+      MOE_ZC_TRY(launch_mfma_gemm(p, kStoreF32, s.ffn_tile_rows, s.smax, stream));
+      p.B0 = w_up; p.C = F(pl.U);
+      MOE_ZC_TRY(launch_mfma_gemm(p, kStoreF32, s.ffn_tile_rows, s.smax, stream));
+    }
     p.A = dy; p.B0 = w_down_t; p.C = F(pl.Q);
     MOE_ZC_TRY(launch_mfma_gemm(p, kStoreF32, s.ffn_tile_rows, s.smax, stream));
     // SwiGLU backward: da | du, h, and the gate gradient of every grouped row
-    MOE_ZC_TRY(launch_swiglu_bwd(F(pl.A), F(pl.U), F(pl.Q), row_gate, offsets, N, (int)I, s.smax,
-                                 B(pl.dau), B(pl.H), row_dg, stream));
+    if (act)
+      MOE_ZC_TRY(launch_swiglu_bwd(act, static_cast<const bf16_t*>(act) + I, 2 * I, true,
+                                   F(pl.Q), row_gate, offsets, N, (int)I, s.smax, B(pl.dau),
+                                   B(pl.H), row_dg, stream));
+    else
+      MOE_ZC_TRY(launch_swiglu_bwd(F(pl.A), F(pl.U), I, false, F(pl.Q), row_gate, offsets, N,
+                                   (int)I, s.smax, B(pl.dau), B(pl.H), row_dg, stream));
     // rows of dx from the experts: [da | du] [W_gate ; W_up]
     GemmProblem q{};
     q.A = B(pl.dau); q.lda = 2 * I; q.a_kwrap = (int)(2 * I); q.K = (int)(2 * I);

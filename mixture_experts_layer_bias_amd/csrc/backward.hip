@@ -215,12 +215,14 @@ __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
 }
 
 // ---- per-row SwiGLU backward --------------------------------------------------
-// Row s of expert rows: a, u, q [S][I] fp32 -> dau [S][2I] bf16 (da | du),
-// h [S][I] bf16, row_dg[s] = <q, h> (the gate gradient of the row's slot).
-// One workgroup of 256 threads per row; the dot product reduces in a fixed
-// tree.
-__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ A,
-                                                         const float* __restrict__ U,
+// Row s of expert rows: a, u (row stride ld_au: fp32 [S][I] recomputed, or
+// the forward's bf16 pre-activations [S][2I]) and q [S][I] fp32 -> dau [S][2I]
+// bf16 (da | du), h [S][I] bf16, row_dg[s] = <q, h> (the gate gradient of
+// the row's slot).  One workgroup of 256 threads per row; the dot product
+// reduces in a fixed tree.
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ A,
+                                                         const T* __restrict__ U, int64_t ld_au,
                                                          const float* __restrict__ Q,
                                                          const float* __restrict__ row_gate,
                                                          const int32_t* __restrict__ offsets,
@@ -234,7 +236,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict
   float dot = 0.f;
   for (int i = threadIdx.x; i < I; i += 256) {
     const int64_t o = s * I + i;
-    const float a = A[o], u = U[o], q = Q[o];
+    const float a = ld_elem(A, s * ld_au + i), u = ld_elem(U, s * ld_au + i), q = Q[o];
     const float sg = 1.0f / (1.0f + __expf(-a));
     const float h = a * sg * u;
     dot += q * h;
@@ -552,12 +554,19 @@ hipError_t launch_transpose(const TrArgsHost& h, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_swiglu_bwd(const float* A, const float* U, const float* Q, const float* row_gate,
-                             const int32_t* offsets, int N, int I, int64_t max_rows, bf16_t* dau,
-                             bf16_t* H, float* row_dg, hipStream_t s) {
+hipError_t launch_swiglu_bwd(const void* A, const void* U, int64_t ld_au, bool au_bf16,
+                             const float* Q, const float* row_gate, const int32_t* offsets, int N,
+                             int I, int64_t max_rows, bf16_t* dau, bf16_t* H, float* row_dg,
+                             hipStream_t s) {
   if (max_rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)max_rows), dim3(256), 0, s, A, U, Q,
-                     row_gate, offsets, N, I, dau, H, row_dg);
+  if (au_bf16)
+    hipLaunchKernelGGL(swiglu_bwd_kernel<bf16_t>, dim3((unsigned)max_rows), dim3(256), 0, s,
+                       static_cast<const bf16_t*>(A), static_cast<const bf16_t*>(U), ld_au, Q,
+                       row_gate, offsets, N, I, dau, H, row_dg);
+  else
+    hipLaunchKernelGGL(swiglu_bwd_kernel<float>, dim3((unsigned)max_rows), dim3(256), 0, s,
+                       static_cast<const float*>(A), static_cast<const float*>(U), ld_au, Q,
+                       row_gate, offsets, N, I, dau, H, row_dg);
   return hipGetLastError();
 }
 

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const bf16_t* __restrict_
 // NA = live 32-row blocks of the tile.  Workgroup of four wavefronts, one per
 // SIMD; wavefront w owns hidden units [32 w, 32 w + 32) of the panel (gate
 // and up columns), for every row.  A stage is two MFMA substeps of 64 k.
-template <int NA>
+template <int NA, bool SAVE>
 __device__ __forceinline__ void run_fp8(const GemmProblem& p, const TileCoord& c, int n_tiles,
                                         char* __restrict__ smem) {
   const int tid = threadIdx.x;
@@ -354,9 +354,11 @@ __device__ __forceinline__ void run_fp8(const GemmProblem& p, const TileCoord& c
 #undef F8_SUB
 #undef F8_STAGE
   ring_barrier<0>();  // every wavefront is done reading the ring before it is reused
-  store_bf16_tile<NA, true>(acc, smem, wave, lane, c, p);
+  store_bf16_tile<NA, true, SAVE>(acc, smem, wave, lane, c, p);
 }
 
+// SAVE: also store the pre-activations to p.C2 (a separate instantiation)
+template <bool SAVE>
 __global__ __launch_bounds__(64 * F8_WAVES, 1) void fp8_gemm_kernel(GemmProblem p, int n_tiles,
                                                                     int total_bound,
                                                                     int tile_rows) {
@@ -369,14 +371,14 @@ __global__ __launch_bounds__(64 * F8_WAVES, 1) void fp8_gemm_kernel(GemmProblem 
   const int nb = (c.m_end - c.m0 + 31) / 32;  // at most F8_MAXRB: checked on the host
   if (nb <= 0) return;
   switch (nb) {
-    case 1: run_fp8<1>(p, c, n_tiles, smem); break;
-    case 2: run_fp8<2>(p, c, n_tiles, smem); break;
-    case 3: run_fp8<3>(p, c, n_tiles, smem); break;
-    case 4: run_fp8<4>(p, c, n_tiles, smem); break;
-    case 5: run_fp8<5>(p, c, n_tiles, smem); break;
-    case 6: run_fp8<6>(p, c, n_tiles, smem); break;
-    case 7: run_fp8<7>(p, c, n_tiles, smem); break;
-    default: run_fp8<F8_MAXRB>(p, c, n_tiles, smem); break;
+    case 1: run_fp8<1, SAVE>(p, c, n_tiles, smem); break;
+    case 2: run_fp8<2, SAVE>(p, c, n_tiles, smem); break;
+    case 3: run_fp8<3, SAVE>(p, c, n_tiles, smem); break;
+    case 4: run_fp8<4, SAVE>(p, c, n_tiles, smem); break;
+    case 5: run_fp8<5, SAVE>(p, c, n_tiles, smem); break;
+    case 6: run_fp8<6, SAVE>(p, c, n_tiles, smem); break;
+    case 7: run_fp8<7, SAVE>(p, c, n_tiles, smem); break;
+    default: run_fp8<F8_MAXRB, SAVE>(p, c, n_tiles, smem); break;
   }
 }
 
@@ -427,8 +429,12 @@ hipError_t launch_fp8_gemm(const GemmProblem& p, int tile_rows, int64_t max_rows
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7ffffff0) return hipErrorInvalidValue;
   blocks = (blocks + 7) / 8 * 8;
-  hipLaunchKernelGGL(fp8_gemm_kernel, dim3((unsigned)blocks), dim3(64 * F8_WAVES), 0, s, p,
-                     n_tiles, (int)(mt_bound * n_tiles), tile_rows);
+  if (p.C2)
+    hipLaunchKernelGGL(fp8_gemm_kernel<true>, dim3((unsigned)blocks), dim3(64 * F8_WAVES), 0, s,
+                       p, n_tiles, (int)(mt_bound * n_tiles), tile_rows);
+  else
+    hipLaunchKernelGGL(fp8_gemm_kernel<false>, dim3((unsigned)blocks), dim3(64 * F8_WAVES), 0, s,
+                       p, n_tiles, (int)(mt_bound * n_tiles), tile_rows);
   return hipGetLastError();
 }
 

@@ -73,7 +73,7 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int WTN = BN / WAVES_N;
   constexpr int CB = WTN / 32;
-  constexpr bool SWIGLU = (EPI == kSwiGLU_BF16);
+  constexpr bool SWIGLU = is_swiglu_bf16(EPI);
   constexpr int HB = CB / 2;
   constexpr int NAc = NA > 0 ? NA : 1;
   constexpr int SLOT_A = BM * ROWB, SLOT_B = BN * ROWB;  // bytes per stage
@@ -318,6 +318,31 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
     __builtin_amdgcn_wave_barrier();
+    if constexpr (EPI == kSwiGLU_BF16_ACT) {  // pre-activations: gate to C2[:, n], up to C2[:, Nout + n]
+      bf16_t* __restrict__ C2 = static_cast<bf16_t*>(p.C2);
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+#pragma unroll
+        for (int j = 0; j < OC / 32; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            ot[(8 * (v >> 2) + lrow4 + (v & 3)) * OS + j * 32 + lcol] =
+                f32_to_bf16(acc[i][j + part * (SWIGLU ? HB : 0)][v]);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = lane; q < 32 * CH; q += 64) {
+          const int r = q / CH, ch = q - r * CH;
+          const int grow = grow0 + r;
+          const int gcol = gcol0 + ch * 8;
+          if (grow < c.m_end && gcol < p.Nout)
+            *reinterpret_cast<u32x4_t*>(&C2[(int64_t)grow * p.ldc2 + part * p.Nout + gcol]) =
+                *reinterpret_cast<const u32x4_t*>(&ot[r * OS + ch * 8]);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
   }
 }
 
@@ -327,7 +352,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void mfma_gemm_kernel(Ge
                                                                                int total_bound) {
   constexpr int WTM = BM / WAVES_M;
   constexpr int RB = WTM / 32;
-  constexpr bool SWIGLU = (EPI == kSwiGLU_BF16);
+  constexpr bool SWIGLU = is_swiglu_bf16(EPI);
   static_assert((BM / WAVES_M) % 32 == 0 && (BN / WAVES_N) % 32 == 0, "wave tile");
   static_assert(!SWIGLU || ((BN / WAVES_N) / 32) % 2 == 0, "SwiGLU needs gate and up blocks");
   // one LDS block: the ring of stages, reused by the epilogue
@@ -356,7 +381,7 @@ __global__ __launch_bounds__(64 * WAVES_M * WAVES_N, 1) void mfma_gemm_kernel(Ge
 template <int EPI, int BM, int BN, int WM, int WN>
 hipError_t launch_cfg(const GemmProblem& p, int64_t max_rows, hipStream_t s) {
   static_assert(BM / WM / 32 <= 4, "at most four row blocks per wavefront");
-  const int n_tiles = (EPI == kSwiGLU_BF16) ? p.Nout / (BN / 2) : (p.Nout + BN - 1) / BN;
+  const int n_tiles = is_swiglu_bf16(EPI) ? p.Nout / (BN / 2) : (p.Nout + BN - 1) / BN;
   int64_t mt_bound;
   if (p.tile_prefix) {
     mt_bound = (max_rows + (int64_t)p.G * (BM - 1)) / BM;
@@ -379,6 +404,9 @@ hipError_t launch_epi(const GemmProblem& p, int epi, int64_t max_rows, hipStream
     case kStoreF32: return launch_cfg<kStoreF32, BM, BN, WM, WN>(p, max_rows, s);
     case kStoreBF16: return launch_cfg<kStoreBF16, BM, BN, WM, WN>(p, max_rows, s);
     case kSwiGLU_BF16: return launch_cfg<kSwiGLU_BF16, BM, BN, WM, WN>(p, max_rows, s);
+    case kSwiGLU_BF16_ACT:
+      if (!p.C2) return hipErrorInvalidValue;
+      return launch_cfg<kSwiGLU_BF16_ACT, BM, BN, WM, WN>(p, max_rows, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -394,7 +422,7 @@ int mfma_tile_rows(int64_t expected_rows_per_group) {
 hipError_t launch_mfma_gemm(const GemmProblem& p, int epilogue, int tile_rows, int64_t max_rows,
                             hipStream_t s) {
   if (p.K % BKS != 0 || p.a_kwrap % BKS != 0) return hipErrorInvalidValue;
-  if (epilogue == kSwiGLU_BF16 && tile_rows != 32 && p.Nout % 128 != 0) return hipErrorInvalidValue;
+  if (is_swiglu_bf16(epilogue) && tile_rows != 32 && p.Nout % 128 != 0) return hipErrorInvalidValue;
   if (tile_rows == 256) return launch_epi<256, 256, 2, 4>(p, epilogue, max_rows, s);
   if (tile_rows == 128) return launch_epi<128, 256, 2, 4>(p, epilogue, max_rows, s);
   if (tile_rows == 32) return launch_epi<32, 256, 1, 4>(p, epilogue, max_rows, s);

@@ -62,7 +62,7 @@ template <typename CFG, int EPI, int NA>
 __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord& c,
                                            int n_tiles, int split, char* __restrict__ smem) {
   constexpr int PK_DEPTH = CFG::DEPTH, PK_DIST = CFG::DIST, PK_SLOT = CFG::SLOT;
-  constexpr bool SWIGLU = (EPI == kSwiGLU_BF16);
+  constexpr bool SWIGLU = is_swiglu_bf16(EPI);
   const int tid = threadIdx.x;
   // the wavefront index is uniform: keep it in a scalar register, so LDS
   // destinations of the direct loads (M0) need no per-load readfirstlane
@@ -266,7 +266,7 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
       }
     return;
   }
-  store_bf16_tile<NA, SWIGLU>(acc, smem, wave, lane, c, p);
+  store_bf16_tile<NA, SWIGLU, EPI == kSwiGLU_BF16_ACT>(acc, smem, wave, lane, c, p);
 }
 
 template <typename CFG, int EPI>
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(64 * PK_WAVES, CFG::OCC) void packed_gemm_kernel(Ge
                                                                              int n_tiles,
                                                                              int total_bound,
                                                                              int tile_rows) {
-  constexpr bool SWIGLU = (EPI == kSwiGLU_BF16);
+  constexpr bool SWIGLU = is_swiglu_bf16(EPI);
   __shared__ __attribute__((aligned(16))) char smem[CFG::DEPTH * CFG::SLOT];
   int logical =
       xcd_logical_tile(p.tile_prefix ? p.tile_prefix[p.G] * n_tiles : total_bound);
@@ -425,7 +425,7 @@ hipError_t launch_packed_gemm(const GemmProblem& p, int epilogue, int tile_rows,
   if (p.K < PK_BKS || p.K % PK_BKS != 0 || p.a_kwrap % PK_BKS != 0) return hipErrorInvalidValue;
   if (tile_rows < 32 || tile_rows > kPackedMaxTileRows || tile_rows % 32 != 0)
     return hipErrorInvalidValue;
-  const bool swiglu = (epilogue == kSwiGLU_BF16);
+  const bool swiglu = is_swiglu_bf16(epilogue);
   if (swiglu && p.Nout % (kPackedPanel / 2) != 0) return hipErrorInvalidValue;
   const int n_tiles = swiglu ? p.Nout / (kPackedPanel / 2) : (p.Nout + kPackedPanel - 1) / kPackedPanel;
   // the down GEMM runs the two-workgroups-per-CU configuration
@@ -460,6 +460,11 @@ hipError_t launch_packed_gemm(const GemmProblem& p, int epilogue, int tile_rows,
     case kSwiGLU_BF16:
       hipLaunchKernelGGL((packed_gemm_kernel<PkWide, kSwiGLU_BF16>), grid, block, 0, s, p, n_tiles,
                          total, tile_rows);
+      break;
+    case kSwiGLU_BF16_ACT:
+      if (!p.C2) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((packed_gemm_kernel<PkWide, kSwiGLU_BF16_ACT>), grid, block, 0, s, p,
+                         n_tiles, total, tile_rows);
       break;
     default: return hipErrorInvalidValue;
   }

@@ -89,8 +89,10 @@ __device__ __forceinline__ void ring_barrier() {
 // and the output is silu(gate) * up (32 columns per wavefront); otherwise 64
 // columns.  Values go through a wavefront-private LDS tile (smem must hold
 // 4 x 32 rows of padded columns), one 32-row block at a time, so that global
-// stores are whole 16-byte row pieces.
-template <int NA, bool SWIGLU>
+// stores are whole 16-byte row pieces.  SAVE (SwiGLU only) also stores the
+// pre-activations gate and up (bf16) the same way, to p.C2 columns n and
+// Nout + n.
+template <int NA, bool SWIGLU, bool SAVE = false>
 __device__ __forceinline__ void store_bf16_tile(const f32x16_t (&acc)[NA][2], char* smem,
                                                 int wave, int lane, const TileCoord& c,
                                                 const GemmProblem& p) {
@@ -132,6 +134,28 @@ __device__ __forceinline__ void store_bf16_tile(const f32x16_t (&acc)[NA][2], ch
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
     __builtin_amdgcn_wave_barrier();
+    if constexpr (SWIGLU && SAVE) {
+      bf16_t* __restrict__ C2 = static_cast<bf16_t*>(p.C2);
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {  // gate, then up
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          ot[(8 * (v >> 2) + lrow4 + (v & 3)) * OS + lcol] = f32_to_bf16(acc[i][part][v]);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = lane; q < 32 * CH; q += 64) {
+          const int r = q / CH, ch = q - r * CH;
+          const int grow = grow0 + r;
+          const int gcol = gcol0 + ch * 8;
+          if (grow < c.m_end && gcol < p.Nout)
+            *reinterpret_cast<u32x4_t*>(&C2[(int64_t)grow * p.ldc2 + part * p.Nout + gcol]) =
+                *reinterpret_cast<const u32x4_t*>(&ot[r * OS + ch * 8]);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
   }
 }
 

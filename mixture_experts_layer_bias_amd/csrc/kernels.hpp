@@ -74,9 +74,17 @@ struct GemmProblem {
   // C + s * c_split_stride (0 or 1: one part, C itself)
   int k_splits;
   int64_t c_split_stride;
+  // kSwiGLU_BF16_ACT (and the block-FP8 GEMM when set): the pre-activations
+  // in bf16, a = x W_gate^T to C2[row][col] and u = x W_up^T to C2[row][Nout + col]
+  void* C2;
+  int64_t ldc2;
 };
 
-enum Epilogue { kStoreF32 = 0, kStoreBF16 = 1, kSwiGLU_BF16 = 2, kSwiGLU_F32 = 3 };
+// kSwiGLU_BF16_ACT: kSwiGLU_BF16 that also stores the pre-activations to C2
+// (a separate instantiation, so the plain SwiGLU kernels are unchanged).
+enum Epilogue { kStoreF32 = 0, kStoreBF16 = 1, kSwiGLU_BF16 = 2, kSwiGLU_F32 = 3,
+                kSwiGLU_BF16_ACT = 4 };
+constexpr bool is_swiglu_bf16(int epi) { return epi == kSwiGLU_BF16 || epi == kSwiGLU_BF16_ACT; }
 
 // bf16 MFMA path (gemm_mfma.hip).  `tile_rows` selects the row-tile variant
 // (128 for many rows per expert, 32 for a few); the scan must have used it.
@@ -152,9 +160,10 @@ struct TrArgsHost {
   int ngroups;
 };
 hipError_t launch_transpose(const TrArgsHost& a, hipStream_t s);
-hipError_t launch_swiglu_bwd(const float* A, const float* U, const float* Q, const float* row_gate,
-                             const int32_t* offsets, int N, int I, int64_t max_rows, bf16_t* dau,
-                             bf16_t* H, float* row_dg, hipStream_t s);
+hipError_t launch_swiglu_bwd(const void* A, const void* U, int64_t ld_au, bool au_bf16,
+                             const float* Q, const float* row_gate, const int32_t* offsets, int N,
+                             int I, int64_t max_rows, bf16_t* dau, bf16_t* H, float* row_dg,
+                             hipStream_t s);
 hipError_t launch_token_bwd(const bf16_t* x, const bf16_t* dy, const float* logits,
                             const int32_t* idx, const float* gate, const int32_t* pos,
                             const float* row_dg, const float* dxg, int64_t T, int d, int E, int K,

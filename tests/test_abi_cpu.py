@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_zc_abi_version() == 1
+    assert lib.moe_zc_abi_version() == 2
     for code in range(5):
         assert lib.moe_zc_status_string(code)
     assert lib.moe_zc_status_string(99) == b"unknown status"
@@ -197,3 +197,24 @@ def test_backward_sizes_and_validation(lib):
     assert tr(FAKE, FAKE, FAKE, -1, 128, 128, FAKE, FAKE, None) == INVALID
     assert tr(FAKE, FAKE, FAKE, 2, 128, 100, FAKE, FAKE, None) == UNSUPPORTED
     assert tr(FAKE, FAKE, FAKE, 2, 128, 128, None, FAKE, None) == INVALID
+
+
+def test_saved_preactivations_validation(lib):
+    """aux.act (ABI version 2) is a bf16 output: an f32 forward refuses it, and
+    a misaligned buffer is rejected; all before anything is enqueued."""
+    aux = _lib.MoeZcAux()
+    aux.act = 1 << 20
+    T, d, I, N, Z, K = 64, 128, 128, 8, 4, 3
+    nb = lib.moe_zc_workspace_size(T, d, I, N, Z, K, F32)
+    assert lib.moe_zc_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, T, d, I, N, Z, K,
+                              F32, ctypes.byref(aux), FAKE, nb, None) == UNSUPPORTED
+    aux.act = (1 << 20) + 2
+    nb = lib.moe_zc_workspace_size(T, d, I, N, Z, K, BF16)
+    assert lib.moe_zc_forward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, T, d, I, N, Z, K,
+                              BF16, ctypes.byref(aux), FAKE, nb, None) == INVALID
+    # backward: without act the row-major gate / up weights are required
+    fwd = _lib.MoeZcAux(*(1 << 20,) * 7, None, None)
+    nbb = lib.moe_zc_backward_workspace_size(T, d, I, N, Z, K)
+    assert lib.moe_zc_backward(FAKE, FAKE, None, None, FAKE, FAKE, ctypes.byref(fwd), FAKE, FAKE,
+                               FAKE, FAKE, FAKE, FAKE, T, d, I, N, Z, K, FAKE, nbb,
+                               None) == INVALID

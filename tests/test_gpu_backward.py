@@ -140,3 +140,110 @@ def test_backward_rejects_f32():
     with pytest.raises(ValueError):
         m.moe_zc_backward(inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], None, aux,
                           inp["x"], w.N, w.Z, w.K, w.I)
+
+
+# ---- pre-activations saved by the forward --------------------------------------
+def _act_reference(w, inp, aux, fp8=False):
+    """a | u of every grouped row in fp64 from the GPU's grouping (perm,
+    offsets), on the dequantized FP8 operands when ``fp8``."""
+    from oracle import mx as omx
+    x = inp["x"].float().cpu().double().numpy()
+    if fp8:
+        x = omx.mx_dequantize(*omx.mx_quantize(x, axis=-1), axis=-1)
+    perm = aux["perm"].cpu().numpy()
+    off = aux["offsets"].cpu().numpy()
+    ref = np.zeros((int(off[w.N]), 2 * w.I))
+    for e in range(w.N):
+        rows = slice(int(off[e]), int(off[e + 1]))
+        if off[e + 1] == off[e]:
+            continue
+        wg = inp["w_gate"][e].float().cpu().double().numpy()
+        wu = inp["w_up"][e].float().cpu().double().numpy()
+        if fp8:
+            wg = omx.mx_dequantize(*omx.mx_quantize(wg, axis=-1), axis=-1)
+            wu = omx.mx_dequantize(*omx.mx_quantize(wu, axis=-1), axis=-1)
+        xe = x[perm[rows]]
+        ref[rows, : w.I] = xe @ wg.T
+        ref[rows, w.I:] = xe @ wu.T
+    return ref
+
+
+@pytest.mark.parametrize("name", ["T65_ragged", "few_rows_32_tiles", "rows_256_tiles", "wide_d"])
+def test_forward_saves_preactivations(name):
+    """Saving a | u leaves y unchanged bit for bit, the saved values match fp64
+    (bf16 storage bar), and the packed and row-major forwards save the same
+    bits; the block-FP8 forward saves its own products."""
+    w = _edge(**CASES[name])
+    print(f"[act {name}] {w.describe()}", flush=True)
+    inp = make_inputs(w, device=DEV)
+    keys = m.AUX_KEYS + ("act",)
+    packed = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    outs = {}
+    for kind in ("rowmajor", "packed", "plain"):
+        aux = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV, keys=keys if kind != "plain" else m.AUX_KEYS,
+                          I=w.I)
+        if kind == "rowmajor":
+            y = m.moe_zc_forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"],
+                                 inp["w_up"], inp["w_down"], w.N, w.Z, w.K, aux=aux)
+        else:
+            y = m.moe_zc_forward_packed(inp["x"], inp["w_router"], inp["bias"], packed[0],
+                                        packed[1], w.N, w.Z, w.K, w.I, aux=aux)
+        torch.cuda.synchronize()
+        outs[kind] = (y, aux)
+    assert torch.equal(outs["plain"][0], outs["packed"][0]), "saving a | u changed y"
+    assert torch.equal(outs["rowmajor"][0], outs["packed"][0])
+    S = int(outs["packed"][1]["offsets"][w.N].item())
+    act_p = outs["packed"][1]["act"][:S]
+    assert torch.equal(act_p, outs["rowmajor"][1]["act"][:S]), "row-major and packed a | u differ"
+    ref = _act_reference(w, inp, outs["packed"][1])
+    err = np.abs(act_p.float().cpu().double().numpy() - ref).max()
+    assert err <= 1e-2 * np.abs(ref).max(), f"a | u off by {err}"
+    if w.d % 128 == 0:
+        fp8w = m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"])
+        y_plain = m.moe_zc_forward_packed_fp8(inp["x"], inp["w_router"], inp["bias"], fp8w,
+                                              packed[1], w.N, w.Z, w.K, w.I)
+        aux = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV, keys=keys, I=w.I)
+        y8 = m.moe_zc_forward_packed_fp8(inp["x"], inp["w_router"], inp["bias"], fp8w, packed[1],
+                                         w.N, w.Z, w.K, w.I, aux=aux)
+        torch.cuda.synchronize()
+        assert torch.equal(y8, y_plain), "saving a | u changed the FP8 forward's y"
+        ref8 = _act_reference(w, inp, aux, fp8=True)
+        err8 = np.abs(aux["act"][:S].float().cpu().double().numpy() - ref8).max()
+        assert err8 <= 1e-2 * np.abs(ref8).max(), f"FP8 a | u off by {err8}"
+
+
+def gpu_forward_backward_saved(w, inp, dy):
+    """Packed forward saving a | u, then the backward without the row-major
+    gate / up weights."""
+    keys = m.AUX_KEYS + ("act",)
+    aux = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV, keys=keys, I=w.I)
+    tr = None
+    gu = dn = None
+    if w.N > 0:
+        gu, dn = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+        tr = m.moe_zc_transpose_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    m.moe_zc_forward_packed(inp["x"], inp["w_router"], inp["bias"], gu, dn, w.N, w.Z, w.K, w.I,
+                            aux=aux)
+    g = m.moe_zc_backward(inp["x"], inp["w_router"], None, None, tr, aux, dy, w.N, w.Z, w.K, w.I)
+    torch.cuda.synchronize()
+    return aux, g
+
+
+@pytest.mark.parametrize("name", ["T1", "T65_ragged", "Z0", "N0_all_identity",
+                                  "few_rows_32_tiles", "rows_256_tiles", "wide_d",
+                                  "many_experts"])
+def test_backward_from_saved_preactivations(name):
+    w = _edge(**CASES[name])
+    print(f"[backward saved {name}] {w.describe()}", flush=True)
+    inp = make_inputs(w, device=DEV)
+    dy = make_upstream_grad(w, DEV)
+    aux, g = gpu_forward_backward_saved(w, inp, dy)
+    print(name, compare(w, inp, dy, aux, g), flush=True)
+
+
+def test_backward_from_saved_preactivations_mid():
+    w = get_workload("mid")
+    inp = make_inputs(w, device=DEV)
+    dy = make_upstream_grad(w, DEV)
+    aux, g = gpu_forward_backward_saved(w, inp, dy)
+    print("mid saved", compare(w, inp, dy, aux, g), flush=True)
