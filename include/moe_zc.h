@@ -286,12 +286,23 @@ moe_zc_status moe_zc_quantize_mx(const void* x, int64_t rows, int64_t d,
  * Requires dt = bf16 and T * d < 2^31 (else MOE_ZC_ERR_UNSUPPORTED); other
  * limits as moe_zc_forward. */
 
-/* Transposed copies of the expert weights the backward reads (device, bf16):
- *   w_gate, w_up [n, I, d], w_down [n, d, I] (16-byte aligned)
- *   -> w_gate_up_t [n, d, 2I]: row j is (W_gate[:, j], W_up[:, j]);
- *      w_down_t    [n, I, d]:  w_down_t[e][i][j] = w_down[e][j][i].
- * Outputs are caller-owned and 16-byte aligned.  Enqueued on `stream`;
- * n_experts = 0 does nothing.  Shape rules of moe_zc_pack_expert_weights. */
+/* Bytes of ONE expert's transposed weights for the backward (host only):
+ * *gate_up_t_bytes for [W_gate; W_up]^T ([d, 2I]) and *down_t_bytes for
+ * W_down^T ([I, d]), each in the packed layout of moe_zc_pack_expert_weights'
+ * down projection (rows padded to 256).  Shape rules of
+ * moe_zc_pack_expert_weights (bf16). */
+moe_zc_status moe_zc_transposed_expert_bytes(int64_t d, int64_t I,
+                                             size_t* gate_up_t_bytes,
+                                             size_t* down_t_bytes);
+
+/* The transposed expert weights the backward reads, packed (device, bf16):
+ *   w_gate, w_up [n, I, d], w_down [n, d, I] (row-major, 16-byte aligned)
+ *   -> w_gate_up_t: n blocks of gate_up_t_bytes holding M[e][j][k] =
+ *      W_gate[e][k][j] (k < I), W_up[e][k - I][j] (k >= I), j < d;
+ *      w_down_t: n blocks of down_t_bytes holding W_down[e]^T [I, d];
+ *   both in the opaque packed layout (sizes: moe_zc_transposed_expert_bytes).
+ * Outputs are caller-owned and 16-byte aligned.  Built once, like the packed
+ * forward weights; enqueued on `stream`; n_experts = 0 does nothing. */
 moe_zc_status moe_zc_transpose_expert_weights(const void* w_gate,
                                               const void* w_up,
                                               const void* w_down,

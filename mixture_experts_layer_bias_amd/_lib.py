@@ -26,7 +26,7 @@ EXPORTS = ("moe_zc_workspace_size", "moe_zc_forward", "moe_zc_packed_expert_byte
            "moe_zc_packed_fp8_expert_bytes", "moe_zc_pack_expert_weights_fp8",
            "moe_zc_workspace_size_fp8", "moe_zc_forward_packed_fp8", "moe_zc_quantize_mx",
            "moe_zc_transpose_expert_weights", "moe_zc_backward_workspace_size",
-           "moe_zc_backward")
+           "moe_zc_backward", "moe_zc_transposed_expert_bytes")
 
 
 class MoeZcAux(ctypes.Structure):
@@ -84,6 +84,9 @@ def load() -> ctypes.CDLL:
     lib.moe_zc_quantize_mx.restype = ctypes.c_int
     lib.moe_zc_transpose_expert_weights.argtypes = [vp, vp, vp, i32, i64, i64, vp, vp, vp]
     lib.moe_zc_transpose_expert_weights.restype = ctypes.c_int
+    lib.moe_zc_transposed_expert_bytes.argtypes = [i64, i64, ctypes.POINTER(sz),
+                                                   ctypes.POINTER(sz)]
+    lib.moe_zc_transposed_expert_bytes.restype = ctypes.c_int
     lib.moe_zc_backward_workspace_size.argtypes = [i64, i64, i64, i32, i32, i32]
     lib.moe_zc_backward_workspace_size.restype = sz
     lib.moe_zc_backward.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(MoeZcAux), vp, vp, vp,

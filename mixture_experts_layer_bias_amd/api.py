@@ -419,12 +419,22 @@ def moe_zc_backward_workspace_size(T: int, d: int, I: int, N: int, Z: int, K: in
     return int(_lib.load().moe_zc_backward_workspace_size(T, d, I, N, Z, K))
 
 
+def moe_zc_transposed_expert_bytes(d: int, I: int):
+    """(gate_up_t_bytes, down_t_bytes) of one expert's packed transposed weights."""
+    gu, dn = ctypes.c_size_t(), ctypes.c_size_t()
+    code = _lib.load().moe_zc_transposed_expert_bytes(d, I, ctypes.byref(gu), ctypes.byref(dn))
+    if code != _lib.MOE_ZC_OK:
+        raise MoeZcError(code, "moe_zc_transposed_expert_bytes")
+    return int(gu.value), int(dn.value)
+
+
 def moe_zc_transpose_expert_weights(w_gate: torch.Tensor, w_up: torch.Tensor,
                                     w_down: torch.Tensor,
                                     w_gate_up_t: Optional[torch.Tensor] = None,
                                     w_down_t: Optional[torch.Tensor] = None):
-    """Transposed bf16 expert weights for moe_zc_backward: returns
-    (w_gate_up_t [n, d, 2I], w_down_t [n, I, d])."""
+    """Packed transposed expert weights for moe_zc_backward: returns
+    (w_gate_up_t, w_down_t), uint8 tensors of n * gate_up_t_bytes and
+    n * down_t_bytes ([W_gate; W_up]^T and W_down^T per expert)."""
     lib = _lib.load()
     n, I, d = w_gate.shape
     dev = w_gate.device
@@ -433,12 +443,13 @@ def moe_zc_transpose_expert_weights(w_gate: torch.Tensor, w_up: torch.Tensor,
     _need(w_gate, "w_gate", torch.bfloat16, (n, I, d), dev)
     _need(w_up, "w_up", torch.bfloat16, (n, I, d), dev)
     _need(w_down, "w_down", torch.bfloat16, (n, d, I), dev)
+    gb, db = moe_zc_transposed_expert_bytes(d, I)
     if w_gate_up_t is None:
-        w_gate_up_t = torch.empty(n, d, 2 * I, dtype=torch.bfloat16, device=dev)
+        w_gate_up_t = torch.empty(n * gb, dtype=torch.uint8, device=dev)
     if w_down_t is None:
-        w_down_t = torch.empty(n, I, d, dtype=torch.bfloat16, device=dev)
-    _need(w_gate_up_t, "w_gate_up_t", torch.bfloat16, (n, d, 2 * I), dev)
-    _need(w_down_t, "w_down_t", torch.bfloat16, (n, I, d), dev)
+        w_down_t = torch.empty(n * db, dtype=torch.uint8, device=dev)
+    _need(w_gate_up_t, "w_gate_up_t", torch.uint8, (n * gb,), dev)
+    _need(w_down_t, "w_down_t", torch.uint8, (n * db,), dev)
     code = lib.moe_zc_transpose_expert_weights(_ptr(w_gate), _ptr(w_up), _ptr(w_down), n, d, I,
                                                _ptr(w_gate_up_t), _ptr(w_down_t), _stream(dev))
     if code != _lib.MOE_ZC_OK:
@@ -488,8 +499,9 @@ def moe_zc_backward(x: torch.Tensor, w_router: torch.Tensor, w_gate: Optional[to
         if act is None or w_up is not None:
             _need(w_up, "w_up", torch.bfloat16, (N, I, d), dev)
         gut, dnt = transposed
-        _need(gut, "w_gate_up_t", torch.bfloat16, (N, d, 2 * I), dev)
-        _need(dnt, "w_down_t", torch.bfloat16, (N, I, d), dev)
+        gb, db = moe_zc_transposed_expert_bytes(d, I)
+        _need(gut, "w_gate_up_t", torch.uint8, (N * gb,), dev)
+        _need(dnt, "w_down_t", torch.uint8, (N * db,), dev)
         weights = (w_gate, w_up, gut, dnt)
     else:
         weights = (None, None, None, None)

@@ -534,21 +534,25 @@ moe_zc_status moe_zc_transpose_expert_weights(const void* w_gate, const void* w_
   if (n_experts < 0) return MOE_ZC_ERR_INVALID;
   if (n_experts == 0) return MOE_ZC_OK;
   if (!w_gate || !w_up || !w_down || !w_gate_up_t || !w_down_t) return MOE_ZC_ERR_INVALID;
-  // w_gate_up_t[e][j][i] = w_gate[e][i][j] (i < I), w_up[e][i - I][j] (i >= I)
-  for (int half = 0; half < 2; ++half) {
-    TrArgsHost a = tr(half ? w_up : w_gate, d, w_gate_up_t, 2 * I, (int)d, I, I);
-    a.src_bstride = I * d;
-    a.dst_bstride = d * 2 * I;
-    a.dst_col0 = half * I;
-    a.batch = n_experts;
-    MOE_ZC_TRY(launch_transpose(a, stream));
-  }
-  // w_down_t[e][i][j] = w_down[e][j][i]
-  TrArgsHost a = tr(w_down, I, w_down_t, d, (int)I, d, d);
-  a.src_bstride = d * I;
-  a.dst_bstride = I * d;
-  a.batch = n_experts;
-  MOE_ZC_TRY(launch_transpose(a, stream));
+  if (!aligned16(w_gate_up_t) || !aligned16(w_down_t)) return MOE_ZC_ERR_INVALID;
+  const bf16_t* wg = static_cast<const bf16_t*>(w_gate);
+  const bf16_t* wu = static_cast<const bf16_t*>(w_up);
+  const bf16_t* wd = static_cast<const bf16_t*>(w_down);
+  // [W_gate; W_up]^T as rows j < d over k < 2I; W_down^T as rows i < I over k < d
+  MOE_ZC_TRY(launch_pack_transposed(wg, wu, static_cast<bf16_t*>(w_gate_up_t), n_experts, (int)d,
+                                    (int)(2 * I), (int)I, (int)d, I * d, stream));
+  MOE_ZC_TRY(launch_pack_transposed(wd, wd, static_cast<bf16_t*>(w_down_t), n_experts, (int)I,
+                                    (int)d, (int)d, (int)I, d * I, stream));
+  return MOE_ZC_OK;
+}
+
+moe_zc_status moe_zc_transposed_expert_bytes(int64_t d, int64_t I, size_t* gate_up_t_bytes,
+                                             size_t* down_t_bytes) {
+  if (!gate_up_t_bytes || !down_t_bytes) return MOE_ZC_ERR_INVALID;
+  const moe_zc_status st = check_pack_shape(d, I, MOE_ZC_BF16);
+  if (st != MOE_ZC_OK) return st;
+  *gate_up_t_bytes = (size_t)packed_bytes(d, 2 * I, false);
+  *down_t_bytes = (size_t)packed_bytes(I, d, false);
   return MOE_ZC_OK;
 }
 
@@ -611,8 +615,9 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
       p.B0 = w_up; p.C = F(pl.U);
       MOE_ZC_TRY(launch_mfma_gemm(p, kStoreF32, s.ffn_tile_rows, s.smax, stream));
     }
-    p.A = dy; p.B0 = w_down_t; p.C = F(pl.Q);
-    MOE_ZC_TRY(launch_mfma_gemm(p, kStoreF32, s.ffn_tile_rows, s.smax, stream));
+    // q on the packed kernel: B = the packed W_down^T (rows i < I over k < d)
+    p.A = dy; p.B0 = w_down_t; p.C = F(pl.Q); p.ldb = 0; p.b_group_stride = 0;
+    MOE_ZC_TRY(launch_packed_gemm(p, kStoreF32, s.ffn_tile_rows, s.smax, stream));
     // SwiGLU backward: da | du, h, and the gate gradient of every grouped row
     if (act)
       MOE_ZC_TRY(launch_swiglu_bwd(act, static_cast<const bf16_t*>(act) + I, 2 * I, true,
@@ -622,12 +627,13 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
       MOE_ZC_TRY(launch_swiglu_bwd(F(pl.A), F(pl.U), I, false, F(pl.Q), row_gate, offsets, N,
                                    (int)I, s.smax, B(pl.dau), B(pl.H), row_dg, stream));
     // rows of dx from the experts: [da | du] [W_gate ; W_up]
+    // (packed [W_gate; W_up]^T: rows j < d over k < 2I)
     GemmProblem q{};
     q.A = B(pl.dau); q.lda = 2 * I; q.a_kwrap = (int)(2 * I); q.K = (int)(2 * I);
-    q.B0 = w_gate_up_t; q.ldb = 2 * I; q.b_group_stride = d * 2 * I;
+    q.B0 = w_gate_up_t;
     q.C = dxg; q.ldc = d; q.Nout = (int)d;
     q.row_offsets = offsets; q.tile_prefix = tiles; q.G = N; q.M = 0;
-    MOE_ZC_TRY(launch_mfma_gemm(q, kStoreF32, s.ffn_tile_rows, s.smax, stream));
+    MOE_ZC_TRY(launch_packed_gemm(q, kStoreF32, s.ffn_tile_rows, s.smax, stream));
     // weight gradients: operands transposed into expert-blocked [dim][rows_e
     // rounded up to 64] blocks (zeros in the padding columns)
     auto blocked = [&](const void* src, int64_t src_ld, void* dst, int64_t dim) {

@@ -351,6 +351,49 @@ __global__ __launch_bounds__(256) void pack_weights_kernel(const bf16_t* __restr
   }
 }
 
+// The packed layout of a transposed operand, gathered from the untransposed
+// weights: packed row r (an output column of the GEMM), reduction index k
+// holds src[k][r] with src = w0 for k < k_split and w1 (at k - k_split)
+// otherwise, rows src_ld elements long.  For the backward: W_gate | W_up as
+// [d][2I] (k_split = I, src_ld = d) and W_down as [I][d] (k_split = d,
+// src_ld = I).  Eight k of one row are eight strided loads; consecutive lanes
+// take consecutive rows, so each load instruction reads whole row segments.
+// One workgroup per 32 KB block, as pack_weights_kernel; runs once, at load.
+__global__ __launch_bounds__(256) void pack_transposed_kernel(const bf16_t* __restrict__ w0,
+                                                              const bf16_t* __restrict__ w1,
+                                                              bf16_t* __restrict__ out, int rows,
+                                                              int K, int k_split, int src_ld,
+                                                              int n_panels,
+                                                              int64_t group_stride) {
+  const int nk = K / PK_BKS;
+  const int64_t b = blockIdx.x;
+  const int64_t per_group = (int64_t)n_panels * nk;
+  const int64_t g = b / per_group;
+  const int rem = (int)(b - g * per_group);
+  const int nt = rem / nk, kt = rem - nt * nk;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int o = (threadIdx.x + 256 * i) * 16;
+    int row, k;
+    bool up;
+    packed_piece(o, false, row, k, up);
+    row += nt * kPackedPanel;
+    k += kt * PK_BKS;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (row < rows) {
+      const bool second = k >= k_split;  // eight k never straddle k_split (a multiple of 8)
+      const bf16_t* src = (second ? w1 : w0) + g * group_stride +
+                          (int64_t)(second ? k - k_split : k) * src_ld + row;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)src[(int64_t)(2 * e) * src_ld] |
+               ((uint32_t)src[(int64_t)(2 * e + 1) * src_ld] << 16);
+    }
+    u32x4_t v = {w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(out) + b * PK_BLOCK + o) = v;
+  }
+}
+
 // fp32 W_router [E, d] -> packed [E, 2d] bf16 split: k < d holds bf16(w),
 // k >= d holds bf16(w - bf16(w)) of column k - d; rows past E are zero.
 // w = hi + lo + r with |r| <= 2^-17 |w|, so x (bf16) times [hi | lo] on MFMA
@@ -394,6 +437,19 @@ int64_t packed_bytes(int64_t rows, int64_t K, bool swiglu) {
   const int64_t panels = swiglu ? rows / (kPackedPanel / 2)
                                 : (rows + kPackedPanel - 1) / kPackedPanel;
   return panels * (K / PK_BKS) * (int64_t)PK_BLOCK;
+}
+
+hipError_t launch_pack_transposed(const bf16_t* w0, const bf16_t* w1, bf16_t* out, int groups,
+                                  int rows, int K, int k_split, int src_ld, int64_t group_stride,
+                                  hipStream_t s) {
+  if (K % PK_BKS != 0 || k_split % 8 != 0 || k_split <= 0) return hipErrorInvalidValue;
+  const int n_panels = (rows + kPackedPanel - 1) / kPackedPanel;
+  const int64_t blocks = (int64_t)groups * n_panels * (K / PK_BKS);
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_transposed_kernel, dim3((unsigned)blocks), dim3(256), 0, s, w0, w1, out,
+                     rows, K, k_split, src_ld, n_panels, group_stride);
+  return hipGetLastError();
 }
 
 hipError_t launch_pack_weights(const bf16_t* w0, const bf16_t* w1, bf16_t* out, int groups,

@@ -102,6 +102,12 @@ constexpr int kPackedMaxTileRows = 256;
 // units, gate and up together) by K.
 int64_t packed_bytes(int64_t rows, int64_t K, bool swiglu);
 // Row-major [groups][rows][K] (gate w0 and up w1 for SwiGLU) -> packed.
+// Packed layout (non-SwiGLU panels) of a transposed operand, gathered from the
+// untransposed weights: row r, reduction index k <- (k < k_split ? w0[k] :
+// w1[k - k_split])[r], source rows src_ld elements long.
+hipError_t launch_pack_transposed(const bf16_t* w0, const bf16_t* w1, bf16_t* out, int groups,
+                                  int rows, int K, int k_split, int src_ld, int64_t group_stride,
+                                  hipStream_t s);
 hipError_t launch_pack_weights(const bf16_t* w0, const bf16_t* w1, bf16_t* out, int groups,
                                int rows, int K, bool swiglu, hipStream_t s);
 // W_router fp32 [E, d] -> packed two-term bf16 split [E, 2d].

@@ -113,15 +113,23 @@ def test_backward_is_deterministic():
                                o[k].view(torch.int16 if k == "dx" else torch.int32)), k
 
 
-@pytest.mark.parametrize("n,d,I", [(3, 128, 256), (2, 320, 128)])
+@pytest.mark.parametrize("n,d,I", [(3, 128, 256), (2, 320, 128), (1, 512, 384)])
 def test_transpose_expert_weights(n, d, I):
+    """The packed transposes equal the packed layout (the down projection's,
+    checked byte for byte against its definition in test_gpu_packed) of
+    [W_gate; W_up]^T and W_down^T."""
+    from test_gpu_packed import _u16, pack_reference
     g = torch.Generator().manual_seed(7 * n + d)
     wg, wu = (torch.randn(n, I, d, generator=g).to(torch.bfloat16) for _ in range(2))
     wd = torch.randn(n, d, I, generator=g).to(torch.bfloat16)
     gut, dnt = m.moe_zc_transpose_expert_weights(wg.to(DEV), wu.to(DEV), wd.to(DEV))
     torch.cuda.synchronize()
-    assert torch.equal(gut.cpu(), torch.cat([wg, wu], dim=1).transpose(1, 2))
-    assert torch.equal(dnt.cpu(), wd.transpose(1, 2))
+    gb, db = m.moe_zc_transposed_expert_bytes(d, I)
+    assert gut.numel() == n * gb and dnt.numel() == n * db
+    ref_gu = pack_reference(_u16(torch.cat([wg, wu], dim=1).transpose(1, 2)), None, False)
+    ref_dn = pack_reference(_u16(wd.transpose(1, 2)), None, False)
+    assert np.array_equal(gut.cpu().numpy().reshape(n, -1), ref_gu)
+    assert np.array_equal(dnt.cpu().numpy().reshape(n, -1), ref_dn)
 
 
 def test_backward_empty_batch():
