@@ -279,10 +279,11 @@ moe_zc_status moe_zc_quantize_mx(const void* x, int64_t rows, int64_t d,
  *   chosen experts (0 elsewhere), p = softmax(l_t);
  *     dx_t += W_router^T dl_t,  dW_router += dl_t x_t^T
  *   The residual's gradient is dy itself and is not returned.
- * Precision: a, u and q are recomputed on bf16 MFMA with fp32 accumulation;
- * da, du and h are rounded to bf16 as operands of the following products
- * (fp32 accumulation); the router's dx term is fp32; dl is rounded to bf16
- * for dW_router; dx is accumulated in fp32 and rounded once to bf16.
+ * Precision: q (and a, u when not saved by the forward) come from bf16 MFMA
+ * with fp32 accumulation; da, du, h, g dy and dl are rounded to bf16 as
+ * operands of the following products (fp32 accumulation), and so is W_router
+ * in the router's dx term; dx is accumulated in fp32 and rounded once to
+ * bf16.
  * Requires dt = bf16 and T * d < 2^31 (else MOE_ZC_ERR_UNSUPPORTED); other
  * limits as moe_zc_forward. */
 

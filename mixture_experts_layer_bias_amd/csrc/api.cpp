@@ -311,16 +311,16 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 struct BwdPlan {
-  int64_t Sp, T64, E16;  // padded grouped columns, padded tokens, padded experts
+  int64_t Sp, T64, E64;  // padded grouped columns, padded tokens, padded experts
   size_t tiles, kofs, kofs_r, colrow, row_gate, row_dg, A, U, Q, dau, H, dxg, XT, ET, DAT, DUT,
-      HT, dl, dlT, xT, wrT, dx_acc, dx_r, total;
+      HT, dl, dlT, xT, wrT, wrP, dx_acc, dx_r, total;
 };
 
 BwdPlan make_bwd_plan(const Shape& s) {
   BwdPlan p{};
   p.Sp = round_up(s.smax + 64 * (int64_t)s.N, 64);
   p.T64 = round_up(s.T, 64);
-  p.E16 = round_up(s.E, 16);
+  p.E64 = round_up(s.E, 64);
   size_t at = 0;
   auto take = [&](size_t bytes) {
     const size_t here = at;
@@ -345,10 +345,11 @@ BwdPlan make_bwd_plan(const Shape& s) {
   p.DAT = take(I * (size_t)p.Sp * 2);
   p.DUT = take(I * (size_t)p.Sp * 2);
   p.HT = take(I * (size_t)p.Sp * 2);
-  p.dl = take((size_t)s.T * p.E16 * 4);
+  p.dl = take((size_t)s.T * p.E64 * 2);
   p.dlT = take((size_t)s.E * p.T64 * 2);
   p.xT = take(d * (size_t)p.T64 * 2);
-  p.wrT = take(d * (size_t)p.E16 * 4);
+  p.wrT = take(d * (size_t)p.E64 * 2);
+  p.wrP = take((size_t)packed_bytes(s.d, p.E64, false));
   p.dx_acc = take((size_t)s.T * d * 4);
   p.dx_r = take((size_t)s.T * d * 4);
   p.total = at;
@@ -662,20 +663,24 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
   }
   // per token: gate gradients, router softmax backward, dx from expert rows and
   // identity slots
-  float* dl = F(pl.dl);
+  bf16_t* dl = B(pl.dl);
   MOE_ZC_TRY(launch_token_bwd(xb, dyb, fwd->logits, fwd->topk_idx, fwd->topk_gate, fwd->pos,
-                              row_dg, dxg, T, (int)d, E, K, N, dl, (int)pl.E16, F(pl.dx_acc),
+                              row_dg, dxg, T, (int)d, E, K, N, dl, (int)pl.E64, F(pl.dx_acc),
                               stream));
-  // router: dx += dl W_r (fp32), dW_r = dl^T x
-  TrArgsHost a = tr(w_router, d, F(pl.wrT), pl.E16, (int)d, pl.E16, E, true, true);
+  // router: dx += dl W_r on the packed kernel (bf16 dl and W_r, fp32
+  // accumulation; W_r^T [d][E rounded up to 64] packed on every call),
+  // dW_r = dl^T x
+  TrArgsHost a = tr(w_router, d, B(pl.wrT), pl.E64, (int)d, pl.E64, E, true, false);
   MOE_ZC_TRY(launch_transpose(a, stream));
+  MOE_ZC_TRY(launch_pack_weights(B(pl.wrT), nullptr, B(pl.wrP), 1, (int)d, (int)pl.E64, false,
+                                 stream));
   GemmProblem r{};
-  r.A = dl; r.lda = pl.E16; r.a_kwrap = (int)pl.E16; r.K = (int)pl.E16;
-  r.B0 = F(pl.wrT); r.ldb = pl.E16;
+  r.A = dl; r.lda = pl.E64; r.a_kwrap = (int)pl.E64; r.K = (int)pl.E64;
+  r.B0 = B(pl.wrP);
   r.C = F(pl.dx_r); r.ldc = d; r.Nout = (int)d; r.G = 1; r.M = (int)T;
-  MOE_ZC_TRY(launch_simt_gemm(r, kStoreF32, T, stream));
+  MOE_ZC_TRY(launch_packed_gemm(r, kStoreF32, router_tile_rows(T, (int)d), T, stream));
   MOE_ZC_TRY(launch_dx_final(F(pl.dx_acc), F(pl.dx_r), static_cast<bf16_t*>(dx), T * d, stream));
-  a = tr(dl, pl.E16, B(pl.dlT), pl.T64, E, pl.T64, T, true, false);
+  a = tr(dl, pl.E64, B(pl.dlT), pl.T64, E, pl.T64, T);
   MOE_ZC_TRY(launch_transpose(a, stream));
   a = tr(x, d, B(pl.xT), pl.T64, (int)d, pl.T64, T);
   MOE_ZC_TRY(launch_transpose(a, stream));

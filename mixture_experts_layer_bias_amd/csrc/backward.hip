@@ -256,14 +256,14 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ A
 
 // ---- per-token backward ---------------------------------------------------------
 // Token t: gate gradients of its K slots (FFN: row_dg; identity: <dy_t, x_t>),
-// dl_t = p_t * (dp_t - <p_t, dp_t>) into dl [T][ldl] (p = softmax of the fp32
-// logits), and dx_acc_t = sum over FFN slots in slot order of dxg[pos] plus the
+// dl_t = p_t * (dp_t - <p_t, dp_t>) into dl [T][ldl] bf16, zeros past E (p =
+// softmax of the fp32 logits), and dx_acc_t = sum over FFN slots in slot order of dxg[pos] plus the
 // identity slots' g dy_t (fp32).  One workgroup of 256 threads per token.
 __global__ __launch_bounds__(256) void token_bwd_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ dy, const float* __restrict__ logits,
     const int32_t* __restrict__ idx, const float* __restrict__ gate, const int32_t* __restrict__ pos,
     const float* __restrict__ row_dg, const float* __restrict__ dxg, int d, int E, int K, int N,
-    float* __restrict__ dl, int ldl, float* __restrict__ dx_acc) {
+    bf16_t* __restrict__ dl, int ldl, float* __restrict__ dx_acc) {
   __shared__ float red[256];
   __shared__ float dg_s[64];
   __shared__ float stat[2];
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256) void token_bwd_kernel(
         if (it[k] == i) dp = dg_s[k];
       v = __expf(lt[i] - mx) * inv * (dp - c);
     }
-    dl[t * ldl + i] = v;
+    dl[t * ldl + i] = f32_to_bf16(v);
   }
   // dx from the expert rows and the identity slots, slot order
   for (int j = tid; j < d; j += 256) {
@@ -573,7 +573,7 @@ hipError_t launch_swiglu_bwd(const void* A, const void* U, int64_t ld_au, bool a
 hipError_t launch_token_bwd(const bf16_t* x, const bf16_t* dy, const float* logits,
                             const int32_t* idx, const float* gate, const int32_t* pos,
                             const float* row_dg, const float* dxg, int64_t T, int d, int E, int K,
-                            int N, float* dl, int ldl, float* dx_acc, hipStream_t s) {
+                            int N, bf16_t* dl, int ldl, float* dx_acc, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (K > 64) return hipErrorInvalidValue;
   hipLaunchKernelGGL(token_bwd_kernel, dim3((unsigned)T), dim3(256), 0, s, x, dy, logits, idx,

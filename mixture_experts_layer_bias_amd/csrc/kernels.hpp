@@ -173,7 +173,7 @@ hipError_t launch_swiglu_bwd(const void* A, const void* U, int64_t ld_au, bool a
 hipError_t launch_token_bwd(const bf16_t* x, const bf16_t* dy, const float* logits,
                             const int32_t* idx, const float* gate, const int32_t* pos,
                             const float* row_dg, const float* dxg, int64_t T, int d, int E, int K,
-                            int N, float* dl, int ldl, float* dx_acc, hipStream_t s);
+                            int N, bf16_t* dl, int ldl, float* dx_acc, hipStream_t s);
 hipError_t launch_set_range(int32_t* out, int a, int b, hipStream_t s);
 hipError_t launch_dx_final(const float* a, const float* b, bf16_t* dx, int64_t n, hipStream_t s);
 // C[g] = A_g B_g^T, fp32 [G][M][N], with A_g [M][R_g] and B_g [N][R_g] the
