@@ -313,7 +313,7 @@ inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 struct BwdPlan {
   int64_t Sp, T64, E64;  // padded grouped columns, padded tokens, padded experts
   size_t tiles, kofs, kofs_r, colrow, row_gate, row_dg, A, U, Q, dau, H, dxg, XT, ET, DAT, DUT,
-      HT, dl, dlT, xT, wrT, wrP, dx_acc, dx_r, total;
+      HT, dl, dlT, xT, wrT, wrP, dx_r, total;
 };
 
 BwdPlan make_bwd_plan(const Shape& s) {
@@ -350,7 +350,6 @@ BwdPlan make_bwd_plan(const Shape& s) {
   p.xT = take(d * (size_t)p.T64 * 2);
   p.wrT = take(d * (size_t)p.E64 * 2);
   p.wrP = take((size_t)packed_bytes(s.d, p.E64, false));
-  p.dx_acc = take((size_t)s.T * d * 4);
   p.dx_r = take((size_t)s.T * d * 4);
   p.total = at;
   return p;
@@ -664,9 +663,8 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
   // per token: gate gradients, router softmax backward, dx from expert rows and
   // identity slots
   bf16_t* dl = B(pl.dl);
-  MOE_ZC_TRY(launch_token_bwd(xb, dyb, fwd->logits, fwd->topk_idx, fwd->topk_gate, fwd->pos,
-                              row_dg, dxg, T, (int)d, E, K, N, dl, (int)pl.E64, F(pl.dx_acc),
-                              stream));
+  MOE_ZC_TRY(launch_token_route_bwd(xb, dyb, fwd->logits, fwd->topk_idx, fwd->pos, row_dg, T,
+                                    (int)d, E, K, N, dl, (int)pl.E64, stream));
   // router: dx += dl W_r on the packed kernel (bf16 dl and W_r, fp32
   // accumulation; W_r^T [d][E rounded up to 64] packed on every call),
   // dW_r = dl^T x
@@ -679,7 +677,9 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
   r.B0 = B(pl.wrP);
   r.C = F(pl.dx_r); r.ldc = d; r.Nout = (int)d; r.G = 1; r.M = (int)T;
   MOE_ZC_TRY(launch_packed_gemm(r, kStoreF32, router_tile_rows(T, (int)d), T, stream));
-  MOE_ZC_TRY(launch_dx_final(F(pl.dx_acc), F(pl.dx_r), static_cast<bf16_t*>(dx), T * d, stream));
+  // dx: the slots' expert rows and identity terms in slot order, then the router term
+  MOE_ZC_TRY(launch_dx_sum(dyb, fwd->topk_idx, fwd->topk_gate, fwd->pos, dxg, F(pl.dx_r), T,
+                           (int)d, K, N, static_cast<bf16_t*>(dx), stream));
   a = tr(dl, pl.E64, B(pl.dlT), pl.T64, E, pl.T64, T);
   MOE_ZC_TRY(launch_transpose(a, stream));
   a = tr(x, d, B(pl.xT), pl.T64, (int)d, pl.T64, T);

@@ -14,13 +14,13 @@
 //
 // Kernels here: bookkeeping (tile prefix, 64-padded group columns, column ->
 // row map, slot of each grouped row), a tiled transpose that gathers, scales
-// and zero-pads rows into [dim][padded rows] operands, the per-row SwiGLU
-// backward, the per-token combine / identity / router-softmax backward, and
-// the weight-gradient GEMM: groups (experts) with their own reduction range
-// over the padded rows, both operands K-contiguous, fp32 output.  The
-// products with the expert weights (recomputing a and u, q, the rows of dx)
-// run on the bf16 MFMA grouped GEMM; the two router products on the fp32
-// grouped GEMM.
+// and zero-pads rows into expert-blocked [dim][rows] operands, the per-row
+// SwiGLU backward, the per-token router-softmax backward, the sum of each
+// token's dx contributions, and the weight-gradient GEMM: groups (experts)
+// with their own reduction range over the padded rows, both operands
+// K-contiguous, fp32 output.  The other products (q, the rows of dx, the
+// router's dx term, and a and u when the forward did not save them) run on
+// the bf16 MFMA grouped GEMMs.
 #include "gemm_tile.hpp"
 
 namespace moezc {
@@ -255,84 +255,125 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ A
 }
 
 // ---- per-token backward ---------------------------------------------------------
-// Token t: gate gradients of its K slots (FFN: row_dg; identity: <dy_t, x_t>),
-// dl_t = p_t * (dp_t - <p_t, dp_t>) into dl [T][ldl] bf16, zeros past E (p =
-// softmax of the fp32 logits), and dx_acc_t = sum over FFN slots in slot order of dxg[pos] plus the
-// identity slots' g dy_t (fp32).  One workgroup of 256 threads per token.
-__global__ __launch_bounds__(256) void token_bwd_kernel(
+// Sum over the 64 lanes of a wavefront, in a fixed butterfly order (every lane
+// ends with the same value).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// Token t, one wavefront per token: the gate gradients of its K slots (FFN:
+// row_dg of the slot's grouped row; identity: <dy_t, x_t>) and the router's
+// softmax backward dl_t = p_t * (dp_t - <p_t, dp_t>) (p = softmax of the fp32
+// logits, dp_t = the gate gradients at the chosen experts) into dl [T][ldl]
+// bf16, zeros past E.
+__global__ __launch_bounds__(256) void token_route_bwd_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ dy, const float* __restrict__ logits,
-    const int32_t* __restrict__ idx, const float* __restrict__ gate, const int32_t* __restrict__ pos,
-    const float* __restrict__ row_dg, const float* __restrict__ dxg, int d, int E, int K, int N,
-    bf16_t* __restrict__ dl, int ldl, float* __restrict__ dx_acc) {
-  __shared__ float red[256];
-  __shared__ float dg_s[64];
-  __shared__ float stat[2];
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x;
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ pos,
+    const float* __restrict__ row_dg, int64_t T, int d, int E, int K, int N,
+    bf16_t* __restrict__ dl, int ldl) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
   const int32_t* it = idx + t * K;
-  const float* gt = gate + t * K;
   const int32_t* pt = pos + t * K;
-  // <dy_t, x_t> for the identity slots
+  // <dy_t, x_t>: lane l takes the 8-element pieces l, l + 64, ...
   float xy = 0.f;
-  for (int j = tid; j < d; j += 256) xy += bf16_to_f32(dy[t * d + j]) * bf16_to_f32(x[t * d + j]);
-  red[tid] = xy;
-  __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
+  for (int j = lane * 8; j < d; j += 512) {
+    const uint4 xv = *reinterpret_cast<const uint4*>(x + t * d + j);
+    const uint4 yv = *reinterpret_cast<const uint4*>(dy + t * d + j);
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, yw[4] = {yv.x, yv.y, yv.z, yv.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      xy += __uint_as_float(xw[q] << 16) * __uint_as_float(yw[q] << 16);
+      xy += __uint_as_float(xw[q] & 0xffff0000u) * __uint_as_float(yw[q] & 0xffff0000u);
+    }
   }
-  const float xyt = red[0];
-  __syncthreads();
-  if (tid < K) dg_s[tid] = it[tid] < N ? row_dg[pt[tid]] : xyt;
-  // softmax statistics of the fp32 logits (max, then sum of exp), fixed trees
+  xy = wave_sum(xy);
+  // softmax statistics of the fp32 logits
   const float* lt = logits + t * E;
   float mx = -INFINITY;
-  for (int i = tid; i < E; i += 256) mx = fmaxf(mx, lt[i]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  mx = red[0];
-  __syncthreads();
+  for (int i = lane; i < E; i += 64) mx = fmaxf(mx, lt[i]);
+  mx = wave_max(mx);
   float se = 0.f;
-  for (int i = tid; i < E; i += 256) se += __expf(lt[i] - mx);
-  red[tid] = se;
-  __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
+  for (int i = lane; i < E; i += 64) se += __expf(lt[i] - mx);
+  const float inv = 1.0f / wave_sum(se);
+  // <p, dp>: only the chosen experts have dp != 0 (every lane the same)
+  float c = 0.f;
+  for (int k = 0; k < K; ++k) {
+    const float dg = it[k] < N ? row_dg[pt[k]] : xy;
+    c += __expf(lt[it[k]] - mx) * inv * dg;
   }
-  if (tid == 0) {
-    const float inv = 1.0f / red[0];
-    float c = 0.f;  // <p, dp>: only the chosen experts have dp != 0
-    for (int k = 0; k < K; ++k) c += __expf(lt[it[k]] - mx) * inv * dg_s[k];
-    stat[0] = inv;
-    stat[1] = c;
-  }
-  __syncthreads();
-  const float inv = stat[0], c = stat[1];
-  for (int i = tid; i < ldl; i += 256) {  // padding columns E .. ldl - 1 get zeros
+  for (int i = lane; i < ldl; i += 64) {  // padding columns E .. ldl - 1 get zeros
     float v = 0.f;
     if (i < E) {
       float dp = 0.f;
       for (int k = 0; k < K; ++k)
-        if (it[k] == i) dp = dg_s[k];
+        if (it[k] == i) dp = it[k] < N ? row_dg[pt[k]] : xy;
       v = __expf(lt[i] - mx) * inv * (dp - c);
     }
     dl[t * ldl + i] = f32_to_bf16(v);
   }
-  // dx from the expert rows and the identity slots, slot order
-  for (int j = tid; j < d; j += 256) {
-    float acc = 0.f;
-    const float dyj = bf16_to_f32(dy[t * d + j]);
-    for (int k = 0; k < K; ++k) {
-      if (it[k] < N) acc += dxg[(int64_t)pt[k] * d + j];
-      else acc += gt[k] * dyj;
+}
+
+// dx[t][j .. j+7] = bf16(sum over the slots of t, in slot order, of the
+// expert row's dx (FFN slot) or g dy_t (identity slot), plus the router term
+// dx_r[t]).  One thread per 8 elements: a pure stream over the rows.
+__global__ __launch_bounds__(256) void dx_sum_kernel(const bf16_t* __restrict__ dy,
+                                                     const int32_t* __restrict__ idx,
+                                                     const float* __restrict__ gate,
+                                                     const int32_t* __restrict__ pos,
+                                                     const float* __restrict__ dxg,
+                                                     const float* __restrict__ dx_r, int64_t T,
+                                                     int d, int K, int N,
+                                                     bf16_t* __restrict__ dx) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int per_t = d / 8;
+  if (q >= T * per_t) return;
+  const int64_t t = q / per_t;
+  const int j = (int)(q - t * per_t) * 8;
+  float yv[8], acc[8];
+  {
+    const uint4 u = *reinterpret_cast<const uint4*>(dy + t * d + j);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      yv[2 * e] = __uint_as_float(w[e] << 16);
+      yv[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
     }
-    dx_acc[t * d + j] = acc;
   }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int k = 0; k < K; ++k) {
+    const int e_k = idx[t * K + k];
+    if (e_k < N) {
+      const float* r = dxg + (int64_t)pos[t * K + k] * d + j;
+      const float4 a0 = *reinterpret_cast<const float4*>(r);
+      const float4 a1 = *reinterpret_cast<const float4*>(r + 4);
+      acc[0] += a0.x; acc[1] += a0.y; acc[2] += a0.z; acc[3] += a0.w;
+      acc[4] += a1.x; acc[5] += a1.y; acc[6] += a1.z; acc[7] += a1.w;
+    } else {
+      const float g = gate[t * K + k];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += g * yv[e];
+    }
+  }
+  const float* rr = dx_r + t * d + j;
+  const float4 r0 = *reinterpret_cast<const float4*>(rr);
+  const float4 r1 = *reinterpret_cast<const float4*>(rr + 4);
+  const float rv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    o[e] = (uint32_t)f32_to_bf16(acc[2 * e] + rv[2 * e]) |
+           ((uint32_t)f32_to_bf16(acc[2 * e + 1] + rv[2 * e + 1]) << 16);
+  *reinterpret_cast<uint4*>(dx + t * d + j) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // out[0] = a, out[1] = b (a one-group reduction range)
@@ -341,14 +382,6 @@ __global__ void set_range_kernel(int32_t* out, int a, int b) {
     out[0] = a;
     out[1] = b;
   }
-}
-
-// dx = bf16(dx_acc + dx_router)
-__global__ __launch_bounds__(256) void dx_final_kernel(const float* __restrict__ a,
-                                                       const float* __restrict__ b,
-                                                       bf16_t* __restrict__ dx, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) dx[i] = f32_to_bf16(a[i] + b[i]);
 }
 
 // ---- weight-gradient GEMM --------------------------------------------------------
@@ -570,25 +603,31 @@ hipError_t launch_swiglu_bwd(const void* A, const void* U, int64_t ld_au, bool a
   return hipGetLastError();
 }
 
-hipError_t launch_token_bwd(const bf16_t* x, const bf16_t* dy, const float* logits,
-                            const int32_t* idx, const float* gate, const int32_t* pos,
-                            const float* row_dg, const float* dxg, int64_t T, int d, int E, int K,
-                            int N, bf16_t* dl, int ldl, float* dx_acc, hipStream_t s) {
+hipError_t launch_token_route_bwd(const bf16_t* x, const bf16_t* dy, const float* logits,
+                                  const int32_t* idx, const int32_t* pos, const float* row_dg,
+                                  int64_t T, int d, int E, int K, int N, bf16_t* dl, int ldl,
+                                  hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  if (K > 64) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(token_bwd_kernel, dim3((unsigned)T), dim3(256), 0, s, x, dy, logits, idx,
-                     gate, pos, row_dg, dxg, d, E, K, N, dl, ldl, dx_acc);
+  if (d % 8 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(token_route_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, x,
+                     dy, logits, idx, pos, row_dg, T, d, E, K, N, dl, ldl);
+  return hipGetLastError();
+}
+
+hipError_t launch_dx_sum(const bf16_t* dy, const int32_t* idx, const float* gate,
+                         const int32_t* pos, const float* dxg, const float* dx_r, int64_t T, int d,
+                         int K, int N, bf16_t* dx, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (d % 8 != 0) return hipErrorInvalidValue;
+  const int64_t n = T * (d / 8);
+  if ((n + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dx_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, dy, idx,
+                     gate, pos, dxg, dx_r, T, d, K, N, dx);
   return hipGetLastError();
 }
 
 hipError_t launch_set_range(int32_t* out, int a, int b, hipStream_t s) {
   hipLaunchKernelGGL(set_range_kernel, dim3(1), dim3(64), 0, s, out, a, b);
-  return hipGetLastError();
-}
-
-hipError_t launch_dx_final(const float* a, const float* b, bf16_t* dx, int64_t n, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(dx_final_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, b, dx, n);
   return hipGetLastError();
 }
 

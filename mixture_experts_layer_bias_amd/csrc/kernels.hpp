@@ -170,12 +170,16 @@ hipError_t launch_swiglu_bwd(const void* A, const void* U, int64_t ld_au, bool a
                              const float* Q, const float* row_gate, const int32_t* offsets, int N,
                              int I, int64_t max_rows, bf16_t* dau, bf16_t* H, float* row_dg,
                              hipStream_t s);
-hipError_t launch_token_bwd(const bf16_t* x, const bf16_t* dy, const float* logits,
-                            const int32_t* idx, const float* gate, const int32_t* pos,
-                            const float* row_dg, const float* dxg, int64_t T, int d, int E, int K,
-                            int N, bf16_t* dl, int ldl, float* dx_acc, hipStream_t s);
+// Per token: gate gradients and the router softmax backward dl [T][ldl] bf16.
+hipError_t launch_token_route_bwd(const bf16_t* x, const bf16_t* dy, const float* logits,
+                                  const int32_t* idx, const int32_t* pos, const float* row_dg,
+                                  int64_t T, int d, int E, int K, int N, bf16_t* dl, int ldl,
+                                  hipStream_t s);
+// dx = bf16(sum over slots of the expert row's dx or g dy, plus dx_r).
+hipError_t launch_dx_sum(const bf16_t* dy, const int32_t* idx, const float* gate,
+                         const int32_t* pos, const float* dxg, const float* dx_r, int64_t T, int d,
+                         int K, int N, bf16_t* dx, hipStream_t s);
 hipError_t launch_set_range(int32_t* out, int a, int b, hipStream_t s);
-hipError_t launch_dx_final(const float* a, const float* b, bf16_t* dx, int64_t n, hipStream_t s);
 // C[g] = A_g B_g^T, fp32 [G][M][N], with A_g [M][R_g] and B_g [N][R_g] the
 // expert-blocked operands (R_g = kofs[g+1] - kofs[g] <= max_rows).
 hipError_t launch_wgrad(const bf16_t* A, const bf16_t* B, const int32_t* kofs, int G, int M,
