@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peak-probe", action="store_true",
                     help="skip measuring the box's stream bandwidths and dense GEMM rate")
-    ap.add_argument("--cpu-experts", type=int, default=24,
+    ap.add_argument("--cpu-experts", type=int, default=96,
                     help="experts the CPU-baseline sample evaluates")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a device copy of known size (for scaling counters)")
