@@ -37,6 +37,8 @@
  *     fixed reduction orders.
  *   - Calls on different streams with disjoint outputs and workspaces may run
  *     concurrently; the library has no mutable global state.
+ *   - No entry point allocates, synchronises or issues a memset, so the
+ *     work-enqueuing calls can be captured in a HIP graph and replayed.
  */
 #ifndef MOE_ZC_H
 #define MOE_ZC_H

@@ -1,0 +1,134 @@
+"""Stream and graph behaviour the C ABI promises: the library has no mutable
+global state, so calls on different streams with their own workspaces may run
+concurrently; it allocates nothing, synchronises nothing and records no memset,
+so a forward (and the bias update) can be captured in a HIP graph and
+replayed.  Every result is compared bit for bit with the same call run eagerly
+on the default stream."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_bias_amd as m
+from workloads import Workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def _w(seed, T=700, d=256, I=256, N=16, Z=8, K=4):
+    return Workload("streams", T=T, d=d, I=I, N=N, Z=Z, K=K, dtype="bf16", seed=seed,
+                    bias=("uniform", 0.05))
+
+
+def _packed_forward(w, inp, packed, ws, out, bias=None, aux=None):
+    return m.moe_zc_forward_packed(inp["x"], inp["w_router"], inp["bias"] if bias is None else bias,
+                                   packed[0], packed[1], w.N, w.Z, w.K, w.I,
+                                   residual=inp["residual"], out=out, aux=aux, workspace=ws)
+
+
+def _ws(w):
+    n = m.moe_zc_workspace_size(w.T, w.d, w.I, w.N, w.Z, w.K, torch.bfloat16)
+    return torch.empty(n, dtype=torch.uint8, device=DEV)
+
+
+def test_concurrent_streams_match_eager():
+    """Two layers (different inputs and weights) on two streams, interleaved
+    three times without synchronisation, give exactly their eager results."""
+    ws_ = [_w(11), _w(12, T=513, N=24, Z=8, K=6)]
+    inps = [make_inputs(w, device=DEV) for w in ws_]
+    packs = [m.moe_zc_pack_expert_weights(i["w_gate"], i["w_up"], i["w_down"]) for i in inps]
+    ref = []
+    for w, inp, pk in zip(ws_, inps, packs):
+        ref.append(_packed_forward(w, inp, pk, _ws(w), None).clone())
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [_ws(w) for w in ws_]
+    outs = [torch.empty_like(r) for r in ref]
+    for _ in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                _packed_forward(ws_[i], inps[i], packs[i], wss[i], outs[i])
+    torch.cuda.synchronize()
+    for i in range(2):
+        assert torch.equal(outs[i], ref[i]), f"stream {i} differs from the eager result"
+
+
+def test_graph_replay_of_the_forward_matches_eager():
+    """A captured forward replayed on new inputs copied into its static input
+    buffer: every replay equals the eager forward of those inputs (eager work
+    and synchronisation between replays)."""
+    w = _w(21)
+    inp = make_inputs(w, device=DEV)
+    pk = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    ws = _ws(w)
+    y = torch.empty(w.T, w.d, dtype=torch.bfloat16, device=DEV)
+    aux = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV)
+    static_x = inp["x"].clone()
+    static = dict(inp, x=static_x)
+    _packed_forward(w, static, pk, ws, y, aux=aux)   # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _packed_forward(w, static, pk, ws, y, aux=aux)
+    gen = torch.Generator().manual_seed(5)
+    for rep in range(3):
+        new_x = torch.randn(w.T, w.d, generator=gen).to(torch.bfloat16).to(DEV)
+        static_x.copy_(new_x)
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        got_idx = aux["topk_idx"].clone()
+        ea = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV)
+        eager = _packed_forward(w, dict(inp, x=new_x), pk, _ws(w), None, aux=ea)
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager), f"replay {rep}: y differs from eager"
+        assert torch.equal(got_idx, ea["topk_idx"]), f"replay {rep}: routing differs"
+
+
+def test_graph_of_forward_and_bias_update_matches_eager_loop():
+    """Forward + PID step captured together and replayed six times follows the
+    same bias trajectory, bit for bit, as the eager closed loop."""
+    w = _w(31)
+    inp = make_inputs(w, device=DEV)
+    pk = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    target = torch.full((w.E,), w.T * w.K / w.E, dtype=torch.float32, device=DEV)
+
+    def loop(use_graph):
+        bias = inp["bias"].clone()
+        pid = m.PidState(w.E, DEV, kp=0.5, ki=0.5, kd=0.1)
+        aux = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV, keys=("loads",))
+        ws = _ws(w)
+        y = torch.empty(w.T, w.d, dtype=torch.bfloat16, device=DEV)
+
+        def step():
+            _packed_forward(w, inp, pk, ws, y, bias=bias, aux=aux)
+            m.moe_zc_bias_update(aux["loads"], target, bias, pid)
+
+        traj = []
+        if use_graph:
+            g = torch.cuda.CUDAGraph()
+            bias0 = bias.clone()
+            step()                               # warm-up outside the capture
+            torch.cuda.synchronize()
+            bias.copy_(bias0)
+            pid.e_prev.zero_()
+            pid.e_prev2.zero_()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                step()
+            for _ in range(6):
+                g.replay()
+                torch.cuda.synchronize()
+                traj.append(bias.cpu().numpy().copy())
+        else:
+            for _ in range(6):
+                step()
+                torch.cuda.synchronize()
+                traj.append(bias.cpu().numpy().copy())
+        return traj
+
+    eager = loop(False)
+    graph = loop(True)
+    for i, (a, b) in enumerate(zip(eager, graph)):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"step {i}: bias differs"
+    assert not np.array_equal(eager[0], eager[-1]), "the bias should move"
