@@ -65,13 +65,20 @@ def parse():
 
 
 COUNTERS_MD = os.path.join(ROOT, "profiles", "gemm_gate_up_prefill_counters.md")
-GEMM_SRC = os.path.join(ROOT, "mixture_experts_layer_bias_amd", "csrc", "gemm_packed.hip")
+# the sources the packed GEMM kernel is compiled from (its epilogue and
+# helpers live in the headers)
+GEMM_SRC = [os.path.join(ROOT, "mixture_experts_layer_bias_amd", "csrc", f)
+            for f in ("gemm_packed.hip", "gemm_tile.hpp", "common.hpp", "kernels.hpp")]
 
 
-def source_sha(path):
+def source_sha(paths):
+    """sha256 (first 16 hex digits) of the files' bytes, concatenated in order."""
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def counter_traffic():

@@ -133,8 +133,7 @@ __device__ __forceinline__ void st16(bf16_t* p, const float (&v)[16]) {
     uint32_t w[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      w[q] = (uint32_t)f32_to_bf16(v[8 * h + 2 * q]) |
-             ((uint32_t)f32_to_bf16(v[8 * h + 2 * q + 1]) << 16);
+      w[q] = f32x2_to_bf16x2(v[8 * h + 2 * q], v[8 * h + 2 * q + 1]);
     reinterpret_cast<uint4*>(p)[h] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
@@ -237,7 +236,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const T* __restrict__ A
   for (int i = threadIdx.x; i < I; i += 256) {
     const int64_t o = s * I + i;
     const float a = ld_elem(A, s * ld_au + i), u = ld_elem(U, s * ld_au + i), q = Q[o];
-    const float sg = 1.0f / (1.0f + __expf(-a));
+    const float sg = sigmoid_fast(a);
     const float h = a * sg * u;
     dot += q * h;
     const float dh = g * q;
@@ -371,8 +370,7 @@ __global__ __launch_bounds__(256) void dx_sum_kernel(const bf16_t* __restrict__ 
   uint32_t o[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    o[e] = (uint32_t)f32_to_bf16(acc[2 * e] + rv[2 * e]) |
-           ((uint32_t)f32_to_bf16(acc[2 * e + 1] + rv[2 * e + 1]) << 16);
+    o[e] = f32x2_to_bf16x2(acc[2 * e] + rv[2 * e], acc[2 * e + 1] + rv[2 * e + 1]);
   *reinterpret_cast<uint4*>(dx + t * d + j) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 

@@ -16,15 +16,26 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 // memcpy through private memory, which keeps staging arrays out of registers)
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
-// fp32 -> bf16, IEEE round to nearest, ties to even (NaN stays a quiet NaN).
-__device__ __host__ inline bf16_t f32_to_bf16(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) {
-    return (bf16_t)((u >> 16) | 0x0040u);
-  }
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+
+// fp32 -> bf16, IEEE round to nearest, ties to even (a NaN stays a NaN):
+// gfx950's v_cvt_pk_bf16_f32, which converts two values in one instruction
+// (fp32 denormals are kept, so it rounds denormals like any other value).
+__device__ inline bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+// a to the low and b to the high half of one dword
+__device__ inline uint32_t f32x2_to_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
+
+// sigmoid(a) = 1 / (1 + e^-a) with the hardware exponential and reciprocal
+// (v_exp_f32 on a * log2(e), v_rcp_f32: about one ulp each), and the SwiGLU
+// product silu(a) * u = (a * sigmoid(a)) * u.  Saturates cleanly: e^-a = inf
+// gives sigmoid 0.  Every bf16 SwiGLU epilogue uses this one definition, so
+// the packed, row-major and FP8 paths round the same values.
+__device__ inline float sigmoid_fast(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
+__device__ inline float swiglu_fast(float a, float u) { return a * sigmoid_fast(a) * u; }
 
 __device__ __host__ inline float bf16_to_f32(bf16_t h) {
   return __builtin_bit_cast(float, (uint32_t)h << 16);
@@ -63,10 +74,10 @@ __device__ inline void store8(float* p, const float (&v)[8]) {
 }
 __device__ inline void store8(bf16_t* p, const float (&v)[8]) {
   uint4 a;
-  a.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-  a.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-  a.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-  a.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+  a.x = f32x2_to_bf16x2(v[0], v[1]);
+  a.y = f32x2_to_bf16x2(v[2], v[3]);
+  a.z = f32x2_to_bf16x2(v[4], v[5]);
+  a.w = f32x2_to_bf16x2(v[6], v[7]);
   *reinterpret_cast<uint4*>(p) = a;
 }
 

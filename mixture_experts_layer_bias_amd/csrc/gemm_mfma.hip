@@ -297,8 +297,7 @@ __device__ __forceinline__ void run_tile(const GemmProblem& p, const TileCoord& 
         const int r = 8 * (v >> 2) + lrow4 + (v & 3);
         float val;
         if (SWIGLU) {
-          const float a = acc[i][j][v];
-          val = a / (1.0f + __expf(-a)) * acc[i][j + HB][v];
+          val = swiglu_fast(acc[i][j][v], acc[i][j + HB][v]);
         } else {
           val = acc[i][j][v];
         }

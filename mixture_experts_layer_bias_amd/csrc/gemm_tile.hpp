@@ -113,8 +113,7 @@ __device__ __forceinline__ void store_bf16_tile(const f32x16_t (&acc)[NA][2], ch
         const int r = 8 * (v >> 2) + lrow4 + (v & 3);
         float val;
         if (SWIGLU) {
-          const float a = acc[i][0][v];
-          val = a / (1.0f + __expf(-a)) * acc[i][1][v];
+          val = swiglu_fast(acc[i][0][v], acc[i][1][v]);
         } else {
           val = acc[i][jj][v];
         }
