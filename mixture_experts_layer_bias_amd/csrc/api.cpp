@@ -634,8 +634,9 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
     q.C = dxg; q.ldc = d; q.Nout = (int)d;
     q.row_offsets = offsets; q.tile_prefix = tiles; q.G = N; q.M = 0;
     MOE_ZC_TRY(launch_packed_gemm(q, kStoreF32, s.ffn_tile_rows, s.smax, stream));
-    // weight gradients: operands transposed into expert-blocked [dim][rows_e
-    // rounded up to 64] blocks (zeros in the padding columns)
+    // weight gradients: operands transposed into expert blocks of rows_e
+    // rounded up to 64 columns (zeros in the padding columns), stored as slabs
+    // of 32 columns
     auto blocked = [&](const void* src, int64_t src_ld, void* dst, int64_t dim) {
       TrArgsHost a = tr(src, src_ld, dst, 0, (int)dim, pl.Sp, 0);
       a.colrow = colrow;
@@ -680,12 +681,16 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
   // dx: the slots' expert rows and identity terms in slot order, then the router term
   MOE_ZC_TRY(launch_dx_sum(dyb, fwd->topk_idx, fwd->topk_gate, fwd->pos, dxg, F(pl.dx_r), T,
                            (int)d, K, N, static_cast<bf16_t*>(dx), stream));
-  a = tr(dl, pl.E64, B(pl.dlT), pl.T64, E, pl.T64, T);
-  MOE_ZC_TRY(launch_transpose(a, stream));
-  a = tr(x, d, B(pl.xT), pl.T64, (int)d, pl.T64, T);
-  MOE_ZC_TRY(launch_transpose(a, stream));
+  // dl^T and x^T as one group of T rows (rounded up to 64), in the
+  // weight-gradient kernel's k-blocked layout
   int32_t* kofs_r = Ix(pl.kofs_r);
   MOE_ZC_TRY(launch_set_range(kofs_r, 0, (int)pl.T64, stream));
+  a = tr(dl, pl.E64, B(pl.dlT), pl.T64, E, pl.T64, T);
+  a.kofs = kofs_r; a.ngroups = 1;
+  MOE_ZC_TRY(launch_transpose(a, stream));
+  a = tr(x, d, B(pl.xT), pl.T64, (int)d, pl.T64, T);
+  a.kofs = kofs_r; a.ngroups = 1;
+  MOE_ZC_TRY(launch_transpose(a, stream));
   MOE_ZC_TRY(launch_wgrad(B(pl.dlT), B(pl.xT), kofs_r, 1, E, (int)d, pl.T64, dw_router, stream));
   return MOE_ZC_OK;
 }

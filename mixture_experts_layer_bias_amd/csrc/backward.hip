@@ -93,10 +93,13 @@ struct TrArgs {
   int64_t dst_ld, dst_col0, dst_bstride;
   int dim;        // destination rows (source columns)
   int64_t ncols;  // destination columns (multiple of 64)
-  // non-null: expert-blocked destination.  Group g owns columns
-  // [kofs[g], kofs[g+1]) (multiples of 64) and stores them as a contiguous
-  // [dim][kofs[g+1] - kofs[g]] block at element offset kofs[g] * dim; columns
-  // at or past kofs[ngroups] are not written.
+  // non-null: expert-blocked, k-blocked destination.  Group g owns columns
+  // [kofs[g], kofs[g+1]) (multiples of 64), stored from element offset
+  // kofs[g] * dim as slabs of 32 columns: column k of the group, row j at
+  // (k / 32) * dim * 32 + j * 32 + k % 32.  One slab holds every row's 32
+  // consecutive columns (64 bytes for bf16) back to back, so a weight-gradient
+  // stage reads one contiguous block.  Columns at or past kofs[ngroups] are
+  // not written.
   const int32_t* kofs;
   int ngroups;
 };
@@ -155,7 +158,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
   const SRC* src = static_cast<const SRC*>(a.src) + (int64_t)blockIdx.z * a.src_bstride;
   DST* dst = static_cast<DST*>(a.dst) + (int64_t)blockIdx.z * a.dst_bstride;
   int64_t dst_ld = a.dst_ld, cbase = c0;  // destination row stride, tile column in it
-  if (a.kofs) {
+  const bool kslab = a.kofs != nullptr;
+  if (kslab) {
     if (c0 >= a.kofs[a.ngroups]) return;
     int lo = 0, hi = a.ngroups;  // kofs[lo] <= c0 < kofs[hi]
     while (hi - lo > 1) {
@@ -163,7 +167,6 @@ __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
       if (a.kofs[mid] <= c0) lo = mid; else hi = mid;
     }
     const int64_t k0 = a.kofs[lo];
-    dst_ld = a.kofs[lo + 1] - k0;
     dst += k0 * a.dim;
     cbase = c0 - k0;
   }
@@ -201,7 +204,10 @@ __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
       float v[16];
 #pragma unroll
       for (int q = 0; q < 16; ++q) v[q] = tile[jl][cc + q];
-      DST* p = dst + (int64_t)j * dst_ld + a.dst_col0 + cbase + cc;
+      // 16 columns from a multiple of 16: inside one 32-column slab
+      const int64_t k = cbase + cc;
+      DST* p = kslab ? dst + (k >> 5) * ((int64_t)a.dim * 32) + (int64_t)j * 32 + (k & 31)
+                     : dst + (int64_t)j * dst_ld + a.dst_col0 + k;
       if (c0 + cc + 16 <= a.ncols) {
         st16(p, v);
       } else {
@@ -384,11 +390,12 @@ __global__ void set_range_kernel(int32_t* out, int a, int b) {
 
 // ---- weight-gradient GEMM --------------------------------------------------------
 // C[g][m][n] = sum over k < R_g of A_g[m][k] B_g[n][k], R_g = kofs[g+1] - kofs[g]
-// (a multiple of 64); A_g [M][R_g] and B_g [N][R_g] bf16 are the contiguous
-// blocks at element offsets kofs[g] * M and kofs[g] * N (the expert-blocked
-// layout of the transposes above); C fp32 [G][M][N].  128 x 128 tiles, four
-// wavefronts (2 x 2, 64 x 64 each), stages of 32 k double-buffered in LDS by
-// direct loads.
+// (a multiple of 64); A_g and B_g bf16 start at element offsets kofs[g] * M
+// and kofs[g] * N in the k-blocked layout of the transposes above (slabs of
+// 32 k: A_g[m][k] at (k / 32) * M * 32 + m * 32 + k % 32); C fp32 [G][M][N].
+// 128 x 128 tiles, four wavefronts (2 x 2, 64 x 64 each), stages of 32 k
+// double-buffered in LDS by direct loads: a stage of a tile is 128 rows of
+// 64 bytes, consecutive in its slab.
 constexpr int WG_BKS = 32, WG_ROWB = 64, WG_TILE = 128;
 constexpr int WG_SLOT = WG_TILE * WG_ROWB;  // 8 KB per operand and stage
 constexpr int WG_PITCH = WG_TILE;           // fp32 epilogue rows in LDS
@@ -431,29 +438,29 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradProblem p, int mtiles, 
   const int lane = tid & 63;
   const int wm = wave & 1, wn = wave >> 1;
   const int64_t k0 = p.kofs[g];
-  const int64_t ld = p.kofs[g + 1] - k0;  // row stride of both blocks
-  const int nk = (int)(ld / WG_BKS);
+  const int nk = (int)((p.kofs[g + 1] - k0) / WG_BKS);
   // direct loads: instruction t of wavefront w fills rows 16 (w + 4 t) .. + 15
   // of the tile (lane l: row + l / 4, position l % 4 holding chunk
   // (l % 4) ^ ((row >> 2) & 3)); rows past M or N repeat the last one
-  const char* A_base = reinterpret_cast<const char*>(p.A + k0 * p.M + (int64_t)m0 * ld);
-  const char* B_base = reinterpret_cast<const char*>(p.B + k0 * p.N + (int64_t)n0 * ld);
+  const char* A_base = reinterpret_cast<const char*>(p.A + k0 * p.M + (int64_t)m0 * WG_BKS);
+  const char* B_base = reinterpret_cast<const char*>(p.B + k0 * p.N + (int64_t)n0 * WG_BKS);
+  const int64_t a_slab = (int64_t)p.M * WG_ROWB, b_slab = (int64_t)p.N * WG_ROWB;  // bytes
   uint32_t a_src[2], b_src[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int r = 16 * (wave + 4 * t) + (lane >> 2);
     const int lc = (lane & 3) ^ ((r >> 2) & 3);
     const int ra = min(r, p.M - 1 - m0), rb = min(r, p.N - 1 - n0);
-    a_src[t] = (uint32_t)((int64_t)ra * ld * 2) + (uint32_t)(lc * 16);
-    b_src[t] = (uint32_t)((int64_t)rb * ld * 2) + (uint32_t)(lc * 16);
+    a_src[t] = (uint32_t)(ra * WG_ROWB + lc * 16);
+    b_src[t] = (uint32_t)(rb * WG_ROWB + lc * 16);
   }
   char* const dstA = smem + wave * 1024;
   char* const dstB = smem + WG_SLOT + wave * 1024;
   auto load_stage = [&](int kt, int slot) {
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(A_base + (int64_t)kt * WG_ROWB), 0, 0x7fffffff, 0x00020000);
+        (void*)(A_base + (int64_t)kt * a_slab), 0, 0x7fffffff, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(B_base + (int64_t)kt * WG_ROWB), 0, 0x7fffffff, 0x00020000);
+        (void*)(B_base + (int64_t)kt * b_slab), 0, 0x7fffffff, 0x00020000);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(

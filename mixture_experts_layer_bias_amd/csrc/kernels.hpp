@@ -159,9 +159,10 @@ struct TrArgsHost {
   int64_t ncols;
   int batch;
   bool src_f32, dst_f32;
-  // non-null: expert-blocked destination (group g's columns [kofs[g],
-  // kofs[g+1]) as a contiguous [dim][kofs[g+1] - kofs[g]] block at element
-  // offset kofs[g] * dim; dst_ld unused; batch 1, dst_col0 0)
+  // non-null: expert-blocked, k-blocked destination (group g's columns
+  // [kofs[g], kofs[g+1]) from element offset kofs[g] * dim as slabs of 32
+  // columns: column k of the group, row j at (k / 32) * dim * 32 + j * 32 +
+  // k % 32; dst_ld unused; batch 1, dst_col0 0)
   const int32_t* kofs;
   int ngroups;
 };
@@ -181,7 +182,8 @@ hipError_t launch_dx_sum(const bf16_t* dy, const int32_t* idx, const float* gate
                          int K, int N, bf16_t* dx, hipStream_t s);
 hipError_t launch_set_range(int32_t* out, int a, int b, hipStream_t s);
 // C[g] = A_g B_g^T, fp32 [G][M][N], with A_g [M][R_g] and B_g [N][R_g] the
-// expert-blocked operands (R_g = kofs[g+1] - kofs[g] <= max_rows).
+// expert-blocked operands in the transposes' k-blocked layout (slabs of 32
+// columns; R_g = kofs[g+1] - kofs[g] <= max_rows).
 hipError_t launch_wgrad(const bf16_t* A, const bf16_t* B, const int32_t* kofs, int G, int M,
                         int N, int64_t max_rows, float* C, hipStream_t s);
 
