@@ -396,9 +396,7 @@ __global__ void set_range_kernel(int32_t* out, int a, int b) {
 // 128 x 128 tiles, four wavefronts (2 x 2, 64 x 64 each), stages of 32 k
 // double-buffered in LDS by direct loads: a stage of a tile is 128 rows of
 // 64 bytes, consecutive in its slab.
-constexpr int WG_BKS = 32, WG_ROWB = 64, WG_TILE = 128;
-constexpr int WG_SLOT = WG_TILE * WG_ROWB;  // 8 KB per operand and stage
-constexpr int WG_PITCH = WG_TILE;           // fp32 epilogue rows in LDS
+constexpr int WG_BKS = 32, WG_ROWB = 64;
 
 struct WgradProblem {
   const bf16_t* A;
@@ -408,17 +406,32 @@ struct WgradProblem {
   float* C;
 };
 
+// Tiles of 64 RB rows (of A) by 64 CB columns (of B): 128 x 128 (32 KB of
+// LDS, five workgroups per CU) for few groups, 256 x 128 (48 KB, three per
+// CU) for the experts' gradients, where the taller tile reads 25% fewer
+// operand bytes per output.  Four wavefronts as 2 x 2, each RB x CB MFMA
+// blocks of 32 x 32.
 // Tile order.  With 8 or more groups, workgroup i (dispatched to XCD i % 8)
 // takes a tile of group (i % 8) + 8 j: each XCD owns whole groups, so a
 // group's operands are fetched into one L2 only.  Within a group the faster
 // index runs over the smaller operand's tiles (m_inner: over A's), which
 // keeps the tiles in flight on an XCD to a few of the larger operand's.
-// 32 KB of LDS (two stages of both operands, later half the fp32 tile) lets
-// five workgroups share a CU, so the loads of one hide behind the others.
-__global__ __launch_bounds__(256) void wgrad_kernel(WgradProblem p, int mtiles, int ntiles,
-                                                     int xcd_major, int m_inner) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * WG_SLOT];
-  static_assert(64 * WG_PITCH * 4 <= 2 * 2 * WG_SLOT, "epilogue half fits");
+// Several workgroups share a CU, so the loads of one hide behind the others.
+template <int RB, int CB>
+constexpr int wg_slot() { return 64 * (RB + CB) * WG_ROWB; }  // bytes of one stage
+
+// (the body is a device function: the host pass of a kernel template
+// instantiates its body, where the gfx950 buffer builtins do not exist)
+template <int RB, int CB>
+__device__ __forceinline__ void wgrad_tile(const WgradProblem& p, int mtiles, int ntiles,
+                                           int xcd_major, int m_inner, char* smem) {
+  constexpr int TM = 64 * RB;                  // tile rows (of A)
+  constexpr int SLOT_A = TM * WG_ROWB;         // bytes of one A stage
+  constexpr int TN = 64 * CB;                  // tile columns (rows of B)
+  constexpr int SLOT = wg_slot<RB, CB>();
+  constexpr int NLA = TM / 64, NLB = TN / 64;  // direct loads per wavefront and stage
+  constexpr int PITCH = TN;                    // fp32 epilogue rows in LDS
+  static_assert(64 * PITCH * 4 <= 2 * SLOT, "a 64-row part of the tile fits");
   const int per_g = mtiles * ntiles;
   int g, rem;
   if (xcd_major) {
@@ -432,7 +445,7 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradProblem p, int mtiles, 
   if (g >= p.G) return;
   const int mt = m_inner ? rem % mtiles : rem / ntiles;
   const int nt = m_inner ? rem / mtiles : rem % ntiles;
-  const int m0 = mt * WG_TILE, n0 = nt * WG_TILE;
+  const int m0 = mt * TM, n0 = nt * TN;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -440,107 +453,124 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradProblem p, int mtiles, 
   const int64_t k0 = p.kofs[g];
   const int nk = (int)((p.kofs[g + 1] - k0) / WG_BKS);
   // direct loads: instruction t of wavefront w fills rows 16 (w + 4 t) .. + 15
-  // of the tile (lane l: row + l / 4, position l % 4 holding chunk
+  // of the operand's tile (lane l: row + l / 4, position l % 4 holding chunk
   // (l % 4) ^ ((row >> 2) & 3)); rows past M or N repeat the last one
   const char* A_base = reinterpret_cast<const char*>(p.A + k0 * p.M + (int64_t)m0 * WG_BKS);
   const char* B_base = reinterpret_cast<const char*>(p.B + k0 * p.N + (int64_t)n0 * WG_BKS);
   const int64_t a_slab = (int64_t)p.M * WG_ROWB, b_slab = (int64_t)p.N * WG_ROWB;  // bytes
-  uint32_t a_src[2], b_src[2];
+  uint32_t a_src[NLA], b_src[NLB];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < NLA; ++t) {
     const int r = 16 * (wave + 4 * t) + (lane >> 2);
     const int lc = (lane & 3) ^ ((r >> 2) & 3);
-    const int ra = min(r, p.M - 1 - m0), rb = min(r, p.N - 1 - n0);
-    a_src[t] = (uint32_t)(ra * WG_ROWB + lc * 16);
-    b_src[t] = (uint32_t)(rb * WG_ROWB + lc * 16);
+    a_src[t] = (uint32_t)(min(r, p.M - 1 - m0) * WG_ROWB + lc * 16);
+  }
+#pragma unroll
+  for (int t = 0; t < NLB; ++t) {
+    const int r = 16 * (wave + 4 * t) + (lane >> 2);
+    const int lc = (lane & 3) ^ ((r >> 2) & 3);
+    b_src[t] = (uint32_t)(min(r, p.N - 1 - n0) * WG_ROWB + lc * 16);
   }
   char* const dstA = smem + wave * 1024;
-  char* const dstB = smem + WG_SLOT + wave * 1024;
-  auto load_stage = [&](int kt, int slot) {
-    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(A_base + (int64_t)kt * a_slab), 0, 0x7fffffff, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(B_base + (int64_t)kt * b_slab), 0, 0x7fffffff, 0x00020000);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_void_t*)(dstA + slot * 2 * WG_SLOT + t * 4096), 16, a_src[t], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (lds_void_t*)(dstB + slot * 2 * WG_SLOT + t * 4096), 16, b_src[t], 0, 0, 0);
-    }
-  };
+  char* const dstB = smem + SLOT_A + wave * 1024;
+#define WG_LOAD_STAGE(kt, slot)                                                       \
+  {                                                                                   \
+    const __amdgpu_buffer_rsrc_t ra_ = __builtin_amdgcn_make_buffer_rsrc(             \
+        (void*)(A_base + (int64_t)(kt) * a_slab), 0, 0x7fffffff, 0x00020000);         \
+    const __amdgpu_buffer_rsrc_t rb_ = __builtin_amdgcn_make_buffer_rsrc(             \
+        (void*)(B_base + (int64_t)(kt) * b_slab), 0, 0x7fffffff, 0x00020000);         \
+    _Pragma("unroll") for (int t = 0; t < NLA; ++t)                                   \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                     \
+            ra_, (lds_void_t*)(dstA + (slot) * SLOT + t * 4096), 16, a_src[t], 0, 0, 0); \
+    _Pragma("unroll") for (int t = 0; t < NLB; ++t)                                   \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(                                     \
+            rb_, (lds_void_t*)(dstB + (slot) * SLOT + t * 4096), 16, b_src[t], 0, 0, 0); \
+  }
   const int swz = ((lane & 31) >> 2) & 3;
-  f32x16_t acc[2][2];
+  f32x16_t acc[RB][CB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < CB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  if (nk > 0) load_stage(0, 0);
+  if (nk > 0) WG_LOAD_STAGE(0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int slot = kt & 1;
     if (kt + 1 < nk) {
-      load_stage(kt + 1, slot ^ 1);
-      ring_barrier<4>();  // this stage's 4 loads are older than the next stage's 4
+      WG_LOAD_STAGE(kt + 1, slot ^ 1);
+      ring_barrier<NLA + NLB>();  // this stage's loads are older than the next stage's
     } else {
       ring_barrier<0>();
     }
-    const char* As = smem + slot * 2 * WG_SLOT;
-    const char* Bs = As + WG_SLOT;
+    const char* As = smem + slot * SLOT;
+    const char* Bs = As + SLOT_A;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int ch = ((2 * ks + (lane >> 5)) ^ swz) * 16;
-      bf16x8_t fa[2], fb[2];
+      bf16x8_t fa[RB], fb[CB];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * 64 + 32 * i + (lane & 31)) * WG_ROWB + ch);
+      for (int i = 0; i < RB; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(
+            As + (wm * (TM / 2) + 32 * i + (lane & 31)) * WG_ROWB + ch);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * 64 + 32 * j + (lane & 31)) * WG_ROWB + ch);
+      for (int j = 0; j < CB; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8_t*>(
+            Bs + (wn * (TN / 2) + 32 * j + (lane & 31)) * WG_ROWB + ch);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < RB; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < CB; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
     // every wavefront is done reading this slot before it is refilled (its LDS
     // reads have landed; the next stage's loads may stay in flight)
     ring_barrier<63>();
   }
+#undef WG_LOAD_STAGE
   // D[i][j] of a 32 x 32 block: lane j + 32 ((i / 4) % 2), register 4 (i / 8) + i % 4.
-  // The tile leaves through LDS in two halves of 64 rows (the wavefronts with
-  // wm = h hold half h), as 16-byte stores of whole 512-byte row segments.
+  // The tile leaves through LDS in parts of 64 rows (part h: wavefronts with
+  // wm = h / (RB / 2), their row blocks 2 (h % (RB / 2)) and the next), as
+  // 16-byte stores of whole 512-byte row segments.
   float* Cs = reinterpret_cast<float*>(smem);
   float* Cg = p.C + (int64_t)g * p.M * p.N;
   const int lrow4 = 4 * (lane >> 5), lcol = lane & 31;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    if (wm == h) {
+  for (int h = 0; h < TM / 64; ++h) {
+    if (wm == h / (RB / 2)) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i2 = 0; i2 < 2; ++i2) {
+        const int i = 2 * (h % (RB / 2)) + i2;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < CB; ++j)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int ml = 32 * i + 8 * (v >> 2) + lrow4 + (v & 3);
-            const int nl = wn * 64 + 32 * j + lcol;
-            Cs[ml * WG_PITCH + nl] = acc[i][j][v];
+            const int ml = 32 * i2 + 8 * (v >> 2) + lrow4 + (v & 3);
+            const int nl = wn * (TN / 2) + 32 * j + lcol;
+            Cs[ml * PITCH + nl] = acc[i][j][v];
           }
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int idx = q * 256 + tid;  // 32 chunks of 4 floats per row
-      const int ml = idx >> 5, nc = (idx & 31) * 4;
+    for (int q = 0; q < TN / 16; ++q) {
+      const int idx = q * 256 + tid;  // TN / 4 chunks of 4 floats per row
+      const int ml = idx / (TN / 4), nc = (idx % (TN / 4)) * 4;
       const int m = m0 + 64 * h + ml, n = n0 + nc;
       if (m < p.M && n < p.N) {
-        const float4 val = *reinterpret_cast<const float4*>(Cs + ml * WG_PITCH + nc);
+        const float4 val = *reinterpret_cast<const float4*>(Cs + ml * PITCH + nc);
         *reinterpret_cast<float4*>(Cg + (int64_t)m * p.N + n) = val;
       }
     }
     __syncthreads();
   }
+}
+
+template <int RB, int CB>
+__global__ __launch_bounds__(256) void wgrad_kernel(WgradProblem p, int mtiles, int ntiles,
+                                                     int xcd_major, int m_inner) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * wg_slot<RB, CB>()];
+  wgrad_tile<RB, CB>(p, mtiles, ntiles, xcd_major, m_inner, smem);
 }
 
 }  // namespace
@@ -641,14 +671,19 @@ hipError_t launch_wgrad(const bf16_t* A, const bf16_t* B, const int32_t* kofs, i
   if (G <= 0 || M <= 0 || N <= 0) return hipSuccess;
   if (N % 4 != 0) return hipErrorInvalidValue;  // 16-byte stores of C rows
   // byte offsets of up to 128 rows of a block within the buffer descriptor
-  if ((int64_t)WG_TILE * max_rows * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  const int mt = (M + WG_TILE - 1) / WG_TILE, nt = (N + WG_TILE - 1) / WG_TILE;
+  (void)max_rows;  // the k-blocked operands keep every load offset within a slab
   const int xcd_major = G >= 8;
+  const int tm = xcd_major ? 256 : 128, tn = 128;  // taller tiles where there are many groups
+  const int mt = (M + tm - 1) / tm, nt = (N + tn - 1) / tn;
   const int64_t tiles = (int64_t)(xcd_major ? (G + 7) / 8 * 8 : G) * mt * nt;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
   WgradProblem p{A, B, kofs, G, M, N, C};
-  hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)tiles), dim3(256), 0, s, p, mt, nt, xcd_major,
-                     (int)(M <= N));
+  if (tm == 256)
+    hipLaunchKernelGGL((wgrad_kernel<4, 2>), dim3((unsigned)tiles), dim3(256), 0, s, p, mt, nt,
+                       xcd_major, (int)(M <= N));
+  else
+    hipLaunchKernelGGL((wgrad_kernel<2, 2>), dim3((unsigned)tiles), dim3(256), 0, s, p, mt, nt,
+                       xcd_major, (int)(M <= N));
   return hipGetLastError();
 }
 
