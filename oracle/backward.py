@@ -43,11 +43,20 @@ from . import moe_zc as _layer
 
 
 def backward(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, K: int, dy,
-             logits32=None):
+             logits32=None, experts=None, want_dx=True):
     """Gradients of sum(y * dy) for the layer of moe_zc.forward.  Routing uses
     ``logits32`` when given (as the forward does), else the fp64 logits rounded
     once to fp32.  Returns dict dx [T, d], dw_router [E, d], dw_gate,
-    dw_up [N, I, d], dw_down [N, d, I] (fp64), and the routing used."""
+    dw_up [N, I, d], dw_down [N, d, I] (fp64), and the routing used.
+
+    Subsets for large layers (the arithmetic is the same):
+    - ``experts``: a list of FFN experts; only their weight gradients are
+      formed, returned as dicts {e: array} under the same keys.  Expert e's
+      gradients depend only on the tokens routed to e, so passing exactly
+      those tokens gives them in full.
+    - ``want_dx=False`` skips dx, dlogits and dw_router.  dx of a token
+      depends only on that token, so passing a sample of tokens gives their
+      rows of dx in full."""
     x64 = _layer._f64(x)
     wr = _layer._f64(w_router)
     dy64 = _layer._f64(dy)
@@ -60,12 +69,21 @@ def backward(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, K: int, dy
     gate = rt["gate"].astype(np.float64)
     I = w_gate.shape[1] if N > 0 else 0
     dx = np.zeros((T, d))
-    dwg = np.zeros((N, I, d))
-    dwu = np.zeros((N, I, d))
-    dwd = np.zeros((N, d, I))
+    if experts is None:
+        dwg = np.zeros((N, I, d))
+        dwu = np.zeros((N, I, d))
+        dwd = np.zeros((N, d, I))
+        loop = np.unique(idx[idx < N])
+    else:
+        dwg = {int(e): np.zeros((I, d)) for e in experts}
+        dwu = {int(e): np.zeros((I, d)) for e in experts}
+        dwd = {int(e): np.zeros((d, I)) for e in experts}
+        loop = np.unique(idx[idx < N]) if want_dx else np.asarray(sorted(dwg), dtype=np.int64)
     dp = np.zeros((T, E))
-    for e in np.unique(idx[idx < N]):
+    for e in loop:
         tt, kk = np.nonzero(idx == e)          # a token chooses an expert at most once
+        if len(tt) == 0:
+            continue
         xe = x64[tt]
         wg, wu, wd = (_layer._f64(w[int(e)]) for w in (w_gate, w_up, w_down))
         a = xe @ wg.T
@@ -79,10 +97,14 @@ def backward(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, K: int, dy
         dh = dE @ wd
         da = dh * u * s * (1.0 + a * (1.0 - s))
         du = dh * a * s
-        dx[tt] += da @ wg + du @ wu
-        dwd[e] += dE.T @ h
-        dwg[e] += da.T @ xe
-        dwu[e] += du.T @ xe
+        if want_dx:
+            dx[tt] += da @ wg + du @ wu
+        if experts is None or int(e) in dwg:
+            dwd[int(e)] += dE.T @ h
+            dwg[int(e)] += da.T @ xe
+            dwu[int(e)] += du.T @ xe
+    if not want_dx:
+        return {"dw_gate": dwg, "dw_up": dwu, "dw_down": dwd, "route": rt}
     tz, kz = np.nonzero(idx >= N)
     dp[tz, idx[tz, kz]] = (dy64[tz] * x64[tz]).sum(axis=1)
     np.add.at(dx, tz, gate[tz, kz][:, None] * dy64[tz])

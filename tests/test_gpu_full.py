@@ -67,3 +67,56 @@ def test_skew_layer_then_pid_step_then_reroute():
     l1, l2 = g1["loads"][: w.N].astype(float), g2["loads"][: w.N].astype(float)
     assert l2.max() / l2.mean() < l1.max() / l1.mean()          # busiest expert relieved
     assert np.abs(g2["loads"] - target).sum() < np.abs(g1["loads"] - target).sum()
+
+
+def test_full_size_backward_prefill():
+    """The training step that `bench.py --pass backward` times, at the prefill
+    size: packed forward saving a | u, then moe_zc_backward from the saved
+    values and the packed weight transposes.  Routing is checked for every
+    token.  dx is checked on a token sample, since a token's dx depends only
+    on that token.  The weight gradients are checked for two experts, each
+    from exactly the tokens routed to it.  Bar: max |G - G_ref| <= 1e-2 *
+    max |G_ref| per checked tensor.  dW_router needs every token's expert
+    outputs and is covered at the mid and edge sizes (its dl enters dx here)."""
+    from oracle import backward as obwd
+    from workloads import make_upstream_grad
+    w = get_workload("prefill")
+    print("[backward prefill] generating inputs", flush=True)
+    inp = make_inputs(w, device=DEV)
+    dy = make_upstream_grad(w, DEV)
+    aux = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV, keys=m.AUX_KEYS + ("act",), I=w.I)
+    gu, dn = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    m.moe_zc_forward_packed(inp["x"], inp["w_router"], inp["bias"], gu, dn, w.N, w.Z, w.K, w.I,
+                            residual=inp["residual"], aux=aux)
+    torch.cuda.synchronize()
+    del gu, dn
+    tr = m.moe_zc_transpose_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    print("[backward prefill] backward", flush=True)
+    g = m.moe_zc_backward(inp["x"], inp["w_router"], None, None, tr, aux, dy, w.N, w.Z, w.K, w.I)
+    torch.cuda.synchronize()
+    del tr
+    l32 = aux["logits"].cpu().numpy()
+    bias = inp["bias"].cpu().numpy()
+    idx = aux["topk_idx"].cpu().numpy()
+    assert np.array_equal(idx, oracle.route(l32, bias, w.K, w.N)["idx"]), "routing"
+
+    def check(name, got, want):
+        scale = np.abs(want).max()
+        err = np.abs(got - want).max()
+        print(f"[backward prefill] {name}: max|err| / max|ref| = {err / scale:.2e}", flush=True)
+        assert err <= 1e-2 * scale, f"{name}: {err:.3e} > 1e-2 * {scale:.3e}"
+
+    rng = np.random.default_rng(3)
+    s = np.sort(rng.choice(w.T, 4, replace=False))
+    st = torch.from_numpy(s).to(DEV)
+    ref = obwd.backward(inp["x"][st], inp["w_router"], bias, inp["w_gate"], inp["w_up"],
+                        inp["w_down"], w.N, w.Z, w.K, dy[st], logits32=l32[s], experts=[])
+    check(f"dx tokens {s.tolist()}", g["dx"][st].float().cpu().double().numpy(), ref["dx"])
+    for e in np.sort(rng.choice(np.unique(idx[idx < w.N]), 2, replace=False)):
+        tt = np.nonzero((idx == e).any(axis=1))[0]
+        ti = torch.from_numpy(tt).to(DEV)
+        ref = obwd.backward(inp["x"][ti], inp["w_router"], bias, inp["w_gate"], inp["w_up"],
+                            inp["w_down"], w.N, w.Z, w.K, dy[ti], logits32=l32[tt],
+                            experts=[int(e)], want_dx=False)
+        for k in ("dw_gate", "dw_up", "dw_down"):
+            check(f"{k}[{e}] ({len(tt)} rows)", g[k][int(e)].cpu().double().numpy(), ref[k][int(e)])
