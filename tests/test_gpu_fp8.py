@@ -142,3 +142,23 @@ def test_fp8_rejects_unsupported_shapes():
     with pytest.raises(m.MoeZcError):
         m.moe_zc_forward_packed_fp8(inp["x"], inp["w_router"], inp["bias"], None, None, 0,
                                     w.N + w.Z, w.K, w.I)
+
+
+def test_fp8_full_size_prefill():
+    """The block-FP8 forward that `bench.py --precision fp8` times, at the
+    prefill size: routing and grouping for every token (equal to the bf16
+    path's, the router is not quantized), and the layer output on a token
+    sample against the oracle's layer on dequantized FP8 operands (tokens are
+    independent, so a sample is exact)."""
+    from gpu_check import gpu_expert_getter
+    w = get_workload("prefill")
+    print("[fp8 prefill] generating inputs", flush=True)
+    inp = make_inputs(w, device=DEV)
+    gu8 = m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"])
+    dn = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])[1]
+    g = run_gpu(w, inp, packed=(gu8, dn), fp8=True)
+    del gu8, dn
+    sample = np.sort(np.random.default_rng(4).choice(w.T, 6, replace=False))
+    print(f"[fp8 prefill] checking tokens {sample.tolist()}", flush=True)
+    print("prefill fp8", check_forward(w, inp, g, y_tokens=sample, fp8=True,
+                                       get_expert=gpu_expert_getter(inp)), flush=True)
