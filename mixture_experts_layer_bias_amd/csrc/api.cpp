@@ -356,17 +356,13 @@ BwdPlan make_bwd_plan(const Shape& s) {
 }
 
 // Conditions of the backward beyond the forward's: bf16, grouped rows of x and
-// dy gathered with 32-bit byte offsets, padded group columns below 2^31,
-// expert blocks addressed with 32-bit byte offsets.
+// dy gathered with 32-bit byte offsets, padded group columns below 2^31.
 moe_zc_status check_bwd_shape(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z, int32_t K,
                               Shape* s) {
   const moe_zc_status st = check_shape(T, d, I, N, Z, K, MOE_ZC_BF16, s);
   if (st != MOE_ZC_OK) return st;
   if (!s->gather) return MOE_ZC_ERR_UNSUPPORTED;
   if (round_up(s->smax + 64 * (int64_t)N, 64) >= (int64_t(1) << 31)) return MOE_ZC_ERR_UNSUPPORTED;
-  // the weight-gradient GEMM addresses 128 rows of an expert block (at most
-  // T rounded up to 64 columns each) with 32-bit byte offsets
-  if (128 * round_up(T, 64) * 2 >= (int64_t(1) << 31)) return MOE_ZC_ERR_UNSUPPORTED;
   return MOE_ZC_OK;
 }
 
@@ -656,10 +652,9 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
     MOE_ZC_TRY(launch_transpose(a, stream));
     a = blocked(B(pl.H), I, B(pl.HT), I);
     MOE_ZC_TRY(launch_transpose(a, stream));
-    const int64_t most = round_up(T, 64);  // rows of one expert: at most T
-    MOE_ZC_TRY(launch_wgrad(B(pl.ET), B(pl.HT), kofs, N, (int)d, (int)I, most, dw_down, stream));
-    MOE_ZC_TRY(launch_wgrad(B(pl.DAT), B(pl.XT), kofs, N, (int)I, (int)d, most, dw_gate, stream));
-    MOE_ZC_TRY(launch_wgrad(B(pl.DUT), B(pl.XT), kofs, N, (int)I, (int)d, most, dw_up, stream));
+    MOE_ZC_TRY(launch_wgrad(B(pl.ET), B(pl.HT), kofs, N, (int)d, (int)I, dw_down, stream));
+    MOE_ZC_TRY(launch_wgrad(B(pl.DAT), B(pl.XT), kofs, N, (int)I, (int)d, dw_gate, stream));
+    MOE_ZC_TRY(launch_wgrad(B(pl.DUT), B(pl.XT), kofs, N, (int)I, (int)d, dw_up, stream));
   }
   // per token: gate gradients, router softmax backward, dx from expert rows and
   // identity slots
@@ -691,7 +686,7 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
   a = tr(x, d, B(pl.xT), pl.T64, (int)d, pl.T64, T);
   a.kofs = kofs_r; a.ngroups = 1;
   MOE_ZC_TRY(launch_transpose(a, stream));
-  MOE_ZC_TRY(launch_wgrad(B(pl.dlT), B(pl.xT), kofs_r, 1, E, (int)d, pl.T64, dw_router, stream));
+  MOE_ZC_TRY(launch_wgrad(B(pl.dlT), B(pl.xT), kofs_r, 1, E, (int)d, dw_router, stream));
   return MOE_ZC_OK;
 }
 

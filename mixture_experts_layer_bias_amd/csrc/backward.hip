@@ -667,11 +667,9 @@ hipError_t launch_set_range(int32_t* out, int a, int b, hipStream_t s) {
 }
 
 hipError_t launch_wgrad(const bf16_t* A, const bf16_t* B, const int32_t* kofs, int G, int M,
-                        int N, int64_t max_rows, float* C, hipStream_t s) {
+                        int N, float* C, hipStream_t s) {
   if (G <= 0 || M <= 0 || N <= 0) return hipSuccess;
   if (N % 4 != 0) return hipErrorInvalidValue;  // 16-byte stores of C rows
-  // byte offsets of up to 128 rows of a block within the buffer descriptor
-  (void)max_rows;  // the k-blocked operands keep every load offset within a slab
   const int xcd_major = G >= 8;
   const int tm = xcd_major ? 256 : 128, tn = 128;  // taller tiles where there are many groups
   const int mt = (M + tm - 1) / tm, nt = (N + tn - 1) / tn;

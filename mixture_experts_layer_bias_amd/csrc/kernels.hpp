@@ -183,9 +183,9 @@ hipError_t launch_dx_sum(const bf16_t* dy, const int32_t* idx, const float* gate
 hipError_t launch_set_range(int32_t* out, int a, int b, hipStream_t s);
 // C[g] = A_g B_g^T, fp32 [G][M][N], with A_g [M][R_g] and B_g [N][R_g] the
 // expert-blocked operands in the transposes' k-blocked layout (slabs of 32
-// columns; R_g = kofs[g+1] - kofs[g] <= max_rows).
+// columns; R_g = kofs[g+1] - kofs[g]).
 hipError_t launch_wgrad(const bf16_t* A, const bf16_t* B, const int32_t* kofs, int G, int M,
-                        int N, int64_t max_rows, float* C, hipStream_t s);
+                        int N, float* C, hipStream_t s);
 
 // fp32 FMA path (gemm_simt.hip).
 hipError_t launch_simt_gemm(const GemmProblem& p, int epilogue, int64_t max_rows,
