@@ -79,39 +79,41 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     key[i] = (j < E) ? __fadd_rn(p32[i], bias[j]) : -INFINITY;
   }
 
+  // K rounds of a wavefront arg-max, branch-free: each lane offers its best
+  // key not yet taken, the xor butterfly keeps (key desc, index asc), and the
+  // winner's lane marks it taken.  Lane r keeps round r's index and gate;
+  // lanes < K store them together at the end.
   uint32_t taken = 0u;
+  int my_idx = 0;
+  float my_gate = 0.f;
   for (int r = 0; r < K; ++r) {
-    float bk = -INFINITY;
+    float bk = -INFINITY, bp = 0.f;
     int bi = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int j = lane + 64 * i;
       // j grows with i, so a strict '>' keeps the lower index on a tie
-      if (j < E && !((taken >> i) & 1u) && (key[i] > bk || bi == 0x7fffffff)) {
-        bk = key[i];
-        bi = j;
-      }
+      const bool better = j < E && !((taken >> i) & 1u) && (key[i] > bk || bi == 0x7fffffff);
+      bk = better ? key[i] : bk;
+      bp = better ? p32[i] : bp;
+      bi = better ? j : bi;
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const float ok = __shfl_xor(bk, off);
       const int oi = __shfl_xor(bi, off);
-      if (ok > bk || (ok == bk && oi < bi)) {
-        bk = ok;
-        bi = oi;
-      }
+      const bool take = ok > bk || (ok == bk && oi < bi);
+      bk = take ? ok : bk;
+      bi = take ? oi : bi;
     }
-    if ((bi & 63) == lane) {
-      const int sel = bi >> 6;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        if (i == sel) {
-          taken |= 1u << i;
-          idx_out[t * K + r] = bi;
-          gate_out[t * K + r] = p32[i];
-        }
-      }
-    }
+    const float gate = __shfl(bp, bi & 63);      // the winner's lane holds its gate
+    taken |= ((bi & 63) == lane) ? (1u << (bi >> 6)) : 0u;
+    my_idx = (lane == r) ? bi : my_idx;
+    my_gate = (lane == r) ? gate : my_gate;
+  }
+  if (lane < K) {
+    idx_out[t * K + lane] = my_idx;
+    gate_out[t * K + lane] = my_gate;
   }
 }
 
