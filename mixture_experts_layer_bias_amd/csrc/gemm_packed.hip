@@ -250,6 +250,35 @@ __device__ __forceinline__ void run_packed(const GemmProblem& p, const TileCoord
   const int lrow4 = 4 * (lane >> 5);
   const int lcol = lane & 31;
   if (EPI == kStoreF32) {
+    float* __restrict__ Cf = static_cast<float*>(p.C) + (int64_t)split * p.c_split_stride;
+    if ((p.Nout & 3) == 0 && (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(Cf) & 15) == 0) {
+      // through a wavefront-private LDS tile (the ring is free), one 32-row
+      // block at a time, so that global stores are whole 16-byte row pieces
+      constexpr int OS = 64 + 4;  // padded LDS row (floats)
+      float* ot = reinterpret_cast<float*>(smem) + wave * (32 * OS);
+      const int gcol0 = c.n0 + wave * 64;
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            ot[(8 * (v >> 2) + lrow4 + (v & 3)) * OS + j * 32 + lcol] = acc[i][j][v];
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS writes landed
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int q = lane; q < 32 * 16; q += 64) {
+          const int r = q >> 4, ch = q & 15;
+          const int grow = c.m0 + i * 32 + r, gcol = gcol0 + ch * 4;
+          if (grow < c.m_end && gcol < p.Nout)
+            *reinterpret_cast<f32x4_t*>(Cf + (int64_t)grow * p.ldc + gcol) =
+                *reinterpret_cast<const f32x4_t*>(ot + r * OS + ch * 4);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block overwrites
+        __builtin_amdgcn_wave_barrier();
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NA; ++i)
 #pragma unroll
