@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MOE_ZC_ABI_VERSION 2
+#define MOE_ZC_ABI_VERSION 3
 
 typedef enum {
   MOE_ZC_OK = 0,
@@ -68,7 +68,9 @@ typedef enum {
 
 /* Limits of this implementation (else MOE_ZC_ERR_UNSUPPORTED):
  *   E = N + Z in [1, 2048]; K in [1, min(E, 32)];
- *   bf16: d a multiple of 64 and I of 128;  f32: d and I multiples of 32;
+ *   bf16: d a multiple of 64 and I of 128 (the gate/up GEMM pairs 128 gate
+ *   and 128 up rows of the same hidden units in one 256-column panel, so
+ *   that SwiGLU needs no second pass);  f32: d and I multiples of 32;
  *   d, I < 2^20, d * I < 2^31, 2 * d * E < 2^31, T * min(K, N) < 2^31 and
  *   T * max(d, I, E) < 2^40. */
 #define MOE_ZC_MAX_EXPERTS 2048
@@ -90,7 +92,8 @@ typedef enum {
  *   loads       [E]     slots routed to each expert (FFN and zero alike);
  *                       this is what moe_zc_bias_update consumes
  *   offsets     [N + 1] exclusive prefix sum of loads[0..N-1]; offsets[N] = S,
- *                       the number of (token, FFN expert) rows
+ *                       the number of (token, FFN expert) rows (there is no
+ *                       separate row-count output: offsets[N] is it)
  *   perm        [T * min(K, N)]  token held by grouped row s (first S valid);
  *                       rows are grouped by expert, tokens ascending
  *   pos         [T, K]  grouped row of slot (t,k), -1 for a zero expert
@@ -331,6 +334,8 @@ size_t moe_zc_backward_workspace_size(int64_t T, int64_t d, int64_t I,
  *   dw_router [E, d] fp32 output
  *   dw_gate, dw_up [N, I, d], dw_down [N, d, I] fp32 outputs (every expert
  *             written; experts no token chose get zeros)
+ *   Every tensor pointer, outputs included, must be 16-byte aligned (else
+ *   MOE_ZC_ERR_INVALID): the kernels use 16-byte vector accesses.
  *   workspace device buffer of moe_zc_backward_workspace_size(...) bytes,
  *             256-byte aligned; contents on entry are ignored.
  * Outputs overwrite (do not accumulate into) their buffers and may not alias
@@ -348,15 +353,22 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router,
 /* Routing alone, from given fp32 logits [T, E] and bias [E]: the softmax,
  * bias key and top-K step of the forward, bit for bit.
  *   topk_idx [T, K] int32 and topk_gate [T, K] fp32 outputs (device).
- * Same validation rules and limits as moe_zc_forward. */
+ *   loads    [E] int32 output (device) or NULL: slots routed to each expert,
+ *            FFN and zero experts alike (what moe_zc_bias_update consumes);
+ *            with T = 0 it is set to zeros.
+ * Same validation rules and limits as moe_zc_forward.  (loads was added in
+ * ABI version 3.) */
 moe_zc_status moe_zc_route(const float* logits, const float* bias, int64_t T,
                            int32_t E, int32_t K, int32_t* topk_idx,
-                           float* topk_gate, hipStream_t stream);
+                           float* topk_gate, int32_t* loads,
+                           hipStream_t stream);
 
 /* PID controller state for moe_zc_bias_update.  Gains live on the host; the
  * error histories are device arrays of E floats, owned by the caller, zeroed
  * before the first step and carried between steps (save and restore them with
- * the bias to resume). */
+ * the bias to resume: that reproduces the uninterrupted run bit for bit).
+ * The velocity form below needs no step counter: the two error histories
+ * are the whole state, so the struct carries none. */
 typedef struct moe_zc_pid {
   float kp, ki, kd;
   float* e_prev;    /* [E] error of the previous step        */

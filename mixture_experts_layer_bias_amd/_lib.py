@@ -92,7 +92,7 @@ def load() -> ctypes.CDLL:
     lib.moe_zc_backward.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.POINTER(MoeZcAux), vp, vp, vp,
                                     vp, vp, vp, i64, i64, i64, i32, i32, i32, vp, sz, vp]
     lib.moe_zc_backward.restype = ctypes.c_int
-    lib.moe_zc_route.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
+    lib.moe_zc_route.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp, vp]
     lib.moe_zc_route.restype = ctypes.c_int
     lib.moe_zc_bias_update.argtypes = [vp, vp, vp, ctypes.POINTER(MoeZcPid), i32, vp]
     lib.moe_zc_bias_update.restype = ctypes.c_int

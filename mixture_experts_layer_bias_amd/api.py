@@ -274,8 +274,10 @@ def moe_zc_forward_packed(x: torch.Tensor, w_router: torch.Tensor, bias: torch.T
 
 def moe_zc_route(logits: torch.Tensor, bias: torch.Tensor, K: int,
                  topk_idx: Optional[torch.Tensor] = None,
-                 topk_gate: Optional[torch.Tensor] = None):
-    """(topk_idx, topk_gate) from fp32 logits [T, E] and bias [E]."""
+                 topk_gate: Optional[torch.Tensor] = None,
+                 loads: Optional[torch.Tensor] = None):
+    """(topk_idx, topk_gate) from fp32 logits [T, E] and bias [E]; the expert
+    loads [E] int32 are written into ``loads`` when it is given."""
     lib = _lib.load()
     T, E = logits.shape
     dev = logits.device
@@ -287,8 +289,10 @@ def moe_zc_route(logits: torch.Tensor, bias: torch.Tensor, K: int,
         topk_gate = torch.empty(T, K, dtype=torch.float32, device=dev)
     _need(topk_idx, "topk_idx", torch.int32, (T, K), dev)
     _need(topk_gate, "topk_gate", torch.float32, (T, K), dev)
+    if loads is not None:
+        _need(loads, "loads", torch.int32, (E,), dev)
     code = lib.moe_zc_route(_ptr(logits), _ptr(bias), T, E, K, _ptr(topk_idx), _ptr(topk_gate),
-                            _stream(dev))
+                            _ptr(loads), _stream(dev))
     if code != _lib.MOE_ZC_OK:
         raise MoeZcError(code, "moe_zc_route")
     return topk_idx, topk_gate

@@ -572,6 +572,8 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
     return MOE_ZC_ERR_INVALID;
   if (N > 0 && !act && (!w_gate || !w_up)) return MOE_ZC_ERR_INVALID;
   if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(w_router) ||
+      !aligned16(dw_router) ||
+      (N > 0 && (!aligned16(dw_gate) || !aligned16(dw_up) || !aligned16(dw_down))) ||
       (N > 0 && (!aligned16(w_gate_up_t) || !aligned16(w_down_t))) ||
       (N > 0 && (act ? !aligned16(act) : (!aligned16(w_gate) || !aligned16(w_up)))))
     return MOE_ZC_ERR_INVALID;
@@ -691,13 +693,18 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
 }
 
 moe_zc_status moe_zc_route(const float* logits, const float* bias, int64_t T, int32_t E,
-                           int32_t K, int32_t* topk_idx, float* topk_gate, hipStream_t stream) {
+                           int32_t K, int32_t* topk_idx, float* topk_gate, int32_t* loads,
+                           hipStream_t stream) {
   if (T < 0 || E < 1 || K < 1 || K > E) return MOE_ZC_ERR_INVALID;
   if (E > MOE_ZC_MAX_EXPERTS || K > MOE_ZC_MAX_TOPK) return MOE_ZC_ERR_UNSUPPORTED;
   if (T * K >= (int64_t(1) << 31) || T >= (int64_t(1) << 33)) return MOE_ZC_ERR_UNSUPPORTED;
-  if (T == 0) return MOE_ZC_OK;
+  if (T == 0) {  // no slots: every load is zero
+    if (loads) MOE_ZC_TRY(launch_count_loads(nullptr, 0, K, E, loads, stream));
+    return MOE_ZC_OK;
+  }
   if (!logits || !bias || !topk_idx || !topk_gate) return MOE_ZC_ERR_INVALID;
   MOE_ZC_TRY(launch_topk(logits, bias, T, E, K, topk_idx, topk_gate, stream));
+  if (loads) MOE_ZC_TRY(launch_count_loads(topk_idx, T, K, E, loads, stream));
   return MOE_ZC_OK;
 }
 

@@ -20,6 +20,9 @@ constexpr int kMaxTopK = 32;
 hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int K,
                        int32_t* idx, float* gate, hipStream_t s, int nsplit = 1,
                        int64_t split_stride = 0, float* logits_out = nullptr);
+// loads[e] = slots of idx [T, K] routed to expert e (zeroed first).
+hipError_t launch_count_loads(const int32_t* idx, int64_t T, int K, int E, int32_t* loads,
+                              hipStream_t s);
 // Per 64-token chunk: expert counts [C, E] and each FFN slot's rank among the
 // chunk's earlier tokens (written to rank[T, K], -1 for zero experts).
 hipError_t launch_chunk_hist(const int32_t* idx, int64_t T, int K, int E, int N,

@@ -7,6 +7,8 @@
 // used for selection, K experts per token; PID tuning of the bias).
 #include <math.h>
 
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace moezc {
@@ -146,6 +148,42 @@ hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E,
                        nsplit, split_stride, logits_out);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Expert loads from top-K indices alone (moe_zc_route): loads[e] = number of
+// slots routed to e.  Integer counts, so the atomics below give the same
+// result in any order.  The first launch zeroes loads (a kernel, not a
+// memset, so the sequence can be captured in a graph); the second counts
+// each workgroup's slots in LDS and adds its nonzero counts to loads.
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void count_loads_kernel(const int32_t* __restrict__ idx,
+                                                          int64_t n, int E,
+                                                          int32_t* __restrict__ loads) {
+  __shared__ int32_t hist[kMaxExperts];
+  for (int e = threadIdx.x; e < E; e += 256) hist[e] = 0;
+  __syncthreads();
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    atomicAdd(&hist[idx[i]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256)
+    if (hist[e]) atomicAdd(&loads[e], hist[e]);
+}
+
+hipError_t launch_count_loads(const int32_t* idx, int64_t T, int K, int E, int32_t* loads,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(zero_i32_kernel, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, s, loads,
+                     E);
+  const int64_t n = T * K;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  if (blocks > 0)
+    hipLaunchKernelGGL(count_loads_kernel, dim3((unsigned)blocks), dim3(256), 0, s, idx, n, E,
+                       loads);
   return hipGetLastError();
 }
 

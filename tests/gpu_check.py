@@ -27,12 +27,16 @@ LOGIT_TOL = 1e-4
 Y_TOL = {"bf16": 1e-2, "f32": 1e-5}
 
 
-def run_gpu(w, inp, residual=True, workspace=None, events=None, packed=None, fp8=False):
+def run_gpu(w, inp, residual=True, workspace=None, events=None, packed=None, fp8=False,
+            act=False):
     """One forward through the C ABI; ``packed`` = (gate_up, down) from
     moe_zc_pack_expert_weights selects moe_zc_forward_packed, and with ``fp8``
-    ``packed`` = (gate_up_fp8, down) selects moe_zc_forward_packed_fp8."""
+    ``packed`` = (gate_up_fp8, down) selects moe_zc_forward_packed_fp8.  With
+    ``act`` the forward also saves the expert pre-activations (aux "act", left
+    on the device as out["act_t"])."""
     dev = inp["x"].device
-    aux = m.alloc_aux(w.T, w.N, w.Z, w.K, dev)
+    keys = m.AUX_KEYS + (("act",) if act else ())
+    aux = m.alloc_aux(w.T, w.N, w.Z, w.K, dev, keys=keys, I=w.I if act else None)
     res = inp["residual"] if residual else None
     if fp8:
         gu, dn = packed if packed is not None else (None, None)
@@ -48,7 +52,9 @@ def run_gpu(w, inp, residual=True, workspace=None, events=None, packed=None, fp8
                                     w.N, w.Z, w.K, w.I, residual=res, aux=aux,
                                     workspace=workspace, events=events)
     torch.cuda.synchronize()
-    out = {k: v.cpu().numpy() for k, v in aux.items()}
+    out = {k: v.cpu().numpy() for k, v in aux.items() if k != "act"}
+    if act:
+        out["act_t"] = aux["act"]
     out["y_t"] = y
     out["y"] = y.float().cpu().double().numpy()
     return out
@@ -151,3 +157,69 @@ def gpu_expert_getter(inp):
     def get(e):
         return inp["w_gate"][e].cpu(), inp["w_up"][e].cpu(), inp["w_down"][e].cpu()
     return get
+
+
+def check_act(w, inp, g, experts, fp8=False, get_expert=None):
+    """Pre-activations a | u that the forward saved (aux "act", bf16) for every
+    grouped row of each expert in ``experts``, against the oracle's fp64
+    a = x W_gate^T and u = x W_up^T of the same tokens (with ``fp8``, on the
+    oracle's dequantized block-FP8 operands).  Every hidden unit of every row
+    is compared, so each weight panel and row block of those experts' tiles
+    is covered.  Bar: max |act - ref| <= 1e-2 * max |ref| per expert (the
+    layer's bf16 bar; the stored values carry one bf16 rounding)."""
+    off = g["offsets"]
+    perm = g["perm"]
+    x = inp["x"].cpu()
+    if get_expert is None:
+        get_expert = gpu_expert_getter(inp)
+    out = {}
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        assert r1 > r0, f"expert {e} has no rows"
+        wg, wu, _ = get_expert(int(e))
+        wg, wu = oracle.moe_zc._f64(wg), oracle.moe_zc._f64(wu)
+        if fp8:
+            wg = oracle.mx.mx_dequantize(*oracle.mx.mx_quantize(wg, axis=-1), axis=-1)
+            wu = oracle.mx.mx_dequantize(*oracle.mx.mx_quantize(wu, axis=-1), axis=-1)
+        xr = oracle.moe_zc._f64(x[torch.from_numpy(perm[r0:r1].astype(np.int64))])
+        if fp8:  # x is quantized per token, so its rows quantize alone
+            xr = oracle.mx.mx_dequantize(*oracle.mx.mx_quantize(xr, axis=-1), axis=-1)
+        ref = np.concatenate([xr @ wg.T, xr @ wu.T], axis=1)
+        got = g["act_t"][r0:r1].float().cpu().double().numpy()
+        scale = np.abs(ref).max()
+        err = np.abs(got - ref).max()
+        assert err <= 1e-2 * scale, f"act of expert {e}: {err:.3e} > 1e-2 * {scale:.3e}"
+        out[int(e)] = {"rows": r1 - r0, "err_frac": float(err / scale)}
+    return out
+
+
+def act_experts(loads, N, rng, tile_rows=256):
+    """Experts whose whole rows check_act covers: the most loaded (split over
+    two row tiles when it holds more than ``tile_rows`` rows), the least loaded
+    touched one, and two random touched ones."""
+    ld = np.asarray(loads[:N])
+    touched = np.nonzero(ld > 0)[0]
+    hi = int(touched[np.argmax(ld[touched])])
+    lo = int(touched[np.argmin(ld[touched])])
+    rest = np.setdiff1d(touched, [hi, lo])
+    pick = rng.choice(rest, min(2, len(rest)), replace=False).tolist()
+    return [hi, lo] + [int(e) for e in pick]
+
+
+def sample_tokens(g, N, rng, n_random=48, n_split=16, tile_rows=256):
+    """Tokens for the layer-output check: ``n_random`` at random plus up to
+    ``n_split`` whose rows sit in the second row part of an expert that the
+    GEMM splits over two tiles (more than ``tile_rows`` rows), so that every
+    tile class is exercised."""
+    T = g["topk_idx"].shape[0]
+    off = g["offsets"]
+    loads = np.diff(off)
+    split = np.nonzero(loads > tile_rows)[0]
+    picks = set(rng.choice(T, min(n_random, T), replace=False).tolist())
+    if len(split):
+        for e in rng.choice(split, min(n_split, len(split)), replace=False):
+            mt = (loads[e] + tile_rows - 1) // tile_rows
+            rpt = ((loads[e] + mt - 1) // mt + 31) // 32 * 32   # rows of the first part
+            r = rng.integers(off[e] + rpt, off[e + 1])
+            picks.add(int(g["perm"][r]))
+    return np.array(sorted(picks))

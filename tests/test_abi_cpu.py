@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.moe_zc_abi_version() == 2
+    assert lib.moe_zc_abi_version() == 3
     for code in range(5):
         assert lib.moe_zc_status_string(code)
     assert lib.moe_zc_status_string(99) == b"unknown status"
@@ -127,12 +127,14 @@ def test_packed_sizes_and_validation(lib):
 
 
 def test_route_and_bias_update_validation(lib):
-    r = lib.moe_zc_route
-    assert r(FAKE, FAKE, 0, 12, 3, FAKE, FAKE, None) == OK
-    assert r(FAKE, FAKE, 10, 12, 13, FAKE, FAKE, None) == INVALID
-    assert r(FAKE, FAKE, 10, 0, 1, FAKE, FAKE, None) == INVALID
-    assert r(None, FAKE, 10, 12, 3, FAKE, FAKE, None) == INVALID
-    assert r(FAKE, FAKE, 10, 4096, 3, FAKE, FAKE, None) == UNSUPPORTED
+    r = lib.moe_zc_route            # (logits, bias, T, E, K, idx, gate, loads, stream)
+    assert r(FAKE, FAKE, 0, 12, 3, FAKE, FAKE, None, None) == OK
+    assert r(FAKE, FAKE, 10, 12, 13, FAKE, FAKE, None, None) == INVALID
+    assert r(FAKE, FAKE, 10, 12, 13, FAKE, FAKE, FAKE, None) == INVALID
+    assert r(FAKE, FAKE, 10, 0, 1, FAKE, FAKE, None, None) == INVALID
+    assert r(None, FAKE, 10, 12, 3, FAKE, FAKE, None, None) == INVALID
+    assert r(None, FAKE, 10, 12, 3, FAKE, FAKE, FAKE, None) == INVALID
+    assert r(FAKE, FAKE, 10, 4096, 3, FAKE, FAKE, None, None) == UNSUPPORTED
     u = lib.moe_zc_bias_update
     pid = _lib.MoeZcPid(0.5, 0.5, 0.0, 1 << 20, 1 << 21)
     assert u(FAKE, FAKE, FAKE, None, 12, None) == INVALID
@@ -178,8 +180,9 @@ def test_backward_sizes_and_validation(lib):
     T, d, I, N, Z, K = 64, 128, 128, 8, 4, 3
     nb = ws(T, d, I, N, Z, K)
     args = lambda **o: [o.get("x", FAKE), FAKE, FAKE, FAKE, o.get("gut", FAKE), FAKE,
-                        o.get("aux", ctypes.byref(aux)), FAKE, o.get("dx", FAKE), FAKE,
-                        o.get("dwg", FAKE), FAKE, FAKE, o.get("T", T), d, I, o.get("N", N), Z, K,
+                        o.get("aux", ctypes.byref(aux)), FAKE, o.get("dx", FAKE),
+                        o.get("dwr", FAKE), o.get("dwg", FAKE), o.get("dwu", FAKE),
+                        o.get("dwd", FAKE), o.get("T", T), d, I, o.get("N", N), Z, K,
                         o.get("ws", FAKE), o.get("nb", nb), None]
     assert bw(*args(T=0)) == OK
     assert bw(*args(x=None)) == INVALID
@@ -190,6 +193,9 @@ def test_backward_sizes_and_validation(lib):
     assert bw(*args(ws=None)) == WORKSPACE
     assert bw(*args(nb=100)) == WORKSPACE
     assert bw(*args(x=ctypes.c_void_p((1 << 20) + 2))) == INVALID
+    # the gradient outputs are written with 16-byte stores: misaligned is refused
+    for k in ("dwr", "dwg", "dwu", "dwd"):
+        assert bw(*args(**{k: ctypes.c_void_p((1 << 20) + 8)})) == INVALID, k
     no_perm = _lib.MoeZcAux(*(1 << 20,) * 5, None, 1 << 20, None)
     assert bw(*args(aux=ctypes.byref(no_perm))) == INVALID
     tr = lib.moe_zc_transpose_expert_weights

@@ -86,3 +86,47 @@ def test_closed_loop_pid_tracks_budget():
     assert gpu_ffn[0] < BUDGET - 1.5
     assert abs(np.mean(gpu_ffn[-4:]) - BUDGET) < 0.25, gpu_ffn
 
+
+
+def test_pid_save_restore_resumes_bit_for_bit():
+    """The controller's whole state is (bias, e_prev, e_prev2): n straight
+    closed-loop steps equal k steps, a save of that state to the host, a
+    restore into fresh device buffers and a fresh PidState, and n - k more
+    steps, bit for bit (bias, both histories, and every step's loads)."""
+    w = W
+    inp = make_inputs(w, device=DEV)
+    packed = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    target = torch.from_numpy(oracle.budget_target(w.T, w.K, w.N, w.Z, 5.0).astype(np.float32)).to(DEV)
+    n, k = 8, 3
+
+    def run(bias, pid, steps, loads_log):
+        aux = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV, keys=("loads", "offsets"))
+        for _ in range(steps):
+            m.moe_zc_forward_packed(inp["x"], inp["w_router"], bias, packed[0], packed[1], w.N,
+                                    w.Z, w.K, w.I, aux=aux)
+            loads_log.append(aux["loads"].cpu().numpy().copy())
+            m.moe_zc_bias_update(aux["loads"], target, bias, pid)
+        torch.cuda.synchronize()
+
+    straight_loads, resumed_loads = [], []
+    b1 = inp["bias"].clone()
+    p1 = m.PidState(w.E, DEV, kp=0.5, ki=0.3, kd=0.2)
+    run(b1, p1, n, straight_loads)
+    b2 = inp["bias"].clone()
+    p2 = m.PidState(w.E, DEV, kp=0.5, ki=0.3, kd=0.2)
+    run(b2, p2, k, resumed_loads)
+    saved = {"bias": b2.cpu().numpy(), "e1": p2.e_prev.cpu().numpy(),
+             "e2": p2.e_prev2.cpu().numpy(), "gains": (p2.kp, p2.ki, p2.kd)}
+    del b2, p2
+    b3 = torch.from_numpy(saved["bias"]).to(DEV)
+    p3 = m.PidState(w.E, DEV, *saved["gains"])
+    p3.e_prev.copy_(torch.from_numpy(saved["e1"]))
+    p3.e_prev2.copy_(torch.from_numpy(saved["e2"]))
+    run(b3, p3, n - k, resumed_loads)
+    for s, (a, b) in enumerate(zip(straight_loads, resumed_loads)):
+        assert np.array_equal(a, b), f"loads differ at step {s}"
+    assert torch.equal(b1, b3)
+    assert torch.equal(p1.e_prev, p3.e_prev)
+    assert torch.equal(p1.e_prev2, p3.e_prev2)
+    # the loop did move the bias (the test would be empty otherwise)
+    assert not torch.equal(b1, inp["bias"])

@@ -129,9 +129,10 @@ def test_fp8_mid_vs_oracle():
     inp = make_inputs(w, device=DEV)
     packed = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
     fp8 = (m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"]), packed[1])
-    g = run_gpu(w, inp, packed=fp8, fp8=True)
+    g = run_gpu(w, inp, residual=False, packed=fp8, fp8=True)
     sample = np.sort(np.random.default_rng(0).choice(w.T, 384, replace=False))
-    print("mid fp8", check_forward(w, inp, g, y_tokens=sample, fp8=True), flush=True)
+    print("mid fp8", check_forward(w, dict(inp, residual=None), g, y_tokens=sample, fp8=True),
+          flush=True)
 
 
 def test_fp8_rejects_unsupported_shapes():
@@ -146,19 +147,27 @@ def test_fp8_rejects_unsupported_shapes():
 
 def test_fp8_full_size_prefill():
     """The block-FP8 forward that `bench.py --precision fp8` times, at the
-    prefill size: routing and grouping for every token (equal to the bf16
-    path's, the router is not quantized), and the layer output on a token
-    sample against the oracle's layer on dequantized FP8 operands (tokens are
-    independent, so a sample is exact)."""
-    from gpu_check import gpu_expert_getter
+    prefill size, with no residual (y is the expert mixture alone): routing
+    and grouping for every token (equal to the bf16 path's, the router is not
+    quantized); the saved pre-activations of four whole experts (every row and
+    hidden unit: the gate/up projection that runs in FP8) against the oracle
+    on dequantized operands; and the layer output on a token sample against
+    the oracle's layer on dequantized FP8 operands (tokens are independent, so
+    a sample is exact).  The sample is small because the oracle quantizes each
+    touched expert's weights in fp64 (about a second per matrix)."""
+    from gpu_check import act_experts, check_act, gpu_expert_getter
     w = get_workload("prefill")
     print("[fp8 prefill] generating inputs", flush=True)
-    inp = make_inputs(w, device=DEV)
+    inp = make_inputs(w, device=DEV, residual=False)
     gu8 = m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"])
     dn = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])[1]
-    g = run_gpu(w, inp, packed=(gu8, dn), fp8=True)
+    g = run_gpu(w, inp, residual=False, packed=(gu8, dn), fp8=True, act=True)
     del gu8, dn
-    sample = np.sort(np.random.default_rng(4).choice(w.T, 6, replace=False))
+    rng = np.random.default_rng(4)
+    experts = act_experts(g["loads"], w.N, rng)
+    print(f"[fp8 prefill] checking the pre-activations of experts {experts}", flush=True)
+    print("prefill fp8 act", check_act(w, inp, g, experts, fp8=True), flush=True)
+    sample = np.sort(rng.choice(w.T, 6, replace=False))
     print(f"[fp8 prefill] checking tokens {sample.tolist()}", flush=True)
     print("prefill fp8", check_forward(w, inp, g, y_tokens=sample, fp8=True,
                                        get_expert=gpu_expert_getter(inp)), flush=True)

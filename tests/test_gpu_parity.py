@@ -36,13 +36,22 @@ def test_route_bit_exact(T, E, K, q):
     if q is not None:
         logits = torch.round(logits * q) / q
         bias = torch.zeros(E)
-    idx, gate = m.moe_zc_route(logits.to(DEV), bias.to(DEV), K)
+    loads = torch.full((E,), -7, dtype=torch.int32, device=DEV)   # overwritten, not added to
+    idx, gate = m.moe_zc_route(logits.to(DEV), bias.to(DEV), K, loads=loads)
     torch.cuda.synchronize()
     rt = oracle.route(logits.numpy(), bias.numpy(), K, min(E, 1))
     assert np.array_equal(idx.cpu().numpy(), rt["idx"])
     assert np.array_equal(gate.cpu().numpy(), rt["gate"])
+    assert np.array_equal(loads.cpu().numpy(), rt["loads"])
     if q is not None:                                  # exact key ties were present
         assert (np.diff(np.sort(rt["key"], axis=1), axis=1) == 0).any()
+
+
+def test_route_loads_with_no_tokens_are_zero():
+    loads = torch.full((40,), 5, dtype=torch.int32, device=DEV)
+    m.moe_zc_route(torch.zeros(0, 40, device=DEV), torch.zeros(40, device=DEV), 3, loads=loads)
+    torch.cuda.synchronize()
+    assert (loads.cpu() == 0).all()
 
 
 def test_route_refuses_topk_above_limit():
@@ -93,10 +102,12 @@ def test_tiny_f32_full():
 
 
 def test_mid_bf16_full_routing_sampled_outputs():
+    """The mid layer with no residual (y is the expert mixture alone, so the
+    bar scales with it); the residual is covered at the edge shapes."""
     w = get_workload("mid")
-    inp = _inputs(w)
+    inp = _inputs(w, residual=None)
     sample = np.random.default_rng(0).choice(w.T, 384, replace=False)
-    rep = check_forward(w, inp, run_gpu(w, inp), y_tokens=np.sort(sample))
+    rep = check_forward(w, inp, run_gpu(w, inp, residual=False), y_tokens=np.sort(sample))
     print(rep)
 
 
