@@ -23,15 +23,23 @@ Readings (the pages name the scheme but define no format):
   * rounding: round to nearest, ties to even, onto the E4M3 grid;
   * mixed precision: the gate/up projection runs in FP8 (x quantized per
     token per 32 channels, W_gate and W_up per output row per 32 inputs); the
-    down projection stays bf16, since its input is where the pages find the
-    extreme activations.
+    down projection stays bf16 by default, since its input is where the pages
+    find the extreme activations, and is FP8 as a per-layer option
+    (down_fp8): the hidden activation h = silu(a) * u of each grouped row is
+    quantized per row in blocks of 32 along I, W_down per output row in
+    blocks of 32 along I, and o = dequant(h) dequant(W_down)^T.  Precision is
+    a per-layer choice on the pages, so both settings are offered.
 
 Pins (tests/pins.py): every code decodes by the closed form of the format and
 re-encodes to itself; rounding of arbitrary values equals a brute-force
 nearest search over the 127 finite non-negative codes with ties to the even
 code; the scale is the minimal one (closed form); the quantization error is
 within half a step; quantization is lossless for values already on a block's
-grid, where the FP8 layer equals the bf16 layer exactly.
+grid, where the FP8 layer equals the bf16 layer exactly.  The FP8 down
+projection (down_projection_fp8) is lossless when h and W_down lie on their
+block grids along I, and a hand-worked block (scale 2^0, a tie rounded to
+the even code, a value rounded down) gives the products written out by hand
+(tests/golden/fp8_down_example.json).
 """
 from __future__ import annotations
 
@@ -113,13 +121,24 @@ def mx_dequantize(codes, scales, axis=-1) -> np.ndarray:
     return np.moveaxis(out.reshape(c.shape), -1, axis)
 
 
+def down_projection_fp8(h, w_down) -> np.ndarray:
+    """o = dequant(quant(h)) dequant(quant(W_down))^T for hidden rows h [m, I]
+    and W_down [d, I]: both quantized along I (the reduction axis) in blocks
+    of 32, h per row, W_down per output row."""
+    h_dq = mx_dequantize(*mx_quantize(h, axis=-1), axis=-1)
+    wd_dq = mx_dequantize(*mx_quantize(w_down, axis=-1), axis=-1)
+    return h_dq @ wd_dq.T
+
+
 def forward_tokens_fp8(x_rows, logits32_rows, bias, get_expert, N: int, K: int,
-                       residual_rows=None):
+                       residual_rows=None, down_fp8: bool = False):
     """Layer output for a set of tokens with the gate/up projection in block
     FP8, given their fp32 logits.  x is quantized per token, so any subset of
     tokens can be evaluated alone; get_expert(e) returns the bf16 (W_gate[e],
     W_up[e], W_down[e]), of which gate and up are quantized per output row.
-    The identity experts pass x itself (they compute nothing)."""
+    With down_fp8 the down projection runs in block FP8 as well
+    (down_projection_fp8 on the fp64 hidden activation).  The identity
+    experts pass x itself (they compute nothing)."""
     x64 = _layer._f64(x_rows)
     xq, xs = mx_quantize(x64, axis=-1)
     x_dq = mx_dequantize(xq, xs, axis=-1)
@@ -132,17 +151,23 @@ def forward_tokens_fp8(x_rows, logits32_rows, bias, get_expert, N: int, K: int,
         wg, wu, wd = (_layer._f64(w) for w in get_expert(int(e)))
         wg = mx_dequantize(*mx_quantize(wg, axis=-1), axis=-1)
         wu = mx_dequantize(*mx_quantize(wu, axis=-1), axis=-1)
-        # gate/up on the dequantized FP8 operands, down on the bf16 weights
-        rows[tt, kk] = _layer.swiglu_ffn(x_dq[tt], wg, wu, wd)
+        if down_fp8:
+            a = x_dq[tt] @ wg.T
+            u = x_dq[tt] @ wu.T
+            rows[tt, kk] = down_projection_fp8(_layer.silu(a) * u, wd)
+        else:
+            # gate/up on the dequantized FP8 operands, down on the bf16 weights
+            rows[tt, kk] = _layer.swiglu_ffn(x_dq[tt], wg, wu, wd)
     y = _layer.combine(x64, idx, g, rows, N, residual_rows)
     return y, rt
 
 
 def forward_fp8_gateup(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, K: int,
-                       residual=None, logits32=None):
-    """The whole layer with the gate/up projection in block FP8 (see
-    forward_tokens_fp8); routing uses ``logits32`` when given, otherwise the
-    fp64 logits rounded once to fp32 (the router itself is not quantized)."""
+                       residual=None, logits32=None, down_fp8: bool = False):
+    """The whole layer with the gate/up projection in block FP8, and the down
+    projection too with ``down_fp8`` (see forward_tokens_fp8); routing uses
+    ``logits32`` when given, otherwise the fp64 logits rounded once to fp32
+    (the router itself is not quantized)."""
     l64 = _layer.router_logits(x, w_router)
     if logits32 is None:
         logits32 = l64.astype(np.float32)
@@ -150,7 +175,7 @@ def forward_fp8_gateup(x, w_router, bias, w_gate, w_up, w_down, N: int, Z: int, 
     def get(e):
         return w_gate[e], w_up[e], w_down[e]
 
-    y, rt = forward_tokens_fp8(x, logits32, bias, get, N, K, residual)
+    y, rt = forward_tokens_fp8(x, logits32, bias, get, N, K, residual, down_fp8=down_fp8)
     rt["logits64"] = l64
     rt["y"] = y
     return rt

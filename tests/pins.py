@@ -467,6 +467,68 @@ def check_fp8_layer_lossless_on_grid(T=24, d=64, I=32, N=5, Z=3, K=3, seed=17):
     assert 1e-4 < rel < 0.1, rel
 
 
+def check_fp8_down_hand_example():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "fp8_down_example.json")))
+    h = np.zeros((1, g["I"]))
+    for k, v in g["h_nonzero"]:
+        h[0, k] = v
+    wd = np.zeros((g["d"], g["I"]))
+    for j, k, v in g["w_down_nonzero"]:
+        wd[j, k] = v
+    o = omx.down_projection_fp8(h, wd)
+    assert np.array_equal(o[0], np.array(g["o"])), o
+    assert np.array_equal(h @ wd.T, np.array([g["o_unquantized_h"]]))
+
+
+def check_fp8_down_lossless_on_grid(m=40, d=48, I=96, seed=21):
+    # h and W_down on their block grids along I: the FP8 product is exact
+    r = _rng(seed)
+    h = _on_block_grid(r, (m, I), I)
+    wd = _on_block_grid(r, (d, I), I)
+    assert np.array_equal(omx.down_projection_fp8(h, wd), h @ wd.T)
+    # off the grid it is the product of the operands' FP8 images: it moves by
+    # about the rounding of both, relative 2^-4 per value at most
+    h2 = r.standard_normal((m, I))
+    wd2 = r.standard_normal((d, I))
+    exact = h2 @ wd2.T
+    rel = np.abs(omx.down_projection_fp8(h2, wd2) - exact).max() / np.abs(exact).max()
+    assert 1e-4 < rel < 0.1, rel
+
+
+def check_fp8_down_layer(T=24, d=64, I=64, N=5, Z=3, K=3, seed=22):
+    r = _rng(seed)
+    x = r.standard_normal((T, d))
+    wr = r.standard_normal((N + Z, d)) / np.sqrt(d)
+    wg = r.standard_normal((N, I, d)) / np.sqrt(d)
+    wu = r.standard_normal((N, I, d)) / np.sqrt(d)
+    wd = r.standard_normal((N, d, I)) / np.sqrt(I)
+    b = r.uniform(-0.05, 0.05, N + Z)
+    a = omx.forward_fp8_gateup(x, wr, b, wg, wu, wd, N, Z, K)
+    c = omx.forward_fp8_gateup(x, wr, b, wg, wu, wd, N, Z, K, down_fp8=True)
+    assert np.array_equal(a["idx"], c["idx"])              # routing is not quantized
+    rel = np.abs(a["y"] - c["y"]).max() / np.abs(a["y"]).max()
+    assert 1e-4 < rel < 0.1, rel
+    # an expert's FP8 down projection is down_projection_fp8 of its fp64
+    # hidden activation (from the dequantized gate/up operands)
+    t = int(np.nonzero((c["idx"] < N).any(axis=1))[0][0])
+    k = int(np.nonzero(c["idx"][t] < N)[0][0])
+    e = int(c["idx"][t, k])
+    q = lambda v: omx.mx_dequantize(*omx.mx_quantize(v, axis=-1), axis=-1)
+    xq = q(x[t:t + 1])
+    hid = om.silu(xq @ q(wg[e]).T) * (xq @ q(wu[e]).T)
+    row = omx.down_projection_fp8(hid, wd[e])[0]
+    y_wo = c["y"][t] - c["gate"][t, k] * row          # the slot's term removed ...
+    y_a = a["y"][t] - a["gate"][t, k] * om.swiglu_ffn(xq, q(wg[e]), q(wu[e]), wd[e])[0]
+    assert np.allclose(y_wo, y_a, rtol=0, atol=1e-12)  # ... leaves the same other terms
+    # identity experts pass x itself: with every slot on one, both agree exactly
+    b3 = np.concatenate([np.full(N, -10.0), np.zeros(Z)])
+    a3 = omx.forward_fp8_gateup(x, wr, b3, wg, wu, wd, N, Z, K)["y"]
+    c3 = omx.forward_fp8_gateup(x, wr, b3, wg, wu, wd, N, Z, K, down_fp8=True)["y"]
+    assert np.array_equal(a3, c3)
+
+
 # ------------------------------------------------------------- backward -----
 def _loss(x, wr, b, wg, wu, wd, N, Z, K, dy):
     rt = om.forward(x, wr, b, wg, wu, wd, N, Z, K)
@@ -564,6 +626,7 @@ ALL_CHECKS = [
     check_closed_loop_conservation_and_positional_form,
     check_closed_loop_integral_settles, check_e4m3_codes, check_e4m3_rounding_bruteforce,
     check_mx_scales_minimal, check_fp8_layer_lossless_on_grid,
+    check_fp8_down_hand_example, check_fp8_down_lossless_on_grid, check_fp8_down_layer,
     check_backward_finite_differences, check_backward_single_ffn_textbook,
     check_backward_identity_closed_form,
 ]

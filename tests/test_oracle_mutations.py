@@ -228,17 +228,36 @@ def m_mx_block16(mp):
 
 def m_fp8_identity_quantized(mp):
     # the identity experts fed the FP8 image of x
-    def fwd(x, w_router, bias, w_gate, w_up, w_down, N, Z, K, residual=None, logits32=None):
+    def fwd(x, w_router, bias, w_gate, w_up, w_down, N, Z, K, residual=None, logits32=None,
+            down_fp8=False):
         xq, xs = _mx["mx_quantize"](np.asarray(x, np.float64))
         x_dq = _mx["mx_dequantize"](xq, xs)
         rt = _mx["forward_fp8_gateup"](x_dq, w_router, bias, w_gate, w_up, w_down, N, Z, K,
-                                       residual, om.router_logits(x, w_router).astype(np.float32))
+                                       residual, om.router_logits(x, w_router).astype(np.float32),
+                                       down_fp8=down_fp8)
         return rt
     mp.setattr(omx, "forward_fp8_gateup", fwd)
 
 
 from oracle import backward as obw
 _bw = obw.backward
+
+
+def m_fp8_down_h_unquantized(mp):
+    # the hidden activation enters the FP8 down projection unquantized
+    def down(h, w_down):
+        wd_dq = _mx["mx_dequantize"](*_mx["mx_quantize"](w_down, axis=-1), axis=-1)
+        return np.asarray(h, np.float64) @ wd_dq.T
+    mp.setattr(omx, "down_projection_fp8", down)
+
+
+def m_fp8_down_weights_along_d(mp):
+    # W_down quantized in blocks along its output axis d instead of along I
+    def down(h, w_down):
+        h_dq = _mx["mx_dequantize"](*_mx["mx_quantize"](h, axis=-1), axis=-1)
+        wd_dq = _mx["mx_dequantize"](*_mx["mx_quantize"](w_down, axis=0), axis=0)
+        return h_dq @ wd_dq.T
+    mp.setattr(omx, "down_projection_fp8", down)
 
 
 def _bw_variant(**flags):
@@ -297,7 +316,8 @@ MUTATIONS = [
     m_unstable_permutation, m_pid_sign, m_pid_p_on_error, m_pid_no_derivative,
     m_loop_without_feedback, m_loop_history_reset, m_budget_swapped,
     m_mx_floor_scale, m_mx_truncate, m_mx_scale_bias_128, m_mx_block16,
-    m_fp8_identity_quantized, m_bwd_no_router_term, m_bwd_silu_derivative_sigmoid,
+    m_fp8_identity_quantized, m_fp8_down_h_unquantized, m_fp8_down_weights_along_d,
+    m_bwd_no_router_term, m_bwd_silu_derivative_sigmoid,
     m_bwd_gate_not_applied, m_bwd_identity_dx_dropped, m_bwd_softmax_jacobian_wrong,
 ]
 
