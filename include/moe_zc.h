@@ -199,6 +199,33 @@ moe_zc_status moe_zc_forward_packed(const void* x, const float* w_router,
                                     void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/* ---- the packed forward without allocation ----------------------------------
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  The library holds one fixed scratch array of
+ * MOE_ZC_NOALLOC_SCRATCH_BYTES per GPU (a static device array: each GPU the
+ * library runs on keeps it until the process ends) and uses it as the
+ * workspace of moe_zc_forward_packed.  The call allocates nothing.  Sizes
+ * whose workspace (moe_zc_workspace_size) exceeds the scratch are refused
+ * with MOE_ZC_ERR_WORKSPACE before anything is enqueued: 64 MiB holds the
+ * decode-shaped layer (d = 6144, I = 2048, N = 512, Z = 256, K = 12) up to
+ * T = 160 tokens.  Every call on one GPU shares that GPU's scratch: calls
+ * that overlap in time on one GPU (for example on two streams) race and
+ * must be serialised by the caller.  Nothing in the scratch needs to start
+ * at zero.  `stream` must belong to the current device (else
+ * MOE_ZC_ERR_INVALID).  Everything else -- arguments, outputs, aux, results
+ * (bitwise equal to moe_zc_forward_packed) -- is as moe_zc_forward_packed. */
+#define MOE_ZC_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_zc_status moe_zc_forward_packed_noalloc(const void* x, const float* w_router,
+                                            const float* bias,
+                                            const void* gate_up_packed,
+                                            const void* down_packed,
+                                            const void* residual, void* y,
+                                            int64_t T, int64_t d, int64_t I,
+                                            int32_t N, int32_t Z, int32_t K,
+                                            moe_zc_dtype dt, moe_zc_aux* aux,
+                                            hipStream_t stream);
+
 /* ---- block-FP8 gate/up projection (mixed precision) -------------------------
  * The LongCat pages report that the model quantizes with DeepSeek-V3's
  * fine-grained block scheme and picks precision layer by layer, because the

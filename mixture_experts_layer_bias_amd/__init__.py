@@ -11,6 +11,6 @@ from .api import (  # noqa: F401
     moe_zc_forward_packed_fp8, moe_zc_pack_expert_weights_fp8, moe_zc_packed_fp8_expert_bytes,
     moe_zc_quantize_mx, moe_zc_workspace_size_fp8, BWD_AUX_KEYS, moe_zc_backward,
     moe_zc_backward_workspace_size, moe_zc_transpose_expert_weights,
-    moe_zc_transposed_expert_bytes,
+    moe_zc_transposed_expert_bytes, moe_zc_forward_packed_noalloc,
 )
 from ._lib import LIB_PATH, STAGE_NAMES  # noqa: F401

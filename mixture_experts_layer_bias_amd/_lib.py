@@ -26,7 +26,9 @@ EXPORTS = ("moe_zc_workspace_size", "moe_zc_forward", "moe_zc_packed_expert_byte
            "moe_zc_packed_fp8_expert_bytes", "moe_zc_pack_expert_weights_fp8",
            "moe_zc_workspace_size_fp8", "moe_zc_forward_packed_fp8", "moe_zc_quantize_mx",
            "moe_zc_transpose_expert_weights", "moe_zc_backward_workspace_size",
-           "moe_zc_backward", "moe_zc_transposed_expert_bytes")
+           "moe_zc_backward", "moe_zc_transposed_expert_bytes",
+           "moe_zc_forward_packed_noalloc")
+MOE_ZC_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeZcAux(ctypes.Structure):
@@ -71,6 +73,10 @@ def load() -> ctypes.CDLL:
     lib.moe_zc_forward_packed.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32,
                                           i32, ctypes.c_int, ctypes.POINTER(MoeZcAux), vp, sz, vp]
     lib.moe_zc_forward_packed.restype = ctypes.c_int
+    lib.moe_zc_forward_packed_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32,
+                                                  i32, i32, ctypes.c_int,
+                                                  ctypes.POINTER(MoeZcAux), vp]
+    lib.moe_zc_forward_packed_noalloc.restype = ctypes.c_int
     lib.moe_zc_packed_fp8_expert_bytes.argtypes = [i64, i64, ctypes.POINTER(sz)]
     lib.moe_zc_packed_fp8_expert_bytes.restype = ctypes.c_int
     lib.moe_zc_pack_expert_weights_fp8.argtypes = [vp, vp, i32, i64, i64, vp, vp]

@@ -272,6 +272,51 @@ def moe_zc_forward_packed(x: torch.Tensor, w_router: torch.Tensor, bias: torch.T
                     out, aux, workspace, events)
 
 
+def moe_zc_forward_packed_noalloc(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
+                                  gate_up_packed: Optional[torch.Tensor],
+                                  down_packed: Optional[torch.Tensor], N: int, Z: int, K: int,
+                                  I: int, residual: Optional[torch.Tensor] = None,
+                                  out: Optional[torch.Tensor] = None,
+                                  aux: Optional[Dict[str, torch.Tensor]] = None,
+                                  events: Optional[StageEvents] = None) -> torch.Tensor:
+    """moe_zc_forward_packed with the library's fixed per-GPU scratch instead of
+    a workspace (no allocation inside the call; ``out`` and ``aux`` must be
+    given for the call as a whole to allocate nothing)."""
+    _check_x(x)
+    lib = _lib.load()
+    T, d = x.shape
+    dev, dt = x.device, x.dtype
+    E = N + Z
+    _need(w_router, "w_router", torch.float32, (E, d), dev)
+    _need(bias, "bias", torch.float32, (E,), dev)
+    if N > 0:
+        gu, dn = moe_zc_packed_expert_bytes(d, I, dt)
+        _need(gate_up_packed, "gate_up_packed", torch.uint8, (N * gu,), dev)
+        _need(down_packed, "down_packed", torch.uint8, (N * dn,), dev)
+    if residual is not None:
+        _need(residual, "residual", dt, (T, d), dev)
+    if out is None:
+        out = torch.empty(T, d, dtype=dt, device=dev)
+    _need(out, "out", dt, (T, d), dev)
+    a = _lib.MoeZcAux()
+    if aux:
+        spec = _aux_spec(T, N, Z, K, I)
+        for k, t in aux.items():
+            if k not in spec:
+                raise ValueError(f"unknown aux key {k!r}")
+            _need(t, f"aux[{k!r}]", spec[k][1], spec[k][0], dev)
+            setattr(a, k, t.data_ptr())
+    if events is not None:
+        a.stage_events = ctypes.cast(events.array, ctypes.c_void_p).value
+    code = lib.moe_zc_forward_packed_noalloc(
+        _ptr(x), _ptr(w_router), _ptr(bias), _ptr(gate_up_packed if N > 0 else None),
+        _ptr(down_packed if N > 0 else None), _ptr(residual), _ptr(out), T, d, I, N, Z, K,
+        _DT[dt], ctypes.byref(a), _stream(dev))
+    if code != _lib.MOE_ZC_OK:
+        raise MoeZcError(code, "moe_zc_forward_packed_noalloc")
+    return out
+
+
 def moe_zc_route(logits: torch.Tensor, bias: torch.Tensor, K: int,
                  topk_idx: Optional[torch.Tensor] = None,
                  topk_gate: Optional[torch.Tensor] = None,

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -385,6 +386,36 @@ moe_zc_status check_pack_shape(int64_t d, int64_t I, moe_zc_dtype dt) {
 
 }  // namespace
 
+// ---- the forward without allocation -----------------------------------------
+// Scratch of moe_zc_forward_packed_noalloc: one fixed array per GPU, alive
+// until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host it is only a stand-in for the device symbol); it uses
+// the device address that hipGetSymbolAddress returns for the current device,
+// looked up once per device and kept in g_scratch.
+static __device__ __align__(256) char scratch[MOE_ZC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the first call there).
+moe_zc_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ZC_ERR_HIP;
+  if (dev >= kMaxDevices) return MOE_ZC_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return MOE_ZC_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return MOE_ZC_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int32_t moe_zc_abi_version(void) { return MOE_ZC_ABI_VERSION; }
@@ -414,6 +445,34 @@ moe_zc_status moe_zc_forward(const void* x, const float* w_router, const float* 
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return forward_impl(x, w_router, bias, w_gate, w_up, w_down, kRowMajor, residual, y, T, d, I,
                       N, Z, K, dt, aux, workspace, workspace_bytes, stream);
+}
+
+moe_zc_status moe_zc_forward_packed_noalloc(const void* x, const float* w_router,
+                                            const float* bias, const void* gate_up_packed,
+                                            const void* down_packed, const void* residual,
+                                            void* y, int64_t T, int64_t d, int64_t I, int32_t N,
+                                            int32_t Z, int32_t K, moe_zc_dtype dt,
+                                            moe_zc_aux* aux, hipStream_t stream) {
+  Shape s;
+  const moe_zc_status st = check_shape(T, d, I, N, Z, K, dt, &s);
+  if (st != MOE_ZC_OK) return st;
+  if (dt != MOE_ZC_BF16) return MOE_ZC_ERR_UNSUPPORTED;
+  const size_t need = make_plan(s).total;
+  if (need > (size_t)MOE_ZC_NOALLOC_SCRATCH_BYTES) return MOE_ZC_ERR_WORKSPACE;
+  if (T == 0) return MOE_ZC_OK;
+  // the stream must belong to the current device: that device's scratch is used
+  if (stream) {
+    int sdev = -1, cur = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess || hipGetDevice(&cur) != hipSuccess)
+      return MOE_ZC_ERR_HIP;
+    if (sdev != cur) return MOE_ZC_ERR_INVALID;
+  }
+  void* ws = nullptr;
+  const moe_zc_status ss = noalloc_scratch(&ws);
+  if (ss != MOE_ZC_OK) return ss;
+  return forward_impl(x, w_router, bias, gate_up_packed, nullptr, down_packed, kPacked, residual,
+                      y, T, d, I, N, Z, K, dt, aux, ws, (size_t)MOE_ZC_NOALLOC_SCRATCH_BYTES,
+                      stream);
 }
 
 moe_zc_status moe_zc_forward_packed(const void* x, const float* w_router, const float* bias,

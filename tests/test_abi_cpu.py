@@ -224,3 +224,18 @@ def test_saved_preactivations_validation(lib):
     assert lib.moe_zc_backward(FAKE, FAKE, None, None, FAKE, FAKE, ctypes.byref(fwd), FAKE, FAKE,
                                FAKE, FAKE, FAKE, FAKE, T, d, I, N, Z, K, FAKE, nbb,
                                None) == INVALID
+
+
+def test_noalloc_forward_refuses_on_the_host(lib):
+    """moe_zc_forward_packed_noalloc checks sizes against its fixed scratch
+    before touching any device: a workspace above MOE_ZC_NOALLOC_SCRATCH_BYTES
+    is MOE_ZC_ERR_WORKSPACE, f32 is unsupported, bad sizes are invalid."""
+    f = lib.moe_zc_forward_packed_noalloc
+    d, I, N, Z, K = 6144, 2048, 512, 256, 12
+    assert lib.moe_zc_workspace_size(256, d, I, N, Z, K, BF16) > _lib.MOE_ZC_NOALLOC_SCRATCH_BYTES
+    args = lambda T, dt=BF16, K=K: (FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, T, d, I, N, Z, K,
+                                    dt, None, None)
+    assert f(*args(256)) == WORKSPACE
+    assert f(*args(64, dt=F32)) == UNSUPPORTED
+    assert f(*args(64, K=0)) == INVALID
+    assert f(*args(0)) == OK                          # no tokens: nothing to do
