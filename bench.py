@@ -1,15 +1,26 @@
 """Benchmark of the MoE layer with zero-computation experts on one MI355X.
 
-One step = one forward of the layer (router GEMM, softmax + bias top-K,
-histogram, scan, permute, grouped GEMM gate/up + SwiGLU, grouped GEMM down,
-combine with the identity experts and the residual) followed by one
-moe_zc_bias_update (PID step toward uniform load) on the same stream.  Inputs
-are seeded and synthetic, resident in HBM before the timed region.  bf16
-expert weights are packed once at setup (moe_zc_pack_expert_weights, as at
-model load) and the step calls moe_zc_forward_packed; --layout rowmajor
+One step = one forward of the layer as configured (router GEMM, softmax +
+bias top-K, histogram, scan, permute, grouped GEMM gate/up + SwiGLU, grouped
+GEMM down, combine with the identity experts and the residual), always with
+the workload's own selection bias, followed by one moe_zc_bias_update (PID
+step toward uniform load) from that routing, on the same stream.  The PID
+step starts every timed step from the configured bias and zero controller
+state, so each step times the same layer and the same single bias update;
+the update is timed as a stage of its own.  A separate, untimed closed loop
+(bias carried over repeated batches) is reported beside it.
+
+Inputs are seeded and synthetic, resident in HBM before the timed region.
+bf16 expert weights are packed once at setup (moe_zc_pack_expert_weights, as
+at model load) and the step calls moe_zc_forward_packed; --layout rowmajor
 times moe_zc_forward on the row-major weights instead.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload prefill]
+
+The headline is --workload (default prefill, bf16).  The same run then times
+the other workloads (tiny, mid, decode, skew in their own dtypes, and the
+prefill layer with the block-FP8 gate/up projection) and reports each under
+"workloads" (skip with --no-extra-workloads).
 
 --pass backward times a training step of the layer instead: the packed
 forward saving its routing and the expert pre-activations (aux.act), then
@@ -61,6 +72,10 @@ def parse():
                     help="experts the CPU-baseline sample evaluates")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a device copy of known size (for scaling counters)")
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="time only the --workload layer (skip the other workloads)")
+    ap.add_argument("--closed-loop-steps", type=int, default=10,
+                    help="batches of the untimed closed-loop PID report")
     return ap.parse_args()
 
 
@@ -315,50 +330,35 @@ def bench_backward(args, w, dev):
     print(json.dumps(out))
 
 
-def main():
-    args = parse()
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; the multi-GPU path (expert "
-              "sharding with all-to-all) is not built. Use --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
+def forward_workload(args, w, dev, precision="bf16", layout="packed", steps=20, warmup=5,
+                     n_cpu=0, keep_inputs=False):
+    """Time the forward of workload ``w`` as configured (its own bias on every
+    timed step) plus one PID step from that routing, each timed step starting
+    from the configured bias and zero PID state.  Returns a dict of results
+    (and the inputs when ``keep_inputs``, for the CPU baseline)."""
     import numpy as np
     import torch
 
     import mixture_experts_layer_bias_amd as m
-    from workloads import get_workload, make_inputs
+    from workloads import make_inputs
 
-    w = get_workload(args.workload)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    if args.which == "backward":
-        bench_backward(args, w, dev)
-        return
-    peaks = None if args.no_peak_probe else measured_peaks(dev)
     inp = make_inputs(w, device=dev)
     dt = inp["x"].dtype
     es = inp["x"].element_size()
-    fp8 = args.precision == "fp8"
-    if fp8 and (w.dtype != "bf16" or args.layout != "packed"):
-        print("bench.py: --precision fp8 needs a bf16 workload and packed weights", file=sys.stderr)
-        sys.exit(2)
+    fp8 = precision == "fp8"
     need = (m.moe_zc_workspace_size_fp8(w.T, w.d, w.I, w.N, w.Z, w.K) if fp8
             else m.moe_zc_workspace_size(w.T, w.d, w.I, w.N, w.Z, w.K, dt))
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     aux = m.alloc_aux(w.T, w.N, w.Z, w.K, dev, keys=("loads", "offsets"))
     y = torch.empty(w.T, w.d, dtype=dt, device=dev)
-    bias = inp["bias"].clone()
+    bias0 = inp["bias"]                      # the configured bias: never modified
+    bias_pid = bias0.clone()
     pid = m.PidState(w.E, dev, kp=0.5, ki=0.5, kd=0.0)
     target = torch.full((w.E,), w.T * w.K / w.E, dtype=torch.float32, device=dev)
     # host copies of the experts the CPU baseline evaluates
-    n_cpu = 0 if args.no_cpu_baseline else min(args.cpu_experts, w.N)
     cpu_weights = [(inp["w_gate"][e].cpu(), inp["w_up"][e].cpu(), inp["w_down"][e].cpu())
-                   for e in range(n_cpu)]
-    packed = args.layout == "packed" and w.dtype == "bf16"
+                   for e in range(min(n_cpu, w.N))]
+    packed = layout == "packed" and w.dtype == "bf16"
     if packed:
         gu, dn = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
         if fp8:
@@ -368,7 +368,7 @@ def main():
             inp[k] = None
         torch.cuda.empty_cache()
 
-    def step(events=None):
+    def forward(bias, events=None):
         if fp8:
             m.moe_zc_forward_packed_fp8(inp["x"], inp["w_router"], bias, gu, dn, w.N, w.Z, w.K,
                                         w.I, residual=inp["residual"], out=y, aux=aux,
@@ -381,70 +381,68 @@ def main():
             m.moe_zc_forward(inp["x"], inp["w_router"], bias, inp["w_gate"], inp["w_up"],
                              inp["w_down"], w.N, w.Z, w.K, residual=inp["residual"], out=y,
                              aux=aux, workspace=ws, events=events)
-        m.moe_zc_bias_update(aux["loads"], target, bias, pid)
+
+    def pid_step():
+        # one bias update from the configured routing: state restored first
+        bias_pid.copy_(bias0)
+        pid.e_prev.zero_()
+        pid.e_prev2.zero_()
+        m.moe_zc_bias_update(aux["loads"], target, bias_pid, pid)
+
+    def step(events=None, pid_ev=None):
+        forward(bias0, events)
+        if pid_ev:
+            pid_ev[0].record()
+        pid_step()
+        if pid_ev:
+            pid_ev[1].record()
 
     def ffn_stats(ld):
         f = ld[: w.N].astype(np.float64)
         return {"ffn_per_token": float(f.sum() / w.T),
                 "max_over_mean_ffn_load": float(f.max() / f.mean()) if f.sum() > 0 else None}
 
-    first_pid = None
-    for i in range(args.warmup):
+    for _ in range(warmup):
         step()
-        if i == 0:  # closed-loop statistics of the first step (untimed)
-            first_pid = ffn_stats(aux["loads"].cpu().numpy())
-    events = [m.StageEvents() for _ in range(args.steps)]
-    S_list, touched_list = [], []
+    events = [m.StageEvents() for _ in range(steps)]
+    pid_evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for i in range(steps):
+        step(events[i], pid_evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    # per-stage averages over the timed steps (events were recorded inside them)
+    ms_per_step = (t1 - t0) * 1e3 / steps
     stage = {k: 0.0 for k in m.STAGE_NAMES}
     for ev in events:
         for k, v in ev.stage_ms().items():
-            stage[k] += v / args.steps
-    # routing statistics of the last step (the PID moves them only slightly)
+            stage[k] += v / steps
+    pid_ms = sum(a.elapsed_time(b) for a, b in pid_evs) / steps
     loads = aux["loads"].cpu().numpy()
     S = int(aux["offsets"][w.N].item())
     touched = int((loads[: w.N] > 0).sum())
-    last_pid = ffn_stats(loads)
-    pid_report = {"gains": [pid.kp, pid.ki, pid.kd], "target": "uniform T*K/E",
-                  "steps_applied": args.warmup + args.steps,
-                  "first_step": first_pid, "last_step": last_pid}
+
+    # untimed: routing after the one PID step of the timed steps ...
+    before = ffn_stats(loads)
+    forward(bias_pid)
+    after = ffn_stats(aux["loads"].cpu().numpy())
+    # ... and a separate closed loop over repeated batches (bias carried)
+    bias_cl = bias0.clone()
+    pid_cl = m.PidState(w.E, dev, kp=0.5, ki=0.5, kd=0.0)
+    loop = []
+    for _ in range(args.closed_loop_steps):
+        forward(bias_cl)
+        loop.append(ffn_stats(aux["loads"].cpu().numpy()))
+        m.moe_zc_bias_update(aux["loads"], target, bias_cl, pid_cl)
+    torch.cuda.synchronize()
+
     alg = algorithmic(w, S, touched, es, fp8)
     flop_act = 2.0 * w.T * w.d * w.E + 6.0 * w.d * w.I * S
     t_step = ms_per_step / 1e3
     gemm_s = (stage["gemm_gate_up_swiglu"] + stage["gemm_down"]) / 1e3
-    # ideal MFMA time of both expert GEMMs at their dtypes' peaks over the measured time
-    t_ideal = 4.0 * w.d * w.I * S / (PEAK_FP8 if fp8 else PEAK_BF16) + 2.0 * w.d * w.I * S / PEAK_BF16
-    mfma_frac = t_ideal / gemm_s if gemm_s > 0 else None
-
-    dom = "gemm_gate_up_swiglu"
-    a = alg[dom]
-    t_dom = stage[dom] / 1e3
-    peak_dom = PEAK_FP8 if fp8 else PEAK_BF16   # a contraction against its own dtype's peak
-    t_b, t_f = a["bytes"] / PEAK_HBM, a["flop"] / peak_dom
-    if t_b >= t_f:
-        roof = {"bound": "hbm", "achieved": a["bytes"] / t_dom / 1e9, "peak": PEAK_HBM / 1e9,
-                "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": a["flop"] / t_dom / 1e12, "peak": peak_dom / 1e12,
-                "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    if peaks:  # the same achieved rate against what the box reaches on a read stream / dense GEMM
-        ref = peaks["hbm_read_GBps"] if roof["bound"] == "hbm" else (
-            None if fp8 else peaks["bf16_gemm_TFLOPs"])
-        roof["frac_of_measured"] = roof["achieved"] / ref if ref else None
-    # the committed counter summary covers the bf16 kernel only
-    roof["traffic"] = None if fp8 else counter_traffic()
-    roof["kernel"] = dom
-    roof["avg_launch_ms"] = stage[dom]
-
+    t_ideal = (4.0 * w.d * w.I * S / (PEAK_FP8 if fp8 else PEAK_BF16)
+               + 2.0 * w.d * w.I * S / PEAK_BF16)
     stage_roof = {}
     for k, v in alg.items():
         ts = stage[k] / 1e3
@@ -459,17 +457,124 @@ def main():
         stage_roof[k] = entry
     for k in ("chunk_hist", "scan"):
         stage_roof[k] = {"ms": round(stage[k], 4)}
+    stage_roof["pid"] = {"ms": round(pid_ms, 4)}
+    res = {
+        "workload": w.name, "precision": precision if fp8 else w.dtype,
+        "expert_weights": "packed" if packed else "row-major",
+        "T": w.T, "d": w.d, "I": w.I, "N": w.N, "Z": w.Z, "K": w.K,
+        "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step, "tokens_per_s": w.T / t_step,
+        "activated_tflops": flop_act / t_step / 1e12,
+        "activated_mfma_frac": flop_act / t_step / PEAK_BF16,
+        "grouped_gemm_mfma_frac": (t_ideal / gemm_s) if (gemm_s > 0 and S > 0) else None,
+        "ffn_rows": S, "ffn_experts_per_token": S / w.T, "touched_experts": touched,
+        "stages": stage_roof,
+        "one_pid_step": {"gains": [pid.kp, pid.ki, pid.kd], "target": "uniform T*K/E",
+                         "routing_before": before, "routing_after": after},
+        "closed_loop": {"steps": args.closed_loop_steps, "first": loop[0] if loop else None,
+                        "last": loop[-1] if loop else None},
+        "_alg": alg, "_stage_ms": stage, "_S": S, "_touched": touched, "_es": es,
+    }
+    if keep_inputs:
+        res["_inp"] = inp
+        res["_cpu_weights"] = cpu_weights
+    return res
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, inp, args.cpu_experts, cpu_weights)
-    ffn_per_token = S / w.T
+
+def roofline_of(res, fp8, peaks):
+    """Roofline entry of the dominant kernel (gate/up + SwiGLU) of one run."""
+    dom = "gemm_gate_up_swiglu"
+    a = res["_alg"][dom]
+    t_dom = res["_stage_ms"][dom] / 1e3
+    peak_dom = PEAK_FP8 if fp8 else PEAK_BF16   # a contraction against its own dtype's peak
+    t_b, t_f = a["bytes"] / PEAK_HBM, a["flop"] / peak_dom
+    if t_b >= t_f:
+        roof = {"bound": "hbm", "achieved": a["bytes"] / t_dom / 1e9, "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": a["flop"] / t_dom / 1e12, "peak": peak_dom / 1e12,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    if peaks:  # the same achieved rate against what the box reaches on a read stream / dense GEMM
+        ref = peaks["hbm_read_GBps"] if roof["bound"] == "hbm" else (
+            None if fp8 else peaks["bf16_gemm_TFLOPs"])
+        roof["frac_of_measured"] = roof["achieved"] / ref if ref else None
+    roof["kernel"] = dom
+    roof["avg_launch_ms"] = res["_stage_ms"][dom]
+    roof["algorithmic_bytes"] = a["bytes"]
+    return roof
+
+
+def public(res):
+    return {k: v for k, v in res.items() if not k.startswith("_")}
+
+
+# the other workloads timed after the headline one, in the same run
+EXTRA = (("tiny", False), ("mid", False), ("decode", False), ("skew", False), ("prefill", True))
+
+
+def main():
+    args = parse()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only; the multi-GPU path (expert "
+              "sharding with all-to-all) is not built. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from workloads import get_workload
+
+    w = get_workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.which == "backward":
+        bench_backward(args, w, dev)
+        return
+    fp8 = args.precision == "fp8"
+    if fp8 and (w.dtype != "bf16" or args.layout != "packed"):
+        print("bench.py: --precision fp8 needs a bf16 workload and packed weights", file=sys.stderr)
+        sys.exit(2)
+    peaks = None if args.no_peak_probe else measured_peaks(dev)
+    n_cpu = 0 if args.no_cpu_baseline else min(args.cpu_experts, w.N)
+    res = forward_workload(args, w, dev, args.precision, args.layout, args.steps, args.warmup,
+                           n_cpu=n_cpu, keep_inputs=not args.no_cpu_baseline)
+    roof = roofline_of(res, fp8, peaks)
+    # the committed counter summary covers the bf16 kernel only
+    roof["traffic"] = None if fp8 else counter_traffic()
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, res["_inp"], args.cpu_experts, res["_cpu_weights"])
+    res.pop("_inp", None)
+    res.pop("_cpu_weights", None)
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if not args.no_extra_workloads:
+        for name, x8 in EXTRA:
+            if name == w.name and x8 == fp8:
+                continue
+            wx = get_workload(name)
+            steps = max(3, min(args.steps, 20))
+            rx = forward_workload(args, wx, dev, "fp8" if x8 else "bf16", "packed", steps,
+                                  min(args.warmup, 3))
+            rx["roofline_gate_up"] = {k: v for k, v in roofline_of(rx, x8, None).items()
+                                      if k in ("bound", "achieved", "peak", "unit", "frac")}
+            extra[f"{name}_fp8" if x8 else name] = public(rx)
+            del rx
+            torch.cuda.empty_cache()
+
     out = {
         "metric": METRIC,
-        "value": w.T / t_step,
+        "value": res["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -479,23 +584,26 @@ def main():
         "config": {"workload": w.name, "T": w.T, "d": w.d, "I": w.I, "N": w.N, "Z": w.Z,
                    "K": w.K, "expert_ffn": "SwiGLU", "residual": True,
                    "step": ("moe_zc_forward_packed_fp8" if fp8 else
-                            "moe_zc_forward_packed" if packed else "moe_zc_forward")
-                   + " + moe_zc_bias_update",
+                            "moe_zc_forward_packed" if res["expert_weights"] == "packed"
+                            else "moe_zc_forward")
+                   + " with the configured bias + one moe_zc_bias_update",
                    "precision": ("gate/up block FP8 (E4M3, power-of-two scale per 32 k); "
                                  "router, down, combine bf16/fp32" if fp8 else "bf16"),
-                   "expert_weights": "packed" if packed else "row-major",
+                   "expert_weights": res["expert_weights"],
                    "parallelism": "none (1 GPU)"},
-        "activated_tflops": flop_act / t_step / 1e12,
-        "activated_mfma_frac": flop_act / t_step / PEAK_BF16,
-        "grouped_gemm_mfma_frac": mfma_frac,
-        "ffn_rows": S,
-        "ffn_experts_per_token": ffn_per_token,
-        "touched_experts": touched,
-        "stages": stage_roof,
-        "pid_closed_loop": pid_report,
+        "activated_tflops": res["activated_tflops"],
+        "activated_mfma_frac": res["activated_mfma_frac"],
+        "grouped_gemm_mfma_frac": res["grouped_gemm_mfma_frac"],
+        "ffn_rows": res["ffn_rows"],
+        "ffn_experts_per_token": res["ffn_experts_per_token"],
+        "touched_experts": res["touched_experts"],
+        "stages": res["stages"],
+        "one_pid_step": res["one_pid_step"],
+        "closed_loop": res["closed_loop"],
         "measured_peaks": peaks,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "workloads": extra,
     }
     print(json.dumps(out))
 
