@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--precision", default="bf16", choices=["bf16", "fp8"],
                     help="fp8: gate/up projection in block FP8 (moe_zc_forward_packed_fp8); "
                          "the down projection stays bf16")
+    ap.add_argument("--fp8-down", action="store_true",
+                    help="with --precision fp8: the down projection in block FP8 as well")
     ap.add_argument("--pass", dest="which", default="forward", choices=["forward", "backward"],
                     help="backward: time forward + moe_zc_backward (a training step)")
     ap.add_argument("--recompute", action="store_true",
@@ -72,6 +74,8 @@ def parse():
                     help="experts the CPU-baseline sample evaluates")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a device copy of known size (for scaling counters)")
+    ap.add_argument("--no-power-probe", action="store_true",
+                    help="skip sampling socket power and clocks (amd-smi) on the headline")
     ap.add_argument("--no-extra-workloads", action="store_true",
                     help="time only the --workload layer (skip the other workloads)")
     ap.add_argument("--closed-loop-steps", type=int, default=10,
@@ -170,7 +174,64 @@ def measured_peaks(dev):
     return {k: round(v, 1) for k, v in out.items()}
 
 
-def algorithmic(w, S, touched, es, fp8=False):
+def power_probe(step, seconds=4.0):
+    """Socket power and graphics clocks while the step runs back to back
+    (untimed), sampled with amd-smi in a thread of its own; None where the
+    tool is missing.  Under the MI355X power cap the clocks the expert GEMMs
+    run at are set by the energy they spend, which is what this records."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+
+    tool = shutil.which("amd-smi")
+    if tool is None:
+        return None
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        time.sleep(0.8)                       # past the first steps
+        while not stop.is_set():
+            try:
+                txt = subprocess.run([tool, "metric", "-p", "-c"], capture_output=True,
+                                     text=True, timeout=10).stdout
+            except Exception:
+                return
+            pw = re.search(r"SOCKET_POWER:\s*([0-9.]+)", txt)
+            clocks, section = [], ""
+            for line in txt.splitlines():
+                st = line.strip()
+                if st.endswith(":") and not st.startswith("CLK"):
+                    section = st[:-1]
+                m_ = re.match(r"CLK:\s*([0-9.]+)\s*MHz", st)
+                if m_ and section.startswith("GFX_"):
+                    clocks.append(float(m_.group(1)))
+            if pw:
+                samples.append((float(pw.group(1)), clocks))
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        step()
+        torch.cuda.synchronize()
+        n += 1
+    stop.set()
+    th.join(timeout=15)
+    if not samples:
+        return None
+    watts = [w_ for w_, _ in samples]
+    clk = [c for _, cs in samples for c in cs]
+    return {"socket_W": watts, "gfx_clock_MHz_mean": (sum(clk) / len(clk)) if clk else None,
+            "gfx_clock_MHz_min": min(clk) if clk else None, "samples": len(samples),
+            "steps_run": n, "source": "amd-smi metric -p -c while the step runs back to back"}
+
+
+def algorithmic(w, S, touched, es, fp8=False, fp8_down=False):
     """Algorithmic bytes / FLOPs per launch of each stage (inputs read once,
     outputs written once).  bf16: the gate/up GEMM gathers its rows from x,
     so its input is x itself and the grouping stage moves only indices.
@@ -189,7 +250,10 @@ def algorithmic(w, S, touched, es, fp8=False):
         "gemm_gate_up_swiglu": {"flop": 4.0 * d * I * S,
                                 "bytes": w_gu + (T if gathered else S) * d * es + S * I * es},
         "gemm_down": {"flop": 2.0 * d * I * S,
-                      "bytes": touched * d * I * es + S * I * es + S * d * es},
+                      # FP8: the FP8 copy of h is internal traffic; h (bf16) is
+                      # read once to be quantized
+                      "bytes": touched * d * I * ((1.0 + 1.0 / 32.0) if fp8_down else es)
+                      + S * I * es + S * d * es},
         "combine": {"bytes": S * d * es + 3 * T * d * es + T * K * 12},
     }
 
@@ -331,7 +395,7 @@ def bench_backward(args, w, dev):
 
 
 def forward_workload(args, w, dev, precision="bf16", layout="packed", steps=20, warmup=5,
-                     n_cpu=0, keep_inputs=False):
+                     n_cpu=0, keep_inputs=False, fp8_down=False):
     """Time the forward of workload ``w`` as configured (its own bias on every
     timed step) plus one PID step from that routing, each timed step starting
     from the configured bias and zero PID state.  Returns a dict of results
@@ -361,7 +425,9 @@ def forward_workload(args, w, dev, precision="bf16", layout="packed", steps=20, 
     packed = layout == "packed" and w.dtype == "bf16"
     if packed:
         gu, dn = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
-        if fp8:
+        if fp8 and fp8_down:
+            gu, dn = m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"], inp["w_down"])
+        elif fp8:
             gu = m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"])
         torch.cuda.synchronize()
         for k in ("w_gate", "w_up", "w_down"):
@@ -372,7 +438,7 @@ def forward_workload(args, w, dev, precision="bf16", layout="packed", steps=20, 
         if fp8:
             m.moe_zc_forward_packed_fp8(inp["x"], inp["w_router"], bias, gu, dn, w.N, w.Z, w.K,
                                         w.I, residual=inp["residual"], out=y, aux=aux,
-                                        workspace=ws, events=events)
+                                        workspace=ws, events=events, down_fp8=fp8_down)
         elif packed:
             m.moe_zc_forward_packed(inp["x"], inp["w_router"], bias, gu, dn, w.N, w.Z, w.K, w.I,
                                     residual=inp["residual"], out=y, aux=aux, workspace=ws,
@@ -423,6 +489,7 @@ def forward_workload(args, w, dev, precision="bf16", layout="packed", steps=20, 
     S = int(aux["offsets"][w.N].item())
     touched = int((loads[: w.N] > 0).sum())
 
+    power = power_probe(step) if getattr(args, "_power_probe", False) else None
     # untimed: routing after the one PID step of the timed steps ...
     before = ffn_stats(loads)
     forward(bias_pid)
@@ -437,12 +504,12 @@ def forward_workload(args, w, dev, precision="bf16", layout="packed", steps=20, 
         m.moe_zc_bias_update(aux["loads"], target, bias_cl, pid_cl)
     torch.cuda.synchronize()
 
-    alg = algorithmic(w, S, touched, es, fp8)
+    alg = algorithmic(w, S, touched, es, fp8, fp8_down)
     flop_act = 2.0 * w.T * w.d * w.E + 6.0 * w.d * w.I * S
     t_step = ms_per_step / 1e3
     gemm_s = (stage["gemm_gate_up_swiglu"] + stage["gemm_down"]) / 1e3
     t_ideal = (4.0 * w.d * w.I * S / (PEAK_FP8 if fp8 else PEAK_BF16)
-               + 2.0 * w.d * w.I * S / PEAK_BF16)
+               + 2.0 * w.d * w.I * S / (PEAK_FP8 if fp8_down else PEAK_BF16))
     stage_roof = {}
     for k, v in alg.items():
         ts = stage[k] / 1e3
@@ -451,7 +518,8 @@ def forward_workload(args, w, dev, precision="bf16", layout="packed", steps=20, 
         entry = {"ms": round(stage[k], 4), "GB/s": round(v["bytes"] / ts / 1e9, 1),
                  "hbm_frac": round(v["bytes"] / ts / PEAK_HBM, 4)}
         if "flop" in v:
-            pk = PEAK_FP8 if (fp8 and k == "gemm_gate_up_swiglu") else PEAK_BF16
+            pk = PEAK_FP8 if ((fp8 and k == "gemm_gate_up_swiglu") or
+                              (fp8_down and k == "gemm_down")) else PEAK_BF16
             entry["TFLOP/s"] = round(v["flop"] / ts / 1e12, 1)
             entry["mfma_frac"] = round(v["flop"] / ts / pk, 4)
         stage_roof[k] = entry
@@ -459,7 +527,9 @@ def forward_workload(args, w, dev, precision="bf16", layout="packed", steps=20, 
         stage_roof[k] = {"ms": round(stage[k], 4)}
     stage_roof["pid"] = {"ms": round(pid_ms, 4)}
     res = {
-        "workload": w.name, "precision": precision if fp8 else w.dtype,
+        "workload": w.name,
+        "precision": (("fp8 gate/up + fp8 down" if fp8_down else "fp8 gate/up") if fp8
+                      else w.dtype),
         "expert_weights": "packed" if packed else "row-major",
         "T": w.T, "d": w.d, "I": w.I, "N": w.N, "Z": w.Z, "K": w.K,
         "steps": steps, "warmup": warmup,
@@ -473,6 +543,7 @@ def forward_workload(args, w, dev, precision="bf16", layout="packed", steps=20, 
                          "routing_before": before, "routing_after": after},
         "closed_loop": {"steps": args.closed_loop_steps, "first": loop[0] if loop else None,
                         "last": loop[-1] if loop else None},
+        "power": power,
         "_alg": alg, "_stage_ms": stage, "_S": S, "_touched": touched, "_es": es,
     }
     if keep_inputs:
@@ -510,7 +581,9 @@ def public(res):
 
 
 # the other workloads timed after the headline one, in the same run
-EXTRA = (("tiny", False), ("mid", False), ("decode", False), ("skew", False), ("prefill", True))
+EXTRA = (("tiny", False, False), ("mid", False, False), ("decode", False, False),
+         ("skew", False, False), ("prefill", True, False), ("prefill", True, True),
+         ("decode", True, True))
 
 
 def main():
@@ -540,8 +613,14 @@ def main():
         sys.exit(2)
     peaks = None if args.no_peak_probe else measured_peaks(dev)
     n_cpu = 0 if args.no_cpu_baseline else min(args.cpu_experts, w.N)
+    if args.fp8_down and not fp8:
+        print("bench.py: --fp8-down needs --precision fp8", file=sys.stderr)
+        sys.exit(2)
+    args._power_probe = not args.no_power_probe
     res = forward_workload(args, w, dev, args.precision, args.layout, args.steps, args.warmup,
-                           n_cpu=n_cpu, keep_inputs=not args.no_cpu_baseline)
+                           n_cpu=n_cpu, keep_inputs=not args.no_cpu_baseline,
+                           fp8_down=args.fp8_down)
+    args._power_probe = False
     roof = roofline_of(res, fp8, peaks)
     # the committed counter summary covers the bf16 kernel only
     roof["traffic"] = None if fp8 else counter_traffic()
@@ -554,16 +633,16 @@ def main():
 
     extra = {}
     if not args.no_extra_workloads:
-        for name, x8 in EXTRA:
-            if name == w.name and x8 == fp8:
+        for name, x8, d8 in EXTRA:
+            if name == w.name and x8 == fp8 and d8 == (fp8 and args.fp8_down):
                 continue
             wx = get_workload(name)
             steps = max(3, min(args.steps, 20))
             rx = forward_workload(args, wx, dev, "fp8" if x8 else "bf16", "packed", steps,
-                                  min(args.warmup, 3))
+                                  min(args.warmup, 3), fp8_down=d8)
             rx["roofline_gate_up"] = {k: v for k, v in roofline_of(rx, x8, None).items()
                                       if k in ("bound", "achieved", "peak", "unit", "frac")}
-            extra[f"{name}_fp8" if x8 else name] = public(rx)
+            extra[name + ("_fp8" if x8 else "") + ("_fp8down" if d8 else "")] = public(rx)
             del rx
             torch.cuda.empty_cache()
 
@@ -578,7 +657,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp8-e4m3 block-scaled gate/up + bf16" if fp8
+        "dtype": (("fp8-e4m3 block-scaled gate/up and down" if args.fp8_down else
+                   "fp8-e4m3 block-scaled gate/up + bf16") if fp8
                   else ("bf16" if w.dtype == "bf16" else "f32")),
         "data": "synthetic (seeded Gaussian inputs, random-init expert weights)",
         "config": {"workload": w.name, "T": w.T, "d": w.d, "I": w.I, "N": w.N, "Z": w.Z,
@@ -587,8 +667,10 @@ def main():
                             "moe_zc_forward_packed" if res["expert_weights"] == "packed"
                             else "moe_zc_forward")
                    + " with the configured bias + one moe_zc_bias_update",
-                   "precision": ("gate/up block FP8 (E4M3, power-of-two scale per 32 k); "
-                                 "router, down, combine bf16/fp32" if fp8 else "bf16"),
+                   "precision": (("gate/up and down block FP8 (E4M3, power-of-two scale "
+                                  "per 32 k); router, combine bf16/fp32") if args.fp8_down else
+                                 ("gate/up block FP8 (E4M3, power-of-two scale per 32 k); "
+                                  "router, down, combine bf16/fp32") if fp8 else "bf16"),
                    "expert_weights": res["expert_weights"],
                    "parallelism": "none (1 GPU)"},
         "activated_tflops": res["activated_tflops"],
@@ -600,6 +682,7 @@ def main():
         "stages": res["stages"],
         "one_pid_step": res["one_pid_step"],
         "closed_loop": res["closed_loop"],
+        "power": res["power"],
         "measured_peaks": peaks,
         "roofline": roof,
         "cpu_baseline": cpu,

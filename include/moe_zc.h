@@ -226,57 +226,75 @@ moe_zc_status moe_zc_forward_packed_noalloc(const void* x, const float* w_router
                                             moe_zc_dtype dt, moe_zc_aux* aux,
                                             hipStream_t stream);
 
-/* ---- block-FP8 gate/up projection (mixed precision) -------------------------
+/* ---- block-FP8 expert projections (mixed precision) -------------------------
  * The LongCat pages report that the model quantizes with DeepSeek-V3's
  * fine-grained block scheme and picks precision layer by layer, because the
  * down projection's input activations reach about 1e6 (『衝上熱搜！美團大模型，
  * 靠「快」火了』, paragraph on quantization in the system-optimisation
- * section).  This path runs the expert gate/up projection in block FP8 and
- * keeps the router, the down projection and the combine in bf16 / fp32:
- *   FP8 block: 32 consecutive values along the reduction axis (d) share one
+ * section).  This path runs the expert gate/up projection in block FP8, and
+ * the down projection in bf16 or (per layer, down_fp8 = 1) block FP8 too; the
+ * router and the combine stay bf16 / fp32.  The block geometry departs from
+ * DeepSeek-V3's (1 x 128 activation tiles and 128 x 128 weight blocks with
+ * fp32 scales): it is the MX form the MI355X matrix cores consume.
+ *   FP8 block: 32 consecutive values along the reduction axis share one
  *   power-of-two scale 2^s, stored as the byte s + 127; s is the smallest
  *   integer with max|v| <= 448 * 2^s, clamped to [-127, 127] (an all-zero
  *   block takes -127); each value is stored as the E4M3 code (1 sign, 4
  *   exponent bits with bias 7, 3 mantissa bits, largest finite 448) of
  *   v / 2^s, rounded to nearest even, sign bit copied from v.
- * x is quantized per token, W_gate and W_up per output row; the matrix cores
- * apply both scales and accumulate in fp32; h is rounded to bf16 as on the
- * bf16 path.  Results differ from moe_zc_forward by the FP8 rounding of the
- * gate/up inputs (about 2^-4 relative per value); routing is unchanged.
- * Requires dt = bf16, d a multiple of 128 and T * d < 2^31 (else
- * MOE_ZC_ERR_UNSUPPORTED); other limits as moe_zc_forward. */
+ * gate/up: x is quantized per token along d, W_gate and W_up per output row;
+ * h is rounded to bf16 as on the bf16 path.  down (FP8): h of each grouped
+ * row is quantized along I from its fp32 value (the gate/up epilogue writes
+ * the codes and scales instead of bf16 h), W_down per output row along I.  The
+ * matrix cores apply both scales and accumulate in fp32.  Results differ from
+ * moe_zc_forward by the FP8 rounding of the quantized inputs (about 2^-4
+ * relative per value); routing is unchanged.
+ * Requires dt = bf16, d a multiple of 128, T * d < 2^31 and
+ * T * min(K, N) * I < 2^31 (else MOE_ZC_ERR_UNSUPPORTED); other limits as
+ * moe_zc_forward. */
 
-/* Bytes of ONE expert's packed FP8 gate/up weights (I / 128 panels by d / 128
- * stages of 33 KB: 2 d I bytes of codes, 2 d I / 32 of scales).  The down
- * projection keeps moe_zc_packed_expert_bytes' down_bytes.  Host only. */
+/* Bytes of ONE expert's packed FP8 weights (host only): *gate_up_bytes for
+ * gate and up (I / 128 panels by d / 128 stages of 33 KB: 2 d I bytes of
+ * codes, 2 d I / 32 of scales); *down_bytes, when down_bytes is not NULL, for
+ * the FP8 down projection (d rounded up to 256 rows, I / 128 stages of 33 KB).
+ * A bf16 down projection keeps moe_zc_packed_expert_bytes' down_bytes.
+ * (down_bytes was added in ABI version 3.) */
 moe_zc_status moe_zc_packed_fp8_expert_bytes(int64_t d, int64_t I,
-                                             size_t* gate_up_bytes);
+                                             size_t* gate_up_bytes,
+                                             size_t* down_bytes);
 
 /* Quantize and pack n_experts experts' gate and up weights (device, bf16,
  * row-major [n_experts, I, d] each, 16-byte aligned) into gate_up_fp8
  * (n_experts * gate_up_bytes, 16-byte aligned, caller-owned; expert e at byte
- * e * gate_up_bytes).  Enqueued on `stream`.  n_experts = 0 does nothing. */
+ * e * gate_up_bytes), and, when w_down ([n_experts, d, I] bf16) and down_fp8
+ * (n_experts * down_bytes) are given, the down weights too (both NULL or both
+ * set, else MOE_ZC_ERR_INVALID).  Enqueued on `stream`.  n_experts = 0 does
+ * nothing.  (w_down and down_fp8 were added in ABI version 3.) */
 moe_zc_status moe_zc_pack_expert_weights_fp8(const void* w_gate,
                                              const void* w_up,
+                                             const void* w_down,
                                              int32_t n_experts, int64_t d,
                                              int64_t I, void* gate_up_fp8,
-                                             hipStream_t stream);
+                                             void* down_fp8, hipStream_t stream);
 
 /* Workspace bytes of moe_zc_forward_packed_fp8 (moe_zc_forward's plus the
- * FP8 codes and scales of x); 0 for unsupported sizes.  Host only. */
+ * FP8 codes and scales of x and of h); 0 for unsupported sizes.  Host only. */
 size_t moe_zc_workspace_size_fp8(int64_t T, int64_t d, int64_t I, int32_t N,
                                  int32_t Z, int32_t K);
 
 /* moe_zc_forward (dt = bf16) with the gate/up projection in block FP8:
- * gate_up_fp8 from moe_zc_pack_expert_weights_fp8, down_packed from
- * moe_zc_pack_expert_weights (N experts each; NULL allowed when N = 0).  The
- * workspace must hold moe_zc_workspace_size_fp8 bytes.  Outputs and the aux
- * contract are those of moe_zc_forward; the FP8 stage of x counts in the
- * gate/up stage event. */
+ * gate_up_fp8 from moe_zc_pack_expert_weights_fp8; down_fp8 = 0: `down` is
+ * the bf16 down projection packed by moe_zc_pack_expert_weights; down_fp8 = 1:
+ * `down` is the FP8 down projection packed by moe_zc_pack_expert_weights_fp8
+ * (any other value: MOE_ZC_ERR_INVALID).  N experts each; NULL allowed when
+ * N = 0.  The workspace must hold moe_zc_workspace_size_fp8 bytes.  Outputs
+ * and the aux contract are those of moe_zc_forward; the FP8 stage of x counts
+ * in the gate/up stage event.
+ * (down_fp8 was added in ABI version 3.) */
 moe_zc_status moe_zc_forward_packed_fp8(const void* x, const float* w_router,
                                         const float* bias,
                                         const void* gate_up_fp8,
-                                        const void* down_packed,
+                                        const void* down, int32_t down_fp8,
                                         const void* residual, void* y,
                                         int64_t T, int64_t d, int64_t I,
                                         int32_t N, int32_t Z, int32_t K,

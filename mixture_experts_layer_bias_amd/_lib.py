@@ -77,14 +77,16 @@ def load() -> ctypes.CDLL:
                                                   i32, i32, ctypes.c_int,
                                                   ctypes.POINTER(MoeZcAux), vp]
     lib.moe_zc_forward_packed_noalloc.restype = ctypes.c_int
-    lib.moe_zc_packed_fp8_expert_bytes.argtypes = [i64, i64, ctypes.POINTER(sz)]
+    lib.moe_zc_packed_fp8_expert_bytes.argtypes = [i64, i64, ctypes.POINTER(sz),
+                                                   ctypes.POINTER(sz)]
     lib.moe_zc_packed_fp8_expert_bytes.restype = ctypes.c_int
-    lib.moe_zc_pack_expert_weights_fp8.argtypes = [vp, vp, i32, i64, i64, vp, vp]
+    lib.moe_zc_pack_expert_weights_fp8.argtypes = [vp, vp, vp, i32, i64, i64, vp, vp, vp]
     lib.moe_zc_pack_expert_weights_fp8.restype = ctypes.c_int
     lib.moe_zc_workspace_size_fp8.argtypes = [i64, i64, i64, i32, i32, i32]
     lib.moe_zc_workspace_size_fp8.restype = sz
-    lib.moe_zc_forward_packed_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i32,
-                                              i32, i32, ctypes.POINTER(MoeZcAux), vp, sz, vp]
+    lib.moe_zc_forward_packed_fp8.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, i64, i64, i64,
+                                              i32, i32, i32, ctypes.POINTER(MoeZcAux), vp, sz,
+                                              vp]
     lib.moe_zc_forward_packed_fp8.restype = ctypes.c_int
     lib.moe_zc_quantize_mx.argtypes = [vp, i64, i64, vp, vp, vp]
     lib.moe_zc_quantize_mx.restype = ctypes.c_int

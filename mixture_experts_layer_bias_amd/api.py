@@ -145,7 +145,10 @@ def _forward(name: str, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Ten
         out = torch.empty(T, d, dtype=dt, device=dev)
     _need(out, "out", dt, (T, d), dev)
     fn = getattr(lib, name)
-    nulls = [None] * len(weights)
+    # weights: tensors (passed as pointers) and, for the FP8 forward, the
+    # integer down-projection precision flag (passed as is)
+    nulls = [w if isinstance(w, int) else None for w in weights]
+    wargs = [w if isinstance(w, int) else _ptr(w) for w in weights]
     dt_arg = [] if fp8 else [_DT[dt]]
     need = (moe_zc_workspace_size_fp8(T, d, I, N, Z, K) if fp8
             else moe_zc_workspace_size(T, d, I, N, Z, K, dt))
@@ -167,7 +170,7 @@ def _forward(name: str, x: torch.Tensor, w_router: torch.Tensor, bias: torch.Ten
             setattr(a, k, t.data_ptr())
     if events is not None:
         a.stage_events = ctypes.cast(events.array, ctypes.c_void_p).value
-    code = fn(_ptr(x), _ptr(w_router), _ptr(bias), *[_ptr(w) for w in weights], _ptr(residual),
+    code = fn(_ptr(x), _ptr(w_router), _ptr(bias), *wargs, _ptr(residual),
               _ptr(out), T, d, I, N, Z, K, *dt_arg, ctypes.byref(a), _ptr(workspace),
               workspace.numel(), _stream(dev))
     if code != _lib.MOE_ZC_OK:
@@ -375,24 +378,27 @@ def moe_zc_bias_update(loads: torch.Tensor, target: torch.Tensor, bias: torch.Te
     return bias
 
 
-# ---- block-FP8 gate/up projection --------------------------------------------
+# ---- block-FP8 expert projections --------------------------------------------
 def moe_zc_workspace_size_fp8(T: int, d: int, I: int, N: int, Z: int, K: int) -> int:
     return int(_lib.load().moe_zc_workspace_size_fp8(T, d, I, N, Z, K))
 
 
-def moe_zc_packed_fp8_expert_bytes(d: int, I: int) -> int:
-    """Bytes of one expert's packed FP8 gate/up weights."""
-    gu = ctypes.c_size_t()
-    code = _lib.load().moe_zc_packed_fp8_expert_bytes(d, I, ctypes.byref(gu))
+def moe_zc_packed_fp8_expert_bytes(d: int, I: int):
+    """(gate_up_bytes, down_bytes) of one expert's packed FP8 weights."""
+    gu, dn = ctypes.c_size_t(), ctypes.c_size_t()
+    code = _lib.load().moe_zc_packed_fp8_expert_bytes(d, I, ctypes.byref(gu), ctypes.byref(dn))
     if code != _lib.MOE_ZC_OK:
         raise MoeZcError(code, "moe_zc_packed_fp8_expert_bytes")
-    return int(gu.value)
+    return int(gu.value), int(dn.value)
 
 
 def moe_zc_pack_expert_weights_fp8(w_gate: torch.Tensor, w_up: torch.Tensor,
-                                   gate_up_fp8: Optional[torch.Tensor] = None) -> torch.Tensor:
+                                   w_down: Optional[torch.Tensor] = None,
+                                   gate_up_fp8: Optional[torch.Tensor] = None,
+                                   down_fp8: Optional[torch.Tensor] = None):
     """Quantize and pack bf16 gate/up weights ([n, I, d] each) for
-    moe_zc_forward_packed_fp8; returns a uint8 tensor of n * gate_up_bytes."""
+    moe_zc_forward_packed_fp8; returns the uint8 tensor of n * gate_up_bytes,
+    or (gate_up_fp8, down_fp8) when w_down ([n, d, I]) is given as well."""
     lib = _lib.load()
     n, I, d = w_gate.shape
     dev = w_gate.device
@@ -400,41 +406,50 @@ def moe_zc_pack_expert_weights_fp8(w_gate: torch.Tensor, w_up: torch.Tensor,
         raise ValueError("weights must be GPU tensors")
     _need(w_gate, "w_gate", torch.bfloat16, (n, I, d), dev)
     _need(w_up, "w_up", torch.bfloat16, (n, I, d), dev)
-    gu = moe_zc_packed_fp8_expert_bytes(d, I)
+    gu, dn = moe_zc_packed_fp8_expert_bytes(d, I)
     if gate_up_fp8 is None:
         gate_up_fp8 = torch.empty(n * gu, dtype=torch.uint8, device=dev)
     _need(gate_up_fp8, "gate_up_fp8", torch.uint8, (n * gu,), dev)
-    code = lib.moe_zc_pack_expert_weights_fp8(_ptr(w_gate), _ptr(w_up), n, d, I,
-                                              _ptr(gate_up_fp8), _stream(dev))
+    if w_down is not None:
+        _need(w_down, "w_down", torch.bfloat16, (n, d, I), dev)
+        if down_fp8 is None:
+            down_fp8 = torch.empty(n * dn, dtype=torch.uint8, device=dev)
+        _need(down_fp8, "down_fp8", torch.uint8, (n * dn,), dev)
+    elif down_fp8 is not None:
+        raise ValueError("down_fp8 needs w_down")
+    code = lib.moe_zc_pack_expert_weights_fp8(_ptr(w_gate), _ptr(w_up), _ptr(w_down), n, d, I,
+                                              _ptr(gate_up_fp8), _ptr(down_fp8), _stream(dev))
     if code != _lib.MOE_ZC_OK:
         raise MoeZcError(code, "moe_zc_pack_expert_weights_fp8")
-    return gate_up_fp8
+    return gate_up_fp8 if w_down is None else (gate_up_fp8, down_fp8)
 
 
 def moe_zc_forward_packed_fp8(x: torch.Tensor, w_router: torch.Tensor, bias: torch.Tensor,
                               gate_up_fp8: Optional[torch.Tensor],
-                              down_packed: Optional[torch.Tensor], N: int, Z: int, K: int, I: int,
+                              down: Optional[torch.Tensor], N: int, Z: int, K: int, I: int,
                               residual: Optional[torch.Tensor] = None,
                               out: Optional[torch.Tensor] = None,
                               aux: Optional[Dict[str, torch.Tensor]] = None,
                               workspace: Optional[torch.Tensor] = None,
-                              events: Optional[StageEvents] = None) -> torch.Tensor:
+                              events: Optional[StageEvents] = None,
+                              down_fp8: bool = False) -> torch.Tensor:
     """moe_zc_forward (bf16) with the gate/up projection in block FP8:
-    gate_up_fp8 from moe_zc_pack_expert_weights_fp8, down_packed the down
-    half of moe_zc_pack_expert_weights."""
+    gate_up_fp8 from moe_zc_pack_expert_weights_fp8; ``down`` is the down half
+    of moe_zc_pack_expert_weights (bf16), or with down_fp8 the FP8 down
+    weights from moe_zc_pack_expert_weights_fp8."""
     _check_x(x)
     T, d = x.shape
     dev = x.device
     if x.dtype != torch.bfloat16:
         raise ValueError("the block-FP8 forward takes bf16 x")
     if N > 0:
-        gu = moe_zc_packed_fp8_expert_bytes(d, I)
+        gu, dn8 = moe_zc_packed_fp8_expert_bytes(d, I)
         _, dn = moe_zc_packed_expert_bytes(d, I, x.dtype)
         _need(gate_up_fp8, "gate_up_fp8", torch.uint8, (N * gu,), dev)
-        _need(down_packed, "down_packed", torch.uint8, (N * dn,), dev)
-        weights = (gate_up_fp8, down_packed)
+        _need(down, "down", torch.uint8, (N * (dn8 if down_fp8 else dn),), dev)
+        weights = (gate_up_fp8, down, int(bool(down_fp8)))
     else:
-        weights = (None, None)
+        weights = (None, None, int(bool(down_fp8)))
     return _forward("moe_zc_forward_packed_fp8", x, w_router, bias, weights, N, Z, K, I,
                     residual, out, aux, workspace, events, fp8=True)
 

@@ -71,12 +71,15 @@ moe_zc_status check_shape(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z,
 moe_zc_status check_fp8_shape(const Shape& s) {
   if (s.dt != MOE_ZC_BF16) return MOE_ZC_ERR_UNSUPPORTED;
   if (s.d % 128 != 0 || s.T * s.d >= (int64_t(1) << 31)) return MOE_ZC_ERR_UNSUPPORTED;
+  // the FP8 copy of h (down projection in FP8): 32-bit row byte offsets
+  if (s.smax * s.I >= (int64_t(1) << 31)) return MOE_ZC_ERR_UNSUPPORTED;
   return MOE_ZC_OK;
 }
 
 struct Plan {
   size_t logits, idx, gate, pos, loads, offsets, perm, counts, tiles, tiles2, wr2, xp, h, o;
   size_t xq, xs;    // FP8 codes and scales of x (block-FP8 forward only)
+  size_t hq, hs;    // FP8 codes and scales of h (block-FP8 down projection)
   size_t lsplit;    // partial router products of a split-K router
   int splits;       // parts of the router's K range (1: not split)
   size_t total;
@@ -110,6 +113,8 @@ Plan make_plan(const Shape& s, bool fp8 = false) {
   p.o = take((size_t)s.smax * s.d * s.es);
   p.xq = take(fp8 ? (size_t)s.T * s.d : 0);
   p.xs = take(fp8 ? (size_t)s.T * (s.d / 32) : 0);
+  p.hq = take(fp8 ? (size_t)s.smax * s.I : 0);
+  p.hs = take(fp8 ? (size_t)s.smax * (s.I / 32) : 0);
   p.lsplit = take(p.splits > 1 ? (size_t)p.splits * s.T * s.E * 4 : 0);
   p.total = at;
   return p;
@@ -154,13 +159,14 @@ enum Layout { kRowMajor = 0, kPacked = 1, kPackedFp8 = 2 };
 // The forward on one of the weight layouts.  kPacked: bf16 expert weights as
 // written by moe_zc_pack_expert_weights (gate_up and down point there);
 // kPackedFp8: the gate/up weights as written by moe_zc_pack_expert_weights_fp8
-// and the down weights packed bf16; x is quantized per forward.
+// and the down weights packed bf16 (or FP8 with down_fp8); x is quantized per
+// forward, and h too when the down projection runs in FP8.
 moe_zc_status forward_impl(const void* x, const float* w_router, const float* bias,
                            const void* w_gate, const void* w_up, const void* w_down,
                            Layout layout, const void* residual, void* y, int64_t T, int64_t d,
                            int64_t I, int32_t N, int32_t Z, int32_t K, moe_zc_dtype dt,
                            moe_zc_aux* aux, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool down_fp8 = false) {
   Shape s;
   const moe_zc_status st = check_shape(T, d, I, N, Z, K, dt, &s);
   if (st != MOE_ZC_OK) return st;
@@ -272,7 +278,15 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
       MOE_ZC_TRY(launch_quantize_mx(static_cast<const bf16_t*>(x), xq, xs, T, d, stream));
       p.A = xq; p.a_rows = perm;
       p.a_scales = xs; p.a_scale_ld = d / 32;
-      MOE_ZC_TRY(launch_fp8_gemm(p, s.ffn_tile_rows, s.smax, stream));
+      if (down_fp8) {
+        // h leaves the epilogue already quantized for the FP8 down projection
+        // (from its fp32 values), instead of as bf16
+        p.C = ws + pl.hq; p.ldc = I;
+        p.c_scales = reinterpret_cast<uint8_t*>(ws + pl.hs); p.c_scale_ld = I / 32;
+        MOE_ZC_TRY(launch_fp8_gemm(p, kSwiGLU_FP8, s.ffn_tile_rows, s.smax, stream));
+      } else {
+        MOE_ZC_TRY(launch_fp8_gemm(p, swiglu_epi, s.ffn_tile_rows, s.smax, stream));
+      }
     } else if (packed)
       MOE_ZC_TRY(launch_packed_gemm(p, swiglu_epi, s.ffn_tile_rows, s.smax, stream));
     else if (bf)
@@ -287,7 +301,16 @@ moe_zc_status forward_impl(const void* x, const float* w_router, const float* bi
     p.B0 = w_down; p.ldb = I; p.b_group_stride = d * I;
     p.C = o; p.ldc = d; p.Nout = (int)d;
     p.row_offsets = offsets; p.tile_prefix = packed ? tiles2 : tiles; p.G = N; p.M = 0;
-    if (packed)
+    if (fp8 && down_fp8) {
+      // block-FP8 down projection on the codes and scales of h that the
+      // gate/up epilogue wrote, on the gate/up tile schedule
+      uint8_t* hq = reinterpret_cast<uint8_t*>(ws + pl.hq);
+      uint8_t* hs = reinterpret_cast<uint8_t*>(ws + pl.hs);
+      p.A = hq; p.lda = I;
+      p.a_scales = hs; p.a_scale_ld = I / 32;
+      p.tile_prefix = tiles;
+      MOE_ZC_TRY(launch_fp8_gemm(p, kStoreBF16, s.ffn_tile_rows, s.smax, stream));
+    } else if (packed)
       MOE_ZC_TRY(launch_packed_gemm(p, kStoreBF16, down_rows, s.smax, stream));
     else if (bf)
       MOE_ZC_TRY(launch_mfma_gemm(p, kStoreBF16, s.ffn_tile_rows, s.smax, stream));
@@ -494,38 +517,49 @@ size_t moe_zc_workspace_size_fp8(int64_t T, int64_t d, int64_t I, int32_t N, int
 }
 
 moe_zc_status moe_zc_forward_packed_fp8(const void* x, const float* w_router, const float* bias,
-                                        const void* gate_up_fp8, const void* down_packed,
-                                        const void* residual, void* y, int64_t T, int64_t d,
-                                        int64_t I, int32_t N, int32_t Z, int32_t K,
-                                        moe_zc_aux* aux, void* workspace, size_t workspace_bytes,
-                                        hipStream_t stream) {
-  return forward_impl(x, w_router, bias, gate_up_fp8, nullptr, down_packed, kPackedFp8, residual,
-                      y, T, d, I, N, Z, K, MOE_ZC_BF16, aux, workspace, workspace_bytes, stream);
+                                        const void* gate_up_fp8, const void* down,
+                                        int32_t down_fp8, const void* residual, void* y,
+                                        int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z,
+                                        int32_t K, moe_zc_aux* aux, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  if (down_fp8 != 0 && down_fp8 != 1) return MOE_ZC_ERR_INVALID;
+  return forward_impl(x, w_router, bias, gate_up_fp8, nullptr, down, kPackedFp8, residual, y, T,
+                      d, I, N, Z, K, MOE_ZC_BF16, aux, workspace, workspace_bytes, stream,
+                      down_fp8 == 1);
 }
 
-moe_zc_status moe_zc_packed_fp8_expert_bytes(int64_t d, int64_t I, size_t* gate_up_bytes) {
+moe_zc_status moe_zc_packed_fp8_expert_bytes(int64_t d, int64_t I, size_t* gate_up_bytes,
+                                             size_t* down_bytes) {
   if (!gate_up_bytes) return MOE_ZC_ERR_INVALID;
   const moe_zc_status st = check_pack_shape(d, I, MOE_ZC_BF16);
   if (st != MOE_ZC_OK) return st;
   if (d % 128 != 0) return MOE_ZC_ERR_UNSUPPORTED;
   *gate_up_bytes = (size_t)fp8_packed_bytes(I, d);
+  if (down_bytes) *down_bytes = (size_t)fp8_packed_down_bytes(d, I);
   return MOE_ZC_OK;
 }
 
 moe_zc_status moe_zc_pack_expert_weights_fp8(const void* w_gate, const void* w_up,
-                                             int32_t n_experts, int64_t d, int64_t I,
-                                             void* gate_up_fp8, hipStream_t stream) {
+                                             const void* w_down, int32_t n_experts, int64_t d,
+                                             int64_t I, void* gate_up_fp8, void* down_fp8,
+                                             hipStream_t stream) {
   const moe_zc_status st = check_pack_shape(d, I, MOE_ZC_BF16);
   if (st != MOE_ZC_OK) return st;
   if (d % 128 != 0) return MOE_ZC_ERR_UNSUPPORTED;
   if (n_experts < 0) return MOE_ZC_ERR_INVALID;
+  if (!w_down != !down_fp8) return MOE_ZC_ERR_INVALID;  // both or neither
   if (n_experts == 0) return MOE_ZC_OK;
   if (!w_gate || !w_up || !gate_up_fp8) return MOE_ZC_ERR_INVALID;
   if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(gate_up_fp8)) return MOE_ZC_ERR_INVALID;
+  if (w_down && (!aligned16(w_down) || !aligned16(down_fp8))) return MOE_ZC_ERR_INVALID;
   MOE_ZC_TRY(launch_pack_weights_fp8(static_cast<const bf16_t*>(w_gate),
                                      static_cast<const bf16_t*>(w_up),
                                      static_cast<uint8_t*>(gate_up_fp8), n_experts, (int)I,
                                      (int)d, stream));
+  if (w_down)
+    MOE_ZC_TRY(launch_pack_down_fp8(static_cast<const bf16_t*>(w_down),
+                                    static_cast<uint8_t*>(down_fp8), n_experts, (int)d, (int)I,
+                                    stream));
   return MOE_ZC_OK;
 }
 

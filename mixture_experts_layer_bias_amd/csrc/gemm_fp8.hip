@@ -1,12 +1,15 @@
-// Block-FP8 expert gate/up projection (gfx950 v_mfma_scale_f32_32x32x64_f8f6f4):
+// Block-FP8 expert projections (gfx950 v_mfma_scale_f32_32x32x64_f8f6f4):
 //
-//   H[rows of expert g, :] = silu(A B_gate_g^T) * (A B_up_g^T)
+//   H[rows of expert g, :] = silu(A B_gate_g^T) * (A B_up_g^T)     (gate/up)
+//   O[rows of expert g, :] = A B_down_g^T                          (down, optional)
 //
-// with A (the token rows of x) and B (W_gate, W_up) in FP8 E4M3, each block of
+// with A (the token rows of x, or of h for the down projection) and B (W_gate,
+// W_up, W_down) in FP8 E4M3, each block of
 // 32 consecutive values along k carrying one power-of-two scale (an 8-bit
 // biased exponent, bias 127).  The matrix cores apply both operands' scales
-// inside the MFMA and accumulate in fp32; the output h is bf16, as on the
-// bf16 path, and the down projection stays bf16.  This is the fine-grained
+// inside the MFMA and accumulate in fp32; the outputs h and o are bf16, as on
+// the bf16 path; the down projection runs in FP8 or bf16, a per-layer choice.
+// This is the fine-grained
 // block quantization the LongCat pages adopt (same scheme family as
 // DeepSeek-V3, mixed per layer: the down projection's inputs carry extreme
 // activations), in the block-scaled form the MI355X matrix cores consume.
@@ -32,6 +35,9 @@
 //     k = 128 stage + 64 ks + 32 half + 16 (l / 32) + 0..15;
 //   scales, 1 KB: 256 bytes per wavefront, 4 per lane; byte 2 ks + j of lane
 //     l is the scale of row (j, l % 32), k block 4 stage + 2 ks + l / 32.
+// Packed down weights: the same blocks over panels of 256 rows of W_down
+// (output columns) and stages of 128 k along I, with column block j of
+// wavefront w holding rows panel * 256 + 64 w + 32 j + l % 32 (zeros past d).
 // Blocks are ordered expert, panel, stage: a tile streams one contiguous range.
 //
 // Activations: x is quantized once per forward into codes [T, d] and scales
@@ -130,14 +136,16 @@ __global__ __launch_bounds__(256) void quantize_mx_kernel(const bf16_t* __restri
   xs[b] = (uint8_t)sc;
 }
 
-// W_gate, W_up [groups][I][d] bf16 -> packed FP8 blocks.  One workgroup per
-// (group, panel, stage) block; 1024 (row, 32-k block) pairs per block, the k
-// block in the low bits so that four consecutive threads read one row's
-// 256 bytes.
+// Weights [groups][rows][K] bf16 -> packed FP8 blocks: SwiGLU (wu set): W_gate
+// and W_up with rows = I hidden units, K = d; otherwise W_down with rows = d,
+// K = I.  One workgroup per (group, panel, stage) block; 1024 (row, 32-k
+// block) pairs per block, the k block in the low bits so that four
+// consecutive threads read one row's 256 bytes.
 __global__ __launch_bounds__(256) void pack_fp8_kernel(const bf16_t* __restrict__ wg,
                                                        const bf16_t* __restrict__ wu,
-                                                       uint8_t* __restrict__ out, int I, int d,
+                                                       uint8_t* __restrict__ out, int rows, int d,
                                                        int n_panels) {
+  const int I = rows;  // rows of one group (SwiGLU: hidden units)
   const int nk = d / F8_BKS;
   const int64_t b = blockIdx.x;
   const int64_t per_group = (int64_t)n_panels * nk;
@@ -150,10 +158,16 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const bf16_t* __restrict_
     const int pidx = threadIdx.x + 256 * i;
     const int kb = pidx & 3, rp = pidx >> 2;
     const int w = rp >> 6, j = (rp >> 5) & 1, cc = rp & 31;
-    const int64_t u = (int64_t)nt * 128 + 32 * w + cc;
-    const bf16_t* src = (j ? wu : wg) + (g * I + u) * (int64_t)d + (int64_t)kt * F8_BKS + kb * 32;
-    uint32_t codes[8];
-    const uint32_t sc = mx_block(src, codes);
+    // SwiGLU: gate (j = 0) or up (j = 1) row of hidden unit u; plain: row u
+    const int64_t u = wu ? (int64_t)nt * 128 + 32 * w + cc
+                         : (int64_t)nt * 256 + 64 * w + 32 * j + cc;
+    uint32_t codes[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    uint32_t sc = 0u;  // rows past the end: zero codes, smallest scale
+    if (u < I) {
+      const bf16_t* src = ((wu && j) ? wu : wg) + (g * I + u) * (int64_t)d +
+                          (int64_t)kt * F8_BKS + kb * 32;
+      sc = mx_block(src, codes);
+    }
     // block kb = 2 ks + half: codes 0-15 to lane cc, 16-31 to lane cc + 32, both
     // in piece 4 ks + 2 j + half; its scale to lane cc + 32 half
     const int ks = kb >> 1, half = kb & 1, q = 4 * ks + 2 * j + half;
@@ -168,7 +182,91 @@ __global__ __launch_bounds__(256) void pack_fp8_kernel(const bf16_t* __restrict_
 // NA = live 32-row blocks of the tile.  Workgroup of four wavefronts, one per
 // SIMD; wavefront w owns hidden units [32 w, 32 w + 32) of the panel (gate
 // and up columns), for every row.  A stage is two MFMA substeps of 64 k.
-template <int NA, bool SAVE>
+// Epilogue of the gate/up tile when the down projection runs in FP8: h =
+// silu(gate) * up in fp32, staged through LDS one 32-row block at a time; the
+// 32 hidden units a wavefront holds for a row are one quantization block
+// (they start at a multiple of 32), so lanes r and r + 32 take columns
+// 0..15 and 16..31 of row r, share the block's amax through one shuffle, and
+// store 16 codes each (16 bytes) and, lane r, the scale byte.
+template <int NA>
+__device__ __forceinline__ void store_fp8_h_tile(const f32x16_t (&acc)[NA][2], char* smem,
+                                                 int wave, int lane, const TileCoord& c,
+                                                 const GemmProblem& p) {
+  constexpr int OS = 33;                      // padded LDS row (floats): conflict-free
+  float* ot = reinterpret_cast<float*>(smem) + wave * (32 * OS);
+  const int lrow4 = 4 * (lane >> 5), lcol = lane & 31;
+  const int r = lane & 31, hf = lane >> 5;
+  const int gcol0 = c.n0 + wave * 32;         // first hidden unit of this wavefront
+  uint8_t* __restrict__ codes = static_cast<uint8_t*>(p.C);
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      ot[(8 * (v >> 2) + lrow4 + (v & 3)) * OS + lcol] = swiglu_fast(acc[i][0][v], acc[i][1][v]);
+    __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): the LDS writes landed
+    __builtin_amdgcn_wave_barrier();
+    float vals[16];
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      vals[e] = ot[r * OS + 16 * hf + e];
+      amax = fmaxf(amax, fabsf(vals[e]));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    const int s = mx_scale_exp(amax);
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[q] = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[q] |= e4m3_code(ldexpf(vals[4 * q + e], -s)) << (8 * e);
+    }
+    const int grow = c.m0 + i * 32 + r;
+    if (grow < c.m_end) {
+      *reinterpret_cast<u32x4_t*>(codes + (int64_t)grow * p.ldc + gcol0 + 16 * hf) =
+          u32x4_t{w[0], w[1], w[2], w[3]};
+      if (hf == 0) p.c_scales[(int64_t)grow * p.c_scale_ld + gcol0 / 32] = (uint8_t)(s + 127);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);       // reads done before the next block overwrites
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Pre-activations of the gate/up tile (a | u, bf16) to p.C2: the saving part
+// of store_bf16_tile alone.
+template <int NA>
+__device__ __forceinline__ void store_act_tile(const f32x16_t (&acc)[NA][2], char* smem, int wave,
+                                               int lane, const TileCoord& c,
+                                               const GemmProblem& p) {
+  constexpr int OS = 40;
+  bf16_t* ot = reinterpret_cast<bf16_t*>(smem) + wave * (32 * OS);
+  const int lrow4 = 4 * (lane >> 5), lcol = lane & 31;
+  const int gcol0 = c.n0 + wave * 32;
+  bf16_t* __restrict__ C2 = static_cast<bf16_t*>(p.C2);
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        ot[(8 * (v >> 2) + lrow4 + (v & 3)) * OS + lcol] = f32_to_bf16(acc[i][part][v]);
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int q = lane; q < 32 * 4; q += 64) {
+        const int rr = q / 4, ch = q - rr * 4;
+        const int grow = c.m0 + i * 32 + rr;
+        if (grow < c.m_end)
+          *reinterpret_cast<u32x4_t*>(&C2[(int64_t)grow * p.ldc2 + part * p.Nout + gcol0 + ch * 8]) =
+              *reinterpret_cast<const u32x4_t*>(&ot[rr * OS + ch * 8]);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// MODE: kSwiGLU_BF16 (h bf16), kSwiGLU_FP8 (h quantized) or kStoreBF16 (down)
+template <int NA, bool SAVE, int MODE>
 __device__ __forceinline__ void run_fp8(const GemmProblem& p, const TileCoord& c, int n_tiles,
                                         char* __restrict__ smem) {
   const int tid = threadIdx.x;
@@ -354,31 +452,39 @@ __device__ __forceinline__ void run_fp8(const GemmProblem& p, const TileCoord& c
 #undef F8_SUB
 #undef F8_STAGE
   ring_barrier<0>();  // every wavefront is done reading the ring before it is reused
-  store_bf16_tile<NA, true, SAVE>(acc, smem, wave, lane, c, p);
+  if constexpr (MODE == kSwiGLU_FP8) {
+    store_fp8_h_tile<NA>(acc, smem, wave, lane, c, p);
+    if constexpr (SAVE) store_act_tile<NA>(acc, smem, wave, lane, c, p);
+  } else {
+    store_bf16_tile<NA, MODE != kStoreBF16, SAVE>(acc, smem, wave, lane, c, p);
+  }
 }
 
-// SAVE: also store the pre-activations to p.C2 (a separate instantiation)
-template <bool SAVE>
+// SAVE: also store the pre-activations to p.C2 (a separate instantiation);
+// MODE: the epilogue (gate/up with h in bf16 or FP8, or the plain down
+// projection)
+template <bool SAVE, int MODE>
 __global__ __launch_bounds__(64 * F8_WAVES, 1) void fp8_gemm_kernel(GemmProblem p, int n_tiles,
                                                                     int total_bound,
                                                                     int tile_rows) {
+  constexpr bool SWIGLU = MODE != kStoreBF16;
   __shared__ __attribute__((aligned(16))) char smem[F8_DEPTH * (F8_SLOT + 1024)];
   const int logical =
       xcd_logical_tile(p.tile_prefix ? p.tile_prefix[p.G] * n_tiles : total_bound);
   if (logical < 0) return;
   TileCoord c;
-  if (!map_tile<kPackedPanel, true>(p, n_tiles, logical, tile_rows, c)) return;
+  if (!map_tile<kPackedPanel, SWIGLU>(p, n_tiles, logical, tile_rows, c)) return;
   const int nb = (c.m_end - c.m0 + 31) / 32;  // at most F8_MAXRB: checked on the host
   if (nb <= 0) return;
   switch (nb) {
-    case 1: run_fp8<1, SAVE>(p, c, n_tiles, smem); break;
-    case 2: run_fp8<2, SAVE>(p, c, n_tiles, smem); break;
-    case 3: run_fp8<3, SAVE>(p, c, n_tiles, smem); break;
-    case 4: run_fp8<4, SAVE>(p, c, n_tiles, smem); break;
-    case 5: run_fp8<5, SAVE>(p, c, n_tiles, smem); break;
-    case 6: run_fp8<6, SAVE>(p, c, n_tiles, smem); break;
-    case 7: run_fp8<7, SAVE>(p, c, n_tiles, smem); break;
-    default: run_fp8<F8_MAXRB, SAVE>(p, c, n_tiles, smem); break;
+    case 1: run_fp8<1, SAVE, MODE>(p, c, n_tiles, smem); break;
+    case 2: run_fp8<2, SAVE, MODE>(p, c, n_tiles, smem); break;
+    case 3: run_fp8<3, SAVE, MODE>(p, c, n_tiles, smem); break;
+    case 4: run_fp8<4, SAVE, MODE>(p, c, n_tiles, smem); break;
+    case 5: run_fp8<5, SAVE, MODE>(p, c, n_tiles, smem); break;
+    case 6: run_fp8<6, SAVE, MODE>(p, c, n_tiles, smem); break;
+    case 7: run_fp8<7, SAVE, MODE>(p, c, n_tiles, smem); break;
+    default: run_fp8<F8_MAXRB, SAVE, MODE>(p, c, n_tiles, smem); break;
   }
 }
 
@@ -386,6 +492,10 @@ __global__ __launch_bounds__(64 * F8_WAVES, 1) void fp8_gemm_kernel(GemmProblem 
 
 int64_t fp8_packed_bytes(int64_t I, int64_t d) {
   return (I / (kPackedPanel / 2)) * (d / F8_BKS) * (int64_t)F8_BLOCK;
+}
+
+int64_t fp8_packed_down_bytes(int64_t d, int64_t I) {
+  return ((d + kPackedPanel - 1) / kPackedPanel) * (I / F8_BKS) * (int64_t)F8_BLOCK;
 }
 
 hipError_t launch_quantize_mx(const bf16_t* x, uint8_t* xq, uint8_t* xs, int64_t rows, int64_t d,
@@ -411,13 +521,35 @@ hipError_t launch_pack_weights_fp8(const bf16_t* wg, const bf16_t* wu, uint8_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_fp8_gemm(const GemmProblem& p, int tile_rows, int64_t max_rows, hipStream_t s) {
+hipError_t launch_pack_down_fp8(const bf16_t* wd, uint8_t* out, int groups, int d, int I,
+                                hipStream_t s) {
+  if (I % F8_BKS != 0) return hipErrorInvalidValue;
+  const int n_panels = (d + kPackedPanel - 1) / kPackedPanel;
+  const int64_t blocks = (int64_t)groups * n_panels * (I / F8_BKS);
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, wd, nullptr, out,
+                     d, I, n_panels);
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm(const GemmProblem& p, int epilogue, int tile_rows, int64_t max_rows,
+                           hipStream_t s) {
   if (p.K < F8_BKS || p.K % F8_BKS != 0 || !p.a_scales || p.a_scale_ld * 32 != p.K)
     return hipErrorInvalidValue;
   if (tile_rows < 32 || tile_rows > 32 * F8_MAXRB || tile_rows % 32 != 0)
     return hipErrorInvalidValue;
-  if (p.Nout % (kPackedPanel / 2) != 0) return hipErrorInvalidValue;
-  const int n_tiles = p.Nout / (kPackedPanel / 2);
+  if (epilogue != kSwiGLU_BF16 && epilogue != kSwiGLU_BF16_ACT && epilogue != kStoreBF16 &&
+      epilogue != kSwiGLU_FP8)
+    return hipErrorInvalidValue;
+  const bool swiglu = epilogue != kStoreBF16;
+  if (epilogue != kSwiGLU_FP8 && (epilogue == kSwiGLU_BF16_ACT) != (p.C2 != nullptr))
+    return hipErrorInvalidValue;
+  if (epilogue == kSwiGLU_FP8 && (!p.c_scales || p.c_scale_ld * 32 != p.Nout))
+    return hipErrorInvalidValue;
+  if (swiglu ? p.Nout % (kPackedPanel / 2) != 0 : p.Nout % 64 != 0) return hipErrorInvalidValue;
+  const int n_tiles = swiglu ? p.Nout / (kPackedPanel / 2)
+                             : (p.Nout + kPackedPanel - 1) / kPackedPanel;
   int64_t mt_bound;
   if (p.tile_prefix) {
     mt_bound = (max_rows + (int64_t)p.G * (tile_rows - 1)) / tile_rows;
@@ -429,12 +561,23 @@ hipError_t launch_fp8_gemm(const GemmProblem& p, int tile_rows, int64_t max_rows
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7ffffff0) return hipErrorInvalidValue;
   blocks = (blocks + 7) / 8 * 8;
-  if (p.C2)
-    hipLaunchKernelGGL(fp8_gemm_kernel<true>, dim3((unsigned)blocks), dim3(64 * F8_WAVES), 0, s,
-                       p, n_tiles, (int)(mt_bound * n_tiles), tile_rows);
+  const dim3 grid((unsigned)blocks), block(64 * F8_WAVES);
+  const int total = (int)(mt_bound * n_tiles);
+  if (!swiglu)
+    hipLaunchKernelGGL((fp8_gemm_kernel<false, kStoreBF16>), grid, block, 0, s, p, n_tiles,
+                       total, tile_rows);
+  else if (epilogue == kSwiGLU_FP8 && p.C2)
+    hipLaunchKernelGGL((fp8_gemm_kernel<true, kSwiGLU_FP8>), grid, block, 0, s, p, n_tiles,
+                       total, tile_rows);
+  else if (epilogue == kSwiGLU_FP8)
+    hipLaunchKernelGGL((fp8_gemm_kernel<false, kSwiGLU_FP8>), grid, block, 0, s, p, n_tiles,
+                       total, tile_rows);
+  else if (p.C2)
+    hipLaunchKernelGGL((fp8_gemm_kernel<true, kSwiGLU_BF16>), grid, block, 0, s, p, n_tiles,
+                       total, tile_rows);
   else
-    hipLaunchKernelGGL(fp8_gemm_kernel<false>, dim3((unsigned)blocks), dim3(64 * F8_WAVES), 0, s,
-                       p, n_tiles, (int)(mt_bound * n_tiles), tile_rows);
+    hipLaunchKernelGGL((fp8_gemm_kernel<false, kSwiGLU_BF16>), grid, block, 0, s, p, n_tiles,
+                       total, tile_rows);
   return hipGetLastError();
 }
 

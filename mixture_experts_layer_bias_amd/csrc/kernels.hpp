@@ -81,12 +81,17 @@ struct GemmProblem {
   // in bf16, a = x W_gate^T to C2[row][col] and u = x W_up^T to C2[row][Nout + col]
   void* C2;
   int64_t ldc2;
+  // kSwiGLU_FP8 (block-FP8 GEMM only): h quantized in blocks of 32 columns,
+  // E4M3 codes to C (ldc bytes per row) and scale bytes to
+  // c_scales[row * c_scale_ld + col / 32]
+  uint8_t* c_scales;
+  int64_t c_scale_ld;
 };
 
 // kSwiGLU_BF16_ACT: kSwiGLU_BF16 that also stores the pre-activations to C2
 // (a separate instantiation, so the plain SwiGLU kernels are unchanged).
 enum Epilogue { kStoreF32 = 0, kStoreBF16 = 1, kSwiGLU_BF16 = 2, kSwiGLU_F32 = 3,
-                kSwiGLU_BF16_ACT = 4 };
+                kSwiGLU_BF16_ACT = 4, kSwiGLU_FP8 = 5 };
 constexpr bool is_swiglu_bf16(int epi) { return epi == kSwiGLU_BF16 || epi == kSwiGLU_BF16_ACT; }
 
 // bf16 MFMA path (gemm_mfma.hip).  `tile_rows` selects the row-tile variant
@@ -121,20 +126,30 @@ hipError_t launch_packed_gemm(const GemmProblem& p, int epilogue, int tile_rows,
                               int64_t max_rows, hipStream_t s);
 int packed_down_tile_rows(int ffn_tile_rows);
 
-// Block-FP8 gate/up path (gemm_fp8.hip): E4M3 codes with one power-of-two
-// scale per 32 values along k; the down projection stays bf16.
-// Bytes of one group's packed FP8 gate/up weights (I hidden units by d).
+// Block-FP8 path (gemm_fp8.hip): E4M3 codes with one power-of-two scale per
+// 32 values along k; gate/up always, the down projection optionally.
+// Bytes of one group's packed FP8 gate/up weights (I hidden units by d), and
+// of its packed FP8 down weights (d rows by I).
 int64_t fp8_packed_bytes(int64_t I, int64_t d);
+int64_t fp8_packed_down_bytes(int64_t d, int64_t I);
 // x [rows][d] bf16 -> codes [rows][d] and scale bytes [rows][d / 32].
 hipError_t launch_quantize_mx(const bf16_t* x, uint8_t* xq, uint8_t* xs, int64_t rows, int64_t d,
                               hipStream_t s);
 // W_gate, W_up [groups][I][d] bf16 -> packed FP8 gate/up blocks.
 hipError_t launch_pack_weights_fp8(const bf16_t* wg, const bf16_t* wu, uint8_t* out, int groups,
                                    int I, int d, hipStream_t s);
-// SwiGLU gate/up GEMM: A = FP8 codes (row stride lda bytes, optional gather
-// a_rows), a_scales / a_scale_ld its scales, B0 = packed FP8 weights, C = h
-// bf16.  Tiles of at most kPackedMaxTileRows rows, as the bf16 packed path.
-hipError_t launch_fp8_gemm(const GemmProblem& p, int tile_rows, int64_t max_rows, hipStream_t s);
+// W_down [groups][d][I] bf16 -> packed FP8 down blocks.
+hipError_t launch_pack_down_fp8(const bf16_t* wd, uint8_t* out, int groups, int d, int I,
+                                hipStream_t s);
+// Grouped GEMM on FP8 operands: A = FP8 codes (row stride lda bytes, optional
+// gather a_rows), a_scales / a_scale_ld its scales, B0 = packed FP8 weights.
+// epilogue kSwiGLU_BF16 (or _ACT with C2): C = h bf16 from gate/up blocks;
+// kSwiGLU_FP8 (C2 optional, as _ACT): h quantized from its fp32 values in
+// blocks of 32 hidden units, codes to C and scales to c_scales;
+// kStoreBF16: C = A B^T bf16 from down blocks.  Tiles of at most
+// kPackedMaxTileRows rows, as the bf16 packed path.
+hipError_t launch_fp8_gemm(const GemmProblem& p, int epilogue, int tile_rows, int64_t max_rows,
+                           hipStream_t s);
 
 // Backward (backward.hip).
 // tile_prefix (row tiles of bm) and kofs (rows rounded up to 64) of the groups.

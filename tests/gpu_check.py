@@ -28,10 +28,11 @@ Y_TOL = {"bf16": 1e-2, "f32": 1e-5}
 
 
 def run_gpu(w, inp, residual=True, workspace=None, events=None, packed=None, fp8=False,
-            act=False):
+            act=False, down_fp8=False):
     """One forward through the C ABI; ``packed`` = (gate_up, down) from
     moe_zc_pack_expert_weights selects moe_zc_forward_packed, and with ``fp8``
-    ``packed`` = (gate_up_fp8, down) selects moe_zc_forward_packed_fp8.  With
+    ``packed`` = (gate_up_fp8, down) selects moe_zc_forward_packed_fp8 (down in
+    FP8 when ``down_fp8``).  With
     ``act`` the forward also saves the expert pre-activations (aux "act", left
     on the device as out["act_t"])."""
     dev = inp["x"].device
@@ -42,7 +43,7 @@ def run_gpu(w, inp, residual=True, workspace=None, events=None, packed=None, fp8
         gu, dn = packed if packed is not None else (None, None)
         y = m.moe_zc_forward_packed_fp8(inp["x"], inp["w_router"], inp["bias"], gu, dn,
                                         w.N, w.Z, w.K, w.I, residual=res, aux=aux,
-                                        workspace=workspace, events=events)
+                                        workspace=workspace, events=events, down_fp8=down_fp8)
     elif packed is None:
         y = m.moe_zc_forward(inp["x"], inp["w_router"], inp["bias"], inp["w_gate"], inp["w_up"],
                              inp["w_down"], w.N, w.Z, w.K, residual=res, aux=aux,
@@ -90,9 +91,11 @@ def validate_grouping(idx, loads, offsets, perm, pos, N, E):
         assert (np.diff(blk) > 0).all(), f"expert {e}: tokens not ascending"
 
 
-def check_forward(w, inp, g, y_tokens=None, max_flip_frac=1e-3, get_expert=None, fp8=False):
+def check_forward(w, inp, g, y_tokens=None, max_flip_frac=1e-3, get_expert=None, fp8=False,
+                  down_fp8=False):
     """Compare a GPU forward (``g`` from run_gpu) with the oracle (with the
-    gate/up projection in block FP8 when ``fp8``)."""
+    gate/up projection in block FP8 when ``fp8``, and the down projection too
+    when ``down_fp8``)."""
     T, N, K, E = w.T, w.N, w.K, w.E
     x = inp["x"].cpu()
     wr = inp["w_router"].cpu()
@@ -141,8 +144,12 @@ def check_forward(w, inp, g, y_tokens=None, max_flip_frac=1e-3, get_expert=None,
 
         def get_expert(e):
             return wg[e], wu[e], wd[e]
-    fwd = oracle.mx.forward_tokens_fp8 if fp8 else oracle.forward_tokens
-    y_ref, _ = fwd(x[toks], l32[toks], b, get_expert, N, K, None if res is None else res[toks])
+    res_t = None if res is None else res[toks]
+    if fp8:
+        y_ref, _ = oracle.mx.forward_tokens_fp8(x[toks], l32[toks], b, get_expert, N, K, res_t,
+                                                down_fp8=down_fp8)
+    else:
+        y_ref, _ = oracle.forward_tokens(x[toks], l32[toks], b, get_expert, N, K, res_t)
     scale = max(np.abs(y_ref).max(), 1e-30)
     err = np.abs(g["y"][toks] - y_ref).max() if len(toks) else 0.0
     tol = Y_TOL[w.dtype] * scale

@@ -239,3 +239,26 @@ def test_noalloc_forward_refuses_on_the_host(lib):
     assert f(*args(64, dt=F32)) == UNSUPPORTED
     assert f(*args(64, K=0)) == INVALID
     assert f(*args(0)) == OK                          # no tokens: nothing to do
+
+
+def test_fp8_entry_points_validation(lib):
+    """The block-FP8 forward's down-projection flag is 0 or 1, and the FP8
+    packing takes the down weights and their destination together or not at
+    all; both checks happen on the host."""
+    T, d, I, N, Z, K = 64, 128, 128, 8, 4, 3
+    nb = lib.moe_zc_workspace_size_fp8(T, d, I, N, Z, K)
+    assert nb > lib.moe_zc_workspace_size(T, d, I, N, Z, K, BF16)   # FP8 copies of x and h
+    f = lib.moe_zc_forward_packed_fp8
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, None, FAKE, T, d, I, N, Z, K, None, FAKE, nb,
+             None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, None, FAKE, 0, d, I, N, Z, K, None, FAKE, nb,
+             None) == OK
+    pk = lib.moe_zc_pack_expert_weights_fp8
+    assert pk(FAKE, FAKE, FAKE, 2, d, I, FAKE, None, None) == INVALID
+    assert pk(FAKE, FAKE, None, 2, d, I, FAKE, FAKE, None) == INVALID
+    assert pk(FAKE, FAKE, None, 0, d, I, FAKE, None, None) == OK
+    gu, dn = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.moe_zc_packed_fp8_expert_bytes(6144, 2048, ctypes.byref(gu), ctypes.byref(dn)) == OK
+    assert gu.value == 16 * 48 * 33792                 # I / 128 panels, d / 128 stages
+    assert dn.value == 24 * 16 * 33792                 # d / 256 panels, I / 128 stages
+    assert lib.moe_zc_packed_fp8_expert_bytes(6144, 2048, ctypes.byref(gu), None) == OK

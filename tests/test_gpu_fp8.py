@@ -1,5 +1,6 @@
-"""Block-FP8 gate/up projection (moe_zc_quantize_mx, moe_zc_pack_expert_weights_fp8,
-moe_zc_forward_packed_fp8) against the oracle.
+"""Block-FP8 expert projections (moe_zc_quantize_mx, moe_zc_pack_expert_weights_fp8,
+moe_zc_forward_packed_fp8 with the down projection in bf16 or FP8) against the
+oracle.
 
 Codes and scales are integer results of the quantization rule and must equal
 the oracle's bit for bit.  The packed weight bytes are checked against a NumPy
@@ -82,7 +83,7 @@ def test_pack_fp8_layout_matches_definition(n, d, I):
     wu[0, 5, 32:64] = 0.0                                 # an all-zero block
     packed = m.moe_zc_pack_expert_weights_fp8(wg.to(DEV), wu.to(DEV))
     torch.cuda.synchronize()
-    assert packed.numel() == n * m.moe_zc_packed_fp8_expert_bytes(d, I)
+    assert packed.numel() == n * m.moe_zc_packed_fp8_expert_bytes(d, I)[0]
     got = packed.cpu().numpy().reshape(n, -1)
     assert np.array_equal(got, pack_fp8_reference(wg, wu))
 
@@ -105,6 +106,48 @@ CASES = {
 }
 
 
+def pack_fp8_down_reference(wd):
+    """[n, d, I] bf16 down weights -> packed FP8 bytes [n, panels * stages * 33792]:
+    the gate/up block layout with column block j of wavefront w holding rows
+    panel * 256 + 64 w + 32 j + lane % 32 (zeros past d)."""
+    n, d, I = wd.shape
+    P, S = (d + 255) // 256, I // 128
+    w = np.zeros((n, P * 256, I))
+    w[:, :d] = wd.float().double().numpy()
+    c, sc = omx.mx_quantize(w, axis=-1)
+    c8, s8 = c.reshape(n, P, 256, S, 4, 32), sc.reshape(n, P, 256, S, 4)
+    out = np.zeros((n, P, S, 33792), np.uint8)
+    for wv in range(4):
+        for j in range(2):
+            for cc in range(32):
+                row = 64 * wv + 32 * j + cc
+                for kb in range(4):
+                    ks, half = kb >> 1, kb & 1
+                    q = 4 * ks + 2 * j + half
+                    blk = c8[:, :, row, :, kb, :]
+                    for h in range(2):
+                        o = wv * 8192 + q * 1024 + (cc + 32 * h) * 16
+                        out[..., o:o + 16] = blk[..., 16 * h:16 * h + 16]
+                    out[..., 32768 + wv * 256 + (cc + 32 * half) * 4 + 2 * ks + j] = \
+                        s8[:, :, row, :, kb]
+    return out.reshape(n, -1)
+
+
+@pytest.mark.parametrize("n,d,I", [(2, 256, 128), (1, 384, 256), (3, 640, 128)])
+def test_pack_fp8_down_layout_matches_definition(n, d, I):
+    """d = 384 and 640 leave the last 256-row panel partly empty (zero rows)."""
+    g = torch.Generator().manual_seed(n * 77 + d + I)
+    wg = (torch.randn(n, I, d, generator=g) * 0.05).to(torch.bfloat16)
+    wd = (torch.randn(n, d, I, generator=g) * 0.05).to(torch.bfloat16)
+    wd[0, 3, 32:64] = 0.0                                 # an all-zero block
+    gu8, dn8 = m.moe_zc_pack_expert_weights_fp8(wg.to(DEV), wg.to(DEV), wd.to(DEV))
+    torch.cuda.synchronize()
+    assert dn8.numel() == n * m.moe_zc_packed_fp8_expert_bytes(d, I)[1]
+    assert np.array_equal(dn8.cpu().numpy().reshape(n, -1), pack_fp8_down_reference(wd))
+    # the gate/up half is what packing gate and up alone gives
+    assert torch.equal(gu8, m.moe_zc_pack_expert_weights_fp8(wg.to(DEV), wg.to(DEV)))
+
+
 @pytest.mark.parametrize("name", list(CASES))
 def test_fp8_forward_vs_oracle(name):
     w = _edge(**CASES[name])
@@ -116,12 +159,26 @@ def test_fp8_forward_vs_oracle(name):
         fp8 = (m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"]), packed[1])
     g_bf = run_gpu(w, inp, packed=packed)
     g_8 = run_gpu(w, inp, packed=fp8, fp8=True)
-    for k in m.AUX_KEYS:                       # the router and the grouping are unquantized
-        assert np.array_equal(g_bf[k], g_8[k]), k
+    S = int(g_bf["offsets"][w.N])
+
+    def same_routing(a, b):                    # the router and the grouping are unquantized
+        for k in m.AUX_KEYS:
+            va, vb = (a[k][:S], b[k][:S]) if k == "perm" else (a[k], b[k])   # perm: S defined
+            assert np.array_equal(va, vb), k
+
+    same_routing(g_bf, g_8)
     rep = check_forward(w, inp, g_8, fp8=True)
     scale = np.abs(g_bf["y"]).max()
     print(name, rep, "fp8 vs bf16 max|dy| / max|y|:",
           float(np.abs(g_8["y"] - g_bf["y"]).max() / max(scale, 1e-30)), flush=True)
+    # the down projection in FP8 as well (the residual off, so the bar
+    # scales with the expert mixture)
+    if w.N > 0:
+        gu8, dn8 = m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"], inp["w_down"])
+        g_88 = run_gpu(w, inp, residual=False, packed=(gu8, dn8), fp8=True, down_fp8=True)
+        same_routing(g_bf, g_88)
+        print(name, "down fp8", check_forward(w, dict(inp, residual=None), g_88, fp8=True,
+                                              down_fp8=True), flush=True)
 
 
 def test_fp8_mid_vs_oracle():
@@ -133,6 +190,10 @@ def test_fp8_mid_vs_oracle():
     sample = np.sort(np.random.default_rng(0).choice(w.T, 384, replace=False))
     print("mid fp8", check_forward(w, dict(inp, residual=None), g, y_tokens=sample, fp8=True),
           flush=True)
+    fp8_all = m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"], inp["w_down"])
+    g2 = run_gpu(w, inp, residual=False, packed=fp8_all, fp8=True, down_fp8=True)
+    print("mid fp8 down fp8", check_forward(w, dict(inp, residual=None), g2, y_tokens=sample,
+                                            fp8=True, down_fp8=True), flush=True)
 
 
 def test_fp8_rejects_unsupported_shapes():
@@ -171,3 +232,24 @@ def test_fp8_full_size_prefill():
     print(f"[fp8 prefill] checking tokens {sample.tolist()}", flush=True)
     print("prefill fp8", check_forward(w, inp, g, y_tokens=sample, fp8=True,
                                        get_expert=gpu_expert_getter(inp)), flush=True)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_fp8_down_full_size(name):
+    """Both expert projections in block FP8 (the configuration `bench.py
+    --precision fp8 --fp8-down` times) at the full decode and prefill sizes,
+    with no residual: routing and grouping for every token (equal to the bf16
+    path's) and the layer output on a token sample against the oracle's layer
+    with both projections on dequantized FP8 operands.  Four tokens: the oracle
+    quantizes three fp64 matrices per touched expert."""
+    from gpu_check import gpu_expert_getter
+    w = get_workload(name)
+    print(f"[fp8 down {name}] generating inputs", flush=True)
+    inp = make_inputs(w, device=DEV, residual=False)
+    gu8, dn8 = m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"], inp["w_down"])
+    g = run_gpu(w, inp, residual=False, packed=(gu8, dn8), fp8=True, down_fp8=True)
+    del gu8, dn8
+    sample = np.sort(np.random.default_rng(5).choice(w.T, 4, replace=False))
+    print(f"[fp8 down {name}] checking tokens {sample.tolist()}", flush=True)
+    print(name, "fp8 down", check_forward(w, inp, g, y_tokens=sample, fp8=True, down_fp8=True,
+                                          get_expert=gpu_expert_getter(inp)), flush=True)
