@@ -30,20 +30,44 @@ namespace {
 // ---- bookkeeping --------------------------------------------------------------
 // tile_prefix[g] = sum over f < g of ceil(rows_f / bm); kofs[g] = sum over f < g
 // of rows_f rounded up to 64 (each group's reduction range in the padded
-// operands).  One thread: N is at most a few thousand.
-__global__ void bwd_prefix_kernel(const int32_t* __restrict__ offsets, int N, int bm,
-                                  int32_t* __restrict__ tile_prefix, int32_t* __restrict__ kofs) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int t = 0, k = 0;
-  for (int e = 0; e < N; ++e) {
+// operands).  One wave: lane l sums a contiguous segment of ceil(N / 64)
+// groups, a shuffle scan over the 64 lane sums gives each segment its start,
+// then every lane writes its own segment.
+__global__ __launch_bounds__(64) void bwd_prefix_kernel(const int32_t* __restrict__ offsets,
+                                                        int N, int bm,
+                                                        int32_t* __restrict__ tile_prefix,
+                                                        int32_t* __restrict__ kofs) {
+  const int lane = threadIdx.x;
+  const int seg = (N + 63) / 64;
+  const int e0 = min(N, lane * seg);
+  const int e1 = min(N, e0 + seg);
+  int st = 0, sk = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int rows = offsets[e + 1] - offsets[e];
+    st += (rows + bm - 1) / bm;
+    sk += (rows + 63) / 64 * 64;
+  }
+  int it = st, ik = sk;  // inclusive scan over lanes
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int a = __shfl_up(it, off), b = __shfl_up(ik, off);
+    if (lane >= off) {
+      it += a;
+      ik += b;
+    }
+  }
+  int t = it - st, k = ik - sk;
+  for (int e = e0; e < e1; ++e) {
     tile_prefix[e] = t;
     kofs[e] = k;
     const int rows = offsets[e + 1] - offsets[e];
     t += (rows + bm - 1) / bm;
     k += (rows + 63) / 64 * 64;
   }
-  tile_prefix[N] = t;
-  kofs[N] = k;
+  if (lane == 63) {
+    tile_prefix[N] = it;
+    kofs[N] = ik;
+  }
 }
 
 // colrow[c] = grouped row s held by padded column c, or -1 for padding and

@@ -97,8 +97,16 @@ def test_full_size_backward_prefill():
     token.  dx is checked on a token sample, since a token's dx depends only
     on that token.  The weight gradients are checked for two experts, each
     from exactly the tokens routed to it.  Bar: max |G - G_ref| <= 1e-2 *
-    max |G_ref| per checked tensor.  dW_router needs every token's expert
-    outputs and is covered at the mid and edge sizes (its dl enters dx here)."""
+    max |G_ref| per checked tensor.
+
+    dW_router sums every token's dl x^T, and dl needs the token's expert
+    outputs, so with a dense dy the oracle cannot form it at this size.  The
+    gradients are linear in dy and each token's share depends only on that
+    token, so a second backward in the same configuration takes a dy that is
+    zero outside 8 sampled tokens: then dW_router is exactly the oracle's sum
+    over those tokens (checked whole, [E, d]), dx is zero on every other token,
+    and the weight gradients are zero for every expert the sample did not
+    choose."""
     from oracle import backward as obwd
     from workloads import make_upstream_grad
     w = get_workload("prefill")
@@ -115,7 +123,6 @@ def test_full_size_backward_prefill():
     print("[backward prefill] backward", flush=True)
     g = m.moe_zc_backward(inp["x"], inp["w_router"], None, None, tr, aux, dy, w.N, w.Z, w.K, w.I)
     torch.cuda.synchronize()
-    del tr
     l32 = aux["logits"].cpu().numpy()
     bias = inp["bias"].cpu().numpy()
     idx = aux["topk_idx"].cpu().numpy()
@@ -141,3 +148,34 @@ def test_full_size_backward_prefill():
                             experts=[int(e)], want_dx=False)
         for k in ("dw_gate", "dw_up", "dw_down"):
             check(f"{k}[{e}] ({len(tt)} rows)", g[k][int(e)].cpu().double().numpy(), ref[k][int(e)])
+    del g
+
+    s8 = np.sort(rng.choice(w.T, 8, replace=False))
+    keep = torch.zeros(w.T, 1, dtype=dy.dtype, device=DEV)
+    keep[torch.from_numpy(s8).to(DEV)] = 1
+    dy8 = (dy * keep).contiguous()
+    del dy
+    print(f"[backward prefill] sparse dy on tokens {s8.tolist()}", flush=True)
+    g8 = m.moe_zc_backward(inp["x"], inp["w_router"], None, None, tr, aux, dy8, w.N, w.Z, w.K,
+                           w.I)
+    torch.cuda.synchronize()
+    del tr
+    chosen = np.unique(idx[s8][idx[s8] < w.N])
+    e8 = int(chosen[0])
+    st8 = torch.from_numpy(s8).to(DEV)
+    ref = obwd.backward(inp["x"][st8], inp["w_router"], bias, inp["w_gate"], inp["w_up"],
+                        inp["w_down"], w.N, w.Z, w.K, dy8[st8], logits32=l32[s8], experts=[e8])
+    check("dW_router (sparse dy)", g8["dw_router"].cpu().double().numpy(), ref["dw_router"])
+    check("dx sampled (sparse dy)", g8["dx"][st8].float().cpu().double().numpy(), ref["dx"])
+    rest = torch.ones(w.T, dtype=torch.bool, device=DEV)
+    rest[st8] = False
+    assert not g8["dx"][rest].any(), "dx nonzero on a token with zero dy"
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        check(f"{k}[{e8}] (sparse dy)", g8[k][e8].cpu().double().numpy(), ref[k][e8])
+    unchosen = torch.ones(w.N, dtype=torch.bool, device=DEV)
+    unchosen[torch.from_numpy(chosen).to(DEV)] = False
+    for k in ("dw_gate", "dw_up", "dw_down"):
+        flat = g8[k].view(w.N, -1)           # per-expert extremes: no copy of the gradients
+        hi, lo = torch.amax(flat, dim=1), torch.amin(flat, dim=1)
+        assert not (hi[unchosen].any() or lo[unchosen].any()), \
+            f"{k} nonzero for an expert the sample did not choose"
