@@ -617,6 +617,7 @@ def main():
         print("bench.py: --fp8-down needs --precision fp8", file=sys.stderr)
         sys.exit(2)
     args._power_probe = not args.no_power_probe
+    print(f"bench.py: timing {w.name} (headline)", file=sys.stderr, flush=True)
     res = forward_workload(args, w, dev, args.precision, args.layout, args.steps, args.warmup,
                            n_cpu=n_cpu, keep_inputs=not args.no_cpu_baseline,
                            fp8_down=args.fp8_down)
@@ -626,6 +627,7 @@ def main():
     roof["traffic"] = None if fp8 else counter_traffic()
     cpu = None
     if not args.no_cpu_baseline:
+        print("bench.py: timing the oracle on the host cores", file=sys.stderr, flush=True)
         cpu = cpu_baseline(w, res["_inp"], args.cpu_experts, res["_cpu_weights"])
     res.pop("_inp", None)
     res.pop("_cpu_weights", None)
@@ -638,6 +640,8 @@ def main():
                 continue
             wx = get_workload(name)
             steps = max(3, min(args.steps, 20))
+            print(f"bench.py: timing {name}{' fp8' if x8 else ''}{' fp8-down' if d8 else ''}",
+                  file=sys.stderr, flush=True)
             rx = forward_workload(args, wx, dev, "fp8" if x8 else "bf16", "packed", steps,
                                   min(args.warmup, 3), fp8_down=d8)
             rx["roofline_gate_up"] = {k: v for k, v in roofline_of(rx, x8, None).items()
