@@ -65,22 +65,17 @@ constexpr int F8_DEPTH = 3, F8_DIST = 2;                 // ring stages, loaded 
 constexpr int F8_SLOT = F8_MAXRB * 32 * F8_BKS;          // LDS bytes of one stage
 static_assert(F8_QUARTER == 8 * 1024, "eight 1 KB pieces per wavefront");
 
-// E4M3 code of y (|y| <= 448), round to nearest even, sign bit copied from y.
-// Below 2^-6 the grid step is 2^-9 and rint(|y| 2^9) = 8 is the first normal
-// code; a normal |y| = m 2^E has code 8 (E + 7) + rint(8 (m - 1)), where a
-// mantissa rounding up to 8 carries into the next binade's first code.  The
-// scalings by powers of two are exact.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t bits = __float_as_uint(y);
-  const float a = fabsf(y);
-  uint32_t code;
-  if (a < 0.015625f) {
-    code = (uint32_t)rintf(a * 512.0f);
-  } else {
-    const int E = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;
-    code = (uint32_t)(8 * (E + 7) - 8) + (uint32_t)rintf(ldexpf(a, 3 - E));
-  }
-  return code | ((bits >> 24) & 0x80u);
+// Four E4M3 codes of (a, b, c, d) (each |y| <= 448) in one dword, a in the
+// low byte: round to nearest, ties to even, sign bit copied (negative values
+// that round to zero give 0x80).  gfx950's v_cvt_pk_fp8_f32 converts to the
+// OCP E4M3 format with exactly this rounding: on the device it agrees with
+// the format's definition (grid step 2^-9 below 2^-6, else 2^(E-3) in binade
+// E) on every fp32 value of that range.  The callers scale by powers of two
+// first, which is exact.
+__device__ __forceinline__ uint32_t e4m3_quad(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);   // bytes 0, 1
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);        // bytes 2, 3
+  return (uint32_t)w;
 }
 
 // Smallest s with amax <= 448 * 2^s, clamped to [-127, 127]; 448 = 1.75 * 2^8,
@@ -112,10 +107,8 @@ __device__ __forceinline__ uint32_t mx_block(const bf16_t* __restrict__ src, uin
   const int s = mx_scale_exp(amax);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w |= e4m3_code(ldexpf(v[4 * i + e], -s)) << (8 * e);
-    codes[i] = w;
+    codes[i] = e4m3_quad(ldexpf(v[4 * i], -s), ldexpf(v[4 * i + 1], -s),
+                         ldexpf(v[4 * i + 2], -s), ldexpf(v[4 * i + 3], -s));
   }
   return (uint32_t)(s + 127);
 }
@@ -216,11 +209,9 @@ __device__ __forceinline__ void store_fp8_h_tile(const f32x16_t (&acc)[NA][2], c
     const int s = mx_scale_exp(amax);
     uint32_t w[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      w[q] = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[q] |= e4m3_code(ldexpf(vals[4 * q + e], -s)) << (8 * e);
-    }
+    for (int q = 0; q < 4; ++q)
+      w[q] = e4m3_quad(ldexpf(vals[4 * q], -s), ldexpf(vals[4 * q + 1], -s),
+                       ldexpf(vals[4 * q + 2], -s), ldexpf(vals[4 * q + 3], -s));
     const int grow = c.m0 + i * 32 + r;
     if (grow < c.m_end) {
       *reinterpret_cast<u32x4_t*>(codes + (int64_t)grow * p.ldc + gcol0 + 16 * hf) =

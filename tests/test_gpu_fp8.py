@@ -50,6 +50,49 @@ def test_quantize_mx_matches_oracle():
     assert np.array_equal(codes.cpu().numpy(), ref_c), "codes"
 
 
+def _every_bf16_blocks(seed=7):
+    """Every finite bf16 value in blocks of 32 whose maximum lies 0 to 20
+    binades above it: the values are sorted by exponent (ties shuffled), cut
+    into groups of 31, and each group gets an anchor j binades above its
+    largest exponent, for j = 0 .. 20.  So each value is quantized at 21
+    scales, which walks its scaled form through the normal and subnormal E4M3
+    ranges, the rounding ties, and the rounding to zero."""
+    r = np.random.default_rng(seed)
+    bits = np.arange(65536, dtype=np.uint32)
+    exp = (bits >> 7) & 0xFF
+    fin = bits[exp != 0xFF]
+    fin = fin[np.lexsort((r.random(len(fin)), (fin >> 7) & 0xFF))]
+    pad = (-len(fin)) % 31
+    fin = np.concatenate([fin, fin[:pad]])
+    groups = fin.reshape(-1, 31)
+    gmax = ((groups >> 7) & 0xFF).max(axis=1)
+    blocks = []
+    for j in range(21):
+        e = np.minimum(np.maximum(gmax + j, 1), 254).astype(np.uint32)
+        a = (r.integers(0, 2, len(groups)).astype(np.uint32) << 15) | (e << 7) | \
+            r.integers(0, 128, len(groups)).astype(np.uint32)
+        blk = np.concatenate([groups, a[:, None]], axis=1)
+        blocks.append(np.take_along_axis(blk, r.random(blk.shape).argsort(axis=1), axis=1))
+    v = np.concatenate(blocks).reshape(-1).astype(np.uint16)
+    d = 512
+    v = np.concatenate([v, np.zeros((-len(v)) % d, np.uint16)])
+    return torch.from_numpy(v.view(np.int16).reshape(-1, d).copy()).view(torch.bfloat16)
+
+
+def test_quantize_mx_every_bf16_value():
+    """Codes and scales of every finite bf16 value at 21 scales each
+    (blocks of _every_bf16_blocks) equal the oracle's bit for bit."""
+    x = _every_bf16_blocks()
+    assert torch.isfinite(x.float()).all()
+    codes, scales = m.moe_zc_quantize_mx(x.to(DEV))
+    torch.cuda.synchronize()
+    ref_c, ref_s = omx.mx_quantize(x.float().double().numpy(), axis=-1)
+    assert np.array_equal(scales.cpu().numpy(), ref_s), "scales"
+    c = codes.cpu().numpy()
+    bad = np.nonzero(c != ref_c)
+    assert bad[0].size == 0, f"{bad[0].size} codes differ, first at {bad[0][0]}, {bad[1][0]}"
+
+
 def pack_fp8_reference(wg, wu):
     """[n, I, d] bf16 gate and up -> packed FP8 bytes [n, panels * stages * 33792]."""
     n, I, d = wg.shape
