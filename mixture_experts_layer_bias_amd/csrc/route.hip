@@ -24,7 +24,31 @@ namespace moezc {
 // run-to-run reproducible value.  A split router product arrives as nsplit
 // partial logits; they are summed in part order (fixed, so reproducible) and
 // the sums are stored as the logits.
-template <int EPL>
+// Bitonic sort of one (key, index, payload) triple per lane over the
+// wavefront into the order (key descending, index ascending): lane 0 ends with
+// the first.  Triples with equal keys and indices (the padding) compare equal
+// and never swap.
+__device__ __forceinline__ void wave_sort_desc(int lane, float& k, int& i, float& p) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const float ok = __shfl_xor(k, stride);
+      const int oi = __shfl_xor(i, stride);
+      const float op = __shfl_xor(p, stride);
+      const bool o_first = ok > k || (ok == k && oi < i);   // the partner's triple comes first
+      const bool m_first = k > ok || (k == ok && i < oi);
+      // the lower lane of a pair keeps the first triple in a descending run and
+      // the second in an ascending one (runs alternate with lane & size)
+      const bool lower = (lane & stride) == 0, desc = (lane & size) == 0;
+      const bool take = (lower == desc) ? o_first : m_first;
+      k = take ? ok : k;
+      i = take ? oi : i;
+      p = take ? op : p;
+    }
+}
+
+template <int EPL, bool SPLIT>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
                                                    const float* __restrict__ bias,
                                                    int64_t T, int E, int K,
@@ -32,31 +56,43 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    float* __restrict__ gate_out, int nsplit,
                                                    int64_t split_stride,
                                                    float* __restrict__ logits_out) {
+  __shared__ float cand_k[4][64];
+  __shared__ int cand_i[4][64];
+  __shared__ float cand_p[4][64];
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + t * E;
 
   float l[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int j = lane + 64 * i;
+    l[i] = j < E ? row[j] : -INFINITY;
+  }
+  // partial logits of a split router product: four parts of every element
+  // in flight at a time (4 EPL loads), each element's parts added in part
+  // order; past E the added zeros leave -inf
+  for (int s = 1; SPLIT && s < nsplit; s += 4) {
+    float q[4][EPL];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int j = lane + 64 * i;
+        q[r][i] = (s + r < nsplit && j < E) ? row[(s + r) * split_stride + j] : 0.f;
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (s + r < nsplit) l[i] += q[r][i];
+  }
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int j = lane + 64 * i;
-    float v = -INFINITY;
-    if (j < E) {
-      v = row[j];
-      int s = 1;
-      for (; s + 8 <= nsplit; s += 8) {  // eight loads in flight, added in part order
-        float q[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) q[r] = row[(s + r) * split_stride + j];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) v += q[r];
-      }
-      for (; s < nsplit; ++s) v += row[s * split_stride + j];
-      if (nsplit > 1) logits_out[t * E + j] = v;
-    }
-    l[i] = v;
+    if (SPLIT && j < E) logits_out[t * E + j] = l[i];
     m = fmaxf(m, l[i]);
   }
 #pragma unroll
@@ -81,37 +117,94 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
     key[i] = (j < E) ? __fadd_rn(p32[i], bias[j]) : -INFINITY;
   }
 
-  // K rounds of a wavefront arg-max, branch-free: each lane offers its best
-  // key not yet taken, the xor butterfly keeps (key desc, index asc), and the
-  // winner's lane marks it taken.  Lane r keeps round r's index and gate;
-  // lanes < K store them together at the end.
-  uint32_t taken = 0u;
+  // Selection in the total order (key descending, index ascending).  Every
+  // lane's best element is a lower bound for the K-th best overall once K
+  // lanes are counted, so with tau = the K-th best of the 64 lane bests, the
+  // K winners are among the elements not worse than tau (tau itself
+  // included): usually a dozen or two.  They are gathered into one element per
+  // lane and sorted across the wavefront; lanes 0 .. K-1 then hold the winners
+  // in order.  Should more than 64 elements qualify, K rounds of a wavefront
+  // arg-max select the winners instead.  Both give the same result.
   int my_idx = 0;
   float my_gate = 0.f;
-  for (int r = 0; r < K; ++r) {
-    float bk = -INFINITY, bp = 0.f;
-    int bi = 0x7fffffff;
+  float bk = -INFINITY;
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int j = lane + 64 * i;
+    // j grows with i, so a strict '>' keeps the lower index on a tie
+    const bool take = j < E && (key[i] > bk || bi == 0x7fffffff);
+    bk = take ? key[i] : bk;
+    bi = take ? j : bi;
+  }
+  float sk = bk;
+  int si = bi;
+  float sp = 0.f;
+  wave_sort_desc(lane, sk, si, sp);
+  const float tk = __shfl(sk, K - 1);
+  const int ti = __shfl(si, K - 1);
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int j = lane + 64 * i;
+    cnt += (j < E && (key[i] > tk || (key[i] == tk && j <= ti))) ? 1 : 0;
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  const int total = __shfl(incl, 63);
+  if (total <= 64) {
+    float* ck = cand_k[threadIdx.x >> 6];
+    int* ci = cand_i[threadIdx.x >> 6];
+    float* cp = cand_p[threadIdx.x >> 6];
+    int at = incl - cnt;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int j = lane + 64 * i;
-      // j grows with i, so a strict '>' keeps the lower index on a tie
-      const bool better = j < E && !((taken >> i) & 1u) && (key[i] > bk || bi == 0x7fffffff);
-      bk = better ? key[i] : bk;
-      bp = better ? p32[i] : bp;
-      bi = better ? j : bi;
+      if (j < E && (key[i] > tk || (key[i] == tk && j <= ti))) {
+        ck[at] = key[i];
+        ci[at] = j;
+        cp[at] = p32[i];
+        ++at;
+      }
     }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wavefront's LDS writes landed
+    __builtin_amdgcn_wave_barrier();
+    sk = lane < total ? ck[lane] : -INFINITY;
+    si = lane < total ? ci[lane] : 0x7fffffff;
+    sp = lane < total ? cp[lane] : 0.f;
+    wave_sort_desc(lane, sk, si, sp);
+    my_idx = si;
+    my_gate = sp;
+  } else {
+    uint32_t taken = 0u;
+    for (int r = 0; r < K; ++r) {
+      float rk = -INFINITY, rp = 0.f;
+      int ri = 0x7fffffff;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ok = __shfl_xor(bk, off);
-      const int oi = __shfl_xor(bi, off);
-      const bool take = ok > bk || (ok == bk && oi < bi);
-      bk = take ? ok : bk;
-      bi = take ? oi : bi;
+      for (int i = 0; i < EPL; ++i) {
+        const int j = lane + 64 * i;
+        const bool take = j < E && !((taken >> i) & 1u) && (key[i] > rk || ri == 0x7fffffff);
+        rk = take ? key[i] : rk;
+        rp = take ? p32[i] : rp;
+        ri = take ? j : ri;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ok = __shfl_xor(rk, off);
+        const int oi = __shfl_xor(ri, off);
+        const bool take = ok > rk || (ok == rk && oi < ri);
+        rk = take ? ok : rk;
+        ri = take ? oi : ri;
+      }
+      const float gate = __shfl(rp, ri & 63);      // the winner's lane holds its gate
+      taken |= ((ri & 63) == lane) ? (1u << (ri >> 6)) : 0u;
+      my_idx = (lane == r) ? ri : my_idx;
+      my_gate = (lane == r) ? gate : my_gate;
     }
-    const float gate = __shfl(bp, bi & 63);      // the winner's lane holds its gate
-    taken |= ((bi & 63) == lane) ? (1u << (bi >> 6)) : 0u;
-    my_idx = (lane == r) ? bi : my_idx;
-    my_gate = (lane == r) ? gate : my_gate;
   }
   if (lane < K) {
     idx_out[t * K + lane] = my_idx;
@@ -119,36 +212,37 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   }
 }
 
+// SPLIT: the instantiation that adds partial logits (more registers)
+template <int EPL>
+hipError_t launch_topk_epl(const float* logits, const float* bias, int64_t T, int E, int K,
+                           int32_t* idx, float* gate, hipStream_t s, int nsplit,
+                           int64_t split_stride, float* logits_out) {
+  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (nsplit > 1)
+    hipLaunchKernelGGL((topk_kernel<EPL, true>), grid, block, 0, s, logits, bias, T, E, K, idx,
+                       gate, nsplit, split_stride, logits_out);
+  else
+    hipLaunchKernelGGL((topk_kernel<EPL, false>), grid, block, 0, s, logits, bias, T, E, K, idx,
+                       gate, 1, split_stride, logits_out);
+  return hipGetLastError();
+}
+
 hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int E, int K,
                        int32_t* idx, float* gate, hipStream_t s, int nsplit,
                        int64_t split_stride, float* logits_out) {
-  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
   const int epl = (E + 63) / 64;
   if (nsplit < 1 || (nsplit > 1 && !logits_out)) return hipErrorInvalidValue;
-  if (epl <= 1)
-    hipLaunchKernelGGL(topk_kernel<1>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
-                       nsplit, split_stride, logits_out);
-  else if (epl <= 2)
-    hipLaunchKernelGGL(topk_kernel<2>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
-                       nsplit, split_stride, logits_out);
-  else if (epl <= 4)
-    hipLaunchKernelGGL(topk_kernel<4>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
-                       nsplit, split_stride, logits_out);
-  else if (epl <= 8)
-    hipLaunchKernelGGL(topk_kernel<8>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
-                       nsplit, split_stride, logits_out);
-  else if (epl <= 12)
-    hipLaunchKernelGGL(topk_kernel<12>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
-                       nsplit, split_stride, logits_out);
-  else if (epl <= 16)
-    hipLaunchKernelGGL(topk_kernel<16>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
-                       nsplit, split_stride, logits_out);
-  else if (epl <= 32)
-    hipLaunchKernelGGL(topk_kernel<32>, grid, block, 0, s, logits, bias, T, E, K, idx, gate,
-                       nsplit, split_stride, logits_out);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+#define MOEZC_TOPK(n) \
+  launch_topk_epl<n>(logits, bias, T, E, K, idx, gate, s, nsplit, split_stride, logits_out)
+  if (epl <= 1) return MOEZC_TOPK(1);
+  if (epl <= 2) return MOEZC_TOPK(2);
+  if (epl <= 4) return MOEZC_TOPK(4);
+  if (epl <= 8) return MOEZC_TOPK(8);
+  if (epl <= 12) return MOEZC_TOPK(12);
+  if (epl <= 16) return MOEZC_TOPK(16);
+  if (epl <= 32) return MOEZC_TOPK(32);
+#undef MOEZC_TOPK
+  return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------

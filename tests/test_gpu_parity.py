@@ -47,6 +47,70 @@ def test_route_bit_exact(T, E, K, q):
         assert (np.diff(np.sort(rt["key"], axis=1), axis=1) == 0).any()
 
 
+@pytest.mark.parametrize("case", ["few_lanes_hold_the_top", "boundary_64", "all_equal",
+                                  "two_levels"])
+def test_route_bit_exact_structured(case):
+    """Routing of logits whose best experts crowd into a few of the 64 lanes
+    of a wavefront (lane l holds experts l, l + 64, ...), so that more than 64
+    elements qualify as candidates and the selection takes its arg-max rounds
+    ("few_lanes_hold_the_top", 6 lanes x 12 experts raised); exactly at and
+    around that count ("boundary_64"); all keys equal (the lowest indices win);
+    and two exact key levels.  Equal to the oracle bit for bit."""
+    T, E, K = 257, 768, 12
+    g = torch.Generator().manual_seed(11)
+    logits = torch.randn(T, E, generator=g)
+    bias = (torch.rand(E, generator=g) - 0.5) * 0.02
+    lane = torch.arange(E) % 64
+    if case == "few_lanes_hold_the_top":
+        logits[:, lane < 6] += 8.0
+        bias = torch.zeros(E)             # a bias would reorder the raised experts' keys
+    elif case == "boundary_64":
+        # token t raises the experts of its first 1 + t % 8 lanes, so the count
+        # of qualifying elements moves across 64 from token to token
+        for t in range(T):
+            logits[t, lane < 1 + t % 8] += 8.0
+        bias = torch.zeros(E)
+    elif case == "all_equal":
+        logits = torch.zeros(T, E)
+        bias = torch.zeros(E)
+    else:
+        logits = torch.where(torch.rand(T, E, generator=g) < 0.05, torch.tensor(3.0),
+                             torch.tensor(0.0))
+        bias = torch.zeros(E)
+    idx, gate = m.moe_zc_route(logits.to(DEV), bias.to(DEV), K)
+    torch.cuda.synchronize()
+    rt = oracle.route(logits.numpy(), bias.numpy(), K, 1)
+    if case == "few_lanes_hold_the_top":
+        assert (candidate_counts(rt["key"], K) > 64).all()
+    if case == "boundary_64":
+        c = candidate_counts(rt["key"], K)
+        assert (c > 64).any() and (c <= 64).any()
+    assert np.array_equal(idx.cpu().numpy(), rt["idx"])
+    assert np.array_equal(gate.cpu().numpy(), rt["gate"])
+
+
+def candidate_counts(key, K):
+    """Per token: elements not worse, in the order (key descending, index
+    ascending), than the K-th best of the 64 lane bests (lane l: experts l,
+    l + 64, ...).  More than 64 sends the kernel to its arg-max rounds."""
+    T, E = key.shape
+    j = np.arange(E)
+    out = np.empty(T, np.int64)
+    for t in range(T):
+        kk = key[t]
+        o = np.lexsort((j, -kk))                       # best first
+        seen, best = set(), []
+        for e in o:
+            if e % 64 not in seen:
+                seen.add(e % 64)
+                best.append(e)
+                if len(best) == K:
+                    break
+        tau = best[-1]
+        out[t] = np.sum((kk > kk[tau]) | ((kk == kk[tau]) & (j <= tau)))
+    return out
+
+
 def test_route_loads_with_no_tokens_are_zero():
     loads = torch.full((40,), 5, dtype=torch.int32, device=DEV)
     m.moe_zc_route(torch.zeros(0, 40, device=DEV), torch.zeros(40, device=DEV), 3, loads=loads)
