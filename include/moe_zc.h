@@ -58,12 +58,16 @@ typedef enum {
   MOE_ZC_ERR_INVALID = 1,      /* bad argument: NULL, negative size, K > E ... */
   MOE_ZC_ERR_WORKSPACE = 2,    /* workspace NULL or smaller than required     */
   MOE_ZC_ERR_UNSUPPORTED = 3,  /* valid but outside what the kernels handle   */
-  MOE_ZC_ERR_HIP = 4           /* a HIP launch or runtime call failed         */
+  MOE_ZC_ERR_HIP = 4,          /* a HIP launch or runtime call failed         */
+  /* not a status: makes every int a valid value of the type, so that an
+   * out-of-range value passed in from C is well defined (and rejected) */
+  MOE_ZC_STATUS_INT32_ = 0x7fffffff
 } moe_zc_status;
 
 typedef enum {
   MOE_ZC_F32 = 0,   /* x, FFN weights, residual, y in fp32 (fp32 FMA path)     */
-  MOE_ZC_BF16 = 1   /* x, FFN weights, residual, y in bf16 (bf16 MFMA path)    */
+  MOE_ZC_BF16 = 1,  /* x, FFN weights, residual, y in bf16 (bf16 MFMA path)    */
+  MOE_ZC_DTYPE_INT32_ = 0x7fffffff  /* not a dtype (as above): rejected as invalid */
 } moe_zc_dtype;
 
 /* Limits of this implementation (else MOE_ZC_ERR_UNSUPPORTED):

@@ -450,8 +450,8 @@ const char* moe_zc_status_string(moe_zc_status s) {
     case MOE_ZC_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ZC_ERR_UNSUPPORTED: return "sizes outside what the kernels support";
     case MOE_ZC_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
   }
-  return "unknown status";
 }
 
 size_t moe_zc_workspace_size(int64_t T, int64_t d, int64_t I, int32_t N, int32_t Z, int32_t K,
