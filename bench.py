@@ -593,7 +593,7 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only; the multi-GPU path (expert "
+        print("bench.py: the library runs on one GPU only; the multi-GPU path (expert "
               "sharding with all-to-all) is not built. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
