@@ -49,7 +49,7 @@ def test_abi_validation_is_clean_under_asan_and_ubsan(tmp_path):
     r = subprocess.run(compile_cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-3000:]
     link_cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC",
-                "-fsanitize=address,undefined", "-shared-libsan", "-o", lib, obj, *objs]
+                "-Xarch_host", "-fsanitize=address,undefined", "-shared-libsan", "-o", lib, obj, *objs]
     r = subprocess.run(link_cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-3000:]
     child = (
