@@ -17,13 +17,14 @@ namespace moezc {
 // Softmax + bias key + top-K.  One wavefront per token; lane l holds experts
 // l, l+64, ...  The softmax runs in fp64 from the fp32 logits (max, exp,
 // sum, divide), its result is rounded once to fp32 (the gate), and the
-// selection key is the fp32 sum fl32(p32 + b).  The K winners are taken one at
-// a time by a wavefront arg-max on (key descending, index ascending), so an
-// exact tie goes to the lower expert index and the output order is the key
-// order.  Reductions are xor butterflies: every lane ends with the same,
-// run-to-run reproducible value.  A split router product arrives as nsplit
-// partial logits; they are summed in part order (fixed, so reproducible) and
-// the sums are stored as the logits.
+// selection key is the fp32 sum fl32(p32 + b).  The K winners are the first K
+// in the order (key descending, index ascending), so an exact tie goes to the
+// lower expert index, and they are written in that order (the selection is
+// described at its code below).  Reductions are xor butterflies: every lane
+// ends with the same, run-to-run reproducible value.  A split router product
+// arrives as nsplit partial logits; they are summed in part order (fixed, so
+// reproducible) and the sums are stored as the logits.
+
 // Bitonic sort of one (key, index, payload) triple per lane over the
 // wavefront into the order (key descending, index ascending): lane 0 ends with
 // the first.  Triples with equal keys and indices (the padding) compare equal
