@@ -74,6 +74,8 @@ def parse():
                     help="experts the CPU-baseline sample evaluates")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a device copy of known size (for scaling counters)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the untimed HIP-graph replay of the step")
     ap.add_argument("--no-power-probe", action="store_true",
                     help="skip sampling socket power and clocks (amd-smi) on the headline")
     ap.add_argument("--no-extra-workloads", action="store_true",
@@ -394,6 +396,36 @@ def bench_backward(args, w, dev):
     print(json.dumps(out))
 
 
+def graph_replay(step, y, replays):
+    """The same step captured once in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed: the step's wall time without per-launch host overhead and gaps.
+    The library allocates, synchronises and memsets nothing, so the forward
+    and the PID update capture as they are.  The output of the last replay is
+    compared bit for bit with the eager result, and the eager run resumes with
+    the same buffers afterwards (the graph is untimed context, not the value)."""
+    import torch
+    try:
+        torch.cuda.synchronize()
+        y_ref = y.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(replays):
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        same = bool(torch.equal(y, y_ref))
+        del g
+        return {"ms_per_step": (t1 - t0) * 1e3 / replays, "replays": replays,
+                "bitwise_equal_to_eager": same}
+    except Exception as e:  # a failed capture is reported, not fatal
+        torch.cuda.synchronize()
+        return {"error": f"{type(e).__name__}: {e}"[:300]}
+
+
 def forward_workload(args, w, dev, precision="bf16", layout="packed", steps=20, warmup=5,
                      n_cpu=0, keep_inputs=False, fp8_down=False):
     """Time the forward of workload ``w`` as configured (its own bias on every
@@ -489,6 +521,7 @@ def forward_workload(args, w, dev, precision="bf16", layout="packed", steps=20, 
     S = int(aux["offsets"][w.N].item())
     touched = int((loads[: w.N] > 0).sum())
 
+    graph = None if getattr(args, "no_graph", False) else graph_replay(step, y, steps)
     power = power_probe(step) if getattr(args, "_power_probe", False) else None
     # untimed: routing after the one PID step of the timed steps ...
     before = ffn_stats(loads)
@@ -544,6 +577,7 @@ def forward_workload(args, w, dev, precision="bf16", layout="packed", steps=20, 
         "closed_loop": {"steps": args.closed_loop_steps, "first": loop[0] if loop else None,
                         "last": loop[-1] if loop else None},
         "power": power,
+        "graph": graph,
         "_alg": alg, "_stage_ms": stage, "_S": S, "_touched": touched, "_es": es,
     }
     if keep_inputs:
@@ -687,6 +721,7 @@ def main():
         "one_pid_step": res["one_pid_step"],
         "closed_loop": res["closed_loop"],
         "power": res["power"],
+        "graph": res["graph"],
         "measured_peaks": peaks,
         "roofline": roof,
         "cpu_baseline": cpu,
