@@ -132,3 +132,45 @@ def test_graph_of_forward_and_bias_update_matches_eager_loop():
     for i, (a, b) in enumerate(zip(eager, graph)):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"step {i}: bias differs"
     assert not np.array_equal(eager[0], eager[-1]), "the bias should move"
+
+
+@pytest.mark.parametrize("down_fp8", [False, True])
+def test_graph_replay_of_the_fp8_forward_matches_eager(down_fp8):
+    """The block-FP8 forward (x quantized in the call, and with down_fp8 h
+    quantized in the gate/up epilogue) captured once and replayed on new
+    inputs: every replay equals the eager FP8 forward of those inputs."""
+    w = _w(41, d=384, I=256)
+    inp = make_inputs(w, device=DEV)
+    if down_fp8:
+        gu, dn = m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"], inp["w_down"])
+    else:
+        gu = m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"])
+        dn = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])[1]
+    n = m.moe_zc_workspace_size_fp8(w.T, w.d, w.I, w.N, w.Z, w.K)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    y = torch.empty(w.T, w.d, dtype=torch.bfloat16, device=DEV)
+    aux = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV)
+    static_x = inp["x"].clone()
+
+    def fwd(x, ws_, out, aux_):
+        return m.moe_zc_forward_packed_fp8(x, inp["w_router"], inp["bias"], gu, dn, w.N, w.Z, w.K,
+                                           w.I, residual=inp["residual"], out=out, aux=aux_,
+                                           workspace=ws_, down_fp8=down_fp8)
+
+    fwd(static_x, ws, y, aux)                    # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd(static_x, ws, y, aux)
+    gen = torch.Generator().manual_seed(9)
+    for rep in range(3):
+        new_x = torch.randn(w.T, w.d, generator=gen).to(torch.bfloat16).to(DEV)
+        static_x.copy_(new_x)
+        g.replay()
+        torch.cuda.synchronize()
+        got = y.clone()
+        ea = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV)
+        eager = fwd(new_x, torch.empty_like(ws), None, ea)
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager), f"replay {rep}: y differs from eager"
+        assert torch.equal(aux["topk_idx"], ea["topk_idx"]), f"replay {rep}: routing differs"
