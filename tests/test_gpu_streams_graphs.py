@@ -1,9 +1,9 @@
-"""Stream and graph behaviour the C ABI promises: the library has no mutable
-global state, so calls on different streams with their own workspaces may run
-concurrently; it allocates nothing, synchronises nothing and records no memset,
-so a forward (and the bias update) can be captured in a HIP graph and
-replayed.  Every result is compared bit for bit with the same call run eagerly
-on the default stream."""
+"""Stream and graph behaviour the C ABI promises: the entry points that take
+a workspace keep no mutable global state, so calls on different streams with
+their own workspaces may run concurrently; they allocate nothing, synchronise
+nothing and record no memset, so a forward, the bias update and the backward
+can be captured in a HIP graph and replayed.  Every result is compared bit for
+bit with the same call run eagerly on the default stream."""
 import numpy as np
 import pytest
 import torch
@@ -174,3 +174,53 @@ def test_graph_replay_of_the_fp8_forward_matches_eager(down_fp8):
         torch.cuda.synchronize()
         assert torch.equal(got, eager), f"replay {rep}: y differs from eager"
         assert torch.equal(aux["topk_idx"], ea["topk_idx"]), f"replay {rep}: routing differs"
+
+
+def test_graph_replay_of_the_training_step_matches_eager():
+    """Forward saving a | u plus the backward, captured together and replayed
+    on new x and dy copied into their static buffers: every gradient of every
+    replay equals, bit for bit, the eager forward and backward of those
+    inputs."""
+    w = _w(51, T=613, N=12, Z=4, K=4)
+    inp = make_inputs(w, device=DEV)
+    pk = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    tr = m.moe_zc_transpose_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    keys = m.AUX_KEYS + ("act",)
+    nb = m.moe_zc_backward_workspace_size(w.T, w.d, w.I, w.N, w.Z, w.K)
+
+    def buffers():
+        aux = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV, keys=keys, I=w.I)
+        y = torch.empty(w.T, w.d, dtype=torch.bfloat16, device=DEV)
+        return aux, y, _ws(w), torch.empty(nb, dtype=torch.uint8, device=DEV)
+
+    def step(x, dy, aux, y, wsf, wsb, out):
+        _packed_forward(w, dict(inp, x=x), pk, wsf, y, aux=aux)
+        return m.moe_zc_backward(x, inp["w_router"], None, None, tr, aux, dy, w.N, w.Z, w.K, w.I,
+                                 out=out, workspace=wsb)
+
+    aux, y, wsf, wsb = buffers()
+    static_x = inp["x"].clone()
+    static_dy = torch.randn(w.T, w.d, generator=torch.Generator().manual_seed(3)).to(
+        torch.bfloat16).to(DEV)
+    g_out = step(static_x, static_dy, aux, y, wsf, wsb, None)   # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(static_x, static_dy, aux, y, wsf, wsb, g_out)
+    gen = torch.Generator().manual_seed(13)
+    for rep in range(3):
+        new_x = torch.randn(w.T, w.d, generator=gen).to(torch.bfloat16).to(DEV)
+        new_dy = torch.randn(w.T, w.d, generator=gen).to(torch.bfloat16).to(DEV)
+        static_x.copy_(new_x)
+        static_dy.copy_(new_dy)
+        g.replay()
+        torch.cuda.synchronize()
+        got = {k: v.clone() for k, v in g_out.items()}
+        got_y = y.clone()
+        ea, ey, ewf, ewb = buffers()
+        eager = step(new_x, new_dy, ea, ey, ewf, ewb, None)
+        torch.cuda.synchronize()
+        assert torch.equal(got_y, ey), f"replay {rep}: y differs from eager"
+        for k in ("dx", "dw_router", "dw_gate", "dw_up", "dw_down"):
+            assert torch.equal(got[k], eager[k]), f"replay {rep}: {k} differs from eager"
+        assert got["dw_gate"].abs().max() > 0, "the gradients should be non-trivial"
