@@ -79,6 +79,8 @@ CASES = {
     "rows_256_tiles": dict(T=1100, N=8, Z=4, K=3, d=256, I=256),
     "wide_d": dict(T=130, d=1344, I=384, N=6, Z=2, K=2),
     "many_experts": dict(T=300, d=128, I=128, N=300, Z=20, K=12),
+    # experts of 257 .. 439 rows: two row parts each in the forward's GEMMs
+    "rows_past_256": dict(T=1300, d=320, I=384, N=10, Z=4, K=3, seed=3),
 }
 
 
@@ -239,7 +241,7 @@ def gpu_forward_backward_saved(w, inp, dy):
 
 @pytest.mark.parametrize("name", ["T1", "T65_ragged", "Z0", "N0_all_identity",
                                   "few_rows_32_tiles", "rows_256_tiles", "wide_d",
-                                  "many_experts"])
+                                  "many_experts", "rows_past_256"])
 def test_backward_from_saved_preactivations(name):
     w = _edge(**CASES[name])
     print(f"[backward saved {name}] {w.describe()}", flush=True)

@@ -91,6 +91,9 @@ CASES = {
     "many_experts_topk32": dict(T=96, N=1024, Z=1024, K=32, I=128),
     "long_k": dict(T=257, d=1024, I=512, N=4, Z=4, K=2),
     "odd_stage_counts": dict(T=200, d=1216, I=640, N=6, Z=2, K=2),   # 19 and 10 k-stages
+    # experts just past one 256-row tile (257, 268, 289, 310 rows) and well past
+    # it (373, 439): each runs as two row parts of whole 32-row blocks
+    "rows_past_256": dict(T=1300, d=320, I=384, N=10, Z=4, K=3),
 }
 
 
@@ -109,6 +112,18 @@ def test_packed_forward_equals_rowmajor_and_oracle(name):
         assert np.array_equal(g_row[k], g_pk[k]), k
     rep = check_forward(w, inp, g_pk)
     print(name, rep, flush=True)
+
+
+def test_rows_past_256_case_holds_its_boundaries():
+    """The rows_past_256 case holds experts of exactly 257 rows (the fewest
+    that split) and 289 rows (ten 32-row blocks), a few of nine and of ten
+    blocks, and one far past 320 rows."""
+    w = _edge(**CASES["rows_past_256"])
+    inp = make_inputs(w, device=DEV)
+    loads = run_gpu(w, inp)["loads"][:w.N]
+    assert 257 in loads and 289 in loads, sorted(loads)
+    assert ((loads > 256) & (loads <= 288)).sum() >= 2 and ((loads > 288) & (loads <= 320)).sum() >= 2
+    assert (loads > 320).sum() >= 1
 
 
 def test_packed_mid_vs_oracle():
