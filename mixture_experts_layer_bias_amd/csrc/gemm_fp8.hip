@@ -62,6 +62,9 @@ constexpr int F8_BLOCK = F8_DATA + F8_SCL;
 constexpr int F8_QUARTER = F8_DATA / F8_WAVES;           // one wavefront's codes
 constexpr int F8_MAXRB = kPackedMaxTileRows / 32;        // 32-row blocks per tile
 constexpr int F8_DEPTH = 3, F8_DIST = 2;                 // ring stages, loaded ahead
+constexpr int F8_WLOADS = 9;                             // weight register loads per stage
+// the wait between a stage's substeps counts only one refill's weight loads
+static_assert(F8_DIST == 2, "one stage's refill in flight across the barrier");
 constexpr int F8_SLOT = F8_MAXRB * 32 * F8_BKS;          // LDS bytes of one stage
 static_assert(F8_QUARTER == 8 * 1024, "eight 1 KB pieces per wavefront");
 
@@ -355,7 +358,7 @@ __device__ __forceinline__ void run_fp8(const GemmProblem& p, const TileCoord& c
         r_, (lds_void_t*)(a_dst + (u) * F8_SLOT + (t) * 4096), 16, a_src[t], 0, 0, 0); \
   }
   // every load of stage kt into set / slot u: 8 code pieces, the weight scale
-  // dword, NA activation rows, the activation scales
+  // dword (F8_WLOADS register loads), NA activation rows, the activation scales
 #define F8_LOAD_STAGE(kt, u)                                                          \
   {                                                                                   \
     const char* b_ = B_pan + (int64_t)(kt) * F8_BLOCK;                                \
@@ -367,8 +370,9 @@ __device__ __forceinline__ void run_fp8(const GemmProblem& p, const TileCoord& c
   // One substep ks of set u.  For each row block g: its two MFMAs (gate and
   // up column blocks), then, when NEXT, the LDS read of block g's fragment
   // for substep nks of slot nu (the register is free once both MFMAs have
-  // read it) and, when nks is 0 (a new stage), of block g's scale dword, then,
-  // when REFILL, block g's share of the loads of stage KN into set NU.  A
+  // read it) and, when nks is 0 (a new stage), of block g's scale dword, then
+  // block g's share of the loads of stage KN into set NU: REFILL 1 the weight
+  // code pieces and scale dword, REFILL 2 the activation rows and scales.  A
   // scheduling fence after each group keeps this order.
 #define F8_SUB(ks, u, NEXT, nu, nks, REFILL, KN, NU)                                  \
   _Pragma("unroll") for (int g_ = 0; g_ < NA; ++g_) {                                 \
@@ -381,22 +385,26 @@ __device__ __forceinline__ void run_fp8(const GemmProblem& p, const TileCoord& c
         2 * (ks), (int)sa_, 2 * (ks) + 1, (int)bsc[u]);                               \
     if (NEXT) F8_FRAG(fa[g_], nu, nks, g_);                                           \
     if ((NEXT) && (nks) == 0) asc[g_] = F8_SCALE(nu, g_);                             \
-    if (REFILL) {                                                                     \
+    if ((REFILL) == 1) {                                                              \
       const char* b_ = B_pan + (int64_t)(KN) * F8_BLOCK;                              \
       _Pragma("unroll") for (int q = (g_ * 8) / NA; q < ((g_ + 1) * 8) / NA; ++q)     \
           F8_PIECE(KN, NU, q);                                                        \
       if (g_ == 0) bsc[NU] = *reinterpret_cast<const uint32_t*>(b_ + bs_off);         \
+    } else if ((REFILL) == 2) {                                                       \
       F8_DMA(KN, NU, g_);                                                             \
       if (g_ == NA - 1) F8_SDMA(KN, NU);                                              \
     }                                                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                \
   }
-  // Stage kt uses set / slot u = kt % F8_DEPTH.  Substep 0 refills the set of
+  // Stage kt uses set / slot u = kt % F8_DEPTH and refills the set and slot of
   // stage kt-1 (every wavefront finished reading that slot before the last
-  // barrier) with stage kt+F8_DIST and reads the substep-1 fragments; then the
-  // wavefront waits for its loads of stage kt+1 (they complete in issue order;
-  // the refill stays in flight) and meets the others; substep 1 reads the first
-  // fragments of stage kt+1.  In the steady loop a refill past the last stage
+  // barrier) with stage kt+F8_DIST: the weights in substep 0, which also reads
+  // the substep-1 fragments, the activations in substep 1, so that each
+  // substep's MFMAs have loads between them (measured: the down GEMM 4-7%
+  // faster than with all loads in substep 0).  Between the two the wavefront
+  // waits for its loads of stage kt+1 (they complete in issue order; only the
+  // F8_WLOADS weight loads of this stage's refill are newer) and meets the
+  // others; substep 1 reads the first fragments of stage kt+1.  In the steady loop a refill past the last stage
   // repeats the last stage's addresses (never read), so every stage keeps the
   // same count of loads in flight.  The stages after the loop issue no loads
   // and wait for all of them (a dummy register load there would be dropped by
@@ -405,10 +413,10 @@ __device__ __forceinline__ void run_fp8(const GemmProblem& p, const TileCoord& c
   {                                                                                   \
     const int kn_ = min((kt) + F8_DIST, nk - 1);                                      \
     const int un_ = ((u) + F8_DIST) % F8_DEPTH;                                       \
-    F8_SUB(0, u, true, u, 1, REFILL, kn_, un_);                                       \
-    ring_barrier<(REFILL) ? (F8_DIST - 1) * (10 + NA) : 0>();                         \
+    F8_SUB(0, u, true, u, 1, (REFILL) ? 1 : 0, kn_, un_);                             \
+    ring_barrier<(REFILL) ? F8_WLOADS : 0>();                                         \
     __builtin_amdgcn_sched_barrier(0);                                                \
-    F8_SUB(1, u, true, ((u) + 1) % F8_DEPTH, 0, false, 0, 0);                         \
+    F8_SUB(1, u, true, ((u) + 1) % F8_DEPTH, 0, (REFILL) ? 2 : 0, kn_, un_);          \
   }
 
   // prologue: stages 0 .. F8_DIST-1 (repeating the last stage where nk is
