@@ -328,7 +328,10 @@ __device__ __forceinline__ void run_fp8(const GemmProblem& p, const TileCoord& c
   i32x8_t fa[NA];
   i32x8_t fb[F8_DEPTH][4];  // [set][2 ks + j]: the two 1 KB pieces of (ks, j)
   uint32_t bsc[F8_DEPTH];
-  uint32_t asc[NA];  // this stage's activation scale dwords, one per row block
+  // this stage's activation scale dwords as read (one per row block); the
+  // lane's byte shift is applied at the MFMA, so that no wait for the read
+  // lands right behind it
+  uint32_t asc[NA];
 
 #define F8_FRAG(dst, slot, ks, i)                                                     \
   {                                                                                   \
@@ -349,7 +352,7 @@ __device__ __forceinline__ void run_fp8(const GemmProblem& p, const TileCoord& c
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r_, (lds_void_t*)(s_dst + (u) * 1024), 4, \
                                              s_off, 0, 0, 0);                         \
   }
-#define F8_SCALE(slot, i) (*reinterpret_cast<const uint32_t*>(smem + s_rd + (slot) * 1024 + (i) * 128) >> s_sh)
+#define F8_SCALE(slot, i) (*reinterpret_cast<const uint32_t*>(smem + s_rd + (slot) * 1024 + (i) * 128))
 #define F8_DMA(kt, u, t)                                                              \
   {                                                                                   \
     const __amdgpu_buffer_rsrc_t r_ = __builtin_amdgcn_make_buffer_rsrc(              \
@@ -376,7 +379,7 @@ __device__ __forceinline__ void run_fp8(const GemmProblem& p, const TileCoord& c
   // scheduling fence after each group keeps this order.
 #define F8_SUB(ks, u, NEXT, nu, nks, REFILL, KN, NU)                                  \
   _Pragma("unroll") for (int g_ = 0; g_ < NA; ++g_) {                                 \
-    const uint32_t sa_ = asc[g_];                                                     \
+    const uint32_t sa_ = asc[g_] >> s_sh;                                             \
     acc[g_][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                     \
         fa[g_], fb[u][2 * (ks)], acc[g_][0], 0, 0, 2 * (ks),                          \
         (int)sa_, 2 * (ks), (int)bsc[u]);                                             \
