@@ -403,15 +403,16 @@ __device__ __forceinline__ void run_fp8(const GemmProblem& p, const TileCoord& c
   // stage kt-1 (every wavefront finished reading that slot before the last
   // barrier) with stage kt+F8_DIST: the weights in substep 0, which also reads
   // the substep-1 fragments, the activations in substep 1, so that each
-  // substep's MFMAs have loads between them (measured: the down GEMM 4-7%
-  // faster than with all loads in substep 0).  Between the two the wavefront
-  // waits for its loads of stage kt+1 (they complete in issue order; only the
+  // substep's MFMAs have loads between them (the down GEMM runs 4-7% faster
+  // than with all loads in substep 0).  Between the two the wavefront waits
+  // for its loads of stage kt+1 (they complete in issue order; only the
   // F8_WLOADS weight loads of this stage's refill are newer) and meets the
-  // others; substep 1 reads the first fragments of stage kt+1.  In the steady loop a refill past the last stage
-  // repeats the last stage's addresses (never read), so every stage keeps the
-  // same count of loads in flight.  The stages after the loop issue no loads
-  // and wait for all of them (a dummy register load there would be dropped by
-  // the compiler as dead and leave a count-based wait short).
+  // others; substep 1 reads the first fragments of stage kt+1.  In the steady
+  // loop a refill past the last stage repeats the last stage's addresses
+  // (never read), so every stage keeps the same count of loads in flight.
+  // The stages after the loop issue no loads and wait for all of them (a
+  // dummy register load there would be dropped by the compiler as dead and
+  // leave a count-based wait short).
 #define F8_STAGE(kt, u, REFILL)                                                       \
   {                                                                                   \
     const int kn_ = min((kt) + F8_DIST, nk - 1);                                      \
