@@ -277,11 +277,11 @@ def test_fp8_full_size_prefill():
                                        get_expert=gpu_expert_getter(inp)), flush=True)
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "skew"])
 def test_fp8_down_full_size(name):
     """Both expert projections in block FP8 (the configuration `bench.py
-    --precision fp8 --fp8-down` times) at the full decode and prefill sizes,
-    with no residual: routing and grouping for every token (equal to the bf16
+    --precision fp8 --fp8-down` times) at the full decode, prefill and skewed
+    sizes (skew: a few experts hold many row tiles), with no residual: routing and grouping for every token (equal to the bf16
     path's) and the layer output on a token sample against the oracle's layer
     with both projections on dequantized FP8 operands.  Four tokens: the oracle
     quantizes three fp64 matrices per touched expert."""
