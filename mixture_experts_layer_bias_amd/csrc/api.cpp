@@ -13,6 +13,8 @@
 
 using namespace moezc;
 
+static_assert(kWgradMaxGroups >= MOE_ZC_MAX_EXPERTS, "the weight-gradient plan covers every expert");
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -336,7 +338,7 @@ inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 struct BwdPlan {
   int64_t Sp, T64, E64;  // padded grouped columns, padded tokens, padded experts
-  size_t tiles, kofs, kofs_r, colrow, row_gate, row_dg, A, U, Q, dau, H, dxg, XT, ET, DAT, DUT,
+  size_t tiles, kofs, kofs_r, xg, colrow, row_gate, row_dg, A, U, Q, dau, H, dxg, XT, ET, DAT, DUT,
       HT, dl, dlT, xT, wrT, wrP, dx_r, total;
 };
 
@@ -355,6 +357,7 @@ BwdPlan make_bwd_plan(const Shape& s) {
   p.tiles = take((size_t)(s.N + 1) * 4);
   p.kofs = take((size_t)(s.N + 1) * 4);
   p.kofs_r = take(2 * 4);
+  p.xg = take((size_t)8 * wgrad_xcd_cap(s.N) * 4);
   p.colrow = take((size_t)p.Sp * 4);
   p.row_gate = take(S * 4);
   p.row_dg = take(S * 4);
@@ -691,6 +694,8 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
     int32_t* colrow = Ix(pl.colrow);
     float* row_gate = F(pl.row_gate);
     MOE_ZC_TRY(launch_bwd_prefix(offsets, N, s.ffn_tile_rows, tiles, kofs, stream));
+    int32_t* xg = Ix(pl.xg);
+    MOE_ZC_TRY(launch_wgrad_plan(kofs, N, xg, stream));
     MOE_ZC_TRY(launch_bwd_colrow(offsets, kofs, N, colrow, (int)pl.Sp, stream));
     MOE_ZC_TRY(launch_bwd_rowgate(fwd->pos, fwd->topk_gate, T * K, row_gate, stream));
     // a = W_gate x and u = W_up x of every grouped row (fp32; unless the
@@ -747,9 +752,9 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
     MOE_ZC_TRY(launch_transpose(a, stream));
     a = blocked(B(pl.H), I, B(pl.HT), I);
     MOE_ZC_TRY(launch_transpose(a, stream));
-    MOE_ZC_TRY(launch_wgrad(B(pl.ET), B(pl.HT), kofs, N, (int)d, (int)I, dw_down, stream));
-    MOE_ZC_TRY(launch_wgrad(B(pl.DAT), B(pl.XT), kofs, N, (int)I, (int)d, dw_gate, stream));
-    MOE_ZC_TRY(launch_wgrad(B(pl.DUT), B(pl.XT), kofs, N, (int)I, (int)d, dw_up, stream));
+    MOE_ZC_TRY(launch_wgrad(B(pl.ET), B(pl.HT), kofs, N, (int)d, (int)I, dw_down, xg, stream));
+    MOE_ZC_TRY(launch_wgrad(B(pl.DAT), B(pl.XT), kofs, N, (int)I, (int)d, dw_gate, xg, stream));
+    MOE_ZC_TRY(launch_wgrad(B(pl.DUT), B(pl.XT), kofs, N, (int)I, (int)d, dw_up, xg, stream));
   }
   // per token: gate gradients, router softmax backward, dx from expert rows and
   // identity slots
@@ -781,7 +786,7 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
   a = tr(x, d, B(pl.xT), pl.T64, (int)d, pl.T64, T);
   a.kofs = kofs_r; a.ngroups = 1;
   MOE_ZC_TRY(launch_transpose(a, stream));
-  MOE_ZC_TRY(launch_wgrad(B(pl.dlT), B(pl.xT), kofs_r, 1, E, (int)d, dw_router, stream));
+  MOE_ZC_TRY(launch_wgrad(B(pl.dlT), B(pl.xT), kofs_r, 1, E, (int)d, dw_router, nullptr, stream));
   return MOE_ZC_OK;
 }
 

@@ -428,7 +428,90 @@ struct WgradProblem {
   const int32_t* kofs;
   int G, M, N;
   float* C;
+  // XCD x owns groups xcd_groups[x * cap + j], j < cap (-1: none); null: the
+  // groups are spread over the XCDs tile by tile
+  const int32_t* xcd_groups;
+  int cap;
 };
+
+// The XCD plan.  A weight-gradient tile's time is about its group's
+// reduction stages plus a fixed store phase (measured at prefill: nine 32-k
+// stages of about 2.2 us against a 9.5 us epilogue, so the epilogue counts as
+// kWgradEpiUnits stages).  Groups differ by their rows only, so with skewed
+// loads (one expert holding a tenth of all rows) an XCD that owns whole
+// groups by index gets far more work than the others.  The plan gives each
+// XCD whole groups by longest processing time first: groups in order of
+// descending work (ties: lower index), each to the XCD with the least work so
+// far (ties: lower XCD) among those holding fewer than cap groups.
+constexpr int kWgradEpiUnits = 4;
+
+__global__ __launch_bounds__(1024) void wgrad_plan_kernel(const int32_t* __restrict__ kofs, int G,
+                                                         int cap,
+                                                         int32_t* __restrict__ xcd_groups) {
+  __shared__ uint64_t key[kWgradMaxGroups];
+  __shared__ int32_t tab[8 * kWgradMaxCap];
+  const int tid = threadIdx.x;
+  int P = 1;
+  while (P < G) P <<= 1;
+  // key: work above, complemented index below, so that a descending sort puts
+  // more work first and, on equal work, the lower index; padding (0) sorts last
+  for (int i = tid; i < P; i += 1024) {
+    uint64_t k = 0;
+    if (i < G) {
+      const uint32_t w = (uint32_t)((kofs[i + 1] - kofs[i]) / WG_BKS) + kWgradEpiUnits;
+      k = ((uint64_t)w << 32) | (uint64_t)(0xffffffffu - (uint32_t)i);
+    }
+    key[i] = k;
+  }
+  for (int i = tid; i < 8 * cap; i += 1024) tab[i] = -1;
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < P; i += 1024) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint64_t a = key[i], b = key[j];
+          const bool desc = (i & size) == 0;
+          if (desc ? (a < b) : (a > b)) {
+            key[i] = b;
+            key[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  // greedy assignment by the first wavefront: lane x < 8 holds XCD x's key
+  // (work << 3 | x, or all ones once it holds cap groups) and group count;
+  // per group the least key, read lane by lane into scalar registers, names
+  // the XCD that takes it (8 cap >= G, so one is always below cap).  The
+  // sorted keys arrive 64 at a time, one per lane.
+  if (tid < 64) {
+    uint32_t kx = (uint32_t)tid;  // work 0
+    int cnt = 0;
+    for (int base = 0; base < G; base += 64) {
+      const uint64_t kk = key[min(base + tid, P - 1)];
+      const int klo = (int)(uint32_t)kk, khi = (int)(uint32_t)(kk >> 32);
+      const int n = min(64, G - base);
+      // the keys are in registers before the loop, so the loop itself never
+      // waits on its table writes
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      for (int j = 0; j < n; ++j) {
+        const uint32_t wk = (uint32_t)__builtin_amdgcn_readlane(khi, j);
+        const int e = (int)(0xffffffffu - (uint32_t)__builtin_amdgcn_readlane(klo, j));
+        uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)kx, 0);
+#pragma unroll
+        for (int x = 1; x < 8; ++x) m = min(m, (uint32_t)__builtin_amdgcn_readlane((int)kx, x));
+        if (tid == (int)(m & 7u)) {
+          tab[tid * cap + cnt] = e;
+          ++cnt;
+          kx = cnt == cap ? 0xffffffffu : kx + (wk << 3);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < 8 * cap; i += 1024) xcd_groups[i] = tab[i];
+}
 
 // Tiles of 64 RB rows (of A) by 64 CB columns (of B): 128 x 128 (32 KB of
 // LDS, five workgroups per CU) for few groups, 256 x 128 (48 KB, three per
@@ -436,8 +519,9 @@ struct WgradProblem {
 // operand bytes per output.  Four wavefronts as 2 x 2, each RB x CB MFMA
 // blocks of 32 x 32.
 // Tile order.  With 8 or more groups, workgroup i (dispatched to XCD i % 8)
-// takes a tile of group (i % 8) + 8 j: each XCD owns whole groups, so a
-// group's operands are fetched into one L2 only.  Within a group the faster
+// takes a tile of a group that the XCD plan gave XCD i % 8: each XCD owns
+// whole groups, so a group's operands are fetched into one L2 only, and the
+// XCDs' shares of the work are balanced.  Within a group the faster
 // index runs over the smaller operand's tiles (m_inner: over A's), which
 // keeps the tiles in flight on an XCD to a few of the larger operand's.
 // Several workgroups share a CU, so the loads of one hide behind the others.
@@ -460,13 +544,15 @@ __device__ __forceinline__ void wgrad_tile(const WgradProblem& p, int mtiles, in
   int g, rem;
   if (xcd_major) {
     const int q = blockIdx.x >> 3;
-    g = (blockIdx.x & 7) + 8 * (q / per_g);
-    rem = q % per_g;
+    const int j = q / per_g;  // the XCD's j-th group, in plan order
+    if (j >= p.cap) return;
+    g = p.xcd_groups[(blockIdx.x & 7) * p.cap + j];
+    rem = q - j * per_g;
   } else {
     g = blockIdx.x / per_g;
     rem = blockIdx.x % per_g;
   }
-  if (g >= p.G) return;
+  if (g < 0 || g >= p.G) return;
   const int mt = m_inner ? rem % mtiles : rem / ntiles;
   const int nt = m_inner ? rem / mtiles : rem % ntiles;
   const int m0 = mt * TM, n0 = nt * TN;
@@ -693,16 +779,28 @@ hipError_t launch_set_range(int32_t* out, int a, int b, hipStream_t s) {
   return hipGetLastError();
 }
 
+int wgrad_xcd_cap(int G) { return (G + 7) / 8 + (G + 63) / 64; }
+
+hipError_t launch_wgrad_plan(const int32_t* kofs, int G, int32_t* xcd_groups, hipStream_t s) {
+  if (G < 8) return hipSuccess;  // no plan: fewer groups than XCDs
+  if (G > kWgradMaxGroups) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(1024), 0, s, kofs, G, wgrad_xcd_cap(G),
+                     xcd_groups);
+  return hipGetLastError();
+}
+
 hipError_t launch_wgrad(const bf16_t* A, const bf16_t* B, const int32_t* kofs, int G, int M,
-                        int N, float* C, hipStream_t s) {
+                        int N, float* C, const int32_t* xcd_groups, hipStream_t s) {
   if (G <= 0 || M <= 0 || N <= 0) return hipSuccess;
   if (N % 4 != 0) return hipErrorInvalidValue;  // 16-byte stores of C rows
   const int xcd_major = G >= 8;
+  if (xcd_major && (!xcd_groups || G > kWgradMaxGroups)) return hipErrorInvalidValue;
+  const int cap = xcd_major ? wgrad_xcd_cap(G) : 0;
   const int tm = xcd_major ? 256 : 128, tn = 128;  // taller tiles where there are many groups
   const int mt = (M + tm - 1) / tm, nt = (N + tn - 1) / tn;
-  const int64_t tiles = (int64_t)(xcd_major ? (G + 7) / 8 * 8 : G) * mt * nt;
+  const int64_t tiles = (int64_t)(xcd_major ? 8 * cap : G) * mt * nt;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  WgradProblem p{A, B, kofs, G, M, N, C};
+  WgradProblem p{A, B, kofs, G, M, N, C, xcd_major ? xcd_groups : nullptr, cap};
   if (tm == 256)
     hipLaunchKernelGGL((wgrad_kernel<4, 2>), dim3((unsigned)tiles), dim3(256), 0, s, p, mt, nt,
                        xcd_major, (int)(M <= N));

@@ -202,8 +202,16 @@ hipError_t launch_set_range(int32_t* out, int a, int b, hipStream_t s);
 // C[g] = A_g B_g^T, fp32 [G][M][N], with A_g [M][R_g] and B_g [N][R_g] the
 // expert-blocked operands in the transposes' k-blocked layout (slabs of 32
 // columns; R_g = kofs[g+1] - kofs[g]).
+// With 8 or more groups each XCD owns whole groups, as the plan that
+// launch_wgrad_plan writes into xcd_groups (8 * wgrad_xcd_cap(G) int32, device)
+// assigns them; the plan depends only on kofs and G, so one serves every
+// launch with the same groups.
 hipError_t launch_wgrad(const bf16_t* A, const bf16_t* B, const int32_t* kofs, int G, int M,
-                        int N, float* C, hipStream_t s);
+                        int N, float* C, const int32_t* xcd_groups, hipStream_t s);
+int wgrad_xcd_cap(int G);
+constexpr int kWgradMaxGroups = 2048;  // the most experts the library accepts
+constexpr int kWgradMaxCap = (kWgradMaxGroups + 7) / 8 + (kWgradMaxGroups + 63) / 64;
+hipError_t launch_wgrad_plan(const int32_t* kofs, int G, int32_t* xcd_groups, hipStream_t s);
 
 // fp32 FMA path (gemm_simt.hip).
 hipError_t launch_simt_gemm(const GemmProblem& p, int epilogue, int64_t max_rows,

@@ -90,14 +90,17 @@ def test_skew_layer_then_pid_step_then_reroute():
     assert np.abs(g2["loads"] - target).sum() < np.abs(g1["loads"] - target).sum()
 
 
-def test_full_size_backward_prefill():
+@pytest.mark.parametrize("name", ["prefill", "skew"])
+def test_full_size_backward(name):
     """The training step that `bench.py --pass backward` times, at the prefill
-    size: packed forward saving a | u, then moe_zc_backward from the saved
-    values and the packed weight transposes.  Routing is checked for every
-    token.  dx is checked on a token sample, since a token's dx depends only
-    on that token.  The weight gradients are checked for two experts, each
-    from exactly the tokens routed to it.  Bar: max |G - G_ref| <= 1e-2 *
-    max |G_ref| per checked tensor.
+    size and at the skewed workload's (where the busiest expert holds
+    thousands of rows, so its weight gradients are long reductions): packed
+    forward saving a | u, then moe_zc_backward from the saved values and the
+    packed weight transposes.  Routing is checked for every token.  dx is
+    checked on a token sample, since a token's dx depends only on that token.
+    The weight gradients are checked for the most loaded expert and a random
+    one, each from exactly the tokens routed to it.  Bar: max |G - G_ref| <=
+    1e-2 * max |G_ref| per checked tensor.
 
     dW_router sums every token's dl x^T, and dl needs the token's expert
     outputs, so with a dense dy the oracle cannot form it at this size.  The
@@ -109,8 +112,9 @@ def test_full_size_backward_prefill():
     choose."""
     from oracle import backward as obwd
     from workloads import make_upstream_grad
-    w = get_workload("prefill")
-    print("[backward prefill] generating inputs", flush=True)
+    w = get_workload(name)
+    tag = f"[backward {name}]"
+    print(f"{tag} generating inputs", flush=True)
     inp = make_inputs(w, device=DEV)
     dy = make_upstream_grad(w, DEV)
     aux = m.alloc_aux(w.T, w.N, w.Z, w.K, DEV, keys=m.AUX_KEYS + ("act",), I=w.I)
@@ -120,7 +124,7 @@ def test_full_size_backward_prefill():
     torch.cuda.synchronize()
     del gu, dn
     tr = m.moe_zc_transpose_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
-    print("[backward prefill] backward", flush=True)
+    print(f"{tag} backward", flush=True)
     g = m.moe_zc_backward(inp["x"], inp["w_router"], None, None, tr, aux, dy, w.N, w.Z, w.K, w.I)
     torch.cuda.synchronize()
     l32 = aux["logits"].cpu().numpy()
@@ -128,11 +132,11 @@ def test_full_size_backward_prefill():
     idx = aux["topk_idx"].cpu().numpy()
     assert np.array_equal(idx, oracle.route(l32, bias, w.K, w.N)["idx"]), "routing"
 
-    def check(name, got, want):
+    def check(what, got, want):
         scale = np.abs(want).max()
         err = np.abs(got - want).max()
-        print(f"[backward prefill] {name}: max|err| / max|ref| = {err / scale:.2e}", flush=True)
-        assert err <= 1e-2 * scale, f"{name}: {err:.3e} > 1e-2 * {scale:.3e}"
+        print(f"{tag} {what}: max|err| / max|ref| = {err / scale:.2e}", flush=True)
+        assert err <= 1e-2 * scale, f"{what}: {err:.3e} > 1e-2 * {scale:.3e}"
 
     rng = np.random.default_rng(3)
     s = np.sort(rng.choice(w.T, 4, replace=False))
@@ -140,7 +144,10 @@ def test_full_size_backward_prefill():
     ref = obwd.backward(inp["x"][st], inp["w_router"], bias, inp["w_gate"], inp["w_up"],
                         inp["w_down"], w.N, w.Z, w.K, dy[st], logits32=l32[s], experts=[])
     check(f"dx tokens {s.tolist()}", g["dx"][st].float().cpu().double().numpy(), ref["dx"])
-    for e in np.sort(rng.choice(np.unique(idx[idx < w.N]), 2, replace=False)):
+    loads = np.bincount(idx[idx < w.N].ravel(), minlength=w.N)
+    busiest = int(np.argmax(loads))
+    others = np.setdiff1d(np.unique(idx[idx < w.N]), [busiest])
+    for e in sorted([busiest, int(rng.choice(others))]):
         tt = np.nonzero((idx == e).any(axis=1))[0]
         ti = torch.from_numpy(tt).to(DEV)
         ref = obwd.backward(inp["x"][ti], inp["w_router"], bias, inp["w_gate"], inp["w_up"],
@@ -155,7 +162,7 @@ def test_full_size_backward_prefill():
     keep[torch.from_numpy(s8).to(DEV)] = 1
     dy8 = (dy * keep).contiguous()
     del dy
-    print(f"[backward prefill] sparse dy on tokens {s8.tolist()}", flush=True)
+    print(f"{tag} sparse dy on tokens {s8.tolist()}", flush=True)
     g8 = m.moe_zc_backward(inp["x"], inp["w_router"], None, None, tr, aux, dy8, w.N, w.Z, w.K,
                            w.I)
     torch.cuda.synchronize()
