@@ -22,8 +22,9 @@ TOL = 1e-2
 GRADS = ("dx", "dw_router", "dw_gate", "dw_up", "dw_down")
 
 
-def _edge(T=200, d=128, I=128, N=8, Z=4, K=3, seed=5, bias=("uniform", 0.05)):
-    return Workload("edge", T=T, d=d, I=I, N=N, Z=Z, K=K, dtype="bf16", seed=seed, bias=bias)
+def _edge(T=200, d=128, I=128, N=8, Z=4, K=3, seed=5, bias=("uniform", 0.05), zipf=None):
+    return Workload("edge", T=T, d=d, I=I, N=N, Z=Z, K=K, dtype="bf16", seed=seed, bias=bias,
+                    zipf=zipf)
 
 
 def gpu_forward_backward(w, inp, dy, repeat=1):
@@ -81,6 +82,12 @@ CASES = {
     "many_experts": dict(T=300, d=128, I=128, N=300, Z=20, K=12),
     # experts of 257 .. 439 rows: two row parts each in the forward's GEMMs
     "rows_past_256": dict(T=1300, d=320, I=384, N=10, Z=4, K=3, seed=3),
+    # the most experts the library takes (E = 2048): the weight gradients'
+    # XCD plan sorts 1800 groups and assigns them in 29 batches of 64
+    "max_experts": dict(T=400, N=1800, Z=248, K=12),
+    # Zipf(2) logit offsets: one expert takes most rows, so its weight
+    # gradients are long reductions and the plan's per-XCD group cap binds
+    "zipf_one_dominant": dict(T=2000, N=16, Z=8, K=4, bias=("zero",), zipf=(2.0, 4.0)),
 }
 
 
