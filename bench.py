@@ -19,8 +19,9 @@ times moe_zc_forward on the row-major weights instead.
 
 The headline is --workload (default prefill, bf16).  The same run then times
 the other workloads (tiny, mid, decode, skew in their own dtypes, and the
-prefill layer with the block-FP8 gate/up projection) and reports each under
-"workloads" (skip with --no-extra-workloads).
+prefill layer with the block-FP8 gate/up projection) and the training step
+of the prefill and skewed layers (as --pass backward times it), and reports
+each under "workloads" (skip with --no-extra-workloads).
 
 --pass backward times a training step of the layer instead: the packed
 forward saving its routing and the expert pre-activations (aux.act), then
@@ -303,9 +304,10 @@ def cpu_baseline(w, inp, n_experts, weights):
             "seconds_measured": round(t3 - t0, 2)}
 
 
-def bench_backward(args, w, dev):
+def bench_backward(args, w, dev, steps=None, warmup=None):
     """Training step = forward (routing saved) + backward; also the backward
-    alone.  FLOPs of the backward's expert products: q (2 d I S), the rows
+    alone.  Returns the JSON record (steps and warmup default to the command
+    line's).  FLOPs of the backward's expert products: q (2 d I S), the rows
     of dx (4 d I S), dW_down, dW_gate, dW_up (6 d I S), and with --recompute
     a and u again (4 d I S); router: dx term and dW_router (4 T d E)."""
     import torch
@@ -351,15 +353,18 @@ def bench_backward(args, w, dev):
         m.moe_zc_backward(inp["x"], inp["w_router"], inp["w_gate"], inp["w_up"], tr, aux, dy,
                           w.N, w.Z, w.K, w.I, out=grads, workspace=ws_b)
 
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+
     def timed(fn):
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(steps):
             fn()
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / args.steps
+        return (time.perf_counter() - t0) * 1e3 / steps
 
     ms_step = timed(lambda: (fwd(), bwd()))
     ms_bwd = timed(bwd)
@@ -373,8 +378,8 @@ def bench_backward(args, w, dev):
         "value": w.T / (ms_step / 1e3),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -393,7 +398,7 @@ def bench_backward(args, w, dev):
         "ffn_rows": S,
         "cpu_baseline": None,
     }
-    print(json.dumps(out))
+    return out
 
 
 def graph_replay(step, y, replays):
@@ -618,6 +623,10 @@ def public(res):
 EXTRA = (("tiny", False, False), ("mid", False, False), ("decode", False, False),
          ("skew", False, False), ("prefill", True, False), ("prefill", True, True),
          ("decode", True, True))
+TRAINING = ("prefill", "skew")
+TRAINING_KEYS = ("metric", "value", "unit", "steps", "warmup", "ms_per_step", "config",
+                 "backward_ms", "backward_tflops", "backward_mfma_frac", "step_tflops",
+                 "ffn_rows")
 
 
 def main():
@@ -639,7 +648,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.which == "backward":
-        bench_backward(args, w, dev)
+        print(json.dumps(bench_backward(args, w, dev)))
         return
     fp8 = args.precision == "fp8"
     if fp8 and (w.dtype != "bf16" or args.layout != "packed"):
@@ -682,6 +691,15 @@ def main():
                                       if k in ("bound", "achieved", "peak", "unit", "frac")}
             extra[name + ("_fp8" if x8 else "") + ("_fp8down" if d8 else "")] = public(rx)
             del rx
+            torch.cuda.empty_cache()
+        # the training step (forward saving a | u, then the backward) of the
+        # prefill and skewed layers, as `--pass backward` times it
+        for name in TRAINING:
+            print(f"bench.py: timing the training step of {name}", file=sys.stderr, flush=True)
+            rt = bench_backward(args, get_workload(name), dev, steps=max(3, min(args.steps, 10)),
+                                warmup=min(args.warmup, 3))
+            extra["training_" + name] = {k: rt[k] for k in TRAINING_KEYS}
+            del rt
             torch.cuda.empty_cache()
 
     out = {
