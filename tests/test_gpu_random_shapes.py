@@ -6,7 +6,9 @@ case, so every run checks the same ones) to reach combinations nobody picked:
 widths d in multiples of 64 and I in multiples of 128, 1 to 70 FFN experts,
 0 to 16 identity experts, K from 1 to min(E, 12), 1 to 699 tokens, a uniform
 bias of three sizes or Zipf(1.2) logit offsets that pile rows onto a few
-experts.  Each case checks, through the C ABI:
+experts; a second set draws many tokens and experts on narrow widths
+(500-3999 tokens, 2-599 FFN and 0-299 identity experts, K up to 32), where
+experts span several row tiles.  Each case checks, through the C ABI:
 - forward: the row-major and packed bf16 forwards give the same bits, and
   the layer output, routing and grouping meet the oracle bars of
   gpu_check.check_forward (with and without the residual);
@@ -37,6 +39,23 @@ def draw(i: int, d_step: int = 64) -> Workload:
     zipf = (1.2, 2.0) if r.random() < 0.25 else None
     bias = ("zero",) if zipf else ("uniform", float(r.choice([0.0, 0.02, 0.1])))
     return Workload(f"random{i}", T=T, d=d, I=I, N=N, Z=Z, K=K, dtype="bf16", seed=100 + i,
+                    bias=bias, zipf=zipf)
+
+
+def draw_wide(i: int) -> Workload:
+    """Many tokens and experts on narrow widths: experts that span several
+    row tiles and split ones, up to 600 FFN and 300 identity experts, K up to
+    32 (the library's limit)."""
+    r = np.random.default_rng(9000 + i)
+    d = 64 * int(r.integers(1, 3))
+    I = 128 * int(r.integers(1, 3))
+    N = int(r.integers(2, 600))
+    Z = int(r.integers(0, 300))
+    K = int(r.integers(1, min(N + Z, 32) + 1))
+    T = int(r.integers(500, 4000))
+    zipf = (1.2, 2.0) if r.random() < 0.25 else None
+    bias = ("zero",) if zipf else ("uniform", float(r.choice([0.0, 0.005, 0.02])))
+    return Workload(f"wide{i}", T=T, d=d, I=I, N=N, Z=Z, K=K, dtype="bf16", seed=300 + i,
                     bias=bias, zipf=zipf)
 
 
@@ -81,3 +100,25 @@ def test_random_shape_backward(i):
     dy = make_upstream_grad(w, DEV)
     aux, (g,) = gpu_forward_backward(w, inp, dy)
     print(i, compare(w, inp, dy, aux, g), flush=True)
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_wide_forward(i):
+    w = draw_wide(i)
+    print(f"[random wide forward {i}] {w.describe()} zipf={w.zipf} bias={w.bias}", flush=True)
+    inp = make_inputs(w, device=DEV, residual=False)
+    g = run_gpu(w, inp, residual=False)
+    packed = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    gp = run_gpu(w, inp, residual=False, packed=packed)
+    assert torch.equal(g["y_t"], gp["y_t"]), "packed and row-major forwards differ"
+    print(i, check_forward(w, dict(inp, residual=None), g), flush=True)
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_wide_backward(i):
+    w = draw_wide(100 + i)
+    print(f"[random wide backward {i}] {w.describe()} zipf={w.zipf} bias={w.bias}", flush=True)
+    inp = make_inputs(w, device=DEV)
+    dy = make_upstream_grad(w, DEV)
+    aux, (g,) = gpu_forward_backward(w, inp, dy)
+    print(i, compare(w, inp, dy, aux, g, dx_tokens=np.arange(min(w.T, 1024))), flush=True)
