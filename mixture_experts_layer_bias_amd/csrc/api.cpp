@@ -9,6 +9,7 @@
 #include <cstdint>
 #include <mutex>
 
+#include "backward.hpp"
 #include "kernels.hpp"
 
 using namespace moezc;
@@ -731,7 +732,7 @@ moe_zc_status moe_zc_backward(const void* x, const float* w_router, const void* 
     q.row_offsets = offsets; q.tile_prefix = tiles; q.G = N; q.M = 0;
     MOE_ZC_TRY(launch_packed_gemm(q, kStoreF32, s.ffn_tile_rows, s.smax, stream));
     // weight gradients: operands transposed into expert blocks of rows_e
-    // rounded up to 64 columns (zeros in the padding columns), stored as slabs
+    // rounded up to 32 columns (zeros in the padding columns), stored as slabs
     // of 32 columns
     auto blocked = [&](const void* src, int64_t src_ld, void* dst, int64_t dim) {
       TrArgsHost a = tr(src, src_ld, dst, 0, (int)dim, pl.Sp, 0);

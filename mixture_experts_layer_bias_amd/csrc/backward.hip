@@ -21,6 +21,7 @@
 // K-contiguous, fp32 output.  The other products (q, the rows of dx, the
 // router's dx term, and a and u when the forward did not save them) run on
 // the bf16 MFMA grouped GEMMs.
+#include "backward.hpp"
 #include "gemm_tile.hpp"
 
 namespace moezc {
@@ -29,7 +30,7 @@ namespace {
 
 // ---- bookkeeping --------------------------------------------------------------
 // tile_prefix[g] = sum over f < g of ceil(rows_f / bm); kofs[g] = sum over f < g
-// of rows_f rounded up to 64 (each group's reduction range in the padded
+// of rows_f rounded up to 32 (each group's reduction range in the padded
 // operands).  One wave: lane l sums a contiguous segment of ceil(N / 64)
 // groups, a shuffle scan over the 64 lane sums gives each segment its start,
 // then every lane writes its own segment.
@@ -45,7 +46,7 @@ __global__ __launch_bounds__(64) void bwd_prefix_kernel(const int32_t* __restric
   for (int e = e0; e < e1; ++e) {
     const int rows = offsets[e + 1] - offsets[e];
     st += (rows + bm - 1) / bm;
-    sk += (rows + 63) / 64 * 64;
+    sk += (rows + 31) / 32 * 32;
   }
   int it = st, ik = sk;  // inclusive scan over lanes
 #pragma unroll
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(64) void bwd_prefix_kernel(const int32_t* __restric
     kofs[e] = k;
     const int rows = offsets[e + 1] - offsets[e];
     t += (rows + bm - 1) / bm;
-    k += (rows + 63) / 64 * 64;
+    k += (rows + 31) / 32 * 32;
   }
   if (lane == 63) {
     tile_prefix[N] = it;
@@ -118,7 +119,7 @@ struct TrArgs {
   int dim;        // destination rows (source columns)
   int64_t ncols;  // destination columns (multiple of 64)
   // non-null: expert-blocked, k-blocked destination.  Group g owns columns
-  // [kofs[g], kofs[g+1]) (multiples of 64), stored from element offset
+  // [kofs[g], kofs[g+1]) (multiples of 32), stored from element offset
   // kofs[g] * dim as slabs of 32 columns: column k of the group, row j at
   // (k / 32) * dim * 32 + j * 32 + k % 32.  One slab holds every row's 32
   // consecutive columns (64 bytes for bf16) back to back, so a weight-gradient
@@ -181,18 +182,36 @@ __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
   const int j0 = blockIdx.y * 64;
   const SRC* src = static_cast<const SRC*>(a.src) + (int64_t)blockIdx.z * a.src_bstride;
   DST* dst = static_cast<DST*>(a.dst) + (int64_t)blockIdx.z * a.dst_bstride;
-  int64_t dst_ld = a.dst_ld, cbase = c0;  // destination row stride, tile column in it
+  const int64_t dst_ld = a.dst_ld;  // destination row stride
   const bool kslab = a.kofs != nullptr;
+  // k-blocked destination: the tile's two 32-column halves may belong to
+  // different groups (groups are 32-column aligned); for each half, the
+  // group's block and the half's first column in it (-1: past the groups)
+  DST* hdst[2] = {dst, dst};
+  int64_t hk[2] = {c0, c0 + 32};
   if (kslab) {
-    if (c0 >= a.kofs[a.ngroups]) return;
-    int lo = 0, hi = a.ngroups;  // kofs[lo] <= c0 < kofs[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.kofs[mid] <= c0) lo = mid; else hi = mid;
+    const int64_t kend = a.kofs[a.ngroups];
+    if (c0 >= kend) return;
+    int g = 0;  // the group of each half: kofs[g] <= column < kofs[g + 1]
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t ch = c0 + 32 * h;
+      if (ch >= kend) {
+        hk[h] = -1;
+        continue;
+      }
+      // the second half searches only when a group ends inside the tile
+      if (h == 0 || a.kofs[g + 1] <= ch) {
+        int lo = g, hi = a.ngroups;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (a.kofs[mid] <= ch) lo = mid; else hi = mid;
+        }
+        g = lo;
+      }
+      hdst[h] = dst + (int64_t)a.kofs[g] * a.dim;
+      hk[h] = ch - a.kofs[g];
     }
-    const int64_t k0 = a.kofs[lo];
-    dst += k0 * a.dim;
-    cbase = c0 - k0;
   }
   const int tid = threadIdx.x;
   {
@@ -229,8 +248,10 @@ __global__ __launch_bounds__(256) void transpose_kernel(TrArgs a) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) v[q] = tile[jl][cc + q];
       // 16 columns from a multiple of 16: inside one 32-column slab
-      const int64_t k = cbase + cc;
-      DST* p = kslab ? dst + (k >> 5) * ((int64_t)a.dim * 32) + (int64_t)j * 32 + (k & 31)
+      const int h = cc >> 5;
+      if (kslab && hk[h] < 0) return;  // this half is past the last group (so is the rest)
+      const int64_t k = kslab ? hk[h] + (cc & 31) : c0 + cc;
+      DST* p = kslab ? hdst[h] + (k >> 5) * ((int64_t)a.dim * 32) + (int64_t)j * 32 + (k & 31)
                      : dst + (int64_t)j * dst_ld + a.dst_col0 + k;
       if (c0 + cc + 16 <= a.ncols) {
         st16(p, v);
@@ -414,7 +435,7 @@ __global__ void set_range_kernel(int32_t* out, int a, int b) {
 
 // ---- weight-gradient GEMM --------------------------------------------------------
 // C[g][m][n] = sum over k < R_g of A_g[m][k] B_g[n][k], R_g = kofs[g+1] - kofs[g]
-// (a multiple of 64); A_g and B_g bf16 start at element offsets kofs[g] * M
+// (a multiple of 32); A_g and B_g bf16 start at element offsets kofs[g] * M
 // and kofs[g] * N in the k-blocked layout of the transposes above (slabs of
 // 32 k: A_g[m][k] at (k / 32) * M * 32 + m * 32 + k % 32); C fp32 [G][M][N].
 // 128 x 128 tiles, four wavefronts (2 x 2, 64 x 64 each), stages of 32 k
