@@ -42,12 +42,12 @@ def draw(i: int, d_step: int = 64) -> Workload:
                     bias=bias, zipf=zipf)
 
 
-def draw_wide(i: int) -> Workload:
+def draw_wide(i: int, d_choices=(64, 128)) -> Workload:
     """Many tokens and experts on narrow widths: experts that span several
     row tiles and split ones, up to 600 FFN and 300 identity experts, K up to
     32 (the library's limit)."""
     r = np.random.default_rng(9000 + i)
-    d = 64 * int(r.integers(1, 3))
+    d = int(r.choice(d_choices))
     I = 128 * int(r.integers(1, 3))
     N = int(r.integers(2, 600))
     Z = int(r.integers(0, 300))
@@ -122,3 +122,19 @@ def test_random_wide_backward(i):
     dy = make_upstream_grad(w, DEV)
     aux, (g,) = gpu_forward_backward(w, inp, dy)
     print(i, compare(w, inp, dy, aux, g, dx_tokens=np.arange(min(w.T, 1024))), flush=True)
+
+
+@pytest.mark.parametrize("i", range(6))
+def test_random_wide_fp8(i):
+    w = draw_wide(200 + i, d_choices=(128,))
+    print(f"[random wide fp8 {i}] {w.describe()} zipf={w.zipf} bias={w.bias}", flush=True)
+    inp = make_inputs(w, device=DEV, residual=False)
+    ref_inp = dict(inp, residual=None)
+    packed = m.moe_zc_pack_expert_weights(inp["w_gate"], inp["w_up"], inp["w_down"])
+    g = run_gpu(w, inp, residual=False, fp8=True,
+                packed=(m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"]), packed[1]))
+    print(i, "gate/up fp8", check_forward(w, ref_inp, g, fp8=True), flush=True)
+    g2 = run_gpu(w, inp, residual=False, fp8=True, down_fp8=True,
+                 packed=m.moe_zc_pack_expert_weights_fp8(inp["w_gate"], inp["w_up"],
+                                                         inp["w_down"]))
+    print(i, "down fp8", check_forward(w, ref_inp, g2, fp8=True, down_fp8=True), flush=True)
